@@ -1,0 +1,179 @@
+/*
+ * kvq.h - C ABI of the Q4 KV-cache codec and of fused-dequant decode attention (MI355X, gfx950).
+ *
+ * Sources the operations follow (cited by page title and section; no page prints code):
+ *   [AMB]  "Agent Memory Below the Prompt: Persistent Q4 KV Cache for Multi-Agent LLM Inference on
+ *          Edge Devices" (gist.science explainer), technical summary, section 2.1 (block pool, Q4
+ *          pipeline, BatchQuantizedKVCache, cross-phase injection) and section 2.2 (GQA).
+ *   [IKV]  IntentKV article (qiita), section on invalidating instead of compacting (sentinel slot).
+ *   [UQ]   UltraQuant news article (poko-everyday), technology section (Walsh-Hadamard rotation,
+ *          asymmetric K/V treatment, decode-attention kernel tuned for AMD GPUs).
+ *   [QKV]  QKVShare explainer (gist.science, French), methodology section (per-token bit widths,
+ *          CacheCard) and claims section (a fused quantized attention kernel is the missing piece).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument except the kvq_layout pointer is a DEVICE pointer to caller-owned memory.
+ *     The library allocates nothing, frees nothing, keeps no pointer after returning, and keeps no
+ *     mutable global state.
+ *   - `stream` is a hipStream_t handle passed as void* (NULL = the null stream). Work is enqueued
+ *     asynchronously; the caller keeps buffers alive until the stream has finished and synchronises
+ *     itself. Calls that do not write the same pool rows may run concurrently.
+ *   - Return value: KVQ_OK (0) or a negative kvq_status. Nothing throws or aborts across the ABI.
+ *     Host-visible arguments (layout, sizes, null pointers, workspace size) are validated; device-resident
+ *     data (block ids, seq_lens, positions) is trusted and must be in range.
+ *   - fp16 values are passed as uint16_t bit patterns (IEEE binary16).
+ *
+ * Pool layout (the block pool of [AMB] 2.1 item 1 with the Q4 format of [AMB] 2.1 item 2)
+ *   A pool holds num_blocks * H_kv tiles; tile (b, h) starts at byte (b * H_kv + h) * kvq_tile_bytes().
+ *   A tile holds the 256 token rows of one KV head of one block, in this order (R = 256, d = head_dim,
+ *   bmax = 8 for mixed pools else 4, S = d * bmax / 8 bytes per code row):
+ *     K codes   R x S bytes      row t at offset t*S
+ *     V codes   R x S bytes
+ *     K params  per-token groups: R x (d / k_group) x 4 bytes, [t][group]; per-channel: d x 4 bytes, [c]
+ *     V params  R x (d / v_group) x 4 bytes, [t][group]
+ *     header    mixed pools only: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes
+ *     padding   zero bytes up to the next multiple of 256
+ *   4-bit codes: element j of a row sits in bits 4*(j % 8) of little-endian uint32 word j / 8 (byte i holds
+ *   elements 2i in its low nibble and 2i+1 in its high nibble). 8-bit codes: one byte per element. In a
+ *   mixed pool a 4-bit row fills the first d/2 bytes of its slot and the rest of the slot is zero.
+ *   A parameter entry is {fp16 scale, fp16 zero} (scale at byte 0, zero at byte 2); the pages store a
+ *   16-bit scale and bias per group, this library stores them as IEEE fp16.
+ *
+ * Codec (one group G of fp32 values x; L = 15 for 4-bit rows, 255 for 8-bit rows)
+ *   If layout.rotate: each fp16 row is first mapped to fp32 and rotated, y = c * H * x, H the natural
+ *   (Sylvester) Hadamard matrix applied as butterflies with stage strides 1, 2, 4, ..., d/2, each pair
+ *   (a, b) -> (a + b, a - b) in fp32, then one multiply by c = fp32(1/sqrt(d)) ([UQ] technology section).
+ *   mn = min G, mx = max G (an extreme equal to zero is taken as +0), scale = fp16(rne((mx - mn) / L)),
+ *   zero = fp16(rne(mn)); s, z = those fp16 values as fp32; if s == 0 every code is 0, else
+ *   r = 1 / s and code = clamp(rint_even((x - z) * r), 0, L). Every step is one IEEE fp32 operation.
+ *   Dequantisation is code * s + z (then the inverse rotation if the pool is rotated).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,          /* null pointer, negative size, bad layout field, H_q not a multiple of H_kv */
+  KVQ_ERR_UNSUPPORTED = -2,  /* valid request this build does not implement (e.g. append into per-channel K) */
+  KVQ_ERR_WORKSPACE = -3,    /* workspace pointer null or smaller than kvq_decode_workspace_bytes() */
+  KVQ_ERR_HIP = -4           /* the HIP runtime reported an error while launching */
+};
+
+/* Geometry and codec options of one pool (the per-architecture cache shape of [AMB] 2.2).
+ * Passed by pointer; the library copies it on every call. */
+typedef struct kvq_layout {
+  int32_t head_dim;     /* d: 64, 128 or 256 */
+  int32_t num_kv_heads; /* H_kv >= 1 */
+  int32_t block_tokens; /* rows per block; must be 256 ([AMB] 2.1 item 1) */
+  int32_t k_group;      /* > 0: K groups are k_group consecutive channels of one token (32, 64 or 128,
+                           dividing d); -1: one K group per channel spanning the block's 256 rows
+                           (asymmetric K/V grouping, [UQ] technology section) */
+  int32_t v_group;      /* > 0: V groups are v_group consecutive channels of one token (32, 64 or 128) */
+  int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of every K and V row before quantisation */
+  int32_t mixed;        /* 0 or 1: each token row is 4-bit or 8-bit, chosen per token ([QKV] methodology);
+                           requires per-token K groups */
+  int32_t reserved;     /* must be 0 */
+} kvq_layout;
+
+/* KVQ_OK if the layout is one this library can store and process, else the status explaining why. */
+int kvq_check_layout(const kvq_layout* L);
+
+/* Bytes of one tile (256 rows of one KV head), a multiple of 256; 0 if the layout is invalid. */
+size_t kvq_tile_bytes(const kvq_layout* L);
+
+/* Bytes of a pool of num_blocks blocks (num_blocks * H_kv tiles); 0 if invalid. */
+size_t kvq_pool_bytes(const kvq_layout* L, int32_t num_blocks);
+
+/* Bytes of device workspace kvq_decode_attention needs for these sizes; 0 if invalid. The value depends
+ * only on the arguments, so a workspace sized here is valid for every call with the same or smaller
+ * n_seqs and max_seq_len. */
+size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_seqs, int32_t num_q_heads,
+                                  int32_t max_seq_len);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* kvq_status_string(int status);
+
+/*
+ * kvq_quantize_blocks - quantise whole 256-token blocks into the pool ([AMB] 2.1 items 1-2; rotation
+ * and asymmetric K/V grouping from [UQ] technology section; per-token widths from [QKV] methodology).
+ *
+ *   pool       device, kvq_pool_bytes(L, num_blocks) bytes; every byte of tiles (block_ids[i], h) for
+ *              all h is overwritten (codes, params, header, zero padding).
+ *   block_ids  device int32 [n_blocks]: physical block receiving input block i. Ids must be distinct
+ *              and < the pool's block count (trusted).
+ *   n_blocks   >= 0 (0 is a no-op).
+ *   k, v       device fp16 [n_blocks * 256][H_kv][d], token-major: row t of input block i for head h
+ *              starts at element ((i * 256 + t) * H_kv + h) * d.
+ *   prec_bits  device uint32 [n_blocks][8] or NULL. Bit (t % 32) of word t / 32 set = token t of block
+ *              i is stored with 8-bit codes (K and V, every head). Must be NULL unless L->mixed; NULL
+ *              in a mixed pool means every token is 4-bit.
+ * Errors: KVQ_ERR_ARG (null pool/k/v/block_ids with n_blocks > 0, prec_bits for a non-mixed layout,
+ * invalid layout), KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP.
+ */
+int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_ids, int32_t n_blocks,
+                        const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
+                        void* stream);
+
+/*
+ * kvq_append_tokens - quantise one new token per sequence into its slot, extending the cached prefix
+ * instead of re-encoding it ([AMB] 2.1 item 4, cross-phase injection). Same arithmetic as
+ * kvq_quantize_blocks on a single row.
+ *
+ *   n_seqs       >= 0.
+ *   k, v         device fp16 [n_seqs][H_kv][d].
+ *   block_table  device int32 [n_seqs][max_blocks_per_seq]: logical block -> physical block.
+ *   positions    device int32 [n_seqs]: slot of the new token (usually the old sequence length). The
+ *                row written is positions[s] % 256 of block block_table[s][positions[s] / 256], which
+ *                the caller must have allocated (trusted). Other rows are untouched.
+ *   prec         device uint8 [n_seqs] holding 4 or 8, or NULL (all 4-bit). Must be NULL unless
+ *                L->mixed. In mixed pools the row's header bit is set or cleared accordingly.
+ * The caller advances its own seq_lens afterwards; this call does not touch them.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (per-channel K groups: a partial block has no defined
+ * channel statistics), KVQ_ERR_HIP.
+ */
+int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k,
+                      const uint16_t* v, const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* positions, const uint8_t* prec, void* stream);
+
+/*
+ * kvq_decode_attention - one decode query per sequence attending over its quantised cache, reading
+ * the packed tiles directly and dequantising in registers ([AMB] 2.1 item 2, direct restore without a
+ * dequantised copy; 2.1 item 3, many agents batched in one launch; 2.2, GQA; [UQ] technology section,
+ * AMD decode-attention kernel; [QKV] claims section, fused quantized attention kernel).
+ *
+ *   q              device fp16 [n_seqs][num_q_heads][d]; query head j reads KV head j / G,
+ *                  G = num_q_heads / H_kv (contiguous GQA groups).
+ *   block_table    device int32 [n_seqs][max_blocks_per_seq].
+ *   seq_lens       device int32 [n_seqs]: slots 0 .. seq_lens[s]-1 are attended; each value must lie in
+ *                  [0, max_seq_len] (trusted) and max_seq_len <= max_blocks_per_seq * 256.
+ *   sentinel_mask  device uint32 [n_seqs][mask_words_per_seq] or NULL. Bit (t % 32) of word t / 32 set
+ *                  = slot t was remapped to the sentinel slot ([IKV] invalidation section): its logit is
+ *                  -1e4 and its value row is 0, so its softmax weight underflows to zero while the
+ *                  surviving slots keep their positions. mask_words_per_seq >= ceil(max_seq_len / 32).
+ *   softmax_scale  logit = softmax_scale * (q . k) for live slots (usually 1/sqrt(d)).
+ *   out            device fp32 [n_seqs][num_q_heads][d]: softmax-weighted sum of the dequantised (and,
+ *                  for rotated pools, un-rotated) V rows. A sequence with seq_lens[s] == 0 gets zeros.
+ *   workspace      device scratch of at least kvq_decode_workspace_bytes(L, n_seqs, num_q_heads,
+ *                  max_seq_len) bytes, 256-byte aligned; contents need no initialisation and are
+ *                  scratch afterwards. Calls sharing one workspace must not overlap.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP.
+ */
+int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+                         int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
+                         int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

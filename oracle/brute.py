@@ -1,0 +1,124 @@
+"""TEST INFRASTRUCTURE: dense fp64 brute force for tiny inputs, written independently of kvq_oracle.c.
+
+It reads the tile bytes with numpy (its own parse of the storage layout), builds the whole dequantised
+K and V of a sequence as matrices, undoes the rotation with an explicit Hadamard matrix
+H[i][j] = (-1)^popcount(i & j) (not with butterflies), and evaluates softmax attention as matrix
+products. It follows the same pages as the C oracle (Agent Memory Below the Prompt, technical summary
+2.1-2.2; UltraQuant technology section; IntentKV invalidation section) and is used only to pin the C
+oracle's decode loops on tiny inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def hadamard(n: int) -> np.ndarray:
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    pop = np.zeros_like(bits)
+    b = bits.copy()
+    while b.any():
+        pop += b & 1
+        b >>= 1
+    return np.where(pop % 2 == 0, 1.0, -1.0)
+
+
+def _layout_offsets(d, k_group, v_group, mixed):
+    rows = 256
+    slot = d * (8 if mixed else 4) // 8
+    off_vc = rows * slot
+    off_kp = 2 * rows * slot
+    kp_bytes = rows * (d // k_group) * 4 if k_group > 0 else d * 4
+    off_vp = off_kp + kp_bytes
+    off_hdr = off_vp + rows * (d // v_group) * 4
+    end = off_hdr + (32 if mixed else 0)
+    tile = (end + 255) // 256 * 256
+    return slot, off_vc, off_kp, off_vp, off_hdr, tile
+
+
+def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
+    """rows_bytes: uint8 [n][slot]; bits: [n] 4 or 8 -> integer codes [n][d]."""
+    n = rows_bytes.shape[0]
+    out = np.zeros((n, d), np.int64)
+    lo = rows_bytes[:, : d // 2] & 0xF
+    hi = rows_bytes[:, : d // 2] >> 4
+    four = np.empty((n, d), np.int64)
+    four[:, 0::2] = lo
+    four[:, 1::2] = hi
+    eight = rows_bytes[:, :d].astype(np.int64) if rows_bytes.shape[1] >= d else four
+    sel = bits == 8
+    out[~sel] = four[~sel]
+    if sel.any():
+        out[sel] = eight[sel]
+    return out
+
+
+def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed):
+    """-> (K [256][d], V [256][d]) fp64 in the stored (rotated) domain."""
+    slot, off_vc, off_kp, off_vp, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
+    rows = 256
+    if mixed:
+        hdr = tile[off_hdr: off_hdr + 32]
+        bits = np.where((hdr[np.arange(rows) // 8] >> (np.arange(rows) % 8)) & 1, 8, 4)
+    else:
+        bits = np.full(rows, 4)
+    kc = _codes(tile[: rows * slot].reshape(rows, slot), d, bits)
+    vc = _codes(tile[off_vc: off_vc + rows * slot].reshape(rows, slot), d, bits)
+    if k_group > 0:
+        kp = tile[off_kp: off_kp + rows * (d // k_group) * 4].view(np.float16).reshape(rows, d // k_group, 2)
+        ks = np.repeat(kp[:, :, 0].astype(np.float64), k_group, axis=1)
+        kz = np.repeat(kp[:, :, 1].astype(np.float64), k_group, axis=1)
+    else:
+        kp = tile[off_kp: off_kp + d * 4].view(np.float16).reshape(d, 2)
+        ks = np.broadcast_to(kp[:, 0].astype(np.float64), (rows, d))
+        kz = np.broadcast_to(kp[:, 1].astype(np.float64), (rows, d))
+    vp = tile[off_vp: off_vp + rows * (d // v_group) * 4].view(np.float16).reshape(rows, d // v_group, 2)
+    vs = np.repeat(vp[:, :, 0].astype(np.float64), v_group, axis=1)
+    vz = np.repeat(vp[:, :, 1].astype(np.float64), v_group, axis=1)
+    return kc * ks + kz, vc * vs + vz
+
+
+def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed, q_bits: np.ndarray,
+                     block_table, seq_lens, sentinel_mask=None, softmax_scale=None) -> np.ndarray:
+    """Dense fp64 attention of every query head over its sequence's dequantised cache."""
+    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[5]
+    q = q_bits.view(np.float16).astype(np.float64)
+    n_seqs, hq, _ = q.shape
+    g = hq // h_kv
+    # the scale crosses the C ABI as fp32
+    scale = float(np.float32(1.0 / np.sqrt(d) if softmax_scale is None else softmax_scale))
+    if rotate:
+        c = float(np.float32(1.0 / np.sqrt(d)))
+        unrot = hadamard(d) / (d * c)
+    out = np.zeros((n_seqs, hq, d))
+    for s in range(n_seqs):
+        n = int(seq_lens[s])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        if sentinel_mask is not None:
+            sent = ((sentinel_mask[s][t // 32] >> (t % 32)) & 1).astype(bool)
+        else:
+            sent = np.zeros(n, bool)
+        for h in range(h_kv):
+            K = np.zeros((n, d))
+            V = np.zeros((n, d))
+            for lb in range((n + 255) // 256):
+                blk = int(block_table[s][lb])
+                base = (blk * h_kv + h) * tile_bytes
+                Kt, Vt = dequant_tile(pool[base: base + tile_bytes], d, k_group, v_group, mixed)
+                m = min(256, n - lb * 256)
+                K[lb * 256: lb * 256 + m] = Kt[:m]
+                V[lb * 256: lb * 256 + m] = Vt[:m]
+            if rotate:
+                K = K @ unrot.T
+                V = V @ unrot.T
+            V[sent] = 0.0
+            Q = q[s, h * g: (h + 1) * g]
+            logits = scale * (Q @ K.T)
+            logits[:, sent] = -1e4
+            logits -= logits.max(axis=1, keepdims=True)
+            w = np.exp(logits)
+            w /= w.sum(axis=1, keepdims=True)
+            out[s, h * g: (h + 1) * g] = w @ V
+    return out
