@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark: Q4 decode-attention effective HBM GB/s (% of peak) + KV tokens/s quantized, on one MI355X.
+
+Workload (default ``llama31_8b_pool_8k``): 12 agents x 8192 cached tokens, 32 query / 8 KV heads,
+head_dim 128, 32 layers, one pool of 256-token Q4 blocks per layer (groups of 64 per token), block tables
+a seeded random permutation of the pool. Every input is seeded synthetic data (kvq_workloads), resident
+in HBM before any timed region.
+
+  step   one decode step over all layers: per layer, kvq_append_tokens (quantise the new token of each
+         agent into its slot 8192) then kvq_decode_attention over 8193 slots. The step is captured once
+         as a HIP graph and replayed; ``value`` = algorithmic bytes of the step / step time.
+  kernel the decode-attention kernel alone, launched per layer between HIP events on the launch stream;
+         ``roofline.achieved`` = its algorithmic bytes per launch / mean launch duration.
+  prefill kvq_quantize_blocks over every cached block of every layer -> KV token-layers quantised / s.
+  cpu     the CPU oracle on a bounded sample (one layer of decode attention, a few blocks of quantise).
+
+Prints one JSON line on rank 0. Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import kvq_workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama31_8b_pool_8k", choices=W.CONFIG_ORDER)
+    ap.add_argument("--kernel-reps", type=int, default=5, help="passes over the layers for the kernel timing")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics only)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def decode_bytes(cfg: W.Config, case: W.Case, tile_bytes: int, live_rows_per_seq: np.ndarray) -> int:
+    """Algorithmic bytes of one decode-attention call: every live row's K and V codes and params once,
+    the mixed-pool bitmaps of the tiles touched, q, out, block tables, lengths and masks."""
+    d, H = cfg.head_dim, cfg.num_kv_heads
+    if cfg.mixed:
+        raise NotImplementedError("mixed pools use per-row widths; see decode_bytes_mixed")
+    kpar = (d // cfg.k_group) * 4 if cfg.k_group > 0 else 0
+    row = 2 * (d // 2) + kpar + (d // cfg.v_group) * 4
+    b = int(live_rows_per_seq.sum()) * H * row
+    if cfg.k_group < 0:  # per-channel K params: once per touched tile
+        b += int(np.ceil(case.seq_lens / W.BLOCK).sum()) * H * d * 4
+    b += case.n_seqs * cfg.num_q_heads * d * (2 + 4)                 # q fp16 in, out fp32
+    b += case.block_table.size * 4 + case.n_seqs * 4
+    if case.sentinel_mask is not None:
+        b += case.sentinel_mask.size * 4
+    return b
+
+
+def append_bytes(cfg: W.Config, n_seqs: int) -> int:
+    d, H = cfg.head_dim, cfg.num_kv_heads
+    kpar = (d // cfg.k_group) * 4
+    row_out = 2 * (d // 2) + kpar + (d // cfg.v_group) * 4
+    return n_seqs * H * (2 * d * 2 + row_out) + n_seqs * 4 * 2
+
+
+def quantize_bytes(cfg: W.Config, n_blocks: int, tile_bytes: int) -> int:
+    return n_blocks * W.BLOCK * cfg.num_kv_heads * cfg.head_dim * 2 * 2 + n_blocks * cfg.num_kv_heads * tile_bytes
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, digest: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this workload, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_attn_%s_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel sources:\s*([0-9a-f]{16})", text)
+    m_b = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != digest:
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_quantized_kv_quantize_amd as kvq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIGS[args.workload]
+    if cfg.mixed or cfg.k_group < 0 or not cfg.append:
+        raise SystemExit("bench.py times the per-token Q4 append + decode step; workload %s is a parity case"
+                         % args.workload)
+    layers = args.layers or cfg.layers
+    case = W.make_case(cfg)
+    lay = kvq.Layout(**cfg.layout())
+    tb = kvq.tile_bytes(lay)
+    n_prefill = case.prefill_blocks.size
+    log("workload %s: %d seqs x %d ctx, %d layers, %d pool blocks, tile %d B" %
+        (cfg.name, case.n_seqs, cfg.context, layers, case.num_blocks, tb))
+
+    # ---------------------------------------------------------------- inputs, resident in HBM
+    t0 = time.time()
+    pools, kin, vin, qs, aks, avs, outs = [], [], [], [], [], [], []
+    for l in range(layers):
+        k, v = W.blocks_kv(cfg, l, case.prefill_blocks, threads=16)
+        kin.append(torch.from_numpy(k).view(torch.float16).to(dev))
+        vin.append(torch.from_numpy(v).view(torch.float16).to(dev))
+        ak, av = W.append_kv(cfg, l, case.n_seqs)
+        aks.append(torch.from_numpy(ak).view(torch.float16).to(dev))
+        avs.append(torch.from_numpy(av).view(torch.float16).to(dev))
+        qs.append(torch.from_numpy(W.queries(cfg, l, case.n_seqs)).view(torch.float16).to(dev))
+        pools.append(kvq.new_pool(lay, case.num_blocks))
+        outs.append(torch.empty((case.n_seqs, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=dev))
+        if l % 8 == 7:
+            log("generated layer %d/%d (%.1f s)" % (l + 1, layers, time.time() - t0))
+    block_ids = torch.from_numpy(case.prefill_blocks).to(dev)
+    table = torch.from_numpy(case.block_table).to(dev)
+    positions = torch.from_numpy(case.positions).to(dev)
+    seq_lens = torch.from_numpy(case.seq_lens).to(dev)
+    max_len = case.max_seq_len
+    ws = kvq.new_workspace(lay, case.n_seqs, cfg.num_q_heads, max_len)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- prefill quantise
+    q_tok_s = None
+    q_gbps = None
+    for l in range(layers):  # untimed pass fills every pool
+        kvq.quantize_blocks(lay, pools[l], block_ids, kin[l], vin[l])
+    torch.cuda.synchronize()
+    if not args.no_prefill:
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for l in range(layers):
+                kvq.quantize_blocks(lay, pools[l], block_ids, kin[l], vin[l])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qs_t = e0.elapsed_time(e1) / 1e3 / reps
+        q_tok_s = n_prefill * W.BLOCK * layers / qs_t
+        q_gbps = quantize_bytes(cfg, n_prefill, tb) * layers / qs_t / 1e9
+        log("prefill quantise: %.3f ms for %d token-layers -> %.3g token-layers/s, %.0f GB/s" %
+            (qs_t * 1e3, n_prefill * W.BLOCK * layers, q_tok_s, q_gbps))
+    del kin, vin
+
+    # ---------------------------------------------------------------- the decode step
+    def step():
+        for l in range(layers):
+            kvq.append_tokens(lay, pools[l], aks[l], avs[l], table, positions)
+            kvq.decode_attention(lay, pools[l], qs[l], table, seq_lens, max_len, out=outs[l], workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    else:
+        run = step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t_start) / args.steps
+    live = case.seq_lens.astype(np.int64)
+    dec_b = decode_bytes(cfg, case, tb, live)
+    app_b = append_bytes(cfg, case.n_seqs)
+    step_bytes = (dec_b + app_b) * layers
+    value = step_bytes / step_s / 1e9
+    log("step: %.3f ms, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)" % (step_s * 1e3, value, value / 80))
+
+    # ---------------------------------------------------------------- the decode kernel alone
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(layers)]
+    durs = []
+    for _ in range(args.kernel_reps):
+        for l in range(layers):
+            evs[l][0].record(stream)
+            kvq.decode_attention(lay, pools[l], qs[l], table, seq_lens, max_len, out=outs[l], workspace=ws)
+            evs[l][1].record(stream)
+        torch.cuda.synchronize()
+        durs.extend(a.elapsed_time(b) / 1e3 for a, b in evs)
+    kern_s = float(np.mean(durs))
+    achieved = dec_b / kern_s / 1e9
+    log("decode kernel: mean %.2f us (p10 %.2f, p90 %.2f) -> %.1f GB/s" %
+        (kern_s * 1e6, np.percentile(durs, 10) * 1e6, np.percentile(durs, 90) * 1e6, achieved))
+
+    # plain device copy of 2 GiB for context (read + write bandwidth the box delivers)
+    a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * a.numel() * 5 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    log("device copy: %.0f GB/s (read + write)" % copy_gbps)
+
+    digest = kernel_source_digest()
+    traffic = recorded_traffic(cfg.name, digest)
+
+    # ---------------------------------------------------------------- CPU oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, case, dec_b)
+
+    line = {
+        "metric": "Q4 decode-attention effective HBM GB/s (% of peak) + KV tokens/s quantized",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4+f32",
+        "data": "synthetic (seeded, kvq_workloads)",
+        "config": {"workload": cfg.name, "agents": case.n_seqs, "context": cfg.context, "layers": layers,
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+                   "group": cfg.k_group, "block_tokens": W.BLOCK, "graph": graph is not None,
+                   "step": "per layer: append 1 token/agent + decode attention over 8193 slots"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "kv_tokens_quantized_per_s": None if q_tok_s is None else round(q_tok_s, 0),
+        "quantize_GBps": None if q_gbps is None else round(q_gbps, 1),
+        "device_copy_GBps": round(copy_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "decode_attn_k", "bytes_per_launch": dec_b, "us_per_launch": round(kern_s * 1e6, 3),
+                     "kernel_sources": digest},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, case, dec_bytes_per_layer):
+    """The oracle as it stands, timed on this host: decode attention for one layer of the workload (all
+    agents) and quantisation of a few blocks; reported in the same units as the GPU figures."""
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 16)
+    lay = oracle.make_layout(**cfg.layout())
+    tb = oracle.tile_bytes(lay)
+    layer = 0
+    k, v = W.blocks_kv(cfg, layer, case.prefill_blocks, threads=threads)
+    pool = np.zeros(tb * cfg.num_kv_heads * case.num_blocks, np.uint8)
+    nq = 32
+    t0 = time.perf_counter()
+    oracle.quantize_blocks(lay, pool, case.prefill_blocks[:nq], k[: nq * W.BLOCK], v[: nq * W.BLOCK])
+    tq = time.perf_counter() - t0
+    oracle.quantize_blocks(lay, pool, case.prefill_blocks[nq:], k[nq * W.BLOCK:], v[nq * W.BLOCK:])
+    ak, av = W.append_kv(cfg, layer, case.n_seqs)
+    oracle.append_tokens(lay, pool, ak, av, case.block_table, case.positions)
+    q = W.queries(cfg, layer, case.n_seqs)
+    t0 = time.perf_counter()
+    oracle.decode_attention(lay, pool, q, case.block_table, case.seq_lens, case.sentinel_mask, n_threads=threads)
+    td = time.perf_counter() - t0
+    log("cpu oracle: decode 1 layer %.2f s (%d threads), quantise %d blocks %.2f s (1 thread)" %
+        (td, threads, nq, tq))
+    return {"value": round(dec_bytes_per_layer / td / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "decode attention of layer 0 (%d agents x %d slots, %d threads); quantise of %d blocks "
+                      "(1 thread)" % (case.n_seqs, int(case.seq_lens[0]), threads, nq),
+            "decode_s_per_layer": round(td, 3),
+            "kv_tokens_quantized_per_s": round(nq * W.BLOCK / tq, 1)}
+
+
+if __name__ == "__main__":
+    main()

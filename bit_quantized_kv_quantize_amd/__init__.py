@@ -1,0 +1,204 @@
+"""Q4 KV-cache codec and fused-dequant decode attention for MI355X (gfx950).
+
+A thin ctypes binding over ``libkvq.so`` (C ABI in ``include/kvq.h``): it checks tensor dtypes, devices,
+shapes and alignment, then passes raw device pointers and torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If ``libkvq.so`` has not been built
+(``python -m bit_quantized_kv_quantize_amd._build``), importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = 0, -1, -2, -3, -4
+BLOCK_TOKENS = 256
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+class Layout(ctypes.Structure):
+    """Mirror of ``kvq_layout`` (include/kvq.h)."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed",
+                 "reserved")]
+
+    def __init__(self, head_dim, num_kv_heads, k_group=64, v_group=64, rotate=0, mixed=0,
+                 block_tokens=BLOCK_TOKENS):
+        super().__init__(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed), 0)
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libkvq.so is not built (%s); run `python -m bit_quantized_kv_quantize_amd._build` "
+                      "(or __graft_entry__.build())" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_LP = ctypes.POINTER(Layout)
+_lib.kvq_check_layout.argtypes = [_LP]
+_lib.kvq_check_layout.restype = ctypes.c_int
+_lib.kvq_tile_bytes.argtypes = [_LP]
+_lib.kvq_tile_bytes.restype = ctypes.c_size_t
+_lib.kvq_pool_bytes.argtypes = [_LP, _I]
+_lib.kvq_pool_bytes.restype = ctypes.c_size_t
+_lib.kvq_decode_workspace_bytes.argtypes = [_LP, _I, _I, _I]
+_lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.kvq_status_string.argtypes = [ctypes.c_int]
+_lib.kvq_status_string.restype = ctypes.c_char_p
+_lib.kvq_quantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P, _P]
+_lib.kvq_quantize_blocks.restype = ctypes.c_int
+_lib.kvq_append_tokens.argtypes = [_LP, _P, _I, _P, _P, _P, _I, _P, _P, _P]
+_lib.kvq_append_tokens.restype = ctypes.c_int
+_lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
+                                      ctypes.c_size_t, _P]
+_lib.kvq_decode_attention.restype = ctypes.c_int
+
+EXPORTS = ("kvq_check_layout", "kvq_tile_bytes", "kvq_pool_bytes", "kvq_decode_workspace_bytes",
+           "kvq_status_string", "kvq_quantize_blocks", "kvq_append_tokens", "kvq_decode_attention")
+
+
+def lib():
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.kvq_status_string(int(status)).decode()
+
+
+def check_layout(layout: Layout) -> int:
+    return int(_lib.kvq_check_layout(ctypes.byref(layout)))
+
+
+def tile_bytes(layout: Layout) -> int:
+    return int(_lib.kvq_tile_bytes(ctypes.byref(layout)))
+
+
+def pool_bytes(layout: Layout, num_blocks: int) -> int:
+    return int(_lib.kvq_pool_bytes(ctypes.byref(layout), int(num_blocks)))
+
+
+def decode_workspace_bytes(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: int) -> int:
+    return int(_lib.kvq_decode_workspace_bytes(ctypes.byref(layout), int(n_seqs), int(num_q_heads),
+                                               int(max_seq_len)))
+
+
+# ----------------------------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t, name, dtypes, align=1, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError("%s is required" % name)
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU torch tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype in %s, got %s" % (name, dtypes, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    p = t.data_ptr()
+    if p % align:
+        raise ValueError("%s must be %d-byte aligned" % (name, align))
+    return ctypes.c_void_p(p)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, st):
+    if st != KVQ_OK:
+        raise KvqError(fn, st)
+
+
+def _f16():
+    torch = _torch()
+    return (torch.float16, torch.int16, torch.uint16) if hasattr(torch, "uint16") else (torch.float16, torch.int16)
+
+
+def new_pool(layout: Layout, num_blocks: int, device="cuda"):
+    """A zero-filled pool tensor (uint8) for ``num_blocks`` blocks."""
+    torch = _torch()
+    n = pool_bytes(layout, num_blocks)
+    if n == 0 and num_blocks:
+        raise KvqError("kvq_pool_bytes", check_layout(layout) or KVQ_ERR_ARG)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def new_workspace(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: int, device="cuda"):
+    """A zero-filled decode workspace (the split-K arrival counters must start at zero; every call leaves
+    them at zero, so the tensor can be reused for later calls of the same or smaller size)."""
+    torch = _torch()
+    need = decode_workspace_bytes(layout, n_seqs, num_q_heads, max_seq_len)
+    return torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+
+
+def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, stream=None) -> None:
+    """k, v: fp16 [n_blocks*256, H_kv, d]; block_ids int32 [n_blocks]; prec_bits int32/uint32 [n_blocks, 8]."""
+    torch = _torch()
+    n_blocks = int(block_ids.numel())
+    st = _lib.kvq_quantize_blocks(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256),
+                                  _ptr(block_ids, "block_ids", (torch.int32,)), n_blocks,
+                                  _ptr(k, "k", _f16(), 16), _ptr(v, "v", _f16(), 16),
+                                  _ptr(prec_bits, "prec_bits", (torch.int32, torch.uint32), 4, True),
+                                  _stream(stream))
+    _check("kvq_quantize_blocks", st)
+
+
+def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None, stream=None) -> None:
+    """k, v: fp16 [n_seqs, H_kv, d]; block_table int32 [n_seqs, max_blocks]; positions int32 [n_seqs];
+    prec uint8 [n_seqs] (4 or 8) or None."""
+    torch = _torch()
+    n = int(positions.numel())
+    st = _lib.kvq_append_tokens(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256), n,
+                                _ptr(k, "k", _f16(), 16), _ptr(v, "v", _f16(), 16),
+                                _ptr(block_table, "block_table", (torch.int32,)), int(block_table.shape[1]),
+                                _ptr(positions, "positions", (torch.int32,)),
+                                _ptr(prec, "prec", (torch.uint8,), 1, True), _stream(stream))
+    _check("kvq_append_tokens", st)
+
+
+def decode_attention(layout: Layout, pool, q, block_table, seq_lens, max_seq_len: int, sentinel_mask=None,
+                     softmax_scale: Optional[float] = None, out=None, workspace=None, stream=None):
+    """q fp16 [n_seqs, H_q, d] -> fp32 [n_seqs, H_q, d]. ``max_seq_len`` must bound every seq_lens
+    entry (it sizes the split plan); sentinel_mask int32/uint32 [n_seqs, words] or None."""
+    torch = _torch()
+    n_seqs, hq, d = (int(x) for x in q.shape)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    if out is None:
+        out = torch.empty((n_seqs, hq, d), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(layout, n_seqs, hq, max_seq_len)
+    if workspace is None:
+        workspace = new_workspace(layout, n_seqs, hq, max_seq_len, q.device)
+    words = 0 if sentinel_mask is None else int(sentinel_mask.shape[1])
+    st = _lib.kvq_decode_attention(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256),
+                                   _ptr(q, "q", _f16(), 16), n_seqs, hq,
+                                   _ptr(block_table, "block_table", (torch.int32,)), int(block_table.shape[1]),
+                                   _ptr(seq_lens, "seq_lens", (torch.int32,)), int(max_seq_len),
+                                   _ptr(sentinel_mask, "sentinel_mask", (torch.int32, torch.uint32), 4, True),
+                                   words, float(softmax_scale), _ptr(out, "out", (torch.float32,), 16),
+                                   _ptr(workspace, "workspace", (torch.uint8,), 256), int(workspace.numel()),
+                                   _stream(stream))
+    _check("kvq_decode_attention", st)
+    return out

@@ -1,0 +1,186 @@
+// kvq_api.hip - the C ABI of libkvq: argument validation, tile geometry, split planning and launches.
+// Every entry point is declared and documented in include/kvq.h.
+#include <math.h>
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+
+static bool is_group(int g, int d) {
+  return (g == 8 || g == 16 || g == 32 || g == 64 || g == 128 || g == 256) && g <= d;
+}
+
+int check_layout(const kvq_layout* L) {
+  if (!L) return KVQ_ERR_ARG;
+  if (!(L->head_dim == 64 || L->head_dim == 128 || L->head_dim == 256)) return KVQ_ERR_ARG;
+  if (L->num_kv_heads <= 0 || L->num_kv_heads > 4096) return KVQ_ERR_ARG;
+  if (L->block_tokens != kRows || L->reserved != 0) return KVQ_ERR_ARG;
+  if (!(L->k_group == -1 || is_group(L->k_group, L->head_dim))) return KVQ_ERR_ARG;
+  if (!is_group(L->v_group, L->head_dim)) return KVQ_ERR_ARG;
+  if ((L->rotate != 0 && L->rotate != 1) || (L->mixed != 0 && L->mixed != 1)) return KVQ_ERR_ARG;
+  if (L->mixed && L->k_group < 0) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+TileGeom make_geom(const kvq_layout* L) {
+  TileGeom g{};
+  g.d = L->head_dim;
+  g.H = L->num_kv_heads;
+  g.kg = L->k_group;
+  g.vg = L->v_group;
+  g.rotate = L->rotate;
+  g.mixed = L->mixed;
+  g.slot = g.d * (g.mixed ? 8 : 4) / 8;
+  g.kpr = g.kg > 0 ? g.d / g.kg : 0;
+  g.vpr = g.d / g.vg;
+  g.off_vc = (uint32_t)(kRows * g.slot);
+  g.off_kp = 2u * kRows * g.slot;
+  uint32_t kp_bytes = g.kg > 0 ? (uint32_t)(kRows * g.kpr * 4) : (uint32_t)(g.d * 4);
+  g.off_vp = g.off_kp + kp_bytes;
+  g.off_hdr = g.off_vp + (uint32_t)(kRows * g.vpr * 4);
+  uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
+  g.tile_bytes = (end + 255u) / 256u * 256u;
+  return g;
+}
+
+SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
+  // Enough workgroups to cover 256 CUs several times over, without cutting below one block per split.
+  const int target_wgs = 1024;
+  int nb = (max_seq_len + kRows - 1) / kRows;
+  if (nb < 1) nb = 1;
+  long units = (long)(n_seqs > 0 ? n_seqs : 1) * g.H;
+  long ns = (target_wgs + units - 1) / units;
+  if (ns < 1) ns = 1;
+  if (ns > nb) ns = nb;
+  int bps = (int)((nb + ns - 1) / ns);
+  SplitPlan p;
+  p.blocks_per_split = bps;
+  p.n_splits = (nb + bps - 1) / bps;
+  return p;
+}
+
+size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
+  SplitPlan p = plan_splits(g, n_seqs, max_seq_len);
+  size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
+  size_t parts = ns * num_q_heads * p.n_splits;
+  size_t ctr = (ns * g.H * sizeof(unsigned) + 255) / 256 * 256;
+  size_t ml = (parts * 2 * sizeof(float) + 255) / 256 * 256;
+  size_t acc = (parts * g.d * sizeof(float) + 255) / 256 * 256;
+  return ctr + ml + acc;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int kvq_check_layout(const kvq_layout* L) { return check_layout(L); }
+
+size_t kvq_tile_bytes(const kvq_layout* L) {
+  if (check_layout(L) != KVQ_OK) return 0;
+  return make_geom(L).tile_bytes;
+}
+
+size_t kvq_pool_bytes(const kvq_layout* L, int32_t num_blocks) {
+  if (check_layout(L) != KVQ_OK || num_blocks < 0) return 0;
+  TileGeom g = make_geom(L);
+  return (size_t)num_blocks * g.H * g.tile_bytes;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_seqs, int32_t num_q_heads,
+                                  int32_t max_seq_len) {
+  if (check_layout(L) != KVQ_OK || n_seqs < 0 || num_q_heads <= 0 || max_seq_len < 0) return 0;
+  TileGeom g = make_geom(L);
+  if (num_q_heads % g.H != 0) return 0;
+  return decode_workspace_bytes(g, n_seqs, num_q_heads, max_seq_len);
+}
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported layout or request";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_ids, int32_t n_blocks,
+                        const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (n_blocks < 0) return KVQ_ERR_ARG;
+  if (prec_bits && !L->mixed) return KVQ_ERR_ARG;
+  if (n_blocks == 0) return KVQ_OK;
+  if (!pool || !block_ids || !k || !v) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  float rot_c = (float)(1.0 / sqrt((double)g.d));
+  return hip_status(launch_quantize_blocks(g, (uint8_t*)pool, block_ids, n_blocks, k, v, prec_bits, rot_c,
+                                           (hipStream_t)stream));
+}
+
+int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k, const uint16_t* v,
+                      const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* positions,
+                      const uint8_t* prec, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (L->k_group < 0) return KVQ_ERR_UNSUPPORTED;
+  if (n_seqs < 0 || max_blocks_per_seq <= 0) return KVQ_ERR_ARG;
+  if (prec && !L->mixed) return KVQ_ERR_ARG;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!pool || !k || !v || !block_table || !positions) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  float rot_c = (float)(1.0 / sqrt((double)g.d));
+  return hip_status(launch_append_tokens(g, (uint8_t*)pool, n_seqs, k, v, block_table, max_blocks_per_seq,
+                                         positions, prec, rot_c, (hipStream_t)stream));
+}
+
+int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+                         int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
+                         int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (n_seqs < 0 || n_seqs > 65535 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return KVQ_ERR_ARG;
+  if (num_q_heads % L->num_kv_heads != 0) return KVQ_ERR_ARG;
+  if ((long)max_seq_len > (long)max_blocks_per_seq * kRows) return KVQ_ERR_ARG;
+  if (sentinel_mask && (long)mask_words_per_seq * 32 < (long)max_seq_len) return KVQ_ERR_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!pool || !q || !block_table || !seq_lens || !out) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  const int G = num_q_heads / g.H;
+  if (G > 16) return KVQ_ERR_UNSUPPORTED;
+  size_t need = decode_workspace_bytes(g, n_seqs, num_q_heads, max_seq_len);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.pool = (const uint8_t*)pool;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.mask = sentinel_mask;
+  a.out = out;
+  a.plan = plan_splits(g, n_seqs, max_seq_len);
+  size_t parts = (size_t)n_seqs * num_q_heads * a.plan.n_splits;
+  size_t ctr_bytes = ((size_t)n_seqs * g.H * sizeof(unsigned) + 255) / 256 * 256;
+  a.ws_ctr = (unsigned*)workspace;
+  a.ws_ml = (float*)((uint8_t*)workspace + ctr_bytes);
+  a.ws_acc = (float*)((uint8_t*)workspace + ctr_bytes + (parts * 2 * sizeof(float) + 255) / 256 * 256);
+  a.n_seqs = n_seqs;
+  a.num_q_heads = num_q_heads;
+  a.G = G;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.mask_words = sentinel_mask ? mask_words_per_seq : 0;
+  a.q_scale = (float)((double)softmax_scale * 1.4426950408889634);
+  float c = (float)(1.0 / sqrt((double)g.d));
+  a.unrot_c = (float)(1.0 / ((double)g.d * (double)c));
+  return hip_status(launch_decode(g, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

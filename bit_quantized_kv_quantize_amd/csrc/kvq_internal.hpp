@@ -1,0 +1,74 @@
+// kvq_internal.hpp - geometry and launch interfaces shared by the HIP translation units of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kRows = 256;  // tokens per block (the block pool of "Agent Memory Below the Prompt", 2.1)
+
+// Byte geometry of one tile, computed once on the host and passed to kernels by value.
+struct TileGeom {
+  int d;            // head_dim
+  int H;            // KV heads
+  int kg;           // K group (channels) or -1 for one group per channel over the block
+  int vg;           // V group (channels)
+  int rotate;       // Walsh-Hadamard rotation applied before quantisation
+  int mixed;        // per-token 4/8-bit rows, 32-byte bitmap at off_hdr
+  int slot;         // bytes per code row: d/2, or d in mixed pools
+  int kpr;          // K param entries per row (d / kg), 0 for per-channel K
+  int vpr;          // V param entries per row (d / vg)
+  uint32_t off_vc;  // V codes
+  uint32_t off_kp;  // K params
+  uint32_t off_vp;  // V params
+  uint32_t off_hdr; // end of V params; the bitmap of mixed pools starts here
+  uint32_t tile_bytes;
+};
+
+int check_layout(const kvq_layout* L);
+TileGeom make_geom(const kvq_layout* L);
+
+// Split-K plan of the decode kernel: every (sequence, KV head) pair is cut into n_splits ranges of
+// blocks_per_split logical blocks.
+struct SplitPlan {
+  int n_splits;
+  int blocks_per_split;
+};
+SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len);
+size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
+
+// Launchers (defined next to their kernels). They return hipSuccess or the launch error.
+hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
+                                  const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
+                                  float rot_c, hipStream_t stream);
+hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, const uint16_t* k,
+                                const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
+                                const int32_t* positions, const uint8_t* prec, float rot_c,
+                                hipStream_t stream);
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  const uint16_t* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const uint32_t* mask;
+  float* out;
+  unsigned* ws_ctr; // [n_seqs][H_kv] arrival counters, zero between calls
+  float* ws_ml;   // [n_seqs][H_q][n_splits] x {m, l}
+  float* ws_acc;  // [n_seqs][H_q][n_splits][d]
+  int n_seqs;
+  int num_q_heads;
+  int G;
+  int max_blocks_per_seq;
+  int mask_words;
+  float q_scale;   // softmax_scale * log2(e): logits are kept in base-2 units
+  float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale
+  SplitPlan plan;
+};
+hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvq

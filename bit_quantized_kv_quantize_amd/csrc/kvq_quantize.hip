@@ -1,0 +1,322 @@
+// kvq_quantize.hip - group-wise Q4 (and per-token Q8) quantisation of K/V rows into 256-token tiles.
+//
+// Follows "Agent Memory Below the Prompt" (technical summary 2.1: 256-token blocks, codes packed in
+// uint32 words, one 16-bit scale and bias per group; 2.1 item 4: extending a cache row by row), the
+// UltraQuant article (technology section: Walsh-Hadamard rotation first, K and V grouped differently)
+// and QKVShare (methodology: width chosen per token). Every arithmetic step is a single IEEE fp32
+// operation in a fixed order, so codes and fp16 parameters are reproducible bit for bit:
+//   rotation: butterflies (a + b, a - b) with strides 1, 2, 4 inside a lane, then 8, 16, ... across lanes
+//             (lane xor 1, 2, ...), then one multiply by c = fp32(1/sqrt(d));
+//   group:    mn, mx (zero extremes canonicalised to +0), scale = fp16((mx - mn) / L), zero = fp16(mn),
+//             r = 1 / fp32(scale), code = clamp(rint((x - fp32(zero)) * r), 0, L).
+// FMA contraction is disabled for this file (contraction would change the rounding of those steps).
+#pragma clang fp contract(off)
+
+#include "kvq_internal.hpp"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ uint32_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Eight consecutive fp16 values (one 16-byte load) -> fp32.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  uint4 raw = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = h2f(w[i] & 0xffffu);
+    x[2 * i + 1] = h2f(w[i] >> 16);
+  }
+}
+
+// y = c * H * x for one row spread over LPR lanes, lane li holding elements li*8 .. li*8+7.
+template <int LPR>
+__device__ __forceinline__ void rotate_row(float (&x)[8], int li, float c) {
+#pragma unroll
+  for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((i & h) == 0) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m *= 2) {
+    const bool upper = (li & m) != 0;  // this lane holds the second element of each pair
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float p = __shfl_xor(x[i], m);
+      x[i] = upper ? (p - x[i]) : (x[i] + p);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * c;
+}
+
+// Quantise this lane's 8 values as part of a group spanning gl lanes (gl a power of two dividing the
+// row's lanes). Returns the 8 codes; every lane of the group gets the same packed {scale, zero}.
+__device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits, uint32_t (&code)[8],
+                                          uint32_t& param) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  for (int m = 1; m < gl; m *= 2) {
+    mn = fminf(mn, __shfl_xor(mn, m));
+    mx = fmaxf(mx, __shfl_xor(mx, m));
+  }
+  mn = mn + 0.0f;  // a -0 extreme becomes +0
+  mx = mx + 0.0f;
+  const float L = bits == 8 ? 255.0f : 15.0f;
+  const float s32 = (mx - mn) / L;
+  const uint32_t sh = f2h(s32), zh = f2h(mn);
+  param = sh | (zh << 16);
+  const float s = h2f(sh), z = h2f(zh);
+  if (s == 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = 0;
+    return;
+  }
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float t = x[i] - z;
+    float u = t * r;
+    float qv = __builtin_rintf(u);
+    qv = fminf(fmaxf(qv, 0.0f), L);
+    code[i] = (uint32_t)qv;
+  }
+}
+
+// Store one lane's share of a code row: 4-bit codes as one uint32 (low nibble first), 8-bit codes as
+// two; in mixed pools a 4-bit row also zeroes its share of the unused half of the slot.
+__device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_slot_bytes, int bits, int mixed,
+                                            const uint32_t (&code)[8]) {
+  if (bits == 8) {
+    uint2 w;
+    w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    *reinterpret_cast<uint2*>(row + li * 8) = w;
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
+    *reinterpret_cast<uint32_t*>(row + li * 4) = w;
+    if (mixed) *reinterpret_cast<uint32_t*>(row + half_slot_bytes + li * 4) = 0u;
+  }
+}
+
+// One row of one tensor (K or V) with per-token groups of grp channels.
+template <int LPR>
+__device__ __forceinline__ void quantize_token_row(const TileGeom& g, float (&x)[8], int li, int grp, int bits,
+                                                   uint8_t* code_row, uint8_t* param_row, float rot_c) {
+  if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+  const int gl = grp / 8;
+  uint32_t code[8];
+  uint32_t param;
+  quantize8(x, gl, bits, code, param);
+  store_codes(code_row, li, LPR * 4, bits, g.mixed, code);
+  if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(param_row)[li / gl] = param;
+}
+
+// Grid (n_blocks, H, n_tensors): one workgroup writes the 256 rows of tensor (blockIdx.z + kv_base) of
+// tile (block_ids[blockIdx.x], blockIdx.y); LPR = d / 8 lanes per row, 256 / LPR rows per pass.
+template <int LPR>
+__global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                       const int32_t* __restrict__ block_ids,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       const uint32_t* __restrict__ prec_bits, float rot_c,
+                                                       int kv_base) {
+  constexpr int D = LPR * 8;
+  constexpr int kRowsPerPass = 256 / LPR;
+  const int i = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
+  const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
+  const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 8;
+  const int grp = kv ? g.vg : g.kg;
+  const int ppr = D / grp;
+  uint8_t* code_base = tile + (kv ? g.off_vc : 0u);
+  uint8_t* par_base = tile + (kv ? g.off_vp : g.off_kp);
+  const uint32_t* bitmap = prec_bits ? prec_bits + (size_t)i * 8 : nullptr;
+  for (int t = r0; t < kRows; t += kRowsPerPass) {
+    float x[8];
+    load8(src + (size_t)t * g.H * D, x);
+    const int bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
+    quantize_token_row<LPR>(g, x, li, grp, bits, code_base + (size_t)t * g.slot, par_base + (size_t)t * ppr * 4,
+                            rot_c);
+  }
+  if (kv == 1) {
+    // zero the tail padding (and write the width bitmap of mixed pools)
+    const uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
+    for (uint32_t o = end + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
+      *reinterpret_cast<uint32_t*>(tile + o) = 0u;
+    if (g.mixed && threadIdx.x < 8)
+      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[threadIdx.x] = bitmap ? bitmap[threadIdx.x] : 0u;
+  }
+}
+
+// K grouped per channel over the block's 256 rows (always 4-bit). Two passes over the rows: the first
+// finds every column's min/max of the (rotated) values, the second recomputes the identical rotated
+// values and encodes them against the column's parameters.
+template <int LPR>
+__global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                        const int32_t* __restrict__ block_ids,
+                                                        const uint16_t* __restrict__ k, float rot_c) {
+  constexpr int D = LPR * 8;
+  constexpr int kRowsPerPass = 256 / LPR;
+  __shared__ float s_min[kRowsPerPass][D];
+  __shared__ float s_max[kRowsPerPass][D];
+  __shared__ float s_z[D], s_r[D];
+  __shared__ int s_zero_scale[D];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
+  const uint16_t* src = k + ((size_t)i * kRows * g.H + h) * D + li * 8;
+
+  float cmin[8], cmax[8];
+  for (int t = r0; t < kRows; t += kRowsPerPass) {
+    float x[8];
+    load8(src + (size_t)t * g.H * D, x);
+    if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      cmin[e] = t == r0 ? x[e] : fminf(cmin[e], x[e]);
+      cmax[e] = t == r0 ? x[e] : fmaxf(cmax[e], x[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s_min[r0][li * 8 + e] = cmin[e];
+    s_max[r0][li * 8 + e] = cmax[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float mn = s_min[0][c], mx = s_max[0][c];
+    for (int r = 1; r < kRowsPerPass; ++r) {
+      mn = fminf(mn, s_min[r][c]);
+      mx = fmaxf(mx, s_max[r][c]);
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    const float s32 = (mx - mn) / 15.0f;
+    const uint32_t sh = f2h(s32), zh = f2h(mn);
+    reinterpret_cast<uint32_t*>(tile + g.off_kp)[c] = sh | (zh << 16);
+    const float s = h2f(sh);
+    s_z[c] = h2f(zh);
+    s_zero_scale[c] = s == 0.0f;
+    s_r[c] = s == 0.0f ? 0.0f : 1.0f / s;
+  }
+  __syncthreads();
+  for (int t = r0; t < kRows; t += kRowsPerPass) {
+    float x[8];
+    load8(src + (size_t)t * g.H * D, x);
+    if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = li * 8 + e;
+      uint32_t code = 0;
+      if (!s_zero_scale[c]) {
+        float tt = x[e] - s_z[c];
+        float u = tt * s_r[c];
+        float qv = __builtin_rintf(u);
+        qv = fminf(fmaxf(qv, 0.0f), 15.0f);
+        code = (uint32_t)qv;
+      }
+      w |= code << (4 * e);
+    }
+    reinterpret_cast<uint32_t*>(tile + (size_t)t * g.slot)[li] = w;
+  }
+}
+
+// Grid (n_seqs, H, 2), LPR threads: row positions[s] % 256 of block block_table[s][positions[s] / 256].
+template <int LPR>
+__global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+                                                const int32_t* __restrict__ positions,
+                                                const uint8_t* __restrict__ prec, float rot_c) {
+  constexpr int D = LPR * 8;
+  const int s = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+  const int li = threadIdx.x;
+  const int p = positions[s];
+  const int row = p % kRows;
+  const int blk = block_table[(size_t)s * max_blocks_per_seq + p / kRows];
+  uint8_t* tile = pool + ((size_t)blk * g.H + h) * g.tile_bytes;
+  const int bits = (prec && prec[s] == 8) ? 8 : 4;
+  const int grp = kv ? g.vg : g.kg;
+  float x[8];
+  load8((kv ? v : k) + ((size_t)s * g.H + h) * D + li * 8, x);
+  quantize_token_row<LPR>(g, x, li, grp, bits, tile + (kv ? g.off_vc : 0u) + (size_t)row * g.slot,
+                          tile + (kv ? g.off_vp : g.off_kp) + (size_t)row * (D / grp) * 4, rot_c);
+  if (g.mixed && kv == 0 && li == 0) {
+    uint32_t* word = reinterpret_cast<uint32_t*>(tile + g.off_hdr) + (row >> 5);
+    const uint32_t bit = 1u << (row & 31);
+    if (bits == 8) atomicOr(word, bit);
+    else atomicAnd(word, ~bit);
+  }
+}
+
+template <int LPR>
+hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
+                             const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, float rot_c,
+                             hipStream_t stream) {
+  if (g.kg > 0) {
+    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, 2), dim3(256), 0, stream, g, pool, block_ids,
+                       k, v, prec_bits, rot_c, 0);
+  } else {
+    hipLaunchKernelGGL(quantize_kchan_k<LPR>, dim3(n_blocks, g.H, 1), dim3(256), 0, stream, g, pool,
+                       block_ids, k, rot_c);
+    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, 1), dim3(256), 0, stream, g, pool, block_ids,
+                       k, v, prec_bits, rot_c, 1);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
+                                  const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
+                                  float rot_c, hipStream_t stream) {
+  switch (g.d) {
+    case 64: return launch_quantize_t<8>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
+    case 128: return launch_quantize_t<16>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
+    case 256: return launch_quantize_t<32>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, const uint16_t* k,
+                                const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
+                                const int32_t* positions, const uint8_t* prec, float rot_c,
+                                hipStream_t stream) {
+  dim3 grid(n_seqs, g.H, 2);
+  switch (g.d) {
+    case 64:
+      hipLaunchKernelGGL(append_k<8>, grid, dim3(8), 0, stream, g, pool, k, v, block_table, max_blocks_per_seq,
+                         positions, prec, rot_c);
+      break;
+    case 128:
+      hipLaunchKernelGGL(append_k<16>, grid, dim3(16), 0, stream, g, pool, k, v, block_table,
+                         max_blocks_per_seq, positions, prec, rot_c);
+      break;
+    case 256:
+      hipLaunchKernelGGL(append_k<32>, grid, dim3(32), 0, stream, g, pool, k, v, block_table,
+                         max_blocks_per_seq, positions, prec, rot_c);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

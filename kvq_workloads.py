@@ -241,7 +241,7 @@ def make_case(cfg: Config, n_seqs: Optional[int] = None, context=None, shared_pr
 def k_norms_sq(k_rows: np.ndarray) -> np.ndarray:
     """Squared L2 norm (fp64) of each token's K over all heads and channels: [n_tokens]."""
     x = k_rows.view(np.float16).astype(np.float64)
-    return (x * x).reshape(x.shape[0], -1).sum(axis=1)
+    return (x * x).reshape(x.shape[0], int(np.prod(x.shape[1:]))).sum(axis=1)
 
 
 def precision_map(norms_sq: np.ndarray, top_fraction: float) -> np.ndarray:

@@ -1,0 +1,94 @@
+"""The C-ABI library builds, loads and exports every entry point declared in include/kvq.h. Only host-side
+calls run here (layout/size helpers and argument errors that return before any launch), so no GPU is
+needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+LIB = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "libkvq.so")
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    if not os.path.exists(LIB):
+        from bit_quantized_kv_quantize_amd import _build
+
+        _build.build()
+    import bit_quantized_kv_quantize_amd as kvq
+
+    return kvq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(kvq):
+    names = declared_functions()
+    assert len(names) == 8, names
+    dyn = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", dyn))
+    assert set(names) <= exported, set(names) - exported
+    assert set(kvq.EXPORTS) == set(names)
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_layout_helpers_match_oracle(kvq, orc):
+    import kvq_workloads as W
+
+    for cfg in W.CONFIGS.values():
+        lay = kvq.Layout(**cfg.layout())
+        assert kvq.check_layout(lay) == 0
+        olay = orc.make_layout(**cfg.layout())
+        assert kvq.tile_bytes(lay) == orc.tile_bytes(olay)
+        assert kvq.pool_bytes(lay, 10) == 10 * cfg.num_kv_heads * orc.tile_bytes(olay)
+        ws = kvq.decode_workspace_bytes(lay, cfg.n_seqs, cfg.num_q_heads, cfg.context + 1)
+        assert ws > 0 and ws % 256 == 0
+
+
+def test_layout_validation_and_status(kvq):
+    assert kvq.check_layout(kvq.Layout(96, 8)) == kvq.KVQ_ERR_ARG
+    assert kvq.check_layout(kvq.Layout(128, 8, 48, 64)) == kvq.KVQ_ERR_ARG
+    assert kvq.check_layout(kvq.Layout(128, 8, -1, 32, 0, 1)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(128, 0)) == kvq.KVQ_ERR_ARG
+    assert kvq.check_layout(kvq.Layout(128, 8, block_tokens=128)) == kvq.KVQ_ERR_ARG
+    assert kvq.tile_bytes(kvq.Layout(96, 8)) == 0
+    assert kvq.decode_workspace_bytes(kvq.Layout(128, 8), 4, 12, 100) == 0   # 12 % 8 != 0
+    for st in (0, -1, -2, -3, -4, -99):
+        assert isinstance(kvq.status_string(st), str) and kvq.status_string(st)
+
+
+def test_host_argument_errors_return_before_launch(kvq):
+    lib = kvq.lib()
+    lay = kvq.Layout(128, 8)
+    P = ctypes.c_void_p
+    bad = kvq.Layout(100, 8)
+    assert lib.kvq_quantize_blocks(ctypes.byref(bad), None, None, 1, None, None, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_quantize_blocks(ctypes.byref(lay), None, None, 0, None, None, None, None) == kvq.KVQ_OK
+    assert lib.kvq_quantize_blocks(ctypes.byref(lay), None, None, 2, None, None, None, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_quantize_blocks(ctypes.byref(lay), P(256), P(256), 1, P(256), P(256), P(256),
+                                   None) == kvq.KVQ_ERR_ARG                    # prec_bits on a non-mixed pool
+    chan = kvq.Layout(128, 8, -1, 32, 1, 0)
+    assert lib.kvq_append_tokens(ctypes.byref(chan), P(256), 1, P(256), P(256), P(256), 1, P(256), None,
+                                 None) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 2, 12, P(256), 4, P(256), 100, None, 0,
+                                    0.1, P(256), P(256), 1 << 20, None) == kvq.KVQ_ERR_ARG   # 12 % 8
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 2, 16, P(256), 1, P(256), 300, None, 0,
+                                    0.1, P(256), P(256), 1 << 20, None) == kvq.KVQ_ERR_ARG   # 300 > 1 block
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 2, 16, P(256), 4, P(256), 1000, P(256), 3,
+                                    0.1, P(256), P(256), 1 << 20, None) == kvq.KVQ_ERR_ARG   # mask too short
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 2, 16, P(256), 4, P(256), 1000, None, 0,
+                                    0.1, P(256), P(256), 16, None) == kvq.KVQ_ERR_WORKSPACE
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 2, 16, P(256), 4, P(256), 1000, None, 0,
+                                    0.1, P(256), P(257), 1 << 20, None) == kvq.KVQ_ERR_WORKSPACE  # misaligned
+    assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 0, 16, P(256), 4, P(256), 1000, None, 0,
+                                    0.1, None, None, 0, None) == kvq.KVQ_OK                 # nothing to do

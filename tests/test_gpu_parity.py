@@ -1,0 +1,125 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Codes, fp16 scales/zeros, width bitmaps and padding must be bit-exact (whole pool bytes compared);
+decode attention must be within 2e-3 max relative error (normwise per sequence and query head).
+Sizes span several tiles with ragged tails; the configurations are the five workloads shrunk so the
+oracle finishes in seconds (full-size sampled checks live in test_gpu_fullsize.py)."""
+import numpy as np
+import pytest
+
+import kvq_workloads as W
+from gpu_cases import TOL, gpu_run, host_inputs, oracle_run, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import bit_quantized_kv_quantize_amd as kvq
+
+    return kvq, torch
+
+
+SMALL = {
+    "tiny_1k": dict(n_seqs=2, context=[1024, 700]),
+    "gemma3_12b_4k": dict(n_seqs=2, context=[1000, 513]),
+    "llama31_8b_pool_8k": dict(n_seqs=4, context=[2048, 777, 1, 0]),
+    "qwen25_14b_prefix_32k": dict(n_seqs=3, shared_prefix=512, context=[768, 612, 1023]),
+    "mixed_sentinel_32k": dict(n_seqs=3, context=[1024, 600, 333]),
+}
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_pool_bytes_bit_exact(env, orc, name):
+    kvq, torch = env
+    case = W.make_case(W.CONFIGS[name], **SMALL[name])
+    inp = host_inputs(case)
+    ref_pool, _ = oracle_run(orc, case, inp, decode=False)
+    got_pool, _ = gpu_run(kvq, torch, case, inp, decode=False)
+    diff = np.nonzero(got_pool != ref_pool)[0]
+    assert diff.size == 0, "first differing bytes at %s" % diff[:16]
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_decode_within_tolerance(env, orc, name):
+    kvq, torch = env
+    case = W.make_case(W.CONFIGS[name], **SMALL[name])
+    inp = host_inputs(case)
+    _, ref = oracle_run(orc, case, inp)
+    _, got = gpu_run(kvq, torch, case, inp)
+    err = rel_err(got, ref)
+    print("%s: max rel err %.3g" % (name, err))
+    assert err <= TOL
+    assert np.all(got[case.seq_lens == 0] == 0)
+
+
+@pytest.mark.parametrize("rotate,mixed,kg,vg,G,d", [
+    (0, 0, 64, 64, 1, 128), (0, 0, 32, 32, 3, 64), (1, 0, 64, 32, 8, 128), (0, 1, 64, 64, 16, 128),
+    (1, 0, -1, 32, 5, 256), (1, 1, 32, 64, 2, 64), (0, 0, 128, 16, 4, 128), (0, 0, 8, 256, 2, 256)])
+def test_layout_variants(env, orc, rotate, mixed, kg, vg, G, d):
+    # Generic layouts beyond the five workloads: group sizes, widths, rotation, G up to 16, ragged
+    # lengths (0, 1, 255, 256, 257, long) and sentinel masks (one sequence entirely sentinel).
+    kvq, torch = env
+    H = 2
+    cfg = W.Config(9, "variant", d, H * G, H, 1, kg, vg, rotate, mixed, 6, 0, "perm", kg > 0, 3, 10.0, 1.0,
+                   dead_fraction=0.5, top_fraction=0.2 if mixed else 0.0)
+    case = W.make_case(cfg, context=[0, 1, 255, 256, 700, 1500] if kg > 0 else [1, 255, 256, 257, 700, 1500])
+    case.sentinel_mask[4] = 0xFFFFFFFF
+    if kg > 0:
+        case.sentinel_mask[4, (int(case.seq_lens[4]) - 1) // 32:] = 0xFFFFFFFF  # include the appended slot
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    assert np.array_equal(got_pool, ref_pool)
+    assert rel_err(got, ref) <= TOL
+    assert not got[4].any()                                  # every slot remapped to the sentinel
+    if case.seq_lens[0] == 0:
+        assert not got[0].any()
+
+
+def test_decode_is_deterministic(env):
+    kvq, torch = env
+    case = W.make_case(W.CONFIGS["llama31_8b_pool_8k"], n_seqs=3, context=[3000, 2048, 100])
+    inp = host_inputs(case)
+    _, a = gpu_run(kvq, torch, case, inp)
+    _, b = gpu_run(kvq, torch, case, inp)
+    assert np.array_equal(a, b)
+
+
+def test_sentinel_terms_count_when_live_logits_are_near_minus_1e4(env, orc):
+    # With every K row identical, every live logit is scale * c for one constant c; choosing the scale so
+    # that this is -1e4 - 1 gives the sentinel slots (logit -1e4, value 0) a weight comparable to the
+    # live ones. Skipping sentinel slots alone would then be wrong; the kernel adds their exact term in
+    # the reduction and must match the definition.
+    kvq, torch = env
+    cfg = W.Config(8, "sentinel_probe", 128, 1, 1, 1, 64, 64, 0, 0, 1, 600, "identity", False, 0, 1.0, 1.0,
+                   dead_fraction=0.5)
+    case = W.make_case(cfg)
+    inp = host_inputs(case)
+    inp["k"][:] = inp["k"][0]
+    lay_o = orc.make_layout(**cfg.layout())
+    pool = np.zeros(orc.tile_bytes(lay_o) * case.num_blocks, np.uint8)
+    orc.quantize_blocks(lay_o, pool, case.prefill_blocks, inp["k"], inp["v"])
+    k0, _, _ = orc.dequant_row(lay_o, pool[:orc.tile_bytes(lay_o)], 0)
+    c = float(inp["q"][0, 0].view(np.float16).astype(np.float64) @ k0)
+    scale = float(np.float32(-(1e4 + 1.0) / c))
+    ref = orc.decode_attention(lay_o, pool, inp["q"], case.block_table, case.seq_lens, case.sentinel_mask,
+                               softmax_scale=scale)
+    lay = kvq.Layout(**cfg.layout())
+    gp = kvq.new_pool(lay, case.num_blocks)
+    kvq.quantize_blocks(lay, gp, torch.from_numpy(case.prefill_blocks).cuda(),
+                        torch.from_numpy(inp["k"]).view(torch.float16).cuda(),
+                        torch.from_numpy(inp["v"]).view(torch.float16).cuda())
+    out = kvq.decode_attention(lay, gp, torch.from_numpy(inp["q"]).view(torch.float16).cuda(),
+                               torch.from_numpy(case.block_table).cuda(), torch.from_numpy(case.seq_lens).cuda(),
+                               case.max_seq_len, torch.from_numpy(case.sentinel_mask.view(np.int32)).cuda(),
+                               softmax_scale=scale).cpu().numpy()
+    assert np.array_equal(gp.cpu().numpy(), pool)
+    assert rel_err(out, ref) <= TOL
+    # the sentinel terms matter here: the live-only average is far from the reference
+    t = np.arange(600)
+    live = ~((case.sentinel_mask[0][t // 32] >> (t % 32)) & 1).astype(bool)
+    assert np.abs(ref[0, 0]).max() < 0.5 * np.abs(np.mean([orc.dequant_row(lay_o, pool[(case.block_table[0, i // 256]) * orc.tile_bytes(lay_o):][:orc.tile_bytes(lay_o)], i % 256)[1] for i in t[live]], axis=0)).max()

@@ -9,7 +9,7 @@ sentinel invariants.
 import numpy as np
 import pytest
 
-from bit_quantized_kv_quantize_amd import workloads as W
+import kvq_workloads as W
 from oracle import brute
 
 

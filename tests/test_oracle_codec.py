@@ -11,7 +11,7 @@ import os
 import numpy as np
 import pytest
 
-from bit_quantized_kv_quantize_amd import workloads as W
+import kvq_workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 

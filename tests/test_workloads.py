@@ -1,7 +1,7 @@
 """Host-side checks of the seeded workload generators (shapes, determinism, table structure)."""
 import numpy as np
 
-from bit_quantized_kv_quantize_amd import workloads as W
+import kvq_workloads as W
 
 
 def test_deterministic_and_shaped():
