@@ -146,11 +146,10 @@ def new_pool(layout: Layout, num_blocks: int, device="cuda"):
 
 
 def new_workspace(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: int, device="cuda"):
-    """A zero-filled decode workspace (the split-K arrival counters must start at zero; every call leaves
-    them at zero, so the tensor can be reused for later calls of the same or smaller size)."""
+    """A decode workspace for calls of this size or smaller (split-K partials; no initialisation needed)."""
     torch = _torch()
     need = decode_workspace_bytes(layout, n_seqs, num_q_heads, max_seq_len)
-    return torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
 
 
 def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, stream=None) -> None:

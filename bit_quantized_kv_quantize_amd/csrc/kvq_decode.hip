@@ -11,33 +11,16 @@
 // -1e4 and value 0, is added in the reduction: it changes the normaliser only when no live logit is far
 // above -1e4, and makes an all-sentinel sequence return zeros, as the definition does.
 //
-// One kernel per call: every split writes its partials, then bumps a per-(sequence, KV head) counter;
-// the split that arrives last merges all partials in split order (so the result does not depend on
-// which split that is), writes the output and resets the counter to zero for the next call.
-#include "kvq_internal.hpp"
+// Every split writes its partials (m, l, acc[d]) per query head; decode_reduce_k merges them in split
+// order in a second kernel (the kernel boundary makes the partials visible across the chip's XCDs).
+#include <stdlib.h>
+
+#include "kvq_decode_common.hpp"
 
 namespace kvq {
 namespace {
 
-constexpr float kSentinelLog2 = -14426.950408889634f;  // -1e4 * log2(e)
-constexpr float kNegInf = -__builtin_huge_valf();
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-
-__device__ __forceinline__ bool is_sentinel(const uint32_t* mask_row, int pos) {
-  return mask_row && ((mask_row[pos >> 5] >> (pos & 31)) & 1u);
-}
+using namespace dec;
 
 // Codes of 8 consecutive channels starting at channel c0 of a row (4-bit or 8-bit).
 __device__ __forceinline__ void codes8(const uint8_t* row, int c0, int bits, float (&c)[8]) {
@@ -52,84 +35,6 @@ __device__ __forceinline__ void codes8(const uint8_t* row, int c0, int bits, flo
     uint32_t w = *reinterpret_cast<const uint32_t*>(row + c0 / 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) c[e] = (float)((w >> (4 * e)) & 0xfu);
-  }
-}
-
-// Called by every split of (seq, h) after its partials are written. The last split to arrive merges the
-// n_splits partials of the G query heads in split order, adds the sentinel term, undoes the rotation and
-// writes the output; it then resets the counter. scratch: at least 2 * D floats of LDS.
-template <int D>
-__device__ void finish_unit(const TileGeom& g, const DecodeArgs& a, int seq, int h, int tid, float* scratch) {
-  constexpr int NT = 256;
-  __shared__ int s_last;
-  __shared__ int s_cnt[NT / 64];
-  __threadfence();  // this thread's partial writes are visible device-wide before the counter moves
-  __syncthreads();
-  if (tid == 0) {
-    unsigned* ctr = a.ws_ctr + (size_t)seq * g.H + h;
-    const unsigned prev = atomicAdd(ctr, 1u);
-    s_last = prev == (unsigned)(a.plan.n_splits - 1);
-    if (s_last) atomicExch(ctr, 0u);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // observe every other split's partials
-
-  const int len = a.seq_lens[seq];
-  // sentinel slots among 0 .. len-1
-  int cnt = 0;
-  if (a.mask && len > 0) {
-    const uint32_t* mrow = a.mask + (size_t)seq * a.mask_words;
-    const int words = (len + 31) / 32;
-    for (int w = tid; w < words; w += NT) {
-      uint32_t bits = mrow[w];
-      const int valid = len - w * 32;
-      if (valid < 32) bits &= (1u << valid) - 1u;
-      cnt += __popc(bits);
-    }
-  }
-  for (int m = 32; m >= 1; m >>= 1) cnt += __shfl_xor(cnt, m);
-  if ((tid & 63) == 0) s_cnt[tid >> 6] = cnt;
-  __syncthreads();
-  int n_sent = 0;
-  for (int w = 0; w < NT / 64; ++w) n_sent += s_cnt[w];
-
-  float* s_o = scratch;
-  for (int jj = 0; jj < a.G; ++jj) {
-    const int j = h * a.G + jj;
-    const size_t p0 = ((size_t)seq * a.num_q_heads + j) * a.plan.n_splits;
-    float M = n_sent > 0 ? kSentinelLog2 : kNegInf;
-    for (int i = 0; i < a.plan.n_splits; ++i)
-      if (a.ws_ml[2 * (p0 + i) + 1] > 0.0f)
-        M = fmaxf(M, a.ws_ml[2 * (p0 + i)]);
-    float L = n_sent > 0 ? (float)n_sent * exp2f(kSentinelLog2 - M) : 0.0f;
-    float o = 0.0f;
-    for (int i = 0; i < a.plan.n_splits; ++i) {
-      const float li = a.ws_ml[2 * (p0 + i) + 1];
-      if (li > 0.0f) {
-        const float w = exp2f(a.ws_ml[2 * (p0 + i)] - M);
-        L += li * w;
-        if (tid < D) o += a.ws_acc[(p0 + i) * D + tid] * w;
-      }
-    }
-    o = (len > 0 && L > 0.0f) ? o / L : 0.0f;
-    if (g.rotate) {
-      if (tid < D) s_o[tid] = o;
-      __syncthreads();
-      for (int hs = 1; hs < D; hs *= 2) {
-        float r = 0.0f;
-        if (tid < D) {
-          const float x = s_o[tid], y = s_o[tid ^ hs];
-          r = (tid & hs) ? (y - x) : (x + y);
-        }
-        __syncthreads();
-        if (tid < D) s_o[tid] = r;
-        __syncthreads();
-      }
-      if (tid < D) o = s_o[tid] * a.unrot_c;
-      __syncthreads();
-    }
-    if (tid < D) a.out[((size_t)seq * a.num_q_heads + j) * D + tid] = o;
   }
 }
 
@@ -165,7 +70,6 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
       a.ws_ml[2 * pi] = kNegInf;
       a.ws_ml[2 * pi + 1] = 0.0f;
     }
-    finish_unit<D>(g, a, seq, h, tid, &s_acc[0][0]);
     return;
   }
 
@@ -360,12 +264,12 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     }
     __syncthreads();
   }
-  finish_unit<D>(g, a, seq, h, tid, &s_acc[0][0]);
 }
 template <int D, int GMAX>
 hipError_t launch_t(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_attn_k<D, GMAX>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
                      g, a);
+  hipLaunchKernelGGL(decode_reduce_k<D>, dim3(a.num_q_heads, a.n_seqs), dim3(D), 0, stream, g, a);
   return hipGetLastError();
 }
 
@@ -379,6 +283,11 @@ hipError_t launch_d(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  if (!getenv("KVQ_FORCE_GENERIC_DECODE") && decode_mfma_supported(g, a.G)) return launch_decode_mfma(g, a, stream);
+  return launch_decode_generic(g, a, stream);
+}
+
+hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   switch (g.d) {
     case 64: return launch_d<64>(g, a, stream);
     case 128: return launch_d<128>(g, a, stream);

@@ -1,0 +1,432 @@
+// kvq_decode_mfma.hip - decode attention over 4-bit per-token-grouped tiles on the matrix cores.
+//
+// Same computation as the generic kernel (single-token decode attention reading the packed Q4 cache of
+// "Agent Memory Below the Prompt", technical summary 2.1, with GQA from 2.2, sentinel slots of the
+// IntentKV article and the rotated cache of the UltraQuant article), organised for gfx950:
+//
+// * Both contractions run as v_mfma_f32_16x16x32_f16. For QK the A operand holds the query rows, one
+//   MFMA row per (query head, K group) so each group's partial dot product stays separate and its scale
+//   and zero apply afterwards; the B operand is the K codes of 16 tokens. For PV the A operand holds
+//   p * v_scale, one row per (query head, V group); the B operand is the V codes of 32 tokens.
+// * Codes become fp16 operands without arithmetic: masking a packed word with 0x000F000F leaves two
+//   nibbles as fp16 subnormals n * 2^-24 (0x00F000F0 gives 16 n * 2^-24). Subnormal fp16 inputs are
+//   exact in the MFMA, and the 2^24 / 16 factors fold into the scales. V codes are transposed to
+//   token-major operands in registers with byte permutes of 8 rows.
+// * The query and p * v_scale are each split into fp16 hi + lo parts (two MFMAs on the same codes): a
+//   dequantised value is scale * code + zero, a difference of two larger terms, so a single fp16
+//   rounding of the scaled operand would cost up to 2^-12 of scale * 15 per element.
+// * Each wave owns 64 rows of every block and keeps its own online softmax (16-lane DPP reductions, no
+//   block-wide barrier in the token loop); the four waves merge at the end of the split. With one split
+//   per (sequence, KV head) the workgroup finalises the output itself; otherwise it writes split-K
+//   partials for decode_reduce_k.
+#include "kvq_decode_common.hpp"
+
+namespace kvq {
+namespace {
+
+using namespace dec;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c,
+                                                0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Row (16-lane) reductions via DPP row rotations: every lane of the row ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0x128>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x122>(v));
+  v = fmaxf(v, dpp<0x121>(v));
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x122>(v);
+  v += dpp<0x121>(v);
+  return v;
+}
+
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kTwo20 = 1048576.0f;
+
+// Grid (n_splits, H_kv, n_seqs), 256 threads = 4 waves; wave w owns rows 64w .. 64w+63 of each block.
+template <int D, int G, int KG, int VG>
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom g, DecodeArgs a) {
+  constexpr int NGK = D / KG;      // K groups per row
+  constexpr int NGV = D / VG;      // V groups per row
+  constexpr int HPL = (G + 3) / 4; // query heads per 16-lane row group
+  static_assert(HPL * NGK <= 4 && HPL * NGV <= 4, "MFMA rows: heads x groups per lane group <= 4");
+  constexpr int KW = D / 32;       // K words per lane per row = QK k-steps
+  constexpr int VW = D / 128;      // V words per lane per row
+  constexpr int NTILE = 8 * VW;    // PV output tiles of 16 channels
+  constexpr int PSTR = 72;         // LDS row stride (halves) of the p * v_scale tiles
+  static_assert(D == 128 || D == 256, "head_dim 128 or 256");
+
+  __shared__ float s_q[G][D];
+  __shared__ float s_qsum[G][NGK];
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[4][2][16][PSTR];  // [wave][hi, lo][row][token]
+  __shared__ float s_wm[4][G], s_wl[4][G];
+  __shared__ float s_wacc[4][G][D];
+
+  const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
+  const int ns = a.plan.n_splits;
+  const int len = a.seq_lens[seq];
+  const int nblk = (len + kRows - 1) / kRows;
+  const int b0 = split * a.plan.blocks_per_split;
+  const int b1 = min(b0 + a.plan.blocks_per_split, nblk);
+  const uint32_t* mask_row = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
+  const size_t part0 = ((size_t)seq * a.num_q_heads + (size_t)h * G) * ns + split;
+
+  if (b0 >= b1) {
+    if (ns == 1) {  // empty sequence: the output row still has to be written
+      __shared__ int s_cnt0[4];
+      const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt0);
+      for (int jj = 0; jj < G; ++jj)
+        finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, kNegInf, 0.0f, 0.0f, tid, &s_wacc[0][0][0]);
+    } else if (tid < G) {
+      a.ws_ml[2 * (part0 + (size_t)tid * ns)] = kNegInf;
+      a.ws_ml[2 * (part0 + (size_t)tid * ns) + 1] = 0.0f;
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- query operands
+  for (int i = tid; i < G * D; i += 256)
+    s_q[i / D][i % D] = h2f(a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D]) * a.q_scale;
+  for (int i = tid; i < 4 * 2 * 16 * PSTR; i += 256) (&s_p[0][0][0][0])[i] = (_Float16)0.0f;
+  __syncthreads();
+  if (g.rotate) {
+    for (int hs = 1; hs < D; hs *= 2) {
+      for (int i = tid; i < G * D / 2; i += 256) {
+        const int j = i / (D / 2), pi = i % (D / 2);
+        const int lo = (pi / hs) * 2 * hs + (pi % hs);
+        const float x = s_q[j][lo], y = s_q[j][lo + hs];
+        s_q[j][lo] = x + y;
+        s_q[j][lo + hs] = x - y;
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] *= a.unrot_c;
+    __syncthreads();
+  }
+  for (int i = tid; i < G * NGK; i += 256) {
+    float sum = 0.0f;
+    for (int c = 0; c < KG; ++c) sum += s_q[i / NGK][(i % NGK) * KG + c];
+    s_qsum[i / NGK][i % NGK] = sum;
+  }
+  __syncthreads();
+
+  // QK A operand: row lj = 4*ai + ri -> head ai*HPL + ri/NGK, K group ri%NGK; lane group la supplies words
+  // la*KW .. la*KW+KW-1, k-step s uses word la*KW + s. Element e of an operand is nibble nib(e) of the
+  // word, pre-divided by 16 for the high nibbles (e & 2) to match the unpacking.
+  u32x4 qa_hi[KW], qa_lo[KW];
+  {
+    const int ai = lj >> 2, ri = lj & 3;
+    const int jj = ai * HPL + ri / NGK, gam = ri % NGK;
+    const bool valid = ri < HPL * NGK && jj < G;
+#pragma unroll
+    for (int s = 0; s < KW; ++s) {
+      const int word = la * KW + s;
+      const bool in_group = valid && (word * 8) / KG == gam;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        _Float16 hi[2], lo[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int e = 2 * p + k;
+          const int nib = (e >> 1) + 4 * (e & 1);  // 0,4,1,5,2,6,3,7
+          const float sc = (e & 2) ? 0.0625f : 1.0f;
+          const float v = in_group ? s_q[jj][word * 8 + nib] * sc : 0.0f;
+          hi[k] = (_Float16)v;
+          lo[k] = (_Float16)(v - (float)hi[k]);
+        }
+        qa_hi[s][p] = pack_h2(hi[0], hi[1]);
+        qa_lo[s][p] = pack_h2(lo[0], lo[1]);
+      }
+    }
+  }
+  float qsum[HPL][NGK];
+#pragma unroll
+  for (int u = 0; u < HPL; ++u)
+#pragma unroll
+    for (int gm = 0; gm < NGK; ++gm) qsum[u][gm] = (la * HPL + u) < G ? s_qsum[la * HPL + u][gm] : 0.0f;
+
+  float m_run[HPL], l_run[HPL], zacc[HPL][NGV];
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) {
+    m_run[u] = kNegInf;
+    l_run[u] = 0.0f;
+#pragma unroll
+    for (int gm = 0; gm < NGV; ++gm) zacc[u][gm] = 0.0f;
+  }
+  floatx4 o[NTILE];
+#pragma unroll
+  for (int t = 0; t < NTILE; ++t) o[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int r0 = w * 64;
+  const uint32_t sel_base = (0x0Cu << 8) | (0x0Cu << 24);
+
+  for (int lb = b0; lb < b1; ++lb) {
+    const int phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + lb];
+    const uint8_t* tile = a.pool + ((size_t)phys * g.H + h) * g.tile_bytes;
+
+    // ------------------------------------------------------------ loads for this wave's 64 rows
+    uint32_t kraw[4][KW];
+    uint32_t kpar[4][NGK], vpar[4][NGV];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = r0 + 16 * c + lj;
+      const uint4* kp = reinterpret_cast<const uint4*>(tile + (size_t)row * (D / 2) + la * KW * 4);
+#pragma unroll
+      for (int q4 = 0; q4 < KW / 4; ++q4) {
+        const uint4 v4 = kp[q4];
+        kraw[c][4 * q4 + 0] = v4.x;
+        kraw[c][4 * q4 + 1] = v4.y;
+        kraw[c][4 * q4 + 2] = v4.z;
+        kraw[c][4 * q4 + 3] = v4.w;
+      }
+      const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.off_kp) + (size_t)row * NGK;
+      const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.off_vp) + (size_t)row * NGV;
+#pragma unroll
+      for (int gm = 0; gm < NGK; ++gm) kpar[c][gm] = kpp[gm];
+#pragma unroll
+      for (int gm = 0; gm < NGV; ++gm) vpar[c][gm] = vpp[gm];
+    }
+    // sentinel bits of this wave's 64 rows: two mask words (zero past the mask's end)
+    uint32_t mw0 = 0u, mw1 = 0u;
+    if (mask_row) {
+      const int w0 = (lb * kRows + r0) >> 5;
+      mw0 = w0 < a.mask_words ? mask_row[w0] : 0u;
+      mw1 = w0 + 1 < a.mask_words ? mask_row[w0 + 1] : 0u;
+    }
+    uint32_t vraw[2][8][VW];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = r0 + 32 * kb + 8 * la + e;
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(tile + g.off_vc + (size_t)row * (D / 2));
+#pragma unroll
+        for (int vw = 0; vw < VW; ++vw) vraw[kb][e][vw] = vp[lj + 16 * vw];
+      }
+
+    // ------------------------------------------------------------ logits: QK on the matrix cores
+    float sc[HPL][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KW; ++s) {
+        const uint32_t wd = kraw[c][s], w8 = wd >> 8;
+        const u32x4 b = {wd & 0x000F000Fu, wd & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+        acc = mfma16(qa_hi[s], b, acc);
+        acc = mfma16(qa_lo[s], b, acc);
+      }
+      const int pos = lb * kRows + r0 + 16 * c + lj;
+      const uint32_t mword = c < 2 ? mw0 : mw1;
+      const bool live = pos < len && !((mword >> ((16 * c + lj) & 31)) & 1u);
+#pragma unroll
+      for (int u = 0; u < HPL; ++u) {
+        float s_ = 0.0f;
+#pragma unroll
+        for (int gm = 0; gm < NGK; ++gm)
+          s_ += h2f(kpar[c][gm] & 0xffffu) * kTwo24 * acc[u * NGK + gm] + h2f(kpar[c][gm] >> 16) * qsum[u][gm];
+        sc[u][c] = (live && la * HPL + u < G) ? s_ : kNegInf;
+      }
+    }
+
+    // ------------------------------------------------------------ online softmax of this wave's rows
+    float p[HPL][4];
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      float mx = fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3]));
+      mx = row_max16(mx);
+      const float mnew = fmaxf(m_run[u], mx);
+      const float alpha = mnew == kNegInf ? 1.0f : exp2f(m_run[u] - mnew);
+      float ps = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        p[u][c] = sc[u][c] == kNegInf ? 0.0f : exp2f(sc[u][c] - mnew);
+        ps += p[u][c];
+      }
+      l_run[u] = l_run[u] * alpha + ps;
+      m_run[u] = mnew;
+#pragma unroll
+      for (int gm = 0; gm < NGV; ++gm) zacc[u][gm] *= alpha;
+#pragma unroll
+      for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+        for (int gm = 0; gm < NGV; ++gm) o[t][u * NGV + gm] *= alpha;
+    }
+
+    // p * v_scale to LDS (A operand of PV), p * v_zero into the per-lane zero term
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int u = 0; u < HPL; ++u) {
+        if (la * HPL + u >= G) continue;
+#pragma unroll
+        for (int gm = 0; gm < NGV; ++gm) {
+          const float pp = p[u][c];
+          const float pv = pp > 0.0f ? pp * h2f(vpar[c][gm] & 0xffffu) : 0.0f;
+          if (pp > 0.0f) zacc[u][gm] += pp * h2f(vpar[c][gm] >> 16);
+          const _Float16 pv_hi = (_Float16)pv;
+          s_p[w][0][la * 4 + u * NGV + gm][16 * c + lj] = pv_hi;
+          s_p[w][1][la * 4 + u * NGV + gm][16 * c + lj] = (_Float16)(pv - (float)pv_hi);
+        }
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ------------------------------------------------------------ PV on the matrix cores
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4 pa_hi = *reinterpret_cast<const u32x4*>(&s_p[w][0][lj][32 * kb + 8 * la]);
+      const u32x4 pa_lo = *reinterpret_cast<const u32x4*>(&s_p[w][1][lj][32 * kb + 8 * la]);
+#pragma unroll
+      for (int vw = 0; vw < VW; ++vw)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const uint32_t sel = sel_base | (uint32_t)bb | ((uint32_t)(4 + bb) << 16);
+          u32x4 blo, bhi;
+#pragma unroll
+          for (int pq = 0; pq < 4; ++pq) {
+            const uint32_t x = __builtin_amdgcn_perm(vraw[kb][2 * pq + 1][vw], vraw[kb][2 * pq][vw], sel);
+            blo[pq] = x & 0x000F000Fu;
+            bhi[pq] = x & 0x00F000F0u;
+          }
+          o[vw * 8 + 2 * bb] = mfma16(pa_hi, blo, o[vw * 8 + 2 * bb]);
+          o[vw * 8 + 2 * bb] = mfma16(pa_lo, blo, o[vw * 8 + 2 * bb]);
+          o[vw * 8 + 2 * bb + 1] = mfma16(pa_hi, bhi, o[vw * 8 + 2 * bb + 1]);
+          o[vw * 8 + 2 * bb + 1] = mfma16(pa_lo, bhi, o[vw * 8 + 2 * bb + 1]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---------------------------------------------------------------- merge the four waves
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) {
+    const float lt = row_sum16(l_run[u]);
+    float zt[NGV];
+#pragma unroll
+    for (int gm = 0; gm < NGV; ++gm) zt[gm] = row_sum16(zacc[u][gm]);
+    const int jj = la * HPL + u;
+    if (jj < G) {
+      if (lj == 0) {
+        s_wm[w][jj] = m_run[u];
+        s_wl[w][jj] = lt;
+      }
+#pragma unroll
+      for (int vw = 0; vw < VW; ++vw)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int c = vw * 128 + 8 * lj + m;
+          const int gc = c / VG;
+          float val = 0.0f;
+#pragma unroll
+          for (int gm = 0; gm < NGV; ++gm)
+            if (gm == gc) val = o[vw * 8 + m][u * NGV + gm] * ((m & 1) ? kTwo20 : kTwo24) + zt[gm];
+          s_wacc[w][jj][c] = val;
+        }
+    }
+  }
+  __syncthreads();
+  if (ns == 1) {
+    // the whole sequence was this workgroup's: finalise the rows here
+    __shared__ int s_cnt[4];
+    __shared__ float s_o[D];
+    const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
+    for (int jj = 0; jj < G; ++jj) {
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_wm[ww][jj]);
+      float acc = 0.0f, L = 0.0f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float sc_w = exp2f(s_wm[ww][jj] - M);
+          if (tid < D) acc += s_wacc[ww][jj][tid] * sc_w;
+          L += s_wl[ww][jj] * sc_w;
+        }
+      }
+      finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, M, L, acc, tid, s_o);
+    }
+    return;
+  }
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_wm[ww][jj]);
+    float acc = 0.0f, L = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float sc_w = exp2f(s_wm[ww][jj] - M);
+        acc += s_wacc[ww][jj][c] * sc_w;
+        L += s_wl[ww][jj] * sc_w;
+      }
+    }
+    const size_t pi = part0 + (size_t)jj * ns;
+    a.ws_acc[pi * D + c] = acc;
+    if (c == 0) {
+      a.ws_ml[2 * pi] = M;
+      a.ws_ml[2 * pi + 1] = L;
+    }
+  }
+}
+
+template <int D, int G, int KG, int VG>
+hipError_t launch_one(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mfma_k<D, G, KG, VG>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
+                     g, a);
+  if (a.plan.n_splits > 1)
+    hipLaunchKernelGGL(decode_reduce_k<D>, dim3(a.num_q_heads, a.n_seqs), dim3(D), 0, stream, g, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Layouts with a compiled matrix-core kernel: 4-bit pools (not mixed) with per-token K and V groups.
+bool decode_mfma_supported(const TileGeom& g, int G) {
+  if (g.mixed || g.kg <= 0) return false;
+  if (g.d == 128 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4 || G == 8;
+  if (g.d == 256 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4;
+  return false;
+}
+
+hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  if (g.d == 128) {
+    switch (a.G) {
+      case 1: return launch_one<128, 1, 64, 64>(g, a, stream);
+      case 2: return launch_one<128, 2, 64, 64>(g, a, stream);
+      case 4: return launch_one<128, 4, 64, 64>(g, a, stream);
+      case 8: return launch_one<128, 8, 64, 64>(g, a, stream);
+    }
+  } else if (g.d == 256) {
+    switch (a.G) {
+      case 1: return launch_one<256, 1, 64, 64>(g, a, stream);
+      case 2: return launch_one<256, 2, 64, 64>(g, a, stream);
+      case 4: return launch_one<256, 4, 64, 64>(g, a, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

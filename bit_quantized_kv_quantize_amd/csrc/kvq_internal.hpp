@@ -57,7 +57,6 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint32_t* mask;
   float* out;
-  unsigned* ws_ctr; // [n_seqs][H_kv] arrival counters, zero between calls
   float* ws_ml;   // [n_seqs][H_q][n_splits] x {m, l}
   float* ws_acc;  // [n_seqs][H_q][n_splits][d]
   int n_seqs;
@@ -69,6 +68,11 @@ struct DecodeArgs {
   float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale
   SplitPlan plan;
 };
+// Decode dispatch: the matrix-core kernel where its layout is compiled, the generic kernel otherwise
+// (or always, when the environment variable KVQ_FORCE_GENERIC_DECODE is set: a test hook).
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
+bool decode_mfma_supported(const TileGeom& g, int G);
+hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq
