@@ -146,10 +146,11 @@ def new_pool(layout: Layout, num_blocks: int, device="cuda"):
 
 
 def new_workspace(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: int, device="cuda"):
-    """A decode workspace for calls of this size or smaller (split-K partials; no initialisation needed)."""
+    """A zero-filled decode workspace for calls of this size or smaller (split-K partials and arrival
+    counters; every call leaves the counters at zero, so it can be reused without clearing)."""
     torch = _torch()
     need = decode_workspace_bytes(layout, n_seqs, num_q_heads, max_seq_len)
-    return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
 
 
 def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, stream=None) -> None:

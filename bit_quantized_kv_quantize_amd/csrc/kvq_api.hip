@@ -1,6 +1,7 @@
 // kvq_api.hip - the C ABI of libkvq: argument validation, tile geometry, split planning and launches.
 // Every entry point is declared and documented in include/kvq.h.
 #include <math.h>
+#include <stdlib.h>
 
 #include "kvq_internal.hpp"
 
@@ -44,15 +45,17 @@ TileGeom make_geom(const kvq_layout* L) {
 }
 
 SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
-  // One round of resident workgroups on MI355X (256 CUs x 3 decode workgroups each): split each
+  // One round of resident workgroups on MI355X (256 CUs x 2 decode workgroups each): split each
   // (sequence, KV head) so the grid fills that round without exceeding it, never below one block per split.
-  const long target_wgs = 256 * 3;
+  const long target_wgs = 256 * 2;
   int nb = (max_seq_len + kRows - 1) / kRows;
   if (nb < 1) nb = 1;
   long units = (long)(n_seqs > 0 ? n_seqs : 1) * g.H;
   long ns = target_wgs / units;
   if (ns < 1) ns = 1;
   if (ns > nb) ns = nb;
+  if (ns > 64) ns = 64;                                // at most 64 splits per (sequence, KV head)
+  if (ns < (nb + 511) / 512) ns = (nb + 511) / 512;  // a split owns at most 512 blocks
   int bps = (int)((nb + ns - 1) / ns);
   SplitPlan p;
   p.blocks_per_split = bps;
@@ -64,9 +67,10 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
   SplitPlan p = plan_splits(g, n_seqs, max_seq_len);
   size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
   size_t parts = ns * num_q_heads * p.n_splits;
+  size_t ctr = (ns * g.H * sizeof(unsigned) + 255) / 256 * 256;
   size_t ml = (parts * 2 * sizeof(float) + 255) / 256 * 256;
   size_t acc = (parts * g.d * sizeof(float) + 255) / 256 * 256;
-  return ml + acc;
+  return ctr + ml + acc;
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
@@ -168,8 +172,10 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.out = out;
   a.plan = plan_splits(g, n_seqs, max_seq_len);
   size_t parts = (size_t)n_seqs * num_q_heads * a.plan.n_splits;
-  a.ws_ml = (float*)workspace;
-  a.ws_acc = (float*)((uint8_t*)workspace + (parts * 2 * sizeof(float) + 255) / 256 * 256);
+  size_t ctr_bytes = ((size_t)n_seqs * g.H * sizeof(unsigned) + 255) / 256 * 256;
+  a.ws_ctr = (unsigned*)workspace;
+  a.ws_ml = (float*)((uint8_t*)workspace + ctr_bytes);
+  a.ws_acc = (float*)((uint8_t*)workspace + ctr_bytes + (parts * 2 * sizeof(float) + 255) / 256 * 256);
   a.n_seqs = n_seqs;
   a.num_q_heads = num_q_heads;
   a.G = G;

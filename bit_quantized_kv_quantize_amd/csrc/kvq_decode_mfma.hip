@@ -17,8 +17,8 @@
 //   rounding of the scaled operand would cost up to 2^-12 of scale * 15 per element.
 // * Each wave owns 64 rows of every block and keeps its own online softmax (16-lane DPP reductions, no
 //   block-wide barrier in the token loop); the four waves merge at the end of the split. With one split
-//   per (sequence, KV head) the workgroup finalises the output itself; otherwise it writes split-K
-//   partials for decode_reduce_k.
+//   per (sequence, KV head) the workgroup finalises the output itself; otherwise the split that arrives
+//   last merges all splits' partials (splitk_arrive) - one kernel per call either way.
 #include "kvq_decode_common.hpp"
 
 namespace kvq {
@@ -60,7 +60,86 @@ __device__ __forceinline__ float row_sum16(float v) {
 }
 
 constexpr float kTwo24 = 16777216.0f;
+constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table slice is staged in LDS)
+constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) (their (m, l) are staged in LDS)
 constexpr float kTwo20 = 1048576.0f;
+
+// Split-K arrival for split `split` of (seq, h) once its partials (m, l, acc[d]) per query head are
+// ready: thread jj * D + c (and ml for c == 0) holds them in part_m / part_l / part_acc. The partials are
+// written with relaxed agent-scope atomic stores, which compile to cache-coherent (sc1) stores, so no
+// L2 write-back is needed; every thread waits for its stores to complete before the barrier, then one
+// thread bumps the unit's arrival counter. The split that arrives last reads all partials back with
+// agent-scope atomic loads (sc1, coherent across XCDs), merges them in split order - so the result does
+// not depend on which split that is - finalises the output and resets the counter to zero.
+template <int D, int G>
+__device__ void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int len, int tid,
+                              const float* part_m, const float* part_l, const float* part_acc, float* s_o) {
+  __shared__ int s_last;
+  __shared__ int s_cnt[4];
+  const int ns = a.plan.n_splits;
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + split;
+    __hip_atomic_store(&a.ws_acc[pi * D + c], part_acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c == 0) {
+      __hip_atomic_store(&a.ws_ml[2 * pi], part_m[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ws_ml[2 * pi + 1], part_l[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    unsigned* ctr = a.ws_ctr + (size_t)seq * g.H + h;
+    const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(ns - 1);
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Merge: one round of parallel loads stages every split's (m, l), the per-head weights follow in LDS,
+  // then one round of independent loads fetches the accumulators.
+  __shared__ float s_sm[G][kMaxSplits], s_sw[G][kMaxSplits];
+  __shared__ float s_hM[G], s_hL[G];
+  for (int i = tid; i < G * ns; i += 256) {
+    const int jj = i / ns, sp = i % ns;
+    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + sp;
+    const float li = __hip_atomic_load(&a.ws_ml[2 * pi + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mi = __hip_atomic_load(&a.ws_ml[2 * pi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_sm[jj][sp] = li > 0.0f ? mi : kNegInf;
+    s_sw[jj][sp] = li;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegInf;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_sm[tid][sp]);
+    float L = 0.0f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float wgt = s_sm[tid][sp] == kNegInf ? 0.0f : exp2f(s_sm[tid][sp] - M);
+      L += s_sw[tid][sp] * wgt;
+      s_sw[tid][sp] = wgt;
+    }
+    s_hM[tid] = M;
+    s_hL[tid] = L;
+  }
+  __syncthreads();
+  float* s_merged = const_cast<float*>(part_acc);  // this split's own partials are no longer needed
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * ns;
+    float o = 0.0f;
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float x = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      o += s_sw[jj][sp] != 0.0f ? x * s_sw[jj][sp] : 0.0f;  // unwritten accumulators are selected away
+    }
+    s_merged[i] = o;
+  }
+  __syncthreads();
+  const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
+  for (int jj = 0; jj < G; ++jj)
+    finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, s_hM[jj], s_hL[jj], tid < D ? s_merged[jj * D + tid] : 0.0f,
+                          tid, s_o);
+}
 
 // Grid (n_splits, H_kv, n_seqs), 256 threads = 4 waves; wave w owns rows 64w .. 64w+63 of each block.
 template <int D, int G, int KG, int VG>
@@ -80,6 +159,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][2][16][PSTR];  // [wave][hi, lo][row][token]
   __shared__ float s_wm[4][G], s_wl[4][G];
   __shared__ float s_wacc[4][G][D];
+  __shared__ int s_tbl[kMaxSplitBlocks];
+  __shared__ uint32_t s_mask[kMaxSplitBlocks * (kRows / 32)];
 
   const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
@@ -97,14 +178,74 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
       const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt0);
       for (int jj = 0; jj < G; ++jj)
         finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, kNegInf, 0.0f, 0.0f, tid, &s_wacc[0][0][0]);
-    } else if (tid < G) {
-      a.ws_ml[2 * (part0 + (size_t)tid * ns)] = kNegInf;
-      a.ws_ml[2 * (part0 + (size_t)tid * ns) + 1] = 0.0f;
+    } else {
+      if (tid < G) {
+        s_wm[0][tid] = kNegInf;
+        s_wl[0][tid] = 0.0f;
+      }
+      for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
+      __syncthreads();
+      splitk_arrive<D, G>(g, a, seq, h, split, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
+                          &s_wacc[0][0][0]);
     }
     return;
   }
 
-  // ---------------------------------------------------------------- query operands
+  const int r0 = w * 64;
+  // Raw codes and parameters of one block for this wave's 64 rows. Two sets alternate so the loads of
+  // block lb + 1 are in flight while block lb is computed.
+  struct Raw {
+    uint32_t kraw[4][KW];
+    uint32_t kpar[4][NGK], vpar[4][NGV];
+    uint32_t vraw[2][8][VW];
+  };
+  // Every load of the loop is unconditional and only fetches codes and parameters (the block table and
+  // sentinel words of the split sit in LDS): with straight-line loads the compiler waits only for the
+  // block being computed.
+  auto load = [&](Raw& r, int phys) __attribute__((always_inline)) {
+    const uint8_t* tile = a.pool + ((size_t)phys * g.H + h) * g.tile_bytes;
+    // ------------------------------------------------------------ loads for this wave's 64 rows
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int row = r0 + 16 * c + lj;
+      const uint4* kp = reinterpret_cast<const uint4*>(tile + (size_t)row * (D / 2) + la * KW * 4);
+#pragma unroll
+      for (int q4 = 0; q4 < KW / 4; ++q4) {
+        const uint4 v4 = kp[q4];
+        r.kraw[c][4 * q4 + 0] = v4.x;
+        r.kraw[c][4 * q4 + 1] = v4.y;
+        r.kraw[c][4 * q4 + 2] = v4.z;
+        r.kraw[c][4 * q4 + 3] = v4.w;
+      }
+      const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.off_kp) + (size_t)row * NGK;
+      const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.off_vp) + (size_t)row * NGV;
+#pragma unroll
+      for (int gm = 0; gm < NGK; ++gm) r.kpar[c][gm] = kpp[gm];
+#pragma unroll
+      for (int gm = 0; gm < NGV; ++gm) r.vpar[c][gm] = vpp[gm];
+    }
+    // sentinel bits of this wave's 64 rows: two mask words (zero past the mask's end)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = r0 + 32 * kb + 8 * la + e;
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(tile + g.off_vc + (size_t)row * (D / 2));
+#pragma unroll
+        for (int vw = 0; vw < VW; ++vw) r.vraw[kb][e][vw] = vp[lj + 16 * vw];
+      }
+
+  };
+  // The first block's codes are requested before the query set-up, so their latency overlaps it.
+  Raw ra, rb;
+  load(ra, a.block_table[(size_t)seq * a.max_blocks_per_seq + b0]);
+
+  // ---------------------------------------------------------------- block table and query operands
+  for (int i = tid; i < b1 - b0; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
+  if (mask_row) {  // sentinel words of this split's slots (zero past the mask's end)
+    const int wbase = b0 * (kRows / 32), nw = (b1 - b0) * (kRows / 32);
+    for (int i = tid; i < nw; i += 256) s_mask[i] = wbase + i < a.mask_words ? mask_row[wbase + i] : 0u;
+  }
   for (int i = tid; i < G * D; i += 256)
     s_q[i / D][i % D] = h2f(a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D]) * a.q_scale;
   for (int i = tid; i < 4 * 2 * 16 * PSTR; i += 256) (&s_p[0][0][0][0])[i] = (_Float16)0.0f;
@@ -176,117 +317,97 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
   floatx4 o[NTILE];
 #pragma unroll
   for (int t = 0; t < NTILE; ++t) o[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float alpha_u[HPL];
 
-  const int r0 = w * 64;
   const uint32_t sel_base = (0x0Cu << 8) | (0x0Cu << 24);
 
-  for (int lb = b0; lb < b1; ++lb) {
-    const int phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + lb];
-    const uint8_t* tile = a.pool + ((size_t)phys * g.H + h) * g.tile_bytes;
-
-    // ------------------------------------------------------------ loads for this wave's 64 rows
-    uint32_t kraw[4][KW];
-    uint32_t kpar[4][NGK], vpar[4][NGV];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int row = r0 + 16 * c + lj;
-      const uint4* kp = reinterpret_cast<const uint4*>(tile + (size_t)row * (D / 2) + la * KW * 4);
-#pragma unroll
-      for (int q4 = 0; q4 < KW / 4; ++q4) {
-        const uint4 v4 = kp[q4];
-        kraw[c][4 * q4 + 0] = v4.x;
-        kraw[c][4 * q4 + 1] = v4.y;
-        kraw[c][4 * q4 + 2] = v4.z;
-        kraw[c][4 * q4 + 3] = v4.w;
-      }
-      const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.off_kp) + (size_t)row * NGK;
-      const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.off_vp) + (size_t)row * NGV;
-#pragma unroll
-      for (int gm = 0; gm < NGK; ++gm) kpar[c][gm] = kpp[gm];
-#pragma unroll
-      for (int gm = 0; gm < NGV; ++gm) vpar[c][gm] = vpp[gm];
-    }
-    // sentinel bits of this wave's 64 rows: two mask words (zero past the mask's end)
-    uint32_t mw0 = 0u, mw1 = 0u;
-    if (mask_row) {
-      const int w0 = (lb * kRows + r0) >> 5;
-      mw0 = w0 < a.mask_words ? mask_row[w0] : 0u;
-      mw1 = w0 + 1 < a.mask_words ? mask_row[w0 + 1] : 0u;
-    }
-    uint32_t vraw[2][8][VW];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = r0 + 32 * kb + 8 * la + e;
-        const uint32_t* vp = reinterpret_cast<const uint32_t*>(tile + g.off_vc + (size_t)row * (D / 2));
-#pragma unroll
-        for (int vw = 0; vw < VW; ++vw) vraw[kb][e][vw] = vp[lj + 16 * vw];
-      }
-
+  auto process = [&](const Raw& r, int lb) __attribute__((always_inline)) {
     // ------------------------------------------------------------ logits: QK on the matrix cores
+    // The four 16-token chunks accumulate side by side (independent MFMA chains).
+    floatx4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KW; ++s)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t wd = r.kraw[c][s], w8 = wd >> 8;
+        const u32x4 b = {wd & 0x000F000Fu, wd & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+        acc[c] = mfma16(qa_hi[s], b, acc[c]);
+        acc[c] = mfma16(qa_lo[s], b, acc[c]);
+      }
     float sc[HPL][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < KW; ++s) {
-        const uint32_t wd = kraw[c][s], w8 = wd >> 8;
-        const u32x4 b = {wd & 0x000F000Fu, wd & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
-        acc = mfma16(qa_hi[s], b, acc);
-        acc = mfma16(qa_lo[s], b, acc);
-      }
       const int pos = lb * kRows + r0 + 16 * c + lj;
-      const uint32_t mword = c < 2 ? mw0 : mw1;
+      const uint32_t mword = mask_row ? s_mask[(lb - b0) * (kRows / 32) + (r0 >> 5) + (c >> 1)] : 0u;
       const bool live = pos < len && !((mword >> ((16 * c + lj) & 31)) & 1u);
 #pragma unroll
       for (int u = 0; u < HPL; ++u) {
-        float s_ = 0.0f;
+        float dotq = 0.0f, zq = 0.0f;
 #pragma unroll
-        for (int gm = 0; gm < NGK; ++gm)
-          s_ += h2f(kpar[c][gm] & 0xffffu) * kTwo24 * acc[u * NGK + gm] + h2f(kpar[c][gm] >> 16) * qsum[u][gm];
-        sc[u][c] = (live && la * HPL + u < G) ? s_ : kNegInf;
+        for (int gm = 0; gm < NGK; ++gm) {
+          dotq += h2f(r.kpar[c][gm] & 0xffffu) * acc[c][u * NGK + gm];
+          zq += h2f(r.kpar[c][gm] >> 16) * qsum[u][gm];
+        }
+        const bool head_ok = (G % 4 == 0) || (la * HPL + u < G);
+        sc[u][c] = (live && head_ok) ? dotq * kTwo24 + zq : kNegInf;
       }
     }
 
     // ------------------------------------------------------------ online softmax of this wave's rows
     float p[HPL][4];
+    bool rescale = false;
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
       float mx = fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3]));
       mx = row_max16(mx);
       const float mnew = fmaxf(m_run[u], mx);
-      const float alpha = mnew == kNegInf ? 1.0f : exp2f(m_run[u] - mnew);
+      const float alpha = mnew == m_run[u] ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - mnew);
+      rescale |= alpha != 1.0f;
       float ps = 0.0f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        p[u][c] = sc[u][c] == kNegInf ? 0.0f : exp2f(sc[u][c] - mnew);
+        p[u][c] = __builtin_amdgcn_exp2f(sc[u][c] - mnew);  // -inf - finite -> 0; an all-dead row keeps 0
+        p[u][c] = mnew == kNegInf ? 0.0f : p[u][c];
         ps += p[u][c];
       }
       l_run[u] = l_run[u] * alpha + ps;
       m_run[u] = mnew;
+      alpha_u[u] = alpha;
+    }
+    if (__builtin_amdgcn_ballot_w64(rescale)) {  // wave-uniform: skip when no running max moved
 #pragma unroll
-      for (int gm = 0; gm < NGV; ++gm) zacc[u][gm] *= alpha;
+      for (int u = 0; u < HPL; ++u) {
 #pragma unroll
-      for (int t = 0; t < NTILE; ++t)
+        for (int gm = 0; gm < NGV; ++gm) zacc[u][gm] *= alpha_u[u];
 #pragma unroll
-        for (int gm = 0; gm < NGV; ++gm) o[t][u * NGV + gm] *= alpha;
+        for (int t = 0; t < NTILE; ++t)
+#pragma unroll
+          for (int gm = 0; gm < NGV; ++gm) o[t][u * NGV + gm] *= alpha_u[u];
+      }
     }
 
-    // p * v_scale to LDS (A operand of PV), p * v_zero into the per-lane zero term
+    // p * v_scale to LDS (A operand of PV), p * v_zero into the per-lane zero term. Dead slots have p = 0
+    // and their (possibly uninitialised) parameters are selected away, never multiplied.
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int u = 0; u < HPL; ++u) {
-        if (la * HPL + u >= G) continue;
 #pragma unroll
         for (int gm = 0; gm < NGV; ++gm) {
           const float pp = p[u][c];
-          const float pv = pp > 0.0f ? pp * h2f(vpar[c][gm] & 0xffffu) : 0.0f;
-          if (pp > 0.0f) zacc[u][gm] += pp * h2f(vpar[c][gm] >> 16);
+          const bool on = pp != 0.0f;
+          const float vs = on ? h2f(r.vpar[c][gm] & 0xffffu) : 0.0f;
+          const float vz = on ? h2f(r.vpar[c][gm] >> 16) : 0.0f;
+          const float pv = pp * vs;
+          zacc[u][gm] += pp * vz;
           const _Float16 pv_hi = (_Float16)pv;
-          s_p[w][0][la * 4 + u * NGV + gm][16 * c + lj] = pv_hi;
-          s_p[w][1][la * 4 + u * NGV + gm][16 * c + lj] = (_Float16)(pv - (float)pv_hi);
+          const int row = la * 4 + u * NGV + gm;
+          if ((G % 4 == 0) || (la * HPL + u < G)) {
+            s_p[w][0][row][16 * c + lj] = pv_hi;
+            s_p[w][1][row][16 * c + lj] = (_Float16)(pv - (float)pv_hi);
+          }
         }
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -306,7 +427,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
           u32x4 blo, bhi;
 #pragma unroll
           for (int pq = 0; pq < 4; ++pq) {
-            const uint32_t x = __builtin_amdgcn_perm(vraw[kb][2 * pq + 1][vw], vraw[kb][2 * pq][vw], sel);
+            const uint32_t x = __builtin_amdgcn_perm(r.vraw[kb][2 * pq + 1][vw], r.vraw[kb][2 * pq][vw], sel);
             blo[pq] = x & 0x000F000Fu;
             bhi[pq] = x & 0x00F000F0u;
           }
@@ -317,6 +438,18 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
         }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  const int blast = b1 - 1;
+  for (int lb = b0; lb < b1; lb += 2) {
+    // sched_barrier keeps the next block's loads ahead of this block's arithmetic, so they are in flight
+    // while it runs (the scheduler would otherwise sink them below the first MFMAs)
+    load(rb, s_tbl[min(lb + 1, blast) - b0]);  // past the end: reloads the last block (an L2 hit), unused
+    __builtin_amdgcn_sched_barrier(0);
+    process(ra, lb);
+    if (lb + 1 >= b1) break;
+    load(ra, s_tbl[min(lb + 2, blast) - b0]);
+    __builtin_amdgcn_sched_barrier(0);
+    process(rb, lb + 1);
   }
 
   // ---------------------------------------------------------------- merge the four waves
@@ -369,6 +502,9 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
     }
     return;
   }
+  // merge the four waves into this split's partials (staged in LDS), then arrive
+  __shared__ float s_pm[G], s_pl[G];
+  __shared__ float s_pacc[G][D];
   for (int i = tid; i < G * D; i += 256) {
     const int jj = i / D, c = i % D;
     float M = kNegInf;
@@ -383,21 +519,21 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
         L += s_wl[ww][jj] * sc_w;
       }
     }
-    const size_t pi = part0 + (size_t)jj * ns;
-    a.ws_acc[pi * D + c] = acc;
+    s_pacc[jj][c] = acc;
     if (c == 0) {
-      a.ws_ml[2 * pi] = M;
-      a.ws_ml[2 * pi + 1] = L;
+      s_pm[jj] = M;
+      s_pl[jj] = L;
     }
   }
+  __syncthreads();
+  splitk_arrive<D, G>(g, a, seq, h, split, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 
 template <int D, int G, int KG, int VG>
 hipError_t launch_one(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_mfma_k<D, G, KG, VG>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
                      g, a);
-  if (a.plan.n_splits > 1)
-    hipLaunchKernelGGL(decode_reduce_k<D>, dim3(a.num_q_heads, a.n_seqs), dim3(D), 0, stream, g, a);
+
   return hipGetLastError();
 }
 

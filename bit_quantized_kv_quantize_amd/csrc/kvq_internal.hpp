@@ -57,6 +57,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint32_t* mask;
   float* out;
+  unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernel); zero between calls
   float* ws_ml;   // [n_seqs][H_q][n_splits] x {m, l}
   float* ws_acc;  // [n_seqs][H_q][n_splits][d]
   int n_seqs;

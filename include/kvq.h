@@ -162,9 +162,11 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
  *   out            device fp32 [n_seqs][num_q_heads][d]: softmax-weighted sum of the dequantised (and,
  *                  for rotated pools, un-rotated) V rows. A sequence with seq_lens[s] == 0 gets zeros.
  *   workspace      device scratch of at least kvq_decode_workspace_bytes(L, n_seqs, num_q_heads,
- *                  max_seq_len) bytes, 256-byte aligned, for the split-K partials; its contents need
- *                  no initialisation and are scratch afterwards. Calls sharing one workspace must not
- *                  overlap on the device.
+ *                  max_seq_len) bytes, 256-byte aligned: split-K partials and, in its first
+ *                  n_seqs * H_kv * 4 bytes, per-(sequence, KV head) arrival counters. Zero-fill it once
+ *                  before its first use; every completed call leaves the counters at zero again, so the
+ *                  same workspace serves later calls of the same or smaller size without clearing.
+ *                  Calls sharing one workspace must not overlap on the device.
  * Errors: KVQ_ERR_ARG (also n_seqs > 65535), KVQ_ERR_UNSUPPORTED (more than 16 query heads per
  * KV head), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP.
  */
