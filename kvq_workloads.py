@@ -276,6 +276,68 @@ def sequence_blocks(case: Case, s: int) -> np.ndarray:
     return case.block_table[s, : (int(case.context[s]) + BLOCK - 1) // BLOCK]
 
 
+def prefill_chunks(case: Case, layer: int, max_blocks: int = 2048, threads: int = 8,
+                   prec_out: Optional[np.ndarray] = None):
+    """Yield (block_ids, K, V, bitmaps) chunks that together cover every prefill block of ``case`` once,
+    each chunk at most ``max_blocks`` blocks (one sequence more for mixed pools), so a full-size pool can
+    be filled without holding all of its fp16 source at once.
+
+    For mixed pools ``bitmaps`` is the uint32 [n][8] precision bitmap of the chunk's blocks (the same
+    per-sequence ranking as ``mixed_precision_inputs``) and, if ``prec_out`` is given, the width of each
+    sequence's appended token is written into it; otherwise ``bitmaps`` is None."""
+    cfg = case.cfg
+    if not cfg.mixed:
+        ids = case.prefill_blocks
+        for i in range(0, ids.size, max_blocks):
+            chunk = ids[i:i + max_blocks]
+            k, v = blocks_kv(cfg, layer, chunk, threads)
+            yield chunk, k, v, None
+        return
+    ak = append_kv(cfg, layer, case.n_seqs)[0] if (case.append and prec_out is not None) else None
+    outl = outlier_channels(cfg, layer)
+    s0 = 0
+    while s0 < case.n_seqs:
+        seqs, n_blk = [], 0
+        while s0 < case.n_seqs and (not seqs or n_blk < max_blocks):
+            seqs.append(s0)
+            n_blk += sequence_blocks(case, s0).size
+            s0 += 1
+        if prec_out is not None:
+            prec_out[seqs] = 4
+        if n_blk == 0:
+            continue
+        ids = np.concatenate([sequence_blocks(case, s) for s in seqs]).astype(np.int32)
+        k = np.empty((n_blk * BLOCK, cfg.num_kv_heads, cfg.head_dim), np.uint16)
+        v = np.empty_like(k)
+        norms = np.empty(n_blk * BLOCK, np.float64)
+
+        def one(i):
+            kb, vb = block_kv(cfg, layer, int(ids[i]), outl)
+            k[i * BLOCK:(i + 1) * BLOCK] = kb
+            v[i * BLOCK:(i + 1) * BLOCK] = vb
+            norms[i * BLOCK:(i + 1) * BLOCK] = k_norms_sq(kb)
+
+        if threads > 1:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(one, range(n_blk)))
+        else:
+            for i in range(n_blk):
+                one(i)
+        bitmaps = np.empty((n_blk, 8), np.uint32)
+        off = 0
+        for s in seqs:
+            nb = sequence_blocks(case, s).size
+            n = int(case.context[s])
+            ns = norms[off * BLOCK: off * BLOCK + n]
+            sel = np.zeros(nb * BLOCK, bool)
+            sel[:n] = precision_map(ns, cfg.top_fraction)
+            bitmaps[off: off + nb] = bits_words(sel)
+            if ak is not None and nb:
+                prec_out[s] = 8 if appended_is_8bit(ns, float(k_norms_sq(ak[s:s + 1])[0]), cfg.top_fraction) else 4
+            off += nb
+        yield ids, k, v, bitmaps
+
+
 def mixed_precision_inputs(case: Case, layer: int, threads: int = 8):
     """For a mixed pool: per prefill block the uint32[8] precision bitmap (aligned with
     case.prefill_blocks) and per sequence the 4/8 width of its appended token.

@@ -53,3 +53,27 @@ def test_sentinel_mask_exact_count_and_precision_map():
     assert W.appended_is_8bit(norms, norms[19], 0.2) and not W.appended_is_8bit(norms, norms[19] - 0.5, 0.2)
     words = W.bits_words(np.arange(512) % 3 == 0)
     assert words.shape == (2, 8) and (words[0, 0] & 1) == 1 and ((words[0, 0] >> 1) & 1) == 0
+
+
+def test_prefill_chunks_cover_every_block_once():
+    for name, kw in [("llama31_8b_pool_8k", dict(n_seqs=3, context=[1000, 513, 0])),
+                     ("mixed_sentinel_32k", dict(n_seqs=4, context=[1024, 600, 0, 333]))]:
+        case = W.make_case(W.CONFIGS[name], **kw)
+        prec = np.zeros(case.n_seqs, np.uint8)
+        ids, ks, bms = [], [], []
+        for chunk, k, v, bm in W.prefill_chunks(case, 0, max_blocks=3, threads=2, prec_out=prec):
+            assert k.shape == v.shape == (chunk.size * W.BLOCK, 8, 128)
+            ids.append(chunk)
+            ks.append(k)
+            bms.append(bm)
+        ids = np.concatenate(ids)
+        assert np.array_equal(np.sort(ids), case.prefill_blocks)
+        order = np.argsort(ids)
+        k_ref, _ = W.blocks_kv(case.cfg, 0, case.prefill_blocks)
+        assert np.array_equal(np.concatenate(ks).reshape(ids.size, W.BLOCK, 8, 128)[order].reshape(k_ref.shape), k_ref)
+        if case.cfg.mixed:
+            bm_ref, prec_ref = W.mixed_precision_inputs(case, 0)
+            assert np.array_equal(np.concatenate(bms)[order], bm_ref)
+            assert np.array_equal(prec, prec_ref)
+        else:
+            assert all(b is None for b in bms)
