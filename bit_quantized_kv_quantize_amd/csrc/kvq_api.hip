@@ -63,14 +63,25 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
   return p;
 }
 
-size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
+WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   SplitPlan p = plan_splits(g, n_seqs, max_seq_len);
   size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
   size_t parts = ns * num_q_heads * p.n_splits;
-  size_t ctr = (ns * g.H * sizeof(unsigned) + 255) / 256 * 256;
-  size_t ml = (parts * 2 * sizeof(float) + 255) / 256 * 256;
-  size_t acc = (parts * g.d * sizeof(float) + 255) / 256 * 256;
-  return ctr + ml + acc;
+  WorkspaceLayout w{};
+  w.ctr = 0;
+  w.ml = up(ns * g.H * sizeof(unsigned));
+  w.acc = w.ml + up(parts * 2 * sizeof(float));
+  w.cnt = w.acc + up(parts * g.d * sizeof(float));
+  w.list = w.cnt + up(ns * 2 * sizeof(int));
+  // row lists only for layouts the row-list kernel reads
+  w.list_cap = decode_rows_supported(g, num_q_heads / g.H) ? (max_seq_len + 63) / 64 * 64 : 0;
+  w.total = w.list + up(ns * 2 * (size_t)w.list_cap * sizeof(uint32_t));
+  return w;
+}
+
+size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
+  return workspace_layout(g, n_seqs, num_q_heads, max_seq_len).total;
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
@@ -171,11 +182,14 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.mask = sentinel_mask;
   a.out = out;
   a.plan = plan_splits(g, n_seqs, max_seq_len);
-  size_t parts = (size_t)n_seqs * num_q_heads * a.plan.n_splits;
-  size_t ctr_bytes = ((size_t)n_seqs * g.H * sizeof(unsigned) + 255) / 256 * 256;
-  a.ws_ctr = (unsigned*)workspace;
-  a.ws_ml = (float*)((uint8_t*)workspace + ctr_bytes);
-  a.ws_acc = (float*)((uint8_t*)workspace + ctr_bytes + (parts * 2 * sizeof(float) + 255) / 256 * 256);
+  const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
+  uint8_t* ws = (uint8_t*)workspace;
+  a.ws_ctr = (unsigned*)(ws + wl.ctr);
+  a.ws_ml = (float*)(ws + wl.ml);
+  a.ws_acc = (float*)(ws + wl.acc);
+  a.ws_cnt = (int*)(ws + wl.cnt);
+  a.ws_list = (uint32_t*)(ws + wl.list);
+  a.list_cap = wl.list_cap;
   a.n_seqs = n_seqs;
   a.num_q_heads = num_q_heads;
   a.G = G;

@@ -14,6 +14,7 @@
 // Every split writes its partials (m, l, acc[d]) per query head; decode_reduce_k merges them in split
 // order in a second kernel (the kernel boundary makes the partials visible across the chip's XCDs).
 #include <stdlib.h>
+#include <string.h>
 
 #include "kvq_decode_common.hpp"
 
@@ -283,7 +284,11 @@ hipError_t launch_d(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  if (!getenv("KVQ_FORCE_GENERIC_DECODE") && decode_mfma_supported(g, a.G)) return launch_decode_mfma(g, a, stream);
+  const char* force = getenv("KVQ_DECODE_KERNEL");
+  const bool generic = force && !strcmp(force, "generic");
+  const bool mfma = force && !strcmp(force, "mfma");
+  if (!generic && !mfma && decode_rows_supported(g, a.G)) return launch_decode_rows(g, a, stream);
+  if (!generic && decode_mfma_supported(g, a.G)) return launch_decode_mfma(g, a, stream);
   return launch_decode_generic(g, a, stream);
 }
 

@@ -1,0 +1,126 @@
+// kvq_decode_mfma_common.hpp - matrix-core helpers shared by the decode kernels: MFMA and DPP wrappers,
+// and the in-kernel split-K merge (the split that arrives last merges every split's partials).
+#pragma once
+
+#include "kvq_decode_common.hpp"
+
+namespace kvq {
+namespace dec {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c,
+                                                0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Row (16-lane) reductions via DPP row rotations: every lane of the row ends with the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<0x128>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x122>(v));
+  v = fmaxf(v, dpp<0x121>(v));
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x122>(v);
+  v += dpp<0x121>(v);
+  return v;
+}
+
+constexpr float kTwo24 = 16777216.0f;
+constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table slice is staged in LDS)
+constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) (their (m, l) are staged in LDS)
+constexpr float kTwo20 = 1048576.0f;
+
+// Split-K arrival for split `split` of (seq, h) once its partials (m, l, acc[d]) per query head are
+// ready: thread jj * D + c (and ml for c == 0) holds them in part_m / part_l / part_acc. The partials are
+// written with relaxed agent-scope atomic stores, which compile to cache-coherent (sc1) stores, so no
+// L2 write-back is needed; every thread waits for its stores to complete before the barrier, then one
+// thread bumps the unit's arrival counter. The split that arrives last reads all partials back with
+// agent-scope atomic loads (sc1, coherent across XCDs), merges them in split order - so the result does
+// not depend on which split that is - finalises the output and resets the counter to zero.
+template <int D, int G>
+__device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int len, int tid,
+                              const float* part_m, const float* part_l, const float* part_acc, float* s_o) {
+  __shared__ int s_last;
+  __shared__ int s_cnt[4];
+  const int ns = a.plan.n_splits;
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + split;
+    __hip_atomic_store(&a.ws_acc[pi * D + c], part_acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c == 0) {
+      __hip_atomic_store(&a.ws_ml[2 * pi], part_m[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&a.ws_ml[2 * pi + 1], part_l[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    unsigned* ctr = a.ws_ctr + (size_t)seq * g.H + h;
+    const unsigned prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)(ns - 1);
+    if (s_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Merge: one round of parallel loads stages every split's (m, l), the per-head weights follow in LDS,
+  // then one round of independent loads fetches the accumulators.
+  __shared__ float s_sm[G][kMaxSplits], s_sw[G][kMaxSplits];
+  __shared__ float s_hM[G], s_hL[G];
+  for (int i = tid; i < G * ns; i += 256) {
+    const int jj = i / ns, sp = i % ns;
+    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + sp;
+    const float li = __hip_atomic_load(&a.ws_ml[2 * pi + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float mi = __hip_atomic_load(&a.ws_ml[2 * pi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_sm[jj][sp] = li > 0.0f ? mi : kNegInf;
+    s_sw[jj][sp] = li;
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegInf;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_sm[tid][sp]);
+    float L = 0.0f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float wgt = s_sm[tid][sp] == kNegInf ? 0.0f : exp2f(s_sm[tid][sp] - M);
+      L += s_sw[tid][sp] * wgt;
+      s_sw[tid][sp] = wgt;
+    }
+    s_hM[tid] = M;
+    s_hL[tid] = L;
+  }
+  __syncthreads();
+  float* s_merged = const_cast<float*>(part_acc);  // this split's own partials are no longer needed
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * ns;
+    float o = 0.0f;
+#pragma unroll 4
+    for (int sp = 0; sp < ns; ++sp) {
+      const float x = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      o += s_sw[jj][sp] != 0.0f ? x * s_sw[jj][sp] : 0.0f;  // unwritten accumulators are selected away
+    }
+    s_merged[i] = o;
+  }
+  __syncthreads();
+  const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
+  for (int jj = 0; jj < G; ++jj)
+    finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, s_hM[jj], s_hL[jj], tid < D ? s_merged[jj * D + tid] : 0.0f,
+                          tid, s_o);
+}
+
+}  // namespace dec
+}  // namespace kvq

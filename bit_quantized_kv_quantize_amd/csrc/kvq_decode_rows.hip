@@ -1,0 +1,567 @@
+// kvq_decode_rows.hip - decode attention on the matrix cores for head_dim 128 pools with per-token K and V
+// groups of 64 and GQA ratios 1, 2 and 4 (single-token decode attention over the packed cache of "Agent
+// Memory Below the Prompt", technical summary 2.1-2.2, with the sentinel slots of the IntentKV article and
+// the per-token bit widths of QKVShare's methodology).
+//
+// Work unit: a chunk of live rows of one (sequence, KV head) - 64 rows of 4-bit codes or 32 rows of 8-bit
+// codes, about 4 KB of codes either way. Pure 4-bit pools without sentinel slots are read block by block
+// (each wave takes 64 rows of every block of its split). Pools with sentinel slots or mixed widths are read
+// as compacted row lists built by compact_rows_k: per sequence, the live 4-bit rows and the live 8-bit rows
+// in slot order, so every chunk is of one width and sentinel rows are never fetched.
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_f16 throughout):
+// * MFMA row r = 4 h + 2 gamma + part: query head h, K (or V) group gamma, part 0/1 = fp16 hi/lo of the
+//   operand. The hi and lo halves of the query and of p * v_scale share one MFMA (rows, not passes), so each
+//   16-token slice of K costs one MFMA per 32 channels.
+// * QK: B = K codes of 16 tokens (lane = token), unpacked without arithmetic: masking a packed word with
+//   0x000F000F leaves two nibbles as fp16 subnormals n * 2^-24 (0x00F000F0 gives 16 n * 2^-24); 8-bit codes
+//   are paired with byte permutes (bytes are exact subnormals too). The 2^24 and 1/16 factors fold into the
+//   group scales and the query.
+// * PV: V rows are staged in LDS as loaded (lane = token) and read back transposed with the gfx950 LDS
+//   transpose loads (16 nibbles or 8 bytes per lane, one output channel per lane), so the B operand of
+//   32 tokens x 16 channels needs no per-element shuffling. The A operand (p * v_scale as hi/lo, one row per
+//   (head, V group, part)) is written position-major and read with the 16-bit transpose load.
+// Online softmax per wave (16-lane DPP reductions), the four waves merge at the end, and the split-K merge
+// runs in the split that arrives last (splitk_arrive).
+#include <type_traits>
+
+#include "kvq_decode_mfma_common.hpp"
+
+namespace kvq {
+namespace {
+
+using namespace dec;
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+__device__ __forceinline__ v2i lds_tr4(const void* p) {
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_v2i*)const_cast<void*>(p));
+}
+__device__ __forceinline__ v2i lds_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)const_cast<void*>(p));
+}
+__device__ __forceinline__ v2i lds_tr16(const void* p) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)const_cast<void*>(p)));
+}
+
+constexpr uint32_t kLo4 = 0x000F000Fu, kHi4 = 0x00F000F0u;
+// byte permute selector: bytes m and m + 4 of {hi:lo} into the low bytes of the two fp16 halves
+__device__ __forceinline__ uint32_t pair_sel(int m) {
+  return (uint32_t)m | (0x0Cu << 8) | ((uint32_t)(4 + m) << 16) | (0x0Cu << 24);
+}
+
+constexpr int kD = 128;
+constexpr int kVP = 80;     // LDS row pitch (bytes) of staged 4-bit V rows
+constexpr int kVP8 = 144;   // LDS row pitch (bytes) of staged 8-bit V rows
+constexpr int kPP = 20;     // halves per position of the position-major p * v_scale tile (16 rows + pad)
+
+// ------------------------------------------------------------------------------------- row compaction
+// Grid (n_seqs), 256 threads. Writes, per sequence, the live 4-bit rows then the live 8-bit rows as
+// (physical block << 8 | row) in slot order, and their counts. A slot is live when it is below seq_len
+// and its sentinel bit is clear; its width comes from the mixed-pool bitmap (KV head 0's tile: every head
+// of a block holds the same per-token widths).
+__global__ __launch_bounds__(256) void compact_rows_k(TileGeom g, DecodeArgs a) {
+  __shared__ int s_c4[4], s_c8[4];
+  const int seq = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
+  const int len = a.seq_lens[seq];
+  const int nblk = (len + kRows - 1) / kRows;
+  uint32_t* l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
+  uint32_t* l8 = l4 + a.list_cap;
+  const uint32_t* mrow = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
+  int base4 = 0, base8 = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const int phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + b];
+    const int t = b * kRows + tid;
+    bool live = t < len;
+    if (live && mrow) live = !((mrow[t >> 5] >> (t & 31)) & 1u);
+    bool wide = false;
+    if (g.mixed) {
+      const uint32_t* hdr = reinterpret_cast<const uint32_t*>(a.pool + (size_t)phys * g.H * g.tile_bytes + g.off_hdr);
+      wide = (hdr[tid >> 5] >> (tid & 31)) & 1u;
+    }
+    const uint64_t b4 = __ballot(live && !wide), b8 = __ballot(live && wide);
+    if ((tid & 63) == 0) {
+      s_c4[w] = __popcll(b4);
+      s_c8[w] = __popcll(b8);
+    }
+    __syncthreads();
+    int o4 = base4, o8 = base8, t4 = 0, t8 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o4 += i < w ? s_c4[i] : 0;
+      o8 += i < w ? s_c8[i] : 0;
+      t4 += s_c4[i];
+      t8 += s_c8[i];
+    }
+    const uint64_t below = (1ull << (tid & 63)) - 1ull;
+    const uint32_t e = ((uint32_t)phys << 8) | (uint32_t)tid;
+    if (live && !wide) l4[o4 + __popcll(b4 & below)] = e;
+    if (live && wide) l8[o8 + __popcll(b8 & below)] = e;
+    base4 += t4;
+    base8 += t8;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    a.ws_cnt[2 * seq] = base4;
+    a.ws_cnt[2 * seq + 1] = base8;
+  }
+}
+
+// ------------------------------------------------------------------------------------- decode
+// Raw codes and parameters of one chunk for one lane. 4-bit chunks: tokens 16c + lj (c = 0..3), 16 bytes
+// each of K and V (channels 32 la .. 32 la + 31). 8-bit chunks: tokens 16c + lj (c = 0, 1), 32 bytes each
+// (k[2c], k[2c + 1]).
+struct Raw {
+  u32x4 k[4];
+  u32x4 v[4];
+  uint32_t kp[4][2], vp[4][2];
+  uint32_t valid;  // bit c: token 16c + lj of the chunk exists
+};
+
+template <int G, bool GATHER>
+__global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a) {
+  static_assert(G == 1 || G == 2 || G == 4, "GQA ratio 1, 2 or 4");
+  constexpr int D = kD;
+  __shared__ float s_q[G][D];
+  __shared__ float s_qsum[G][2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][64 * kVP];   // staged V rows, per wave
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[4][64 * kPP];  // p * v_scale, position-major, per wave
+  __shared__ float s_wm[4][G], s_wl[4][G];
+  __shared__ float s_wacc[4][G][D];
+  __shared__ int s_tbl[GATHER ? 1 : kMaxSplitBlocks];
+
+  const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
+  const int ns = a.plan.n_splits;
+  const int len = a.seq_lens[seq];
+  const uint32_t S = (uint32_t)g.slot;
+  const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;
+  const size_t tstride = (size_t)g.H * g.tile_bytes;  // bytes between consecutive blocks of one KV head
+
+  // ------------------------------------------------------------ this workgroup's chunks
+  // Streaming: chunk i of wave w = rows 64w .. 64w+63 of logical block b0 + i. Gather: chunks c0 + w + 4i
+  // of the sequence's chunk list (4-bit chunks of 64 rows first, then 8-bit chunks of 32 rows).
+  int b0 = 0, nchunk = 0, n4 = 0, n8 = 0, nc4 = 0, c0 = 0;
+  bool wg_empty;
+  const uint32_t* l4 = nullptr;
+  const uint32_t* l8 = nullptr;
+  if (GATHER) {
+    n4 = a.ws_cnt[2 * seq];
+    n8 = a.ws_cnt[2 * seq + 1];
+    nc4 = (n4 + 63) / 64;
+    const int nc = nc4 + (n8 + 31) / 32;
+    c0 = (int)(((long)split * nc) / ns);
+    const int c1 = (int)(((long)(split + 1) * nc) / ns);
+    nchunk = c1 - c0 > w ? (c1 - c0 - w + 3) / 4 : 0;
+    wg_empty = c1 <= c0;
+    l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
+    l8 = l4 + a.list_cap;
+  } else {
+    const int nblk = (len + kRows - 1) / kRows;
+    b0 = split * a.plan.blocks_per_split;
+    const int b1 = min(b0 + a.plan.blocks_per_split, nblk);
+    nchunk = max(b1 - b0, 0);
+    wg_empty = nchunk == 0;
+  }
+
+  if (wg_empty) {
+    if (ns == 1) {  // nothing live in the sequence: the output row still has to be written
+      __shared__ int s_cnt0[4];
+      const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt0);
+      for (int jj = 0; jj < G; ++jj)
+        finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, kNegInf, 0.0f, 0.0f, tid, &s_wacc[0][0][0]);
+    } else {
+      if (tid < G) {
+        s_wm[0][tid] = kNegInf;
+        s_wl[0][tid] = 0.0f;
+      }
+      for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
+      __syncthreads();
+      splitk_arrive<D, G>(g, a, seq, h, split, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
+                          &s_wacc[0][0][0]);
+    }
+    return;
+  }
+  if (!GATHER) {
+    for (int i = tid; i < nchunk; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
+    __syncthreads();
+  }
+
+  // Issue the loads of the wave's chunk i into r (addresses clamped into range; r.valid marks real tokens).
+  auto load = [&](Raw& r, int i) __attribute__((always_inline)) {
+    const uint8_t* tile[4];
+    uint32_t row[4];
+    uint32_t valid = 0;
+    bool w8 = false;
+    if (GATHER) {
+      const int ci = c0 + w + 4 * i;
+      w8 = ci >= nc4;
+      const uint32_t* lst = w8 ? l8 : l4;
+      const int n = w8 ? n8 : n4;
+      const int e0 = w8 ? (ci - nc4) * 32 : ci * 64;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        int idx = e0 + 16 * c + lj;
+        const bool ok = idx < n && (c < 2 || !w8);
+        valid |= ok ? (1u << c) : 0u;
+        idx = ok ? idx : e0;  // the chunk's first row always exists
+        const uint32_t e = lst[idx];
+        tile[c] = pool_h + (size_t)(e >> 8) * tstride;
+        row[c] = e & 255u;
+      }
+    } else {
+      const uint8_t* t0 = pool_h + (size_t)s_tbl[i] * tstride;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        tile[c] = t0;
+        row[c] = 64 * w + 16 * c + lj;
+        valid |= ((b0 + i) * kRows + (int)row[c] < len) ? (1u << c) : 0u;
+      }
+    }
+    r.valid = valid;
+    if (!w8) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint8_t* rp = tile[c] + (size_t)row[c] * S + la * 16;
+        r.k[c] = *reinterpret_cast<const u32x4*>(rp);
+        r.v[c] = *reinterpret_cast<const u32x4*>(rp + g.off_vc);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint8_t* rp = tile[c] + (size_t)row[c] * S + la * 32;
+        r.k[2 * c] = *reinterpret_cast<const u32x4*>(rp);
+        r.k[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + 16);
+        r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + g.off_vc);
+        r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + g.off_vc + 16);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint2 kpv = *reinterpret_cast<const uint2*>(tile[c] + g.off_kp + (size_t)row[c] * 8);
+      const uint2 vpv = *reinterpret_cast<const uint2*>(tile[c] + g.off_vp + (size_t)row[c] * 8);
+      r.kp[c][0] = kpv.x;
+      r.kp[c][1] = kpv.y;
+      r.vp[c][0] = vpv.x;
+      r.vp[c][1] = vpv.y;
+    }
+  };
+
+  // The first chunk's loads are issued before the query set-up, so their latency overlaps it.
+  Raw ra, rb;
+  if (nchunk > 0) load(ra, 0);
+
+  // ------------------------------------------------------------ query: scale, rotation, group sums
+  for (int i = tid; i < G * D; i += 256)
+    s_q[i / D][i % D] = h2f(a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D]) * a.q_scale;
+  for (int i = tid; i < 4 * 64 * kPP; i += 256) (&s_p[0][0])[i] = (_Float16)0.0f;
+  __syncthreads();
+  if (g.rotate) {
+    for (int hs = 1; hs < D; hs *= 2) {
+      for (int i = tid; i < G * D / 2; i += 256) {
+        const int j = i / (D / 2), pi = i % (D / 2);
+        const int lo = (pi / hs) * 2 * hs + (pi % hs);
+        const float x = s_q[j][lo], y = s_q[j][lo + hs];
+        s_q[j][lo] = x + y;
+        s_q[j][lo + hs] = x - y;
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] *= a.unrot_c;
+    __syncthreads();
+  }
+  for (int i = tid; i < G * 2; i += 256) {
+    float sum = 0.0f;
+    for (int c = 0; c < 64; ++c) sum += s_q[i / 2][(i % 2) * 64 + c];
+    s_qsum[i / 2][i % 2] = sum;
+  }
+  __syncthreads();
+
+  // QK A operand for k-step s: row lj = 4 hq + 2 gam + part; lane group la supplies channels
+  // 32 la + 8 s + nib(e), e = 0..7, nib = 0,4,1,5,2,6,3,7 (the unpacking order of both widths); 4-bit
+  // chunks see the odd-position nibbles multiplied by 16, so their query entries are divided by 16.
+  u32x4 qa[4];
+  auto build_qa = [&](bool w8) __attribute__((always_inline)) {
+    const int hq = lj >> 2, gam = (lj >> 1) & 1, part = lj & 1;
+    const bool in_group = hq < G && (la >> 1) == gam;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        _Float16 x[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int e = 2 * p + k;
+          const int nib = (e >> 1) + 4 * (e & 1);
+          const float f = (!w8 && (e & 2)) ? 0.0625f : 1.0f;
+          const float v = in_group ? s_q[hq][32 * la + 8 * s + nib] * f : 0.0f;
+          const _Float16 hi = (_Float16)v;
+          x[k] = part ? (_Float16)(v - (float)hi) : hi;
+        }
+        qa[s][p] = pack_h2(x[0], x[1]);
+      }
+    }
+  };
+  build_qa(false);
+  bool cur8 = false;
+  const bool head_ok = la < G;
+  const float qs0 = head_ok ? s_qsum[la][0] : 0.0f, qs1 = head_ok ? s_qsum[la][1] : 0.0f;
+
+  float m_run = kNegInf, l_run = 0.0f, zacc0 = 0.0f, zacc1 = 0.0f;
+  floatx4 o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint8_t* sv = s_v[w];
+  _Float16* sp = s_p[w];
+
+  auto process = [&](const Raw& r, auto w8c) __attribute__((always_inline)) {
+    constexpr bool W8 = decltype(w8c)::value;
+    constexpr int NC = W8 ? 2 : 4;  // 16-token slices
+    // ---------------------------------------------------------- stage V rows (lane = token) in LDS
+    if (!W8) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP + la * 16) = r.v[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP8 + la * 32) = r.v[2 * c];
+        *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP8 + la * 32 + 16) = r.v[2 * c + 1];
+      }
+    }
+    // ---------------------------------------------------------- logits: QK on the matrix cores
+    floatx4 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 b;
+        if (!W8) {
+          const uint32_t wd = r.k[c][s], w8 = wd >> 8;
+          b = u32x4{wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
+        } else {
+          const uint32_t lo = r.k[2 * c + (s >> 1)][2 * (s & 1)], hi = r.k[2 * c + (s >> 1)][2 * (s & 1) + 1];
+          b = u32x4{__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
+                    __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
+        }
+        acc[c] = mfma16(qa[s], b, acc[c]);
+      }
+    float sc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bool live = head_ok && ((r.valid >> c) & 1u);
+      const float dot = h2f(r.kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
+                        h2f(r.kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
+      const float zq = h2f(r.kp[c][0] >> 16) * qs0 + h2f(r.kp[c][1] >> 16) * qs1;
+      sc[c] = live ? dot * kTwo24 + zq : kNegInf;
+    }
+    // ---------------------------------------------------------- online softmax (head la, 16-lane rows)
+    float mx = sc[0];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) mx = fmaxf(mx, sc[c]);
+    mx = row_max16(mx);
+    const float mnew = fmaxf(m_run, mx);
+    const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
+    float p[NC], ps = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      p[c] = __builtin_amdgcn_exp2f(sc[c] - mnew);  // -inf - finite -> 0
+      p[c] = mnew == kNegInf ? 0.0f : p[c];
+      ps += p[c];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = mnew;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {  // wave-uniform: skip when no running max moved
+      zacc0 *= alpha;
+      zacc1 *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
+    // ---------------------------------------------------------- p * v_scale (hi, lo) to LDS
+    // Position of token t: (t & ~7) | sinv(t & 7), sinv(u) = 2 (u & 3) + (u >> 2), the inverse of the
+    // token order 0,4,1,5,2,6,3,7 of the V operand; odd tokens of 4-bit chunks are divided by 16.
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int t = 16 * c + lj, u = lj & 7;
+      const int pos = (t & ~7) | (((u & 3) << 1) | (u >> 2));
+      const float pp = p[c];
+      const bool on = pp != 0.0f;
+      const float f = (!W8 && (u & 1)) ? 0.0625f : 1.0f;
+      const float vs0 = on ? h2f(r.vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(r.vp[c][0] >> 16) : 0.0f;
+      const float vs1 = on ? h2f(r.vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(r.vp[c][1] >> 16) : 0.0f;
+      zacc0 += pp * vz0;
+      zacc1 += pp * vz1;
+      const float pv0 = (pp * f) * vs0, pv1 = (pp * f) * vs1;
+      const _Float16 h0 = (_Float16)pv0, h1 = (_Float16)pv1;
+      const _Float16 e0 = (_Float16)(pv0 - (float)h0), e1 = (_Float16)(pv1 - (float)h1);
+      if (head_ok) {
+        uint2 wv;
+        wv.x = pack_h2(h0, e0);
+        wv.y = pack_h2(h1, e1);
+        *reinterpret_cast<uint2*>(sp + pos * kPP + la * 4) = wv;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---------------------------------------------------------- PV on the matrix cores
+    constexpr int NKB = W8 ? 1 : 2;  // 32-token k-blocks
+    u32x4 pa[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int base = 32 * kb + 8 * la + (lj >> 2);
+      const v2i x0 = lds_tr16(sp + base * kPP + (lj & 3) * 4);
+      const v2i x1 = lds_tr16(sp + (base + 4) * kPP + (lj & 3) * 4);
+      pa[kb] = u32x4{(uint32_t)x0.x, (uint32_t)x0.y, (uint32_t)x1.x, (uint32_t)x1.y};
+    }
+    if (!W8) {
+      const int tok = lj < 8 ? 8 * la + lj : 32 + 8 * la + (lj - 8);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v2i x = lds_tr4(sv + tok * kVP + 8 * t);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint32_t wd = (uint32_t)(kb ? x.y : x.x), w8 = wd >> 8;
+          const u32x4 b = {wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
+          o[t] = mfma16(pa[kb], b, o[t]);
+        }
+      }
+    } else {
+      const int tok = 8 * la + (lj >> 1);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v2i x = lds_tr8(sv + tok * kVP8 + 16 * t + 8 * (lj & 1));
+        const uint32_t lo = (uint32_t)x.x, hi = (uint32_t)x.y;
+        const u32x4 b = {__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
+                         __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
+        o[t] = mfma16(pa[0], b, o[t]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto run = [&](const Raw& r, int i) __attribute__((always_inline)) {
+    if (GATHER) {
+      const bool w8 = (c0 + w + 4 * i) >= nc4;
+      if (w8 != cur8) {
+        build_qa(w8);
+        cur8 = w8;
+      }
+      if (w8) {
+        process(r, std::true_type{});
+        return;
+      }
+    }
+    process(r, std::false_type{});
+  };
+
+  for (int i = 0; i < nchunk; i += 2) {
+    // sched_barrier keeps the next chunk's loads ahead of this chunk's arithmetic, so they are in flight
+    // while it runs; past the end the last chunk is reloaded (an L2 hit) and not used.
+    load(rb, min(i + 1, nchunk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    run(ra, i);
+    if (i + 1 >= nchunk) break;
+    load(ra, min(i + 2, nchunk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    run(rb, i + 1);
+  }
+
+  // ---------------------------------------------------------------- merge the four waves
+  {
+    const float lt = row_sum16(l_run);
+    const float zt0 = row_sum16(zacc0), zt1 = row_sum16(zacc1);
+    if (head_ok) {
+      if (lj == 0) {
+        s_wm[w][la] = m_run;
+        s_wl[w][la] = lt;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int gam = t >> 2;  // channel 16t + lj lies in V group t / 4
+        const float val = gam ? (o[t][2] + o[t][3]) * kTwo24 + zt1 : (o[t][0] + o[t][1]) * kTwo24 + zt0;
+        s_wacc[w][la][16 * t + lj] = val;
+      }
+    }
+  }
+  __syncthreads();
+  if (ns == 1) {
+    __shared__ int s_cnt[4];
+    __shared__ float s_o[D];
+    const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
+    for (int jj = 0; jj < G; ++jj) {
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_wm[ww][jj]);
+      float acc = 0.0f, L = 0.0f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const float sc_w = exp2f(s_wm[ww][jj] - M);
+          if (tid < D) acc += s_wacc[ww][jj][tid] * sc_w;
+          L += s_wl[ww][jj] * sc_w;
+        }
+      }
+      finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, M, L, acc, tid, s_o);
+    }
+    return;
+  }
+  __shared__ float s_pm[G], s_pl[G];
+  __shared__ float s_pacc[G][D];
+  for (int i = tid; i < G * D; i += 256) {
+    const int jj = i / D, c = i % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_wm[ww][jj]);
+    float acc = 0.0f, L = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float sc_w = exp2f(s_wm[ww][jj] - M);
+        acc += s_wacc[ww][jj][c] * sc_w;
+        L += s_wl[ww][jj] * sc_w;
+      }
+    }
+    s_pacc[jj][c] = acc;
+    if (c == 0) {
+      s_pm[jj] = M;
+      s_pl[jj] = L;
+    }
+  }
+  __syncthreads();
+  splitk_arrive<D, G>(g, a, seq, h, split, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
+}
+
+template <int G>
+hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.plan.n_splits, g.H, a.n_seqs);
+  if (a.mask || g.mixed) {
+    hipLaunchKernelGGL(compact_rows_k, dim3(a.n_seqs), dim3(256), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, true>), grid, dim3(256), 0, stream, g, a);
+  } else {
+    hipLaunchKernelGGL((decode_rows_k<G, false>), grid, dim3(256), 0, stream, g, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Layouts with this kernel: head_dim 128, per-token K and V groups of 64, 4-bit or mixed pools, G = 1, 2, 4.
+bool decode_rows_supported(const TileGeom& g, int G) {
+  return g.d == 128 && g.kg == 64 && g.vg == 64 && (G == 1 || G == 2 || G == 4);
+}
+
+hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  switch (a.G) {
+    case 1: return launch_g<1>(g, a, stream);
+    case 2: return launch_g<2>(g, a, stream);
+    case 4: return launch_g<4>(g, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

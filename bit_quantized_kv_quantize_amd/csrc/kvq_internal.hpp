@@ -40,6 +40,13 @@ struct SplitPlan {
 };
 SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len);
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
+// Byte offsets of the workspace regions (split-K counters, partial (m, l), partial accumulators, row
+// counts, row lists) for a call of this size; `total` is the size.
+struct WorkspaceLayout {
+  size_t ctr, ml, acc, cnt, list, total;
+  int list_cap;
+};
+WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 
 // Launchers (defined next to their kernels). They return hipSuccess or the launch error.
 hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
@@ -60,6 +67,9 @@ struct DecodeArgs {
   unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernel); zero between calls
   float* ws_ml;   // [n_seqs][H_q][n_splits] x {m, l}
   float* ws_acc;  // [n_seqs][H_q][n_splits][d]
+  int* ws_cnt;       // [n_seqs][2] live 4-bit / 8-bit rows (row-list kernel)
+  uint32_t* ws_list; // [n_seqs][2][list_cap] live rows as (physical block << 8 | row)
+  int list_cap;
   int n_seqs;
   int num_q_heads;
   int G;
@@ -69,9 +79,12 @@ struct DecodeArgs {
   float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale
   SplitPlan plan;
 };
-// Decode dispatch: the matrix-core kernel where its layout is compiled, the generic kernel otherwise
-// (or always, when the environment variable KVQ_FORCE_GENERIC_DECODE is set: a test hook).
+// Decode dispatch: the row-list matrix-core kernel where its layout is compiled, then the block matrix-core
+// kernel, then the generic kernel. The environment variable KVQ_DECODE_KERNEL (a test hook) may name
+// "generic" or "mfma" to skip the kernels before it.
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
+bool decode_rows_supported(const TileGeom& g, int G);
+hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const TileGeom& g, int G);
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);

@@ -43,14 +43,15 @@ def test_pool_bytes_bit_exact(env, orc, name):
     assert diff.size == 0, "first differing bytes at %s" % diff[:16]
 
 
-@pytest.fixture(params=["dispatch", "generic"])
+@pytest.fixture(params=["dispatch", "mfma", "generic"])
 def decode_path(request, monkeypatch):
-    """Run decode through the library's normal dispatch (matrix-core kernel where compiled) and through the
-    generic kernel (forced by the library's test hook)."""
-    if request.param == "generic":
-        monkeypatch.setenv("KVQ_FORCE_GENERIC_DECODE", "1")
+    """Run decode through the library's normal dispatch (the row-list matrix-core kernel where compiled),
+    through the block matrix-core kernel and through the generic kernel (the latter two forced by the
+    library's test hook, KVQ_DECODE_KERNEL; a layout a forced kernel lacks falls through to the next)."""
+    if request.param == "dispatch":
+        monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     else:
-        monkeypatch.delenv("KVQ_FORCE_GENERIC_DECODE", raising=False)
+        monkeypatch.setenv("KVQ_DECODE_KERNEL", request.param)
     return request.param
 
 
