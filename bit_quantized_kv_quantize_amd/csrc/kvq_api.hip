@@ -32,13 +32,13 @@ TileGeom make_geom(const kvq_layout* L) {
   g.rotate = L->rotate;
   g.mixed = L->mixed;
   g.slot = g.d * (g.mixed ? 8 : 4) / 8;
+  g.rec = 2 * g.slot;
   g.kpr = g.kg > 0 ? g.d / g.kg : 0;
   g.vpr = g.d / g.vg;
-  g.off_vc = (uint32_t)(kRows * g.slot);
-  g.off_kp = 2u * kRows * g.slot;
-  uint32_t kp_bytes = g.kg > 0 ? (uint32_t)(kRows * g.kpr * 4) : (uint32_t)(g.d * 4);
-  g.off_vp = g.off_kp + kp_bytes;
-  g.off_hdr = g.off_vp + (uint32_t)(kRows * g.vpr * 4);
+  g.prow = (g.kpr + g.vpr) * 4;
+  g.off_kch = (uint32_t)(kRows * g.rec);
+  g.off_prow = g.off_kch + (g.kg > 0 ? 0u : (uint32_t)(g.d * 4));
+  g.off_hdr = g.off_prow + (uint32_t)(kRows * g.prow);
   uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
   g.tile_bytes = (end + 255u) / 256u * 256u;
   return g;

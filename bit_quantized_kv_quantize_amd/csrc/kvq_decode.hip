@@ -126,13 +126,13 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
       // per-channel K: fold scale into q and the zero into a per-head constant for this block
       for (int i = tid; i < GMAX * D; i += NT) {
         const int j = i / D, c = i % D;
-        const uint32_t p = reinterpret_cast<const uint32_t*>(tile + g.off_kp)[c];
+        const uint32_t p = reinterpret_cast<const uint32_t*>(tile + g.off_kch)[c];
         s_qk[j][c] = s_q[j][c] * h2f(p & 0xffffu);
       }
       if (tid < GMAX) {
         float cst = 0.0f;
         for (int c = 0; c < D; ++c)
-          cst += s_q[tid][c] * h2f(reinterpret_cast<const uint32_t*>(tile + g.off_kp)[c] >> 16);
+          cst += s_q[tid][c] * h2f(reinterpret_cast<const uint32_t*>(tile + g.off_kch)[c] >> 16);
         s_kconst[tid] = cst;
       }
       __syncthreads();
@@ -146,9 +146,9 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < GMAX; ++j) score[j] = 0.0f;
     if (live) {
-      const uint8_t* krow = tile + (size_t)tid * g.slot;
+      const uint8_t* krow = tile + g.kcode(tid);
       if (g.kg > 0) {
-        const uint32_t* kpar = reinterpret_cast<const uint32_t*>(tile + g.off_kp) + (size_t)tid * g.kpr;
+        const uint32_t* kpar = reinterpret_cast<const uint32_t*>(tile + g.kpar(tid));
         float part[GMAX];
 #pragma unroll
         for (int j = 0; j < GMAX; ++j) part[j] = 0.0f;
@@ -225,8 +225,8 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
       if (!any) continue;
       const int vbits = (g.mixed && ((hdr[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
       float c[8];
-      codes8(tile + g.off_vc + (size_t)t * g.slot, cl * 8, vbits, c);
-      const uint32_t p = reinterpret_cast<const uint32_t*>(tile + g.off_vp)[(size_t)t * g.vpr + vgi];
+      codes8(tile + g.vcode(t, vbits), cl * 8, vbits, c);
+      const uint32_t p = reinterpret_cast<const uint32_t*>(tile + g.vpar(t))[vgi];
       const float sc = h2f(p & 0xffffu), zc = h2f(p >> 16);
 #pragma unroll
       for (int j = 0; j < GMAX; ++j) {

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int row = r0 + 16 * c + lj;
-      const uint4* kp = reinterpret_cast<const uint4*>(tile + (size_t)row * (D / 2) + la * KW * 4);
+      const uint4* kp = reinterpret_cast<const uint4*>(tile + g.kcode(row) + la * KW * 4);
 #pragma unroll
       for (int q4 = 0; q4 < KW / 4; ++q4) {
         const uint4 v4 = kp[q4];
@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
         r.kraw[c][4 * q4 + 2] = v4.z;
         r.kraw[c][4 * q4 + 3] = v4.w;
       }
-      const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.off_kp) + (size_t)row * NGK;
-      const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.off_vp) + (size_t)row * NGV;
+      const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.kpar(row));
+      const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.vpar(row));
 #pragma unroll
       for (int gm = 0; gm < NGK; ++gm) r.kpar[c][gm] = kpp[gm];
 #pragma unroll
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int row = r0 + 32 * kb + 8 * la + e;
-        const uint32_t* vp = reinterpret_cast<const uint32_t*>(tile + g.off_vc + (size_t)row * (D / 2));
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(tile + g.vcode(row, 4));
 #pragma unroll
         for (int vw = 0; vw < VW; ++vw) r.vraw[kb][e][vw] = vp[lj + 16 * vw];
       }

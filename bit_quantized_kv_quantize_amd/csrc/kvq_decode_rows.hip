@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
   const int ns = a.plan.n_splits;
   const int len = a.seq_lens[seq];
-  const uint32_t S = (uint32_t)g.slot;
+  const uint32_t R = (uint32_t)g.rec;  // bytes of a row record
   const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;
   const size_t tstride = (size_t)g.H * g.tile_bytes;  // bytes between consecutive blocks of one KV head
 
@@ -190,59 +190,80 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     __syncthreads();
   }
 
-  // Issue the loads of the wave's chunk i into r (addresses clamped into range; r.valid marks real tokens).
-  auto load = [&](Raw& r, int i) __attribute__((always_inline)) {
-    const uint8_t* tile[4];
-    uint32_t row[4];
-    uint32_t valid = 0;
-    bool w8 = false;
+  // Rows of the wave's chunk i for this lane: tokens 16c + lj. In gather mode the list entries are fetched
+  // one chunk ahead of the codes (fetch, then load), so the codes' addresses never wait on the list.
+  struct Ent {
+    uint32_t e[4];   // gather: list entries (physical block << 8 | row)
+    uint32_t valid;  // bit c: token 16c + lj exists
+  };
+  auto fetch = [&](Ent& en, int i) __attribute__((always_inline)) {
     if (GATHER) {
       const int ci = c0 + w + 4 * i;
-      w8 = ci >= nc4;
+      const bool w8 = ci >= nc4;
       const uint32_t* lst = w8 ? l8 : l4;
       const int n = w8 ? n8 : n4;
       const int e0 = w8 ? (ci - nc4) * 32 : ci * 64;
+      uint32_t valid = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         int idx = e0 + 16 * c + lj;
         const bool ok = idx < n && (c < 2 || !w8);
         valid |= ok ? (1u << c) : 0u;
-        idx = ok ? idx : e0;  // the chunk's first row always exists
-        const uint32_t e = lst[idx];
-        tile[c] = pool_h + (size_t)(e >> 8) * tstride;
-        row[c] = e & 255u;
+        en.e[c] = lst[ok ? idx : e0];  // the chunk's first row always exists
+      }
+      en.valid = valid;
+    } else {
+      uint32_t valid = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) valid |= ((b0 + i) * kRows + 64 * w + 16 * c + lj < len) ? (1u << c) : 0u;
+      en.valid = valid;
+    }
+  };
+  // Issue the code and parameter loads of chunk i (rows from en) into r.
+  auto load = [&](Raw& r, const Ent& en, int i) __attribute__((always_inline)) {
+    const uint8_t* tile[4];
+    uint32_t row[4];
+    bool w8 = false;
+    if (GATHER) {
+      w8 = (c0 + w + 4 * i) >= nc4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        tile[c] = pool_h + (size_t)(en.e[c] >> 8) * tstride;
+        row[c] = en.e[c] & 255u;
       }
     } else {
-      const uint8_t* t0 = pool_h + (size_t)s_tbl[i] * tstride;
+      // the block's tile base is wave-uniform: scalar base, 32-bit per-lane offsets
+      const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
+      const uint8_t* t0 = pool_h + (size_t)phys * tstride;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         tile[c] = t0;
         row[c] = 64 * w + 16 * c + lj;
-        valid |= ((b0 + i) * kRows + (int)row[c] < len) ? (1u << c) : 0u;
       }
     }
-    r.valid = valid;
+    r.valid = en.valid;
     if (!w8) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint8_t* rp = tile[c] + (size_t)row[c] * S + la * 16;
+        const uint8_t* rp = tile[c] + (row[c] * R + la * 16);
         r.k[c] = *reinterpret_cast<const u32x4*>(rp);
-        r.v[c] = *reinterpret_cast<const u32x4*>(rp + g.off_vc);
+        r.v[c] = *reinterpret_cast<const u32x4*>(rp + kD / 2);  // V codes follow the row's 4-bit K codes
       }
     } else {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint8_t* rp = tile[c] + (size_t)row[c] * S + la * 32;
+        const uint8_t* rp = tile[c] + (row[c] * R + la * 32);
         r.k[2 * c] = *reinterpret_cast<const u32x4*>(rp);
         r.k[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + 16);
-        r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + g.off_vc);
-        r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + g.off_vc + 16);
+        r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + kD);  // V codes follow the row's 8-bit K codes
+        r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + kD + 16);
       }
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint2 kpv = *reinterpret_cast<const uint2*>(tile[c] + g.off_kp + (size_t)row[c] * 8);
-      const uint2 vpv = *reinterpret_cast<const uint2*>(tile[c] + g.off_vp + (size_t)row[c] * 8);
+      // parameter record of the row: K groups {scale, zero} x 2, then V groups x 2
+      const uint4 pr = *reinterpret_cast<const uint4*>(tile[c] + (g.off_prow + row[c] * 16));
+      const uint2 kpv = {pr.x, pr.y}, vpv = {pr.z, pr.w};
       r.kp[c][0] = kpv.x;
       r.kp[c][1] = kpv.y;
       r.vp[c][0] = vpv.x;
@@ -252,7 +273,12 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 
   // The first chunk's loads are issued before the query set-up, so their latency overlaps it.
   Raw ra, rb;
-  if (nchunk > 0) load(ra, 0);
+  Ent en;
+  if (nchunk > 0) {
+    fetch(en, 0);
+    load(ra, en, 0);
+    fetch(en, min(1, nchunk - 1));
+  }
 
   // ------------------------------------------------------------ query: scale, rotation, group sums
   for (int i = tid; i < G * D; i += 256)
@@ -460,13 +486,16 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   };
 
   for (int i = 0; i < nchunk; i += 2) {
-    // sched_barrier keeps the next chunk's loads ahead of this chunk's arithmetic, so they are in flight
-    // while it runs; past the end the last chunk is reloaded (an L2 hit) and not used.
-    load(rb, min(i + 1, nchunk - 1));
+    // sched_barrier keeps the next chunk's loads (and the list entries of the one after) ahead of this
+    // chunk's arithmetic, so they are in flight while it runs; past the end the last chunk is reloaded
+    // (an L2 hit) and not used.
+    load(rb, en, min(i + 1, nchunk - 1));
+    fetch(en, min(i + 2, nchunk - 1));
     __builtin_amdgcn_sched_barrier(0);
     run(ra, i);
     if (i + 1 >= nchunk) break;
-    load(ra, min(i + 2, nchunk - 1));
+    load(ra, en, min(i + 2, nchunk - 1));
+    fetch(en, min(i + 3, nchunk - 1));
     __builtin_amdgcn_sched_barrier(0);
     run(rb, i + 1);
   }

@@ -11,7 +11,11 @@ namespace kvq {
 
 constexpr int kRows = 256;  // tokens per block (the block pool of "Agent Memory Below the Prompt", 2.1)
 
-// Byte geometry of one tile, computed once on the host and passed to kernels by value.
+// Byte geometry of one tile, computed once on the host and passed to kernels by value. A tile holds 256
+// row records (the K codes of one token immediately followed by its V codes, d * width / 8 bytes each;
+// the rest of a 4-bit row's record in a mixed pool is zero), the per-channel K parameters when K is grouped per
+// channel, 256 parameter records (K groups then V groups of one token, each {fp16 scale, fp16 zero}),
+// the width bitmap of mixed pools, and zero padding to a multiple of 256 bytes.
 struct TileGeom {
   int d;            // head_dim
   int H;            // KV heads
@@ -19,14 +23,20 @@ struct TileGeom {
   int vg;           // V group (channels)
   int rotate;       // Walsh-Hadamard rotation applied before quantisation
   int mixed;        // per-token 4/8-bit rows, 32-byte bitmap at off_hdr
-  int slot;         // bytes per code row: d/2, or d in mixed pools
+  int slot;         // code bytes of one row of K (or V): d/2, or d in mixed pools
+  int rec;          // bytes of one row record (2 * slot)
   int kpr;          // K param entries per row (d / kg), 0 for per-channel K
   int vpr;          // V param entries per row (d / vg)
-  uint32_t off_vc;  // V codes
-  uint32_t off_kp;  // K params
-  uint32_t off_vp;  // V params
-  uint32_t off_hdr; // end of V params; the bitmap of mixed pools starts here
+  int prow;         // bytes of one parameter record ((kpr + vpr) * 4)
+  uint32_t off_kch; // per-channel K params, d entries (kg < 0 only)
+  uint32_t off_prow;// parameter record of row 0
+  uint32_t off_hdr; // end of the parameter records; the bitmap of mixed pools starts here
   uint32_t tile_bytes;
+  __host__ __device__ uint32_t kcode(int t) const { return (uint32_t)t * (uint32_t)rec; }
+  // a row's V codes follow its K codes: d/2 bytes in for a 4-bit row, d for an 8-bit row
+  __host__ __device__ uint32_t vcode(int t, int bits) const { return kcode(t) + (uint32_t)(d * bits / 8); }
+  __host__ __device__ uint32_t kpar(int t) const { return off_prow + (uint32_t)t * (uint32_t)prow; }
+  __host__ __device__ uint32_t vpar(int t) const { return off_prow + (uint32_t)t * (uint32_t)prow + (uint32_t)kpr * 4u; }
 };
 
 int check_layout(const kvq_layout* L);

@@ -98,8 +98,9 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
 }
 
 // Store one lane's share of a code row: 4-bit codes as one uint32 (low nibble first), 8-bit codes as
-// two; in mixed pools a 4-bit row also zeroes its share of the unused half of the slot.
-__device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_slot_bytes, int bits, int mixed,
+// two. With zero_tail (the V row of a 4-bit row in a mixed pool) the lane also zeroes its share of the
+// d bytes after the row, the unused rest of the record.
+__device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_row_bytes, int bits, bool zero_tail,
                                             const uint32_t (&code)[8]) {
   if (bits == 8) {
     uint2 w;
@@ -111,20 +112,21 @@ __device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_slot_
 #pragma unroll
     for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
     *reinterpret_cast<uint32_t*>(row + li * 4) = w;
-    if (mixed) *reinterpret_cast<uint32_t*>(row + half_slot_bytes + li * 4) = 0u;
+    if (zero_tail) *reinterpret_cast<uint2*>(row + half_row_bytes + li * 8) = uint2{0u, 0u};
   }
 }
 
 // One row of one tensor (K or V) with per-token groups of grp channels.
 template <int LPR>
 __device__ __forceinline__ void quantize_token_row(const TileGeom& g, float (&x)[8], int li, int grp, int bits,
-                                                   uint8_t* code_row, uint8_t* param_row, float rot_c) {
+                                                   bool zero_tail, uint8_t* code_row, uint8_t* param_row,
+                                                   float rot_c) {
   if (g.rotate) rotate_row<LPR>(x, li, rot_c);
   const int gl = grp / 8;
   uint32_t code[8];
   uint32_t param;
   quantize8(x, gl, bits, code, param);
-  store_codes(code_row, li, LPR * 4, bits, g.mixed, code);
+  store_codes(code_row, li, LPR * 4, bits, zero_tail, code);
   if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(param_row)[li / gl] = param;
 }
 
@@ -144,15 +146,13 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
   uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
   const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 8;
   const int grp = kv ? g.vg : g.kg;
-  const int ppr = D / grp;
-  uint8_t* code_base = tile + (kv ? g.off_vc : 0u);
-  uint8_t* par_base = tile + (kv ? g.off_vp : g.off_kp);
   const uint32_t* bitmap = prec_bits ? prec_bits + (size_t)i * 8 : nullptr;
   for (int t = r0; t < kRows; t += kRowsPerPass) {
     float x[8];
     load8(src + (size_t)t * g.H * D, x);
     const int bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
-    quantize_token_row<LPR>(g, x, li, grp, bits, code_base + (size_t)t * g.slot, par_base + (size_t)t * ppr * 4,
+    quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
+                            tile + (kv ? g.vcode(t, bits) : g.kcode(t)), tile + (kv ? g.vpar(t) : g.kpar(t)),
                             rot_c);
   }
   if (kv == 1) {
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
     mx = mx + 0.0f;
     const float s32 = (mx - mn) / 15.0f;
     const uint32_t sh = f2h(s32), zh = f2h(mn);
-    reinterpret_cast<uint32_t*>(tile + g.off_kp)[c] = sh | (zh << 16);
+    reinterpret_cast<uint32_t*>(tile + g.off_kch)[c] = sh | (zh << 16);
     const float s = h2f(sh);
     s_z[c] = h2f(zh);
     s_zero_scale[c] = s == 0.0f;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
       }
       w |= code << (4 * e);
     }
-    reinterpret_cast<uint32_t*>(tile + (size_t)t * g.slot)[li] = w;
+    reinterpret_cast<uint32_t*>(tile + g.kcode(t))[li] = w;
   }
 }
 
@@ -257,8 +257,9 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
   const int grp = kv ? g.vg : g.kg;
   float x[8];
   load8((kv ? v : k) + ((size_t)s * g.H + h) * D + li * 8, x);
-  quantize_token_row<LPR>(g, x, li, grp, bits, tile + (kv ? g.off_vc : 0u) + (size_t)row * g.slot,
-                          tile + (kv ? g.off_vp : g.off_kp) + (size_t)row * (D / grp) * 4, rot_c);
+  quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
+                          tile + (kv ? g.vcode(row, bits) : g.kcode(row)), tile + (kv ? g.vpar(row) : g.kpar(row)),
+                          rot_c);
   if (g.mixed && kv == 0 && li == 0) {
     uint32_t* word = reinterpret_cast<uint32_t*>(tile + g.off_hdr) + (row >> 5);
     const uint32_t bit = 1u << (row & 31);

@@ -26,16 +26,19 @@
  * Pool layout (the block pool of [AMB] 2.1 item 1 with the Q4 format of [AMB] 2.1 item 2)
  *   A pool holds num_blocks * H_kv tiles; tile (b, h) starts at byte (b * H_kv + h) * kvq_tile_bytes().
  *   A tile holds the 256 token rows of one KV head of one block, in this order (R = 256, d = head_dim,
- *   bmax = 8 for mixed pools else 4, S = d * bmax / 8 bytes per code row):
- *     K codes   R x S bytes      row t at offset t*S
- *     V codes   R x S bytes
- *     K params  per-token groups: R x (d / k_group) x 4 bytes, [t][group]; per-channel: d x 4 bytes, [c]
- *     V params  R x (d / v_group) x 4 bytes, [t][group]
- *     header    mixed pools only: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes
- *     padding   zero bytes up to the next multiple of 256
+ *   S = d/2, or d in mixed pools):
+ *     row records   R x 2S bytes: record t at t * 2S holds row t's K codes (d * b / 8 bytes, b = the row's
+ *                   width, 4 or 8) immediately followed by its V codes (d * b / 8 bytes); in a mixed pool
+ *                   the last d bytes of a 4-bit row's record are zero
+ *     K per channel when k_group == -1: d x 4 bytes, [c] {scale, zero}
+ *     param records R x P bytes, P = 4 * (d / k_group + d / v_group) (4 * d / v_group when K is grouped
+ *                   per channel): record t holds row t's K params [group] {scale, zero}, then its V params
+ *     header        mixed pools only: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes
+ *     padding       zero bytes up to the next multiple of 256
+ *   A 4-bit row's K and V codes are one contiguous d-byte span, so a decode that gathers live rows reads
+ *   each row's codes as one piece (one 128-byte line at d = 128).
  *   4-bit codes: element j of a row sits in bits 4*(j % 8) of little-endian uint32 word j / 8 (byte i holds
- *   elements 2i in its low nibble and 2i+1 in its high nibble). 8-bit codes: one byte per element. In a
- *   mixed pool a 4-bit row fills the first d/2 bytes of its slot and the rest of the slot is zero.
+ *   elements 2i in its low nibble and 2i+1 in its high nibble). 8-bit codes: one byte per element.
  *   A parameter entry is {fp16 scale, fp16 zero} (scale at byte 0, zero at byte 2); the pages store a
  *   16-bit scale and bias per group, this library stores them as IEEE fp16.
  *

@@ -24,16 +24,18 @@ def hadamard(n: int) -> np.ndarray:
 
 
 def _layout_offsets(d, k_group, v_group, mixed):
+    """Byte geometry of a tile: row records (K codes then V codes of the row's width, 2 * slot bytes), the per-channel K
+    parameters (if K is grouped per channel), per-row parameter records (K groups then V groups), header."""
     rows = 256
     slot = d * (8 if mixed else 4) // 8
-    off_vc = rows * slot
-    off_kp = 2 * rows * slot
-    kp_bytes = rows * (d // k_group) * 4 if k_group > 0 else d * 4
-    off_vp = off_kp + kp_bytes
-    off_hdr = off_vp + rows * (d // v_group) * 4
+    off_par = rows * 2 * slot
+    kpr = d // k_group if k_group > 0 else 0
+    prow = (kpr + d // v_group) * 4
+    off_prow = off_par + (0 if k_group > 0 else d * 4)
+    off_hdr = off_prow + rows * prow
     end = off_hdr + (32 if mixed else 0)
     tile = (end + 255) // 256 * 256
-    return slot, off_vc, off_kp, off_vp, off_hdr, tile
+    return slot, off_par, off_prow, prow, kpr, off_hdr, tile
 
 
 def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
@@ -55,24 +57,29 @@ def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
 
 def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed):
     """-> (K [256][d], V [256][d]) fp64 in the stored (rotated) domain."""
-    slot, off_vc, off_kp, off_vp, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
+    slot, off_par, off_prow, prow, kpr, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
     rows = 256
     if mixed:
         hdr = tile[off_hdr: off_hdr + 32]
         bits = np.where((hdr[np.arange(rows) // 8] >> (np.arange(rows) % 8)) & 1, 8, 4)
     else:
         bits = np.full(rows, 4)
-    kc = _codes(tile[: rows * slot].reshape(rows, slot), d, bits)
-    vc = _codes(tile[off_vc: off_vc + rows * slot].reshape(rows, slot), d, bits)
+    rec = tile[: rows * 2 * slot].reshape(rows, 2 * slot)
+    kc = _codes(rec[:, :slot], d, bits)
+    # V codes follow the row's own K codes: d/2 bytes in for 4-bit rows, d for 8-bit rows
+    vc = _codes(rec[:, d // 2: d], d, np.full(rows, 4))
+    if mixed:
+        vc = np.where((bits == 8)[:, None], _codes(rec[:, d: 2 * d], d, np.full(rows, 8)), vc)
+    par = tile[off_prow: off_prow + rows * prow].reshape(rows, prow)
     if k_group > 0:
-        kp = tile[off_kp: off_kp + rows * (d // k_group) * 4].view(np.float16).reshape(rows, d // k_group, 2)
+        kp = par[:, : kpr * 4].copy().view(np.float16).reshape(rows, kpr, 2)
         ks = np.repeat(kp[:, :, 0].astype(np.float64), k_group, axis=1)
         kz = np.repeat(kp[:, :, 1].astype(np.float64), k_group, axis=1)
     else:
-        kp = tile[off_kp: off_kp + d * 4].view(np.float16).reshape(d, 2)
+        kp = tile[off_par: off_par + d * 4].view(np.float16).reshape(d, 2)
         ks = np.broadcast_to(kp[:, 0].astype(np.float64), (rows, d))
         kz = np.broadcast_to(kp[:, 1].astype(np.float64), (rows, d))
-    vp = tile[off_vp: off_vp + rows * (d // v_group) * 4].view(np.float16).reshape(rows, d // v_group, 2)
+    vp = par[:, kpr * 4:].copy().view(np.float16).reshape(rows, d // v_group, 2)
     vs = np.repeat(vp[:, :, 0].astype(np.float64), v_group, axis=1)
     vz = np.repeat(vp[:, :, 1].astype(np.float64), v_group, axis=1)
     return kc * ks + kz, vc * vs + vz
@@ -81,7 +88,7 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed):
 def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed, q_bits: np.ndarray,
                      block_table, seq_lens, sentinel_mask=None, softmax_scale=None) -> np.ndarray:
     """Dense fp64 attention of every query head over its sequence's dequantised cache."""
-    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[5]
+    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[6]
     q = q_bits.view(np.float16).astype(np.float64)
     n_seqs, hq, _ = q.shape
     g = hq // h_kv

@@ -210,16 +210,34 @@ int orc_check_layout(const orc_layout* L) {
   return ORC_OK;
 }
 
+/* Tile layout (one block of 256 rows, one KV head):
+ *   row records       256 x (2 * slot) bytes (slot = d/2, or d in mixed pools): record t at t * 2 * slot
+ *                     holds the row's K codes (d * b / 8 bytes, b its width) immediately followed by its
+ *                     V codes (d * b / 8 bytes); in mixed pools the rest of a 4-bit row's record is zero;
+ *   per-channel K     K grouped per channel: d x {fp16 scale, fp16 zero};
+ *   parameter records 256 x prow bytes: record t holds K params [group] {scale, zero} (per-token K
+ *                     groups only) then V params [group] {scale, zero};
+ *   header            mixed pools: 8 uint32 words, bit t % 32 of word t / 32 set = row t is 8-bit;
+ *   zero padding to a multiple of 256 bytes.
+ * The pages fix only the content (codes and a 16-bit scale and bias per group); this arrangement keeps a
+ * row's K and V codes in one record so a row is one contiguous read. */
 static size_t row_slot_bytes(const orc_layout* L) { return (size_t)L->head_dim * (L->mixed ? 8 : 4) / 8; }
-static size_t off_vcodes(const orc_layout* L) { return (size_t)ORC_ROWS * row_slot_bytes(L); }
-static size_t off_kparams(const orc_layout* L) { return 2 * (size_t)ORC_ROWS * row_slot_bytes(L); }
-static size_t kparam_bytes(const orc_layout* L) {
-  return L->k_group > 0 ? (size_t)ORC_ROWS * (L->head_dim / L->k_group) * 4 : (size_t)L->head_dim * 4;
+static size_t kcodes_off(const orc_layout* L, int32_t t) { return (size_t)t * 2 * row_slot_bytes(L); }
+static size_t vcodes_off(const orc_layout* L, int32_t t, int32_t bits) {
+  return kcodes_off(L, t) + (size_t)L->head_dim * bits / 8;
 }
-static size_t off_vparams(const orc_layout* L) { return off_kparams(L) + kparam_bytes(L); }
-static size_t off_header(const orc_layout* L) {
-  return off_vparams(L) + (size_t)ORC_ROWS * (L->head_dim / L->v_group) * 4;
+static size_t off_params(const orc_layout* L) { return (size_t)ORC_ROWS * 2 * row_slot_bytes(L); }
+static size_t kparams_per_row(const orc_layout* L) { return L->k_group > 0 ? (size_t)(L->head_dim / L->k_group) : 0; }
+static size_t prow_bytes(const orc_layout* L) {
+  return (kparams_per_row(L) + (size_t)(L->head_dim / L->v_group)) * 4;
 }
+static size_t off_prows(const orc_layout* L) {
+  return off_params(L) + (L->k_group > 0 ? 0 : (size_t)L->head_dim * 4);
+}
+static size_t kparams_off(const orc_layout* L, int32_t t) { return off_prows(L) + (size_t)t * prow_bytes(L); }
+static size_t vparams_off(const orc_layout* L, int32_t t) { return kparams_off(L, t) + kparams_per_row(L) * 4; }
+static size_t kchan_off(const orc_layout* L, int32_t c) { return off_params(L) + (size_t)c * 4; }
+static size_t off_header(const orc_layout* L) { return off_prows(L) + (size_t)ORC_ROWS * prow_bytes(L); }
 
 size_t orc_tile_bytes(const orc_layout* L) {
   if (orc_check_layout(L) != ORC_OK) return 0;
@@ -234,10 +252,10 @@ static uint8_t* tile_ptr(const orc_layout* L, uint8_t* pool, int64_t block, int3
 static void put_u16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] = (uint8_t)(v >> 8); }
 static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
-/* Pack one row's codes into its slot: 4-bit rows two per byte, low nibble first; 8-bit rows one per
- * byte; unused slot bytes zero. */
-static void pack_row(const uint8_t* codes, int32_t d, int32_t bits, size_t slot, uint8_t* dst) {
-  memset(dst, 0, slot);
+/* Pack one row's codes (d * bits / 8 bytes): 4-bit rows two per byte, low nibble first; 8-bit rows one
+ * per byte. */
+static void pack_row(const uint8_t* codes, int32_t d, int32_t bits, uint8_t* dst) {
+  memset(dst, 0, (size_t)d * bits / 8);
   if (bits == 8) {
     for (int32_t j = 0; j < d; ++j) dst[j] = codes[j];
   } else {
@@ -252,7 +270,7 @@ static uint8_t unpack_code(const uint8_t* row, int32_t j, int32_t bits) {
 
 /* Quantise one token row (already fp32 and, if requested, rotated) with per-token groups of g. */
 static void quantize_row_groups(const float* x, int32_t d, int32_t g, int32_t bits, uint8_t* code_dst,
-                                size_t slot, uint8_t* param_dst) {
+                                uint8_t* param_dst) {
   uint8_t codes[4096];
   for (int32_t k = 0; k < d / g; ++k) {
     uint16_t sh, zh;
@@ -260,7 +278,7 @@ static void quantize_row_groups(const float* x, int32_t d, int32_t g, int32_t bi
     put_u16(param_dst + 4 * k, sh);
     put_u16(param_dst + 4 * k + 2, zh);
   }
-  pack_row(codes, d, bits, slot, code_dst);
+  pack_row(codes, d, bits, code_dst);
 }
 
 static int row_bits(const uint32_t* bitmap, int32_t t) {
@@ -271,7 +289,6 @@ static int row_bits(const uint32_t* bitmap, int32_t t) {
 static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_rows,
                           const uint16_t* v_rows, size_t row_stride, const uint32_t* bitmap) {
   const int32_t d = L->head_dim;
-  const size_t slot = row_slot_bytes(L);
   memset(tile, 0, orc_tile_bytes(L));
   float* xk = (float*)malloc(sizeof(float) * ORC_ROWS * d);
   float* xv = (float*)malloc(sizeof(float) * ORC_ROWS * d);
@@ -288,8 +305,8 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
   /* K */
   if (L->k_group > 0) {
     for (int32_t t = 0; t < ORC_ROWS; ++t)
-      quantize_row_groups(xk + (size_t)t * d, d, L->k_group, row_bits(bitmap, t), tile + (size_t)t * slot,
-                          slot, tile + off_kparams(L) + (size_t)t * (d / L->k_group) * 4);
+      quantize_row_groups(xk + (size_t)t * d, d, L->k_group, row_bits(bitmap, t), tile + kcodes_off(L, t),
+                          tile + kparams_off(L, t));
   } else {
     /* one group per channel over the 256 rows of the block; always 4-bit (mixed is rejected) */
     uint8_t* codes = (uint8_t*)malloc((size_t)ORC_ROWS * d);
@@ -298,17 +315,16 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
       uint16_t sh, zh;
       orc_quantize_group(xk + c, ORC_ROWS, d, 4, col, &sh, &zh);
       for (int32_t t = 0; t < ORC_ROWS; ++t) codes[(size_t)t * d + c] = col[t];
-      put_u16(tile + off_kparams(L) + 4 * (size_t)c, sh);
-      put_u16(tile + off_kparams(L) + 4 * (size_t)c + 2, zh);
+      put_u16(tile + kchan_off(L, c), sh);
+      put_u16(tile + kchan_off(L, c) + 2, zh);
     }
-    for (int32_t t = 0; t < ORC_ROWS; ++t) pack_row(codes + (size_t)t * d, d, 4, slot, tile + (size_t)t * slot);
+    for (int32_t t = 0; t < ORC_ROWS; ++t) pack_row(codes + (size_t)t * d, d, 4, tile + kcodes_off(L, t));
     free(codes);
   }
   /* V */
   for (int32_t t = 0; t < ORC_ROWS; ++t)
     quantize_row_groups(xv + (size_t)t * d, d, L->v_group, row_bits(bitmap, t),
-                        tile + off_vcodes(L) + (size_t)t * slot, slot,
-                        tile + off_vparams(L) + (size_t)t * (d / L->v_group) * 4);
+                        tile + vcodes_off(L, t, row_bits(bitmap, t)), tile + vparams_off(L, t));
   if (L->mixed) {
     uint8_t* hdr = tile + off_header(L);
     for (int32_t w = 0; w < 8; ++w) {
@@ -360,14 +376,15 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
     int32_t bits = (prec && prec[s] == 8) ? 8 : 4;
     for (int32_t h = 0; h < H; ++h) {
       uint8_t* tile = tile_ptr(L, pool, blk, h);
+      memset(tile + kcodes_off(L, row), 0, 2 * slot); /* the whole record: a wider row may have been here */
       for (int32_t which = 0; which < 2; ++which) {
         const uint16_t* src = (which == 0 ? k : v) + ((size_t)s * H + h) * d;
         for (int32_t c = 0; c < d; ++c) x[c] = orc_f16_to_f32(src[c]);
         if (L->rotate) rotate_row(x, d);
         int32_t g = which == 0 ? L->k_group : L->v_group;
-        size_t code_off = (which == 0 ? 0 : off_vcodes(L)) + (size_t)row * slot;
-        size_t par_off = (which == 0 ? off_kparams(L) : off_vparams(L)) + (size_t)row * (d / g) * 4;
-        quantize_row_groups(x, d, g, bits, tile + code_off, slot, tile + par_off);
+        size_t code_off = which == 0 ? kcodes_off(L, row) : vcodes_off(L, row, bits);
+        size_t par_off = which == 0 ? kparams_off(L, row) : vparams_off(L, row);
+        quantize_row_groups(x, d, g, bits, tile + code_off, tile + par_off);
       }
       if (L->mixed) {
         uint8_t* byte = tile + off_header(L) + row / 8;
@@ -385,16 +402,14 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
  * value = code * scale + zero, exact in fp64. Returns the row's bit width. */
 int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, double* k_out, double* v_out) {
   const int32_t d = L->head_dim;
-  const size_t slot = row_slot_bytes(L);
   int32_t bits = 4;
   if (L->mixed) bits = ((tile[off_header(L) + t / 8] >> (t % 8)) & 1u) ? 8 : 4;
-  const uint8_t* kr = tile + (size_t)t * slot;
-  const uint8_t* vr = tile + off_vcodes(L) + (size_t)t * slot;
+  const uint8_t* kr = tile + kcodes_off(L, t);
+  const uint8_t* vr = tile + vcodes_off(L, t, bits);
   for (int32_t c = 0; c < d; ++c) {
-    const uint8_t* kp = L->k_group > 0
-                            ? tile + off_kparams(L) + ((size_t)t * (d / L->k_group) + c / L->k_group) * 4
-                            : tile + off_kparams(L) + (size_t)c * 4;
-    const uint8_t* vp = tile + off_vparams(L) + ((size_t)t * (d / L->v_group) + c / L->v_group) * 4;
+    const uint8_t* kp = L->k_group > 0 ? tile + kparams_off(L, t) + (size_t)(c / L->k_group) * 4
+                                       : tile + kchan_off(L, c);
+    const uint8_t* vp = tile + vparams_off(L, t) + (size_t)(c / L->v_group) * 4;
     k_out[c] = (double)unpack_code(kr, c, bits) * (double)orc_f16_to_f32(get_u16(kp)) +
                (double)orc_f16_to_f32(get_u16(kp + 2));
     v_out[c] = (double)unpack_code(vr, c, bits) * (double)orc_f16_to_f32(get_u16(vp)) +

@@ -193,9 +193,11 @@ def grid_rows(rng, n_rows, d, g, bits):
 
 @pytest.mark.parametrize("mixed", [0, 1])
 def test_tile_byte_positions(orc, mixed):
-    # Codes, params and header land where the layout says: K codes row t at t * S, V codes after
-    # 256 * S, K params [t][group] {scale, zero} after 2 * 256 * S, V params next, header last; 4-bit codes
-    # low nibble first (codes (2, 4) -> byte 0x42); unused slot bytes and tail padding are zero.
+    # Codes, params and header land where the layout says: row record t at t * 2S holds the row's K codes
+    # then, right after them, its V codes (d/2 bytes each for a 4-bit row, d for an 8-bit row); parameter
+    # record t at 2 * 256 * S + t * P holds K params [group] {scale, zero} then V params; header last;
+    # 4-bit codes low nibble first (codes (2, 4) -> byte 0x42); the rest of a record and the tail padding
+    # are zero.
     d, H, g = 64, 2, 32
     rng = np.random.default_rng(5)
     lay = orc.make_layout(d, H, g, g, 0, mixed)
@@ -219,18 +221,22 @@ def test_tile_byte_positions(orc, mixed):
     orc.quantize_blocks(lay, pool, [1], k, v, prec)
     assert not pool[: H * tb].any() and not pool[2 * H * tb:].any()
     S = d * (8 if mixed else 4) // 8
+    P = 2 * (d // g) * 4
     for h in range(H):
         tile = pool[(1 * H + h) * tb: (1 * H + h + 1) * tb]
-        for name, base_c, base_p in (("k", 0, 2 * 256 * S), ("v", 256 * S, 2 * 256 * S + 256 * (d // g) * 4)):
+        for name, base_p in (("k", 2 * 256 * S), ("v", 2 * 256 * S + (d // g) * 4)):
             codes, s, z = ref[(name, h)]
             for t in range(256):
-                row = tile[base_c + t * S: base_c + (t + 1) * S]
+                rec = tile[t * 2 * S: (t + 1) * 2 * S]
+                n = d if wide[t] else d // 2          # code bytes of this row, for K and for V
+                row = rec[:n] if name == "k" else rec[n: 2 * n]
                 if wide[t]:
                     assert np.array_equal(row, codes[t].astype(np.uint8))
                 else:
                     packed = (codes[t][0::2] | (codes[t][1::2] << 4)).astype(np.uint8)
-                    assert np.array_equal(row[: d // 2], packed) and not row[d // 2:].any()
-                par = tile[base_p + t * (d // g) * 4: base_p + (t + 1) * (d // g) * 4].view(np.float16)
+                    assert np.array_equal(row, packed)
+                assert not rec[2 * n:].any()
+                par = tile[base_p + t * P: base_p + t * P + (d // g) * 4].view(np.float16)
                 assert np.array_equal(par[0::2].astype(np.float64), s[t])
                 assert np.array_equal(par[1::2].astype(np.float64), z[t])
         end = 2 * 256 * S + 2 * 256 * (d // g) * 4
@@ -261,7 +267,7 @@ def test_per_channel_groups_are_columns(orc):
     orc.quantize_blocks(lay, pool, [0], x, x)
     S = d // 2
     got = np.zeros((256, d), np.int64)
-    kc = pool[: 256 * S].reshape(256, S)
+    kc = pool[: 256 * 2 * S].reshape(256, 2 * S)[:, :S]
     got[:, 0::2] = kc & 0xF
     got[:, 1::2] = kc >> 4
     assert np.array_equal(got, codes)
