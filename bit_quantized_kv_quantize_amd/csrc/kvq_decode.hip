@@ -288,6 +288,7 @@ hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t str
   const bool generic = force && !strcmp(force, "generic");
   const bool mfma = force && !strcmp(force, "mfma");
   if (!generic && !mfma && decode_rows_supported(g, a.G)) return launch_decode_rows(g, a, stream);
+  if (!generic && !mfma && decode_kchan_supported(g, a.G)) return launch_decode_kchan(g, a, stream);
   if (!generic && decode_mfma_supported(g, a.G)) return launch_decode_mfma(g, a, stream);
   return launch_decode_generic(g, a, stream);
 }

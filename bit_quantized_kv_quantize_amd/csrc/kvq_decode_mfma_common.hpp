@@ -41,6 +41,23 @@ __device__ __forceinline__ float row_sum16(float v) {
 }
 
 constexpr float kTwo24 = 16777216.0f;
+
+// Wave-uniform power-of-two scale for the fp16 p * v_scale operands of one chunk, from the chunk's largest
+// V scale vmax (this lane's value; reduced over the wave here): with p <= 1 every p * v_scale * scale is
+// below 2^15, and the weights that matter stay far above the fp16 subnormal range instead of flushing to
+// zero (a flushed product would drop the token's code term but keep its zero-point term). Returns the
+// scale and sets inv to its inverse; both are exact powers of two.
+__device__ __forceinline__ float chunk_pv_scale(float vmax, float& inv) {
+  vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x128, 0xf, 0xf, false)));
+  vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x124, 0xf, 0xf, false)));
+  vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x122, 0xf, 0xf, false)));
+  vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x121, 0xf, 0xf, false)));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+  const int ex = vmax > 0.0f ? ((__float_as_int(vmax) >> 23) & 0xff) - 126 : 0;  // vmax < 2^ex
+  inv = __builtin_amdgcn_ldexpf(1.0f, ex - 15);
+  return __builtin_amdgcn_ldexpf(1.0f, 15 - ex);
+}
 constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table slice is staged in LDS)
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) (their (m, l) are staged in LDS)
 constexpr float kTwo20 = 1048576.0f;

@@ -410,18 +410,31 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     }
     // ---------------------------------------------------------- p * v_scale (hi, lo) to LDS
     // Position of token t: (t & ~7) | sinv(t & 7), sinv(u) = 2 (u & 3) + (u >> 2), the inverse of the
-    // token order 0,4,1,5,2,6,3,7 of the V operand; odd tokens of 4-bit chunks are divided by 16.
+    // token order 0,4,1,5,2,6,3,7 of the V operand; odd tokens of 4-bit chunks are divided by 16. The
+    // chunk's operands carry the wave-uniform scale of chunk_pv_scale (undone when the chunk is added).
+    // Odd tokens (u odd) enter the MFMA as -p * v_scale times the complemented code (L - code, L = 15 or
+    // 255) and add p * (v_zero + L * v_scale) to the zero-point term, which is the same value: the
+    // products then carry both signs, so the matrix core's rounding of long all-positive sums does not
+    // bias the code term (which cancels against the zero-point term down to the much smaller output).
+    float vmax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vmax = fmaxf(vmax, fmaxf(h2f(r.vp[c][0] & 0xffffu), h2f(r.vp[c][1] & 0xffffu)));
+    float pv_inv;
+    const float pv_scale = chunk_pv_scale(vmax, pv_inv);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int t = 16 * c + lj, u = lj & 7;
       const int pos = (t & ~7) | (((u & 3) << 1) | (u >> 2));
       const float pp = p[c];
       const bool on = pp != 0.0f;
-      const float f = (!W8 && (u & 1)) ? 0.0625f : 1.0f;
+      const bool odd = u & 1;
+      const float f = odd ? (W8 ? -pv_scale : -0.0625f * pv_scale) : pv_scale;
+      const float Lc = odd ? (W8 ? 255.0f : 15.0f) : 0.0f;
       const float vs0 = on ? h2f(r.vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(r.vp[c][0] >> 16) : 0.0f;
       const float vs1 = on ? h2f(r.vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(r.vp[c][1] >> 16) : 0.0f;
-      zacc0 += pp * vz0;
-      zacc1 += pp * vz1;
+      zacc0 += pp * (vz0 + Lc * vs0);
+      zacc1 += pp * (vz1 + Lc * vs1);
       const float pv0 = (pp * f) * vs0, pv1 = (pp * f) * vs1;
       const _Float16 h0 = (_Float16)pv0, h1 = (_Float16)pv1;
       const _Float16 e0 = (_Float16)(pv0 - (float)h0), e1 = (_Float16)(pv1 - (float)h1);
@@ -436,6 +449,12 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---------------------------------------------------------- PV on the matrix cores
+    // The chunk accumulates into fresh MFMA tiles that are then added to the running output in fp32: the
+    // code sum p * v_scale * code is much larger than the output it cancels down to (the group zeros'
+    // term is added separately), and a long chain of MFMA accumulations would lose that difference.
+    floatx4 ob[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ob[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int NKB = W8 ? 1 : 2;  // 32-token k-blocks
     u32x4 pa[NKB];
 #pragma unroll
@@ -452,9 +471,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         const v2i x = lds_tr4(sv + tok * kVP + 8 * t);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t wd = (uint32_t)(kb ? x.y : x.x), w8 = wd >> 8;
+          // high nibbles (odd tokens) complemented: 15 - code
+          const uint32_t wd = (uint32_t)(kb ? x.y : x.x) ^ 0xF0F0F0F0u, w8 = wd >> 8;
           const u32x4 b = {wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
-          o[t] = mfma16(pa[kb], b, o[t]);
+          ob[t] = mfma16(pa[kb], b, ob[t]);
         }
       }
     } else {
@@ -463,11 +483,16 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       for (int t = 0; t < 8; ++t) {
         const v2i x = lds_tr8(sv + tok * kVP8 + 16 * t + 8 * (lj & 1));
         const uint32_t lo = (uint32_t)x.x, hi = (uint32_t)x.y;
-        const u32x4 b = {__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
-                         __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
-        o[t] = mfma16(pa[0], b, o[t]);
+        // tokens 1, 5 and 3, 7 (odd) complemented: 255 - code
+        const u32x4 b = {__builtin_amdgcn_perm(hi, lo, pair_sel(0)),
+                         __builtin_amdgcn_perm(hi, lo, pair_sel(1)) ^ 0x00FF00FFu,
+                         __builtin_amdgcn_perm(hi, lo, pair_sel(2)),
+                         __builtin_amdgcn_perm(hi, lo, pair_sel(3)) ^ 0x00FF00FFu};
+        ob[t] = mfma16(pa[0], b, ob[t]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] += ob[t] * pv_inv;
     __builtin_amdgcn_wave_barrier();
   };
   auto run = [&](const Raw& r, int i) __attribute__((always_inline)) {

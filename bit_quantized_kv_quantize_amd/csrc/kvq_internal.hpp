@@ -89,11 +89,14 @@ struct DecodeArgs {
   float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale
   SplitPlan plan;
 };
-// Decode dispatch: the row-list matrix-core kernel where its layout is compiled, then the block matrix-core
-// kernel, then the generic kernel. The environment variable KVQ_DECODE_KERNEL (a test hook) may name
-// "generic" or "mfma" to skip the kernels before it.
+// Decode dispatch: the row-list matrix-core kernel (per-token K groups) or the per-channel-K matrix-core
+// kernel where their layouts are compiled, then the block matrix-core kernel, then the generic kernel.
+// The environment variable KVQ_DECODE_KERNEL (a test hook) may name "generic" or "mfma" to skip the
+// kernels before it.
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_rows_supported(const TileGeom& g, int G);
+bool decode_kchan_supported(const TileGeom& g, int G);
+hipError_t launch_decode_kchan(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const TileGeom& g, int G);
