@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics only)")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload decode table")
     return ap.parse_args()
 
 
@@ -54,17 +55,55 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def decode_bytes(cfg: W.Config, case: W.Case, tile_bytes: int, live_rows_per_seq: np.ndarray) -> int:
-    """Algorithmic bytes of one decode-attention call: every live row's K and V codes and params once,
-    the mixed-pool bitmaps of the tiles touched, q, out, block tables, lengths and masks."""
+def live_rows(case: W.Case, wide_bits=None, appended_prec=None):
+    """(live 4-bit rows, live 8-bit rows) per sequence of one decode call: slots below seq_len whose
+    sentinel bit is clear; a row is 8-bit when its block's width bitmap (``wide_bits``: physical block ->
+    uint32[8]) or, for the appended slot, ``appended_prec`` says so."""
+    n4 = np.zeros(case.n_seqs, np.int64)
+    n8 = np.zeros(case.n_seqs, np.int64)
+    for s in range(case.n_seqs):
+        L = int(case.seq_lens[s])
+        t = np.arange(L)
+        live = np.ones(L, bool)
+        if case.sentinel_mask is not None:
+            live = ~((case.sentinel_mask[s][t // 32] >> (t % 32).astype(np.uint32)) & 1).astype(bool)
+        wide = np.zeros(L, bool)
+        if wide_bits is not None:
+            for bi in range((L + W.BLOCK - 1) // W.BLOCK):
+                words = wide_bits.get(int(case.block_table[s, bi]))
+                if words is not None:
+                    tt = np.arange(min(W.BLOCK, L - bi * W.BLOCK))
+                    wide[bi * W.BLOCK: bi * W.BLOCK + tt.size] = (words[tt // 32] >> (tt % 32).astype(np.uint32)) & 1
+            if case.append and appended_prec is not None and appended_prec[s] == 8:
+                wide[L - 1] = True
+        n4[s] = int((live & ~wide).sum())
+        n8[s] = int((live & wide).sum())
+    return n4, n8
+
+
+def decode_bytes(cfg: W.Config, case: W.Case, n4: np.ndarray, n8: np.ndarray, unique: bool = True) -> int:
+    """Algorithmic bytes of one decode-attention call: every live row's K and V codes and parameters once
+    (a block shared by several block tables counted once when ``unique``), the per-channel K parameters
+    and width bitmaps of the tiles touched, q, out, block tables, lengths and masks."""
     d, H = cfg.head_dim, cfg.num_kv_heads
-    if cfg.mixed:
-        raise NotImplementedError("mixed pools use per-row widths; see decode_bytes_mixed")
     kpar = (d // cfg.k_group) * 4 if cfg.k_group > 0 else 0
-    row = 2 * (d // 2) + kpar + (d // cfg.v_group) * 4
-    b = int(live_rows_per_seq.sum()) * H * row
-    if cfg.k_group < 0:  # per-channel K params: once per touched tile
-        b += int(np.ceil(case.seq_lens / W.BLOCK).sum()) * H * d * 4
+    vpar = (d // cfg.v_group) * 4
+    row4, row8 = d + kpar + vpar, 2 * d + kpar + vpar
+    if unique and cfg.table == "shared_prefix":
+        # every physical block read once: its live rows are the rows below the longest sequence using it
+        rows = 0
+        for b in np.unique(case.block_table[case.block_table >= 0]):
+            hits = np.argwhere(case.block_table == b)
+            rows += max(min(W.BLOCK, int(case.seq_lens[s]) - int(j) * W.BLOCK) for s, j in hits)
+        b = rows * H * row4
+        tiles = np.unique(case.block_table).size
+    else:
+        b = int((n4 * row4 + n8 * row8).sum()) * H
+        tiles = int(np.ceil(case.seq_lens / W.BLOCK).sum())
+    if cfg.k_group < 0:
+        b += tiles * H * d * 4
+    if cfg.mixed:
+        b += tiles * H * 32
     b += case.n_seqs * cfg.num_q_heads * d * (2 + 4)                 # q fp16 in, out fp32
     b += case.block_table.size * 4 + case.n_seqs * 4
     if case.sentinel_mask is not None:
@@ -208,8 +247,8 @@ def main():
         run()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t_start) / args.steps
-    live = case.seq_lens.astype(np.int64)
-    dec_b = decode_bytes(cfg, case, tb, live)
+    n4, n8 = live_rows(case)
+    dec_b = decode_bytes(cfg, case, n4, n8)
     app_b = append_bytes(cfg, case.n_seqs)
     step_bytes = (dec_b + app_b) * layers
     value = step_bytes / step_s / 1e9
@@ -262,6 +301,19 @@ def main():
     digest = kernel_source_digest()
     traffic = recorded_traffic(cfg.name, digest)
 
+    # ---------------------------------------------------------------- every workload's decode kernel
+    workloads = None
+    if not args.no_workloads:
+        del pools, aks, avs, qs, outs
+        torch.cuda.empty_cache()
+        workloads = {}
+        for name in W.CONFIG_ORDER:
+            if name != cfg.name:
+                workloads[name] = measure_workload(kvq, torch, name)
+        workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
+                               "GBps": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
+                               "pool_instances": layers, "append_us": None}
+
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -290,11 +342,99 @@ def main():
         "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "decode_attn_k", "bytes_per_launch": dec_b, "us_per_launch": round(kern_s * 1e6, 3),
+                     "kernel": "decode_rows_k<4, false>", "bytes_per_launch": dec_b,
+                     "us_per_launch": round(kern_s * 1e6, 3),
                      "kernel_sources": digest},
         "cpu_baseline": cpu,
+        "workloads": workloads,
     }
     print(json.dumps(line), flush=True)
+
+
+# Pool instances cycled through when one workload's decode is timed on its own: enough distinct copies that
+# the working set exceeds the 256 MB Infinity Cache (the multi-layer workloads use their layer count).
+INSTANCES = {"tiny_1k": 1, "gemma3_12b_4k": 48, "llama31_8b_pool_8k": 32, "qwen25_14b_prefix_32k": 16,
+             "mixed_sentinel_32k": 1}
+
+
+def measure_workload(kvq, torch, name, launches=16):
+    """One workload at full size: its layer quantised on the GPU (copied to INSTANCES pools), the append
+    where the workload appends, then decode kernels captured back to back in a HIP graph (cycling the
+    pools) and timed between events on the launch stream. Returns per-launch times and algorithmic bytes."""
+    cfg = W.CONFIGS[name]
+    case = W.make_case(cfg)
+    lay = kvq.Layout(**cfg.layout())
+    pool = kvq.new_pool(lay, case.num_blocks)
+    prec = np.full(case.n_seqs, 4, np.uint8) if cfg.mixed else None
+    wide = {} if cfg.mixed else None
+    for ids, k, v, bm in W.prefill_chunks(case, 0, max_blocks=2048, threads=16, prec_out=prec):
+        kvq.quantize_blocks(lay, pool, torch.from_numpy(ids).cuda(), torch.from_numpy(k).view(torch.float16).cuda(),
+                            torch.from_numpy(v).view(torch.float16).cuda(),
+                            None if bm is None else torch.from_numpy(bm.view(np.int32)).cuda())
+        if bm is not None:
+            for i, b in enumerate(ids):
+                wide[int(b)] = bm[i]
+    table = torch.from_numpy(case.block_table).cuda()
+    positions = torch.from_numpy(case.positions).cuda()
+    seq_lens = torch.from_numpy(case.seq_lens).cuda()
+    mask = None if case.sentinel_mask is None else torch.from_numpy(case.sentinel_mask.view(np.int32)).cuda()
+    q = torch.from_numpy(W.queries(cfg, 0, case.n_seqs)).view(torch.float16).cuda()
+    out = torch.empty((case.n_seqs, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    ws = kvq.new_workspace(lay, case.n_seqs, cfg.num_q_heads, case.max_seq_len)
+    app = None
+    if case.append:
+        ak, av = W.append_kv(cfg, 0, case.n_seqs)
+        app = (torch.from_numpy(ak).view(torch.float16).cuda(), torch.from_numpy(av).view(torch.float16).cuda(),
+               None if prec is None else torch.from_numpy(prec).cuda())
+        kvq.append_tokens(lay, pool, app[0], app[1], table, positions, app[2])
+    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name, 1) - 1)]
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(launches):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(launches):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / launches)
+        return float(np.median(ts))
+
+    dec_us = timed(lambda i: kvq.decode_attention(lay, pools[i % len(pools)], q, table, seq_lens, case.max_seq_len,
+                                                   mask, out=out, workspace=ws))
+    app_us = None
+    if app is not None:
+        app_us = timed(lambda i: kvq.append_tokens(lay, pools[i % len(pools)], app[0], app[1], table, positions,
+                                                   app[2]))
+    n4, n8 = live_rows(case, wide, prec)
+    b = decode_bytes(cfg, case, n4, n8, unique=True)
+    res = {"decode_us": round(dec_us, 2), "bytes": b, "GBps": round(b / dec_us / 1e3, 1),
+           "frac_of_hbm_peak": round(b / dec_us / 1e3 / HBM_PEAK_GBPS, 4), "pool_instances": len(pools),
+           "append_us": None if app_us is None else round(app_us, 2)}
+    b_log = decode_bytes(cfg, case, n4, n8, unique=False)
+    if b_log != b:
+        res["logical_bytes"] = b_log
+        res["logical_GBps"] = round(b_log / dec_us / 1e3, 1)
+    log("workload %s: decode %.2f us/launch, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)%s" %
+        (name, dec_us, b / dec_us / 1e3, b / dec_us / 1e3 / 80, "" if app_us is None else ", append %.2f us" % app_us))
+    del pools, pool
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cfg, case, dec_bytes_per_layer):
