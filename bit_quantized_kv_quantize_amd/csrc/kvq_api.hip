@@ -56,10 +56,9 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
   if (ns > nb) ns = nb;
   if (ns > 64) ns = 64;                                // at most 64 splits per (sequence, KV head)
   if (ns < (nb + 511) / 512) ns = (nb + 511) / 512;  // a split owns at most 512 blocks
-  int bps = (int)((nb + ns - 1) / ns);
   SplitPlan p;
-  p.blocks_per_split = bps;
-  p.n_splits = (nb + bps - 1) / bps;
+  p.n_splits = (int)ns;
+  p.blocks_per_split = (int)((nb + ns - 1) / ns);
   return p;
 }
 

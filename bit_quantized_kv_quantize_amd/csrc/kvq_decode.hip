@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
   const int G = a.G;
   const int len = a.seq_lens[seq];
   const int nblk = (len + kRows - 1) / kRows;
-  const int b0 = split * a.plan.blocks_per_split;
-  const int b1 = min(b0 + a.plan.blocks_per_split, nblk);
+  int b0, b1;
+  split_range(split, a.plan.n_splits, nblk, b0, b1);
   const uint32_t* mask_row = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
   const size_t part0 = ((size_t)seq * a.num_q_heads + (size_t)h * G) * a.plan.n_splits + split;
 

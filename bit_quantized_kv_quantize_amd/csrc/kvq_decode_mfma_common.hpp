@@ -42,6 +42,16 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 constexpr float kTwo24 = 16777216.0f;
 
+// Workgroup barrier for LDS traffic only: the fences are limited to the local address space, so the
+// barrier waits for this wave's LDS operations but not for its outstanding global loads (__syncthreads
+// waits for those too, which would drain every prefetch in flight). Not for code with DMA into LDS
+// pending (the local fence then waits for the DMA).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-uniform power-of-two scale for the fp16 p * v_scale operands of one chunk, from the chunk's largest
 // V scale vmax (this lane's value; reduced over the wave here): with p <= 1 every p * v_scale * scale is
 // below 2^15, and the weights that matter stay far above the fp16 subnormal range instead of flushing to
@@ -59,7 +69,7 @@ __device__ __forceinline__ float chunk_pv_scale(float vmax, float& inv) {
   return __builtin_amdgcn_ldexpf(1.0f, 15 - ex);
 }
 constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table slice is staged in LDS)
-constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) (their (m, l) are staged in LDS)
+constexpr int kMaxSplits = 64;        // splits per (sequence, KV head)
 constexpr float kTwo20 = 1048576.0f;
 
 // Split-K arrival for split `split` of (seq, h) once its partials (m, l, acc[d]) per query head are
@@ -94,43 +104,47 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
   }
   __syncthreads();
   if (!s_last) return;
-  // Merge: one round of parallel loads stages every split's (m, l), the per-head weights follow in LDS,
-  // then one round of independent loads fetches the accumulators.
-  __shared__ float s_sm[G][kMaxSplits], s_sw[G][kMaxSplits];
+  // Merge in one round of loads: thread (head jj, channel c) reads (m, l) and the accumulator of up to
+  // eight splits at a time and folds them into a running (M, L, o); the merged rows go through LDS to
+  // the finalisation, which wants channel c of one head in thread c.
   __shared__ float s_hM[G], s_hL[G];
-  for (int i = tid; i < G * ns; i += 256) {
-    const int jj = i / ns, sp = i % ns;
-    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + sp;
-    const float li = __hip_atomic_load(&a.ws_ml[2 * pi + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float mi = __hip_atomic_load(&a.ws_ml[2 * pi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_sm[jj][sp] = li > 0.0f ? mi : kNegInf;
-    s_sw[jj][sp] = li;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = kNegInf;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, s_sm[tid][sp]);
-    float L = 0.0f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float wgt = s_sm[tid][sp] == kNegInf ? 0.0f : exp2f(s_sm[tid][sp] - M);
-      L += s_sw[tid][sp] * wgt;
-      s_sw[tid][sp] = wgt;
-    }
-    s_hM[tid] = M;
-    s_hL[tid] = L;
-  }
-  __syncthreads();
   float* s_merged = const_cast<float*>(part_acc);  // this split's own partials are no longer needed
   for (int i = tid; i < G * D; i += 256) {
     const int jj = i / D, c = i % D;
     const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * ns;
-    float o = 0.0f;
-#pragma unroll 4
-    for (int sp = 0; sp < ns; ++sp) {
-      const float x = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      o += s_sw[jj][sp] != 0.0f ? x * s_sw[jj][sp] : 0.0f;  // unwritten accumulators are selected away
+    float M = kNegInf, L = 0.0f, o = 0.0f;
+    for (int base = 0; base < ns; base += 8) {
+      float mi[8], li[8], xi[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sp = min(base + k, ns - 1);
+        li[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mi[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        xi[k] = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float mb = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (base + k < ns && li[k] > 0.0f) mb = fmaxf(mb, mi[k]);
+      if (mb == kNegInf) continue;
+      const float r = M == kNegInf ? 0.0f : exp2f(M - mb);
+      L *= r;
+      o *= r;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (base + k < ns && li[k] > 0.0f) {  // splits without live rows left their accumulators unwritten
+          const float wgt = exp2f(mi[k] - mb);
+          L += li[k] * wgt;
+          o += xi[k] * wgt;
+        }
+      }
+      M = mb;
     }
     s_merged[i] = o;
+    if (c == 0) {
+      s_hM[jj] = M;
+      s_hL[jj] = L;
+    }
   }
   __syncthreads();
   const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);

@@ -160,11 +160,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
     l8 = l4 + a.list_cap;
   } else {
-    const int nblk = (len + kRows - 1) / kRows;
-    b0 = split * a.plan.blocks_per_split;
-    const int b1 = min(b0 + a.plan.blocks_per_split, nblk);
-    nchunk = max(b1 - b0, 0);
-    wg_empty = nchunk == 0;
+    int b1;
+    split_range(split, ns, (len + kRows - 1) / kRows, b0, b1);
+    nchunk = b1 - b0;
+    wg_empty = nchunk <= 0;
   }
 
   if (wg_empty) {
@@ -184,6 +183,15 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
                           &s_wacc[0][0][0]);
     }
     return;
+  }
+  // The query goes into registers first and the block table (streaming) into LDS: the chunks' loads
+  // are issued after both, and the query set-up below waits only for the query.
+  constexpr int kQPer = (G * D + 255) / 256;
+  uint16_t qraw[kQPer];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = min(tid + 256 * k, G * D - 1);  // unconditional loads: no branch waits for them
+    qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D];
   }
   if (!GATHER) {
     for (int i = tid; i < nchunk; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
@@ -232,13 +240,14 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         row[c] = en.e[c] & 255u;
       }
     } else {
-      // the block's tile base is wave-uniform: scalar base, 32-bit per-lane offsets
+      // the block's tile base is wave-uniform: scalar base, 32-bit per-lane offsets; a row past the
+      // sequence's end reads row 0 instead (live, and fetched for wave 0 anyway, so an L2 hit)
       const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
       const uint8_t* t0 = pool_h + (size_t)phys * tstride;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         tile[c] = t0;
-        row[c] = 64 * w + 16 * c + lj;
+        row[c] = ((en.valid >> c) & 1u) ? (uint32_t)(64 * w + 16 * c + lj) : 0u;
       }
     }
     r.valid = en.valid;
@@ -271,20 +280,29 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     }
   };
 
-  // The first chunk's loads are issued before the query set-up, so their latency overlaps it.
-  Raw ra, rb;
+  // The first chunks' loads are issued before the query set-up, so their latency overlaps it: one chunk
+  // in gather mode, two in streaming mode (which keeps two chunks in flight).
+  Raw ra, rb, rc;
   Ent en;
   if (nchunk > 0) {
     fetch(en, 0);
     load(ra, en, 0);
     fetch(en, min(1, nchunk - 1));
+    if (!GATHER) {
+      load(rb, en, min(1, nchunk - 1));
+      fetch(en, min(2, nchunk - 1));
+    }
   }
 
   // ------------------------------------------------------------ query: scale, rotation, group sums
-  for (int i = tid; i < G * D; i += 256)
-    s_q[i / D][i % D] = h2f(a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D]) * a.q_scale;
+  // (LDS-only barriers: the chunks' loads stay in flight)
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = tid + 256 * k;
+    if (i < G * D) s_q[i / D][i % D] = h2f(qraw[k]) * a.q_scale;
+  }
   for (int i = tid; i < 4 * 64 * kPP; i += 256) (&s_p[0][0])[i] = (_Float16)0.0f;
-  __syncthreads();
+  lds_barrier();
   if (g.rotate) {
     for (int hs = 1; hs < D; hs *= 2) {
       for (int i = tid; i < G * D / 2; i += 256) {
@@ -294,17 +312,17 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         s_q[j][lo] = x + y;
         s_q[j][lo + hs] = x - y;
       }
-      __syncthreads();
+      lds_barrier();
     }
     for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] *= a.unrot_c;
-    __syncthreads();
+    lds_barrier();
   }
   for (int i = tid; i < G * 2; i += 256) {
     float sum = 0.0f;
     for (int c = 0; c < 64; ++c) sum += s_q[i / 2][(i % 2) * 64 + c];
     s_qsum[i / 2][i % 2] = sum;
   }
-  __syncthreads();
+  lds_barrier();
 
   // QK A operand for k-step s: row lj = 4 hq + 2 gam + part; lane group la supplies channels
   // 32 la + 8 s + nib(e), e = 0..7, nib = 0,4,1,5,2,6,3,7 (the unpacking order of both widths); 4-bit
@@ -510,19 +528,41 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     process(r, std::false_type{});
   };
 
-  for (int i = 0; i < nchunk; i += 2) {
-    // sched_barrier keeps the next chunk's loads (and the list entries of the one after) ahead of this
-    // chunk's arithmetic, so they are in flight while it runs; past the end the last chunk is reloaded
-    // (an L2 hit) and not used.
-    load(rb, en, min(i + 1, nchunk - 1));
-    fetch(en, min(i + 2, nchunk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    run(ra, i);
-    if (i + 1 >= nchunk) break;
-    load(ra, en, min(i + 2, nchunk - 1));
-    fetch(en, min(i + 3, nchunk - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    run(rb, i + 1);
+  // sched_barrier keeps a chunk's loads (and the list entries of the one after) ahead of the arithmetic
+  // that follows, so they are in flight while it runs; past the end the last chunk is reloaded (an L2 hit)
+  // and not used.
+  if constexpr (!GATHER) {
+    // Streaming: three register sets, two chunks in flight while one is processed. The loop runs over
+    // whole triples with no exit in between (an exit there gives the compiler a path into the loop head
+    // on which it places over-strict waits); the last one or two chunks follow it.
+    auto issue = [&](Raw& r, int j) __attribute__((always_inline)) {
+      fetch(en, min(j, nchunk - 1));
+      load(r, en, min(j, nchunk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int i = 0;
+    for (; i + 2 < nchunk; i += 3) {
+      issue(rc, i + 2);
+      run(ra, i);
+      issue(ra, i + 3);
+      run(rb, i + 1);
+      issue(rb, i + 4);
+      run(rc, i + 2);
+    }
+    if (i < nchunk) run(ra, i);
+    if (i + 1 < nchunk) run(rb, i + 1);
+  } else {
+    for (int i = 0; i < nchunk; i += 2) {
+      load(rb, en, min(i + 1, nchunk - 1));
+      fetch(en, min(i + 2, nchunk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      run(ra, i);
+      if (i + 1 >= nchunk) break;
+      load(ra, en, min(i + 2, nchunk - 1));
+      fetch(en, min(i + 3, nchunk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      run(rb, i + 1);
+    }
   }
 
   // ---------------------------------------------------------------- merge the four waves

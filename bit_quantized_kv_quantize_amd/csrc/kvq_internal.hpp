@@ -42,12 +42,18 @@ struct TileGeom {
 int check_layout(const kvq_layout* L);
 TileGeom make_geom(const kvq_layout* L);
 
-// Split-K plan of the decode kernel: every (sequence, KV head) pair is cut into n_splits ranges of
-// blocks_per_split logical blocks.
+// Split-K plan of the decode kernels: the logical blocks of every (sequence, KV head) pair are cut into
+// n_splits even ranges (split_range); no range is longer than blocks_per_split.
 struct SplitPlan {
   int n_splits;
   int blocks_per_split;
 };
+// Blocks [b0, b1) of split `split` out of ns over a sequence of nblk blocks: even ranges, so the
+// splits of a pair differ by at most one block.
+__host__ __device__ inline void split_range(int split, int ns, int nblk, int& b0, int& b1) {
+  b0 = (int)(((long)split * nblk) / ns);
+  b1 = (int)(((long)(split + 1) * nblk) / ns);
+}
 SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len);
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 // Byte offsets of the workspace regions (split-K counters, partial (m, l), partial accumulators, row
