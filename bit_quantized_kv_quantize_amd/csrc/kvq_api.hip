@@ -75,7 +75,10 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   w.list = w.cnt + up(ns * 2 * sizeof(int));
   // row lists only for layouts the row-list kernel reads
   w.list_cap = decode_rows_supported(g, num_q_heads / g.H) ? (max_seq_len + 63) / 64 * 64 : 0;
-  w.total = w.list + up(ns * 2 * (size_t)w.list_cap * sizeof(uint32_t));
+  w.bcnt = w.list + up(ns * 2 * (size_t)w.list_cap * sizeof(uint32_t));
+  // at least one block per sequence, so the count kernels always have a grid
+  w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
+  w.total = w.bcnt + up(ns * 2 * (size_t)w.bcnt_blocks * sizeof(int));
   return w;
 }
 
@@ -189,6 +192,8 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.ws_cnt = (int*)(ws + wl.cnt);
   a.ws_list = (uint32_t*)(ws + wl.list);
   a.list_cap = wl.list_cap;
+  a.ws_bcnt = (int*)(ws + wl.bcnt);
+  a.bcnt_blocks = wl.bcnt_blocks;
   a.n_seqs = n_seqs;
   a.num_q_heads = num_q_heads;
   a.G = G;

@@ -59,54 +59,128 @@ constexpr int kVP8 = 144;   // LDS row pitch (bytes) of staged 8-bit V rows
 constexpr int kPP = 20;     // halves per position of the position-major p * v_scale tile (16 rows + pad)
 
 // ------------------------------------------------------------------------------------- row compaction
-// Grid (n_seqs), 256 threads. Writes, per sequence, the live 4-bit rows then the live 8-bit rows as
-// (physical block << 8 | row) in slot order, and their counts. A slot is live when it is below seq_len
-// and its sentinel bit is clear; its width comes from the mixed-pool bitmap (KV head 0's tile: every head
-// of a block holds the same per-token widths).
-__global__ __launch_bounds__(256) void compact_rows_k(TileGeom g, DecodeArgs a) {
-  __shared__ int s_c4[4], s_c8[4];
-  const int seq = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
+// Per sequence, the live 4-bit rows then the live 8-bit rows as (physical block << 8 | row) in slot
+// order, and their counts. A slot is live when it is below seq_len and its sentinel bit is clear; its
+// width comes from the mixed-pool bitmap (KV head 0's tile: every head of a block holds the same
+// per-token widths). Grid (n_seqs), 1024 threads. A wave takes 8 logical blocks at a time, 8 lanes per
+// block and 32 rows per lane (one word of the sentinel mask and of the width bitmap): the waves count
+// every block's live rows, the counts are scanned in the workspace, and the waves write each block's
+// entries at its offsets.
+constexpr int kCompactThreads = 1024;
+
+struct RowBits {
+  int b, phys;     // logical block (or -1 past the end), physical block
+  uint32_t w4, w8;  // rows 32k .. 32k + 31 of the block (k = lane & 7): live 4-bit, live 8-bit
+};
+__device__ __forceinline__ RowBits row_bits(const TileGeom& g, const DecodeArgs& a, int seq, int bb, int nblk, int len,
+                                            int l) {
+  RowBits r;
+  const int k = l & 7;
+  r.b = bb + (l >> 3);
+  if (r.b >= nblk) {
+    r.b = -1;
+    r.phys = 0;
+    r.w4 = r.w8 = 0u;
+    return r;
+  }
+  r.phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + r.b];
+  const int t0 = r.b * kRows + 32 * k;
+  const int nvalid = min(max(len - t0, 0), 32);
+  uint32_t live = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
+  if (a.mask) live &= ~a.mask[(size_t)seq * a.mask_words + (t0 >> 5)];
+  const uint32_t wide =
+      g.mixed ? reinterpret_cast<const uint32_t*>(a.pool + (size_t)r.phys * g.H * g.tile_bytes + g.off_hdr)[k] : 0u;
+  r.w4 = live & ~wide;
+  r.w8 = live & wide;
+  return r;
+}
+
+__global__ __launch_bounds__(kCompactThreads) void compact_rows_k(TileGeom g, DecodeArgs a) {
+  constexpr int NW = kCompactThreads / 64;
+  __shared__ int s_tot[NW][2];
+  __shared__ int s_carry[2];
+  const int seq = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int len = a.seq_lens[seq];
   const int nblk = (len + kRows - 1) / kRows;
-  uint32_t* l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
-  uint32_t* l8 = l4 + a.list_cap;
-  const uint32_t* mrow = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
-  int base4 = 0, base8 = 0;
-  for (int b = 0; b < nblk; ++b) {
-    const int phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + b];
-    const int t = b * kRows + tid;
-    bool live = t < len;
-    if (live && mrow) live = !((mrow[t >> 5] >> (t & 31)) & 1u);
-    bool wide = false;
-    if (g.mixed) {
-      const uint32_t* hdr = reinterpret_cast<const uint32_t*>(a.pool + (size_t)phys * g.H * g.tile_bytes + g.off_hdr);
-      wide = (hdr[tid >> 5] >> (tid & 31)) & 1u;
+  int* cnt = a.ws_bcnt + (size_t)seq * a.bcnt_blocks * 2;
+  // counts of each block (the 8 lanes of a block add theirs up)
+  for (int bb = 8 * w; bb < nblk; bb += 8 * NW) {
+    const RowBits r = row_bits(g, a, seq, bb, nblk, len, l);
+    int c4 = __popc(r.w4), c8 = __popc(r.w8);
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      c4 += __shfl_xor(c4, m);
+      c8 += __shfl_xor(c8, m);
     }
-    const uint64_t b4 = __ballot(live && !wide), b8 = __ballot(live && wide);
-    if ((tid & 63) == 0) {
-      s_c4[w] = __popcll(b4);
-      s_c8[w] = __popcll(b8);
+    if ((l & 7) == 0 && r.b >= 0) {
+      cnt[2 * r.b] = c4;
+      cnt[2 * r.b + 1] = c8;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the counts, kCompactThreads blocks at a time (thread = block)
+  if (tid == 0) {
+    s_carry[0] = 0;
+    s_carry[1] = 0;
+  }
+  __syncthreads();
+  for (int b0 = 0; b0 < nblk; b0 += kCompactThreads) {
+    const int b = b0 + tid;
+    const int c4 = b < nblk ? cnt[2 * b] : 0, c8 = b < nblk ? cnt[2 * b + 1] : 0;
+    int i4 = c4, i8 = c8;  // inclusive scan within the wave
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int u4 = __shfl_up(i4, m), u8 = __shfl_up(i8, m);
+      if (l >= m) {
+        i4 += u4;
+        i8 += u8;
+      }
+    }
+    if (l == 63) {
+      s_tot[w][0] = i4;
+      s_tot[w][1] = i8;
     }
     __syncthreads();
-    int o4 = base4, o8 = base8, t4 = 0, t8 = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o4 += i < w ? s_c4[i] : 0;
-      o8 += i < w ? s_c8[i] : 0;
-      t4 += s_c4[i];
-      t8 += s_c8[i];
+    int o4 = s_carry[0] + i4 - c4, o8 = s_carry[1] + i8 - c8;
+    for (int j = 0; j < w; ++j) {
+      o4 += s_tot[j][0];
+      o8 += s_tot[j][1];
     }
-    const uint64_t below = (1ull << (tid & 63)) - 1ull;
-    const uint32_t e = ((uint32_t)phys << 8) | (uint32_t)tid;
-    if (live && !wide) l4[o4 + __popcll(b4 & below)] = e;
-    if (live && wide) l8[o8 + __popcll(b8 & below)] = e;
-    base4 += t4;
-    base8 += t8;
+    __syncthreads();
+    if (b < nblk) {
+      cnt[2 * b] = o4;
+      cnt[2 * b + 1] = o8;
+    }
+    if (tid == kCompactThreads - 1) {
+      s_carry[0] = o4 + c4;
+      s_carry[1] = o8 + c8;
+    }
     __syncthreads();
   }
   if (tid == 0) {
-    a.ws_cnt[2 * seq] = base4;
-    a.ws_cnt[2 * seq + 1] = base8;
+    a.ws_cnt[2 * seq] = s_carry[0];
+    a.ws_cnt[2 * seq + 1] = s_carry[1];
+  }
+  // entries of each block at its offsets: lane k of a block starts after the live rows of lanes 0 .. k-1
+  uint32_t* l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
+  uint32_t* l8 = l4 + a.list_cap;
+  for (int bb = 8 * w; bb < nblk; bb += 8 * NW) {
+    const RowBits r = row_bits(g, a, seq, bb, nblk, len, l);
+    const int c4 = __popc(r.w4), c8 = __popc(r.w8);
+    int i4 = c4, i8 = c8;  // inclusive scan over the block's 8 lanes
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      const int u4 = __shfl_up(i4, m), u8 = __shfl_up(i8, m);
+      if ((l & 7) >= m) {
+        i4 += u4;
+        i8 += u8;
+      }
+    }
+    if (r.b < 0) continue;
+    int o4 = cnt[2 * r.b] + i4 - c4, o8 = cnt[2 * r.b + 1] + i8 - c8;
+    const uint32_t hi = ((uint32_t)r.phys << 8) | (uint32_t)(32 * (l & 7));
+    for (uint32_t m = r.w4; m; m &= m - 1u) l4[o4++] = hi | (uint32_t)(__ffs(m) - 1);
+    for (uint32_t m = r.w8; m; m &= m - 1u) l8[o8++] = hi | (uint32_t)(__ffs(m) - 1);
   }
 }
 
@@ -634,7 +708,7 @@ template <int G>
 hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.plan.n_splits, g.H, a.n_seqs);
   if (a.mask || g.mixed) {
-    hipLaunchKernelGGL(compact_rows_k, dim3(a.n_seqs), dim3(256), 0, stream, g, a);
+    hipLaunchKernelGGL(compact_rows_k, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
     hipLaunchKernelGGL((decode_rows_k<G, true>), grid, dim3(256), 0, stream, g, a);
   } else {
     hipLaunchKernelGGL((decode_rows_k<G, false>), grid, dim3(256), 0, stream, g, a);

@@ -59,8 +59,9 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
 // Byte offsets of the workspace regions (split-K counters, partial (m, l), partial accumulators, row
 // counts, row lists) for a call of this size; `total` is the size.
 struct WorkspaceLayout {
-  size_t ctr, ml, acc, cnt, list, total;
+  size_t ctr, ml, acc, cnt, list, bcnt, total;
   int list_cap;
+  int bcnt_blocks;  // blocks per sequence in the per-block live-row counts
 };
 WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 
@@ -86,6 +87,8 @@ struct DecodeArgs {
   int* ws_cnt;       // [n_seqs][2] live 4-bit / 8-bit rows (row-list kernel)
   uint32_t* ws_list; // [n_seqs][2][list_cap] live rows as (physical block << 8 | row)
   int list_cap;
+  int* ws_bcnt;      // [n_seqs][bcnt_blocks][2] live 4-bit / 8-bit rows of each logical block
+  int bcnt_blocks;
   int n_seqs;
   int num_q_heads;
   int G;
