@@ -59,6 +59,20 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
   SplitPlan p;
   p.n_splits = (int)ns;
   p.blocks_per_split = (int)((nb + ns - 1) / ns);
+  // Row-list kernel: the same round of 512 workgroups, but as one-dimensional grid in which pairs may get
+  // k or k + 1 splits, so that the grid is exactly full; at most 64 splits per pair and 512 blocks per
+  // split, at least one block per workgroup and one workgroup per pair.
+  long W = target_wgs;
+  if (W > units * nb) W = units * nb;
+  if (W > units * 64) W = units * 64;
+  if (W < units * ((nb + 511) / 512)) W = units * ((nb + 511) / 512);
+  if (W < units) W = units;
+  p.wgs = (int)W;
+  p.k = (int)(W / units);
+  p.nA = (int)(units - (W - (long)p.k * units));
+  p.max_blocks = nb;
+  const int rows_max = p.nA < units ? p.k + 1 : p.k;
+  p.stride = p.n_splits > rows_max ? p.n_splits : rows_max;
   return p;
 }
 
@@ -66,7 +80,7 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   SplitPlan p = plan_splits(g, n_seqs, max_seq_len);
   size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
-  size_t parts = ns * num_q_heads * p.n_splits;
+  size_t parts = ns * num_q_heads * p.stride;
   WorkspaceLayout w{};
   w.ctr = 0;
   w.ml = up(ns * g.H * sizeof(unsigned));

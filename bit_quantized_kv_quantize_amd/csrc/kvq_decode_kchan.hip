@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
       }
       for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
       __syncthreads();
-      splitk_arrive<D, G>(g, a, seq, h, split, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
+      splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
                           &s_wacc[0][0][0]);
     }
     return;
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     }
   }
   __syncthreads();
-  splitk_arrive<D, G>(g, a, seq, h, split, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
+  splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 
 template <int VG>

@@ -72,7 +72,7 @@ constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head)
 constexpr float kTwo20 = 1048576.0f;
 
-// Split-K arrival for split `split` of (seq, h) once its partials (m, l, acc[d]) per query head are
+// Split-K arrival for split `split` of the `ns` splits of (seq, h) once its partials (m, l, acc[d]) per query head are
 // ready: thread jj * D + c (and ml for c == 0) holds them in part_m / part_l / part_acc. The partials are
 // written with relaxed agent-scope atomic stores, which compile to cache-coherent (sc1) stores, so no
 // L2 write-back is needed; every thread waits for its stores to complete before the barrier, then one
@@ -80,14 +80,14 @@ constexpr float kTwo20 = 1048576.0f;
 // agent-scope atomic loads (sc1, coherent across XCDs), merges them in split order - so the result does
 // not depend on which split that is - finalises the output and resets the counter to zero.
 template <int D, int G>
-__device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int len, int tid,
-                              const float* part_m, const float* part_l, const float* part_acc, float* s_o) {
+__device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int ns, int len,
+                              int tid, const float* part_m, const float* part_l, const float* part_acc, float* s_o) {
   __shared__ int s_last;
   __shared__ int s_cnt[4];
-  const int ns = a.plan.n_splits;
+  const int st = a.plan.stride;
   for (int i = tid; i < G * D; i += 256) {
     const int jj = i / D, c = i % D;
-    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * ns + split;
+    const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * st + split;
     __hip_atomic_store(&a.ws_acc[pi * D + c], part_acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c == 0) {
       __hip_atomic_store(&a.ws_ml[2 * pi], part_m[jj], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -111,7 +111,7 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
   float* s_merged = const_cast<float*>(part_acc);  // this split's own partials are no longer needed
   for (int i = tid; i < G * D; i += 256) {
     const int jj = i / D, c = i % D;
-    const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * ns;
+    const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * st;
     float M = kNegInf, L = 0.0f, o = 0.0f;
     for (int base = 0; base < ns; base += 8) {
       float mi[8], li[8], xi[8];

@@ -207,9 +207,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   __shared__ float s_wacc[4][G][D];
   __shared__ int s_tbl[GATHER ? 1 : kMaxSplitBlocks];
 
-  const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
-  const int ns = a.plan.n_splits;
+  int pair, split, ns;  // ns: the split count of this workgroup's (sequence, KV head) pair
+  rows_work(a.plan, a.n_seqs * g.H, blockIdx.x, pair, split, ns);
+  const int seq = pair / g.H, h = pair - seq * g.H;
   const int len = a.seq_lens[seq];
   const uint32_t R = (uint32_t)g.rec;  // bytes of a row record
   const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;
@@ -218,7 +219,26 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   // ------------------------------------------------------------ this workgroup's chunks
   // Streaming: chunk i of wave w = rows 64w .. 64w+63 of logical block b0 + i. Gather: chunks c0 + w + 4i
   // of the sequence's chunk list (4-bit chunks of 64 rows first, then 8-bit chunks of 32 rows).
-  int b0 = 0, nchunk = 0, n4 = 0, n8 = 0, nc4 = 0, c0 = 0;
+  // The query and (streaming) the block-table slice are loaded into registers first: neither depends on the
+  // sequence length, so their loads overlap its load. Streaming splits cut the longest sequence's blocks;
+  // a shorter sequence clips them.
+  constexpr int kQPer = (G * D + 255) / 256;
+  uint16_t qraw[kQPer];
+#pragma unroll
+  for (int k = 0; k < kQPer; ++k) {
+    const int i = min(tid + 256 * k, G * D - 1);  // unconditional loads: no branch waits for them
+    qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D];
+  }
+  int b0 = 0, ntbl = 0, nchunk = 0, n4 = 0, n8 = 0, nc4 = 0, c0 = 0;
+  int tb0 = 0, tb1 = 0;
+  if (!GATHER) {
+    int b1;
+    piece_range(split, ns, a.plan.max_blocks, b0, b1);
+    ntbl = b1 - b0;  // 1 .. kMaxSplitBlocks
+    const int32_t* bt = a.block_table + (size_t)seq * a.max_blocks_per_seq + b0;
+    tb0 = bt[min(tid, ntbl - 1)];
+    if (ntbl > 256) tb1 = bt[min(tid + 256, ntbl - 1)];
+  }
   bool wg_empty;
   const uint32_t* l4 = nullptr;
   const uint32_t* l8 = nullptr;
@@ -234,9 +254,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
     l8 = l4 + a.list_cap;
   } else {
-    int b1;
-    split_range(split, ns, (len + kRows - 1) / kRows, b0, b1);
-    nchunk = b1 - b0;
+    nchunk = min(b0 + ntbl, (len + kRows - 1) / kRows) - b0;
     wg_empty = nchunk <= 0;
   }
 
@@ -253,22 +271,16 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
       for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
       __syncthreads();
-      splitk_arrive<D, G>(g, a, seq, h, split, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
+      splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
                           &s_wacc[0][0][0]);
     }
     return;
   }
-  // The query goes into registers first and the block table (streaming) into LDS: the chunks' loads
-  // are issued after both, and the query set-up below waits only for the query.
-  constexpr int kQPer = (G * D + 255) / 256;
-  uint16_t qraw[kQPer];
-#pragma unroll
-  for (int k = 0; k < kQPer; ++k) {
-    const int i = min(tid + 256 * k, G * D - 1);  // unconditional loads: no branch waits for them
-    qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D];
-  }
+  // The chunks' loads are issued after the table slice is in LDS; the query set-up below waits only for
+  // the query.
   if (!GATHER) {
-    for (int i = tid; i < nchunk; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
+    if (tid < nchunk) s_tbl[tid] = tb0;
+    if (tid + 256 < nchunk) s_tbl[tid + 256] = tb1;
     __syncthreads();
   }
 
@@ -701,12 +713,12 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     }
   }
   __syncthreads();
-  splitk_arrive<D, G>(g, a, seq, h, split, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
+  splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 
 template <int G>
 hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.plan.n_splits, g.H, a.n_seqs);
+  const dim3 grid(a.plan.wgs);
   if (a.mask || g.mixed) {
     hipLaunchKernelGGL(compact_rows_k, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
     hipLaunchKernelGGL((decode_rows_k<G, true>), grid, dim3(256), 0, stream, g, a);

@@ -42,17 +42,53 @@ struct TileGeom {
 int check_layout(const kvq_layout* L);
 TileGeom make_geom(const kvq_layout* L);
 
-// Split-K plan of the decode kernels: the logical blocks of every (sequence, KV head) pair are cut into
-// n_splits even ranges (split_range); no range is longer than blocks_per_split.
+// Split-K plan of the decode kernels.
+// The block kernels cut the logical blocks of every (sequence, KV head) pair into n_splits even ranges
+// (split_range) on a (split, KV head, sequence) grid; no range is longer than blocks_per_split.
+// The row-list kernel runs a one-dimensional grid of `wgs` workgroups: the first nA pairs get k splits and
+// the others k + 1 (rows_work), which fills exactly two workgroups per CU when there are fewer pairs.
+// `stride` is the number of partial slots per (sequence, query head) in the workspace: the largest split
+// count of either plan.
 struct SplitPlan {
   int n_splits;
   int blocks_per_split;
+  int stride;
+  int wgs;
+  int k;
+  int nA;
+  int max_blocks;  // logical blocks of the longest sequence
 };
 // Blocks [b0, b1) of split `split` out of ns over a sequence of nblk blocks: even ranges, so the
 // splits of a pair differ by at most one block.
 __host__ __device__ inline void split_range(int split, int ns, int nblk, int& b0, int& b1) {
   b0 = (int)(((long)split * nblk) / ns);
   b1 = (int)(((long)(split + 1) * nblk) / ns);
+}
+// Even ranges with the longer ones first: split j of ns over nblk blocks.
+__host__ __device__ inline void piece_range(int j, int ns, int nblk, int& b0, int& b1) {
+  const int q = nblk / ns, rem = nblk % ns;
+  b0 = j * q + (j < rem ? j : rem);
+  b1 = b0 + q + (j < rem ? 1 : 0);
+}
+// Work of workgroup wg of the row-list kernel: the (sequence, KV head) pair, its split and that pair's split
+// count. Slots are numbered split-major, first over the nA pairs with k splits, then over the pairs with
+// k + 1, so with longer pieces first the slot sizes never grow along the numbering. The first half of the
+// grid takes slots in order and the second half in reverse, so workgroups wg and wg + half pair the
+// longest pieces with the shortest. (A full launch of 2 x 256 workgroups places those two on one CU.)
+__host__ __device__ inline void rows_work(const SplitPlan& p, int n_pairs, int wg, int& pair, int& split, int& nsp) {
+  const int half = (p.wgs + 1) / 2;
+  const int s = wg < half ? wg : p.wgs - 1 - (wg - half);
+  const int sa = p.k * p.nA;
+  if (s < sa) {
+    split = s / p.nA;
+    pair = s - split * p.nA;
+    nsp = p.k;
+  } else {
+    const int nB = n_pairs - p.nA, t = s - sa;
+    split = t / nB;
+    pair = p.nA + (t - split * nB);
+    nsp = p.k + 1;
+  }
 }
 SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len);
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
@@ -82,8 +118,8 @@ struct DecodeArgs {
   const uint32_t* mask;
   float* out;
   unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernel); zero between calls
-  float* ws_ml;   // [n_seqs][H_q][n_splits] x {m, l}
-  float* ws_acc;  // [n_seqs][H_q][n_splits][d]
+  float* ws_ml;   // [n_seqs][H_q][plan.stride] x {m, l} (the generic kernel: [plan.n_splits])
+  float* ws_acc;  // [n_seqs][H_q][plan.stride][d]
   int* ws_cnt;       // [n_seqs][2] live 4-bit / 8-bit rows (row-list kernel)
   uint32_t* ws_list; // [n_seqs][2][list_cap] live rows as (physical block << 8 | row)
   int list_cap;
