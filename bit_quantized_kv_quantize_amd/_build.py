@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_rows.hip", "kvq_decode_kchan.hip"]
+SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_rows.hip", "kvq_decode_kchan.hip",
+           "kvq_decode_cascade.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

@@ -44,7 +44,7 @@ TileGeom make_geom(const kvq_layout* L) {
   return g;
 }
 
-SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
+SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
   // One round of resident workgroups on MI355X (256 CUs x 2 decode workgroups each): split each
   // (sequence, KV head) so the grid fills that round without exceeding it, never below one block per split.
   const long target_wgs = 256 * 2;
@@ -72,13 +72,28 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len) {
   p.nA = (int)(units - (W - (long)p.k * units));
   p.max_blocks = nb;
   const int rows_max = p.nA < units ? p.k + 1 : p.k;
-  p.stride = p.n_splits > rows_max ? p.n_splits : rows_max;
+  // Cascade (per-channel K layouts, two or more sequences): one workgroup per CU, 64 rows each; block
+  // ranges of at most 512 blocks.
+  const int G = g.H > 0 ? num_q_heads / g.H : 1;
+  p.casc = 0;
+  p.casc_rg = 0;
+  if (n_seqs >= 2 && decode_cascade_supported(g, G)) {
+    const long rg = ((long)n_seqs * G + kCascRows - 1) / kCascRows;
+    long S = 256 / (rg * g.H);
+    if (S > 64) S = 64;
+    if (S > nb) S = nb;
+    if (S < (nb + 511) / 512) S = (nb + 511) / 512;
+    if (S < 1) S = 1;
+    p.casc = (int)S;
+    p.casc_rg = (int)rg;
+  }
+  p.stride = (p.n_splits > rows_max ? p.n_splits : rows_max) + p.casc;
   return p;
 }
 
 WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  SplitPlan p = plan_splits(g, n_seqs, max_seq_len);
+  SplitPlan p = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
   size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
   size_t parts = ns * num_q_heads * p.stride;
   WorkspaceLayout w{};
@@ -92,7 +107,8 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   w.bcnt = w.list + up(ns * 2 * (size_t)w.list_cap * sizeof(uint32_t));
   // at least one block per sequence, so the count kernels always have a grid
   w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
-  w.total = w.bcnt + up(ns * 2 * (size_t)w.bcnt_blocks * sizeof(int));
+  w.cflag = w.bcnt + up(ns * 2 * (size_t)w.bcnt_blocks * sizeof(int));
+  w.total = w.cflag + up(p.casc > 0 ? (size_t)p.max_blocks * sizeof(int) : 0);
   return w;
 }
 
@@ -197,7 +213,7 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.seq_lens = seq_lens;
   a.mask = sentinel_mask;
   a.out = out;
-  a.plan = plan_splits(g, n_seqs, max_seq_len);
+  a.plan = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
   const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
   uint8_t* ws = (uint8_t*)workspace;
   a.ws_ctr = (unsigned*)(ws + wl.ctr);
@@ -208,6 +224,8 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.list_cap = wl.list_cap;
   a.ws_bcnt = (int*)(ws + wl.bcnt);
   a.bcnt_blocks = wl.bcnt_blocks;
+  a.ws_cflag = (int*)(ws + wl.cflag);
+  a.casc = 0;  // set by the dispatcher when the cascade kernel runs
   a.n_seqs = n_seqs;
   a.num_q_heads = num_q_heads;
   a.G = G;

@@ -13,7 +13,8 @@
 //   position-major and read with the 16-bit LDS transpose load; B = V codes staged in LDS and read with the
 //   4-bit transpose load, one output channel per lane; each 16-channel output tile uses its group's A.
 // Sentinel slots are skipped (their exact term is added when the output is finalised), and the split-K
-// merge runs in the split that arrives last (splitk_arrive).
+// merge runs in the split that arrives last (splitk_arrive). After the cascade kernel (a.casc > 0) the blocks
+// it flagged as shared by every sequence are skipped, and its partials join the merge.
 #include "kvq_decode_mfma_common.hpp"
 
 namespace kvq {
@@ -59,6 +60,8 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][NGV][64 * kPP];
   __shared__ float s_wm[4][G], s_wl[4][G];
   __shared__ int s_tbl[kMaxSplitBlocks];
+  __shared__ int s_col[kMaxSplitBlocks];
+  __shared__ int s_ccnt[4];
   static_assert(sizeof(float) * 4 * G * D <= sizeof(_Float16) * 4 * NGV * 64 * kPP, "s_wacc fits in s_p");
   float (*s_wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&s_p[0][0][0]);  // used after the token loop
 
@@ -69,13 +72,17 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   const int nblk = (len + kRows - 1) / kRows;
   int b0, b1;
   split_range(split, a.plan.n_splits, nblk, b0, b1);
-  const int nchunk = max(b1 - b0, 0);
+  // Blocks the cascade kernel took for every sequence are skipped here; its partials join the merge.
+  const int n_pre = a.casc;
+  const int nchunk = stage_columns(
+      max(b1 - b0, 0), tid, s_tbl, s_col, s_ccnt, [&](int i) { return n_pre == 0 || a.ws_cflag[b0 + i] == 0; },
+      [&](int i) { return a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i]; });
   const uint32_t* mask_row = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
   const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;
   const size_t tstride = (size_t)g.H * g.tile_bytes;
 
   if (nchunk == 0) {
-    if (ns == 1) {
+    if (ns == 1 && n_pre == 0) {
       __shared__ int s_cnt0[4];
       const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt0);
       for (int jj = 0; jj < G; ++jj)
@@ -88,13 +95,10 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
       for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
       __syncthreads();
       splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
-                          &s_wacc[0][0][0]);
+                          &s_wacc[0][0][0], n_pre);
     }
     return;
   }
-
-  for (int i = tid; i < nchunk; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
-  __syncthreads();
 
   auto load = [&](RawC& r, int i) __attribute__((always_inline)) {
     const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
         const uint2 x = *reinterpret_cast<const uint2*>(pp);
         r.vp[c] = u32x4{x.x, x.y, 0u, 0u};
       }
-      const int pos = (b0 + i) * kRows + (int)row;
+      const int pos = (b0 + s_col[i]) * kRows + (int)row;
       const uint32_t mw = (mask_row && pos < len) ? mask_row[pos >> 5] : 0u;
       live |= (pos < len && !((mw >> (row & 31)) & 1u)) ? (1u << c) : 0u;
     }
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     }
   }
   __syncthreads();
-  if (ns == 1) {
+  if (ns == 1 && n_pre == 0) {
     __shared__ int s_cnt[4];
     __shared__ float s_o[D];
     const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     }
   }
   __syncthreads();
-  splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
+  splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0], n_pre);
 }
 
 template <int VG>

@@ -72,16 +72,45 @@ constexpr int kMaxSplitBlocks = 512;  // blocks one workgroup may own (its table
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head)
 constexpr float kTwo20 = 1048576.0f;
 
+// Stages into s_tbl, in order, the block-table entries phys(i) of the columns 0 <= i < n for which keep(i)
+// holds (both evaluated by thread i mod 256, all 256 threads taking part) and returns their number.
+template <class Keep, class Phys>
+__device__ int stage_columns(int n, int tid, int* s_tbl, int* s_idx, int* s_cnt, Keep keep, Phys phys) {
+  const int w = tid >> 6, lane = tid & 63;
+  int total = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int i = base + tid;
+    const bool k = i < n && keep(i);
+    const int e = k ? phys(i) : 0;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(k);
+    if (lane == 0) s_cnt[w] = __builtin_popcountll(m);
+    __syncthreads();
+    int off = total;
+    for (int ww = 0; ww < w; ++ww) off += s_cnt[ww];
+    if (k) {
+      const int o = off + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      s_tbl[o] = e;
+      s_idx[o] = i;
+    }
+    total += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+    __syncthreads();
+  }
+  return total;
+}
+
 // Split-K arrival for split `split` of the `ns` splits of (seq, h) once its partials (m, l, acc[d]) per query head are
 // ready: thread jj * D + c (and ml for c == 0) holds them in part_m / part_l / part_acc. The partials are
 // written with relaxed agent-scope atomic stores, which compile to cache-coherent (sc1) stores, so no
 // L2 write-back is needed; every thread waits for its stores to complete before the barrier, then one
 // thread bumps the unit's arrival counter. The split that arrives last reads all partials back with
 // agent-scope atomic loads (sc1, coherent across XCDs), merges them in split order - so the result does
-// not depend on which split that is - finalises the output and resets the counter to zero.
+// not depend on which split that is - finalises the output and resets the counter to zero. The merge also
+// takes the n_pre partials that the cascade kernel left in the last n_pre slots of each row (earlier in
+// stream order, so plain loads see them); those carry no arrival.
 template <int D, int G>
 __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int ns, int len,
-                              int tid, const float* part_m, const float* part_l, const float* part_acc, float* s_o) {
+                              int tid, const float* part_m, const float* part_l, const float* part_acc, float* s_o,
+                              int n_pre = 0) {
   __shared__ int s_last;
   __shared__ int s_cnt[4];
   const int st = a.plan.stride;
@@ -113,11 +142,13 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
     const int jj = i / D, c = i % D;
     const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * st;
     float M = kNegInf, L = 0.0f, o = 0.0f;
-    for (int base = 0; base < ns; base += 8) {
+    const int nt = ns + n_pre, pre0 = st - n_pre - ns;  // slot of merged index k >= ns: k + pre0
+    for (int base = 0; base < nt; base += 8) {
       float mi[8], li[8], xi[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int sp = min(base + k, ns - 1);
+        const int kk = min(base + k, nt - 1);
+        const int sp = kk < ns ? kk : kk + pre0;
         li[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         mi[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         xi[k] = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -125,14 +156,14 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
       float mb = M;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (base + k < ns && li[k] > 0.0f) mb = fmaxf(mb, mi[k]);
+        if (base + k < nt && li[k] > 0.0f) mb = fmaxf(mb, mi[k]);
       if (mb == kNegInf) continue;
       const float r = M == kNegInf ? 0.0f : exp2f(M - mb);
       L *= r;
       o *= r;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (base + k < ns && li[k] > 0.0f) {  // splits without live rows left their accumulators unwritten
+        if (base + k < nt && li[k] > 0.0f) {  // splits without live rows left their accumulators unwritten
           const float wgt = exp2f(mi[k] - mb);
           L += li[k] * wgt;
           o += xi[k] * wgt;

@@ -47,8 +47,11 @@ TileGeom make_geom(const kvq_layout* L);
 // (split_range) on a (split, KV head, sequence) grid; no range is longer than blocks_per_split.
 // The row-list kernel runs a one-dimensional grid of `wgs` workgroups: the first nA pairs get k splits and
 // the others k + 1 (rows_work), which fills exactly two workgroups per CU when there are fewer pairs.
+// The cascade kernel (blocks shared by every sequence of the batch, per-channel K layouts) cuts the logical
+// block range into casc even ranges and the (sequence, query head) rows of each KV head into casc_rg
+// groups; its partials take the last casc slots of each row's partial slots.
 // `stride` is the number of partial slots per (sequence, query head) in the workspace: the largest split
-// count of either plan.
+// count of the per-sequence plans, plus casc.
 struct SplitPlan {
   int n_splits;
   int blocks_per_split;
@@ -57,6 +60,8 @@ struct SplitPlan {
   int k;
   int nA;
   int max_blocks;  // logical blocks of the longest sequence
+  int casc;        // cascade block ranges (0: no cascade slots)
+  int casc_rg;     // cascade row groups per KV head
 };
 // Blocks [b0, b1) of split `split` out of ns over a sequence of nblk blocks: even ranges, so the
 // splits of a pair differ by at most one block.
@@ -90,12 +95,12 @@ __host__ __device__ inline void rows_work(const SplitPlan& p, int n_pairs, int w
     nsp = p.k + 1;
   }
 }
-SplitPlan plan_splits(const TileGeom& g, int n_seqs, int max_seq_len);
+SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 // Byte offsets of the workspace regions (split-K counters, partial (m, l), partial accumulators, row
 // counts, row lists) for a call of this size; `total` is the size.
 struct WorkspaceLayout {
-  size_t ctr, ml, acc, cnt, list, bcnt, total;
+  size_t ctr, ml, acc, cnt, list, bcnt, cflag, total;
   int list_cap;
   int bcnt_blocks;  // blocks per sequence in the per-block live-row counts
 };
@@ -125,6 +130,8 @@ struct DecodeArgs {
   int list_cap;
   int* ws_bcnt;      // [n_seqs][bcnt_blocks][2] live 4-bit / 8-bit rows of each logical block
   int bcnt_blocks;
+  int* ws_cflag;     // [plan.max_blocks] 1 where the cascade kernel took the logical block for every sequence
+  int casc;          // cascade partial slots merged by the per-sequence kernel in this call (0 or plan.casc)
   int n_seqs;
   int num_q_heads;
   int G;
@@ -137,7 +144,7 @@ struct DecodeArgs {
 // Decode dispatch: the row-list matrix-core kernel (per-token K groups) or the per-channel-K matrix-core
 // kernel where their layouts are compiled, then the block matrix-core kernel, then the generic kernel.
 // The environment variable KVQ_DECODE_KERNEL (a test hook) may name "generic" or "mfma" to skip the
-// kernels before it.
+// kernels before it, or "nocascade" to keep shared blocks in the per-sequence kernel.
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_rows_supported(const TileGeom& g, int G);
 bool decode_kchan_supported(const TileGeom& g, int G);
@@ -145,6 +152,11 @@ hipError_t launch_decode_kchan(const TileGeom& g, const DecodeArgs& a, hipStream
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const TileGeom& g, int G);
+// Cascade kernel for blocks shared by all sequences: layouts of the per-channel-K kernel; the caller then
+// runs that kernel with a.casc set.
+bool decode_cascade_supported(const TileGeom& g, int G);
+constexpr int kCascRows = 32;  // (sequence, query head) rows of one cascade workgroup
+hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace kvq

@@ -151,6 +151,9 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
  * the packed tiles directly and dequantising in registers ([AMB] 2.1 item 2, direct restore without a
  * dequantised copy; 2.1 item 3, many agents batched in one launch; 2.2, GQA; [UQ] technology section,
  * AMD decode-attention kernel; [QKV] claims section, fused quantized attention kernel).
+ * Pools with K grouped per channel and no sentinel mask: a logical block that every sequence of the
+ * call maps to the same physical block, full in every sequence (a shared prompt prefix, [UQ] results
+ * section), is read once for the whole batch and its partial results merged into each sequence's.
  *
  *   q              device fp16 [n_seqs][num_q_heads][d]; query head j reads KV head j / G,
  *                  G = num_q_heads / H_kv (contiguous GQA groups).

@@ -144,3 +144,36 @@ def test_sentinel_terms_count_when_live_logits_are_near_minus_1e4(env, orc, deco
     t = np.arange(600)
     live = ~((case.sentinel_mask[0][t // 32] >> (t % 32)) & 1).astype(bool)
     assert np.abs(ref[0, 0]).max() < 0.5 * np.abs(np.mean([orc.dequant_row(lay_o, pool[(case.block_table[0, i // 256]) * orc.tile_bytes(lay_o):][:orc.tile_bytes(lay_o)], i % 256)[1] for i in t[live]], axis=0)).max()
+
+
+@pytest.fixture(params=["cascade", "nocascade"])
+def cascade_mode(request, monkeypatch):
+    """Shared blocks through the cascade kernel (the normal dispatch) or left to the per-sequence kernel
+    (the library's test hook, KVQ_DECODE_KERNEL=nocascade)."""
+    if request.param == "cascade":
+        monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("KVQ_DECODE_KERNEL", "nocascade")
+    return request.param
+
+
+CASCADE_CASES = {
+    # 40 sequences x 5 query heads = 200 rows: seven row groups of 32, the last one partial; ragged suffixes
+    "rows_40": dict(n_seqs=40, shared_prefix=1024, context=[1024 + (97 * i) % 1100 for i in range(40)]),
+    # more block ranges than shared blocks (empty cascade units); one sequence ends where the prefix ends
+    "prefix_8": dict(n_seqs=4, shared_prefix=2048, context=[2048, 2100, 4000, 2304]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASCADE_CASES))
+def test_cascade_shared_blocks(env, orc, name, cascade_mode):
+    # The shared-prefix layout (K per channel, V groups of 32, rotation, G = 5) with the prefix blocks
+    # aliased in every sequence's table, against the oracle (which reads each sequence's table as given).
+    kvq, torch = env
+    case = W.make_case(W.CONFIGS["qwen25_14b_prefix_32k"], **CASCADE_CASES[name])
+    inp = host_inputs(case)
+    _, ref = oracle_run(orc, case, inp)
+    _, got = gpu_run(kvq, torch, case, inp)
+    err = rel_err(got, ref)
+    print("cascade %s [%s]: max rel err %.3g" % (name, cascade_mode, err))
+    assert err <= TOL
