@@ -1,10 +1,10 @@
 // kvq_decode_cascade.hip - decode attention over the blocks that every sequence of a batch shares, for head_dim
 // 128 pools whose K is grouped per channel over each 256-token block (the long shared-prefix serving workload
-// of the UltraQuant article's results, with the prefix reuse of "Agent Memory Below the Prompt", technical
-// summary 2.1-2.2, and its packed-block decode).
+// of the UltraQuant article's technology section, with the prefix reuse of "Agent Memory Below the Prompt",
+// technical summary 2.1-2.2, and its packed-block decode).
 //
 // A logical block that all sequences map to the same physical block (a shared prompt prefix) is read once for
-// all of them. The work unit is (range of logical blocks, KV head, 64 query rows), a query row being one
+// all of them. The work unit is (range of logical blocks, KV head, kCascRows query rows), a query row being one
 // (sequence, query head) pair of that KV head. The unit's partial softmax state per row goes to the split-K
 // workspace; the per-sequence kernel (decode_kchan_k) then skips those blocks and merges these partials with
 // its own. Every unit finds the shared blocks of its range itself (same physical block in every sequence's

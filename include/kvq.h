@@ -152,7 +152,7 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
  * dequantised copy; 2.1 item 3, many agents batched in one launch; 2.2, GQA; [UQ] technology section,
  * AMD decode-attention kernel; [QKV] claims section, fused quantized attention kernel).
  * Pools with K grouped per channel and no sentinel mask: a logical block that every sequence of the
- * call maps to the same physical block, full in every sequence (a shared prompt prefix, [UQ] results
+ * call maps to the same physical block, full in every sequence (a shared prompt prefix, [UQ] technology
  * section), is read once for the whole batch and its partial results merged into each sequence's.
  *
  *   q              device fp16 [n_seqs][num_q_heads][d]; query head j reads KV head j / G,
