@@ -59,6 +59,8 @@ _lib.kvq_status_string.argtypes = [ctypes.c_int]
 _lib.kvq_status_string.restype = ctypes.c_char_p
 _lib.kvq_quantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P, _P]
 _lib.kvq_quantize_blocks.restype = ctypes.c_int
+_lib.kvq_dequantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P]
+_lib.kvq_dequantize_blocks.restype = ctypes.c_int
 _lib.kvq_append_tokens.argtypes = [_LP, _P, _I, _P, _P, _P, _I, _P, _P, _P]
 _lib.kvq_append_tokens.restype = ctypes.c_int
 _lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
@@ -66,7 +68,8 @@ _lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _
 _lib.kvq_decode_attention.restype = ctypes.c_int
 
 EXPORTS = ("kvq_check_layout", "kvq_tile_bytes", "kvq_pool_bytes", "kvq_decode_workspace_bytes",
-           "kvq_status_string", "kvq_quantize_blocks", "kvq_append_tokens", "kvq_decode_attention")
+           "kvq_status_string", "kvq_quantize_blocks", "kvq_dequantize_blocks", "kvq_append_tokens",
+           "kvq_decode_attention")
 
 
 def lib():
@@ -163,6 +166,26 @@ def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, strea
                                   _ptr(prec_bits, "prec_bits", (torch.int32, torch.uint32), 4, True),
                                   _stream(stream))
     _check("kvq_quantize_blocks", st)
+
+
+def dequantize_blocks(layout: Layout, pool, block_ids, k_out=None, v_out=None, stream=None):
+    """fp16 k, v [n_blocks*256, H_kv, d] of the listed blocks (un-rotated for rotated pools); allocated
+    here unless given."""
+    torch = _torch()
+    n_blocks = int(block_ids.numel())
+    shape = (n_blocks * 256, layout.num_kv_heads, layout.head_dim)
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=torch.float16, device=pool.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=torch.float16, device=pool.device)
+    if tuple(k_out.shape) != shape or tuple(v_out.shape) != shape:
+        raise ValueError("k_out and v_out must have shape %s" % (shape,))
+    st = _lib.kvq_dequantize_blocks(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256),
+                                    _ptr(block_ids, "block_ids", (torch.int32,)), n_blocks,
+                                    _ptr(k_out, "k_out", _f16(), 16), _ptr(v_out, "v_out", _f16(), 16),
+                                    _stream(stream))
+    _check("kvq_dequantize_blocks", st)
+    return k_out, v_out
 
 
 def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None, stream=None) -> None:

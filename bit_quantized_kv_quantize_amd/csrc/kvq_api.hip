@@ -170,6 +170,20 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
                                            (hipStream_t)stream));
 }
 
+int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* block_ids, int32_t n_blocks,
+                          uint16_t* k_out, uint16_t* v_out, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (n_blocks < 0) return KVQ_ERR_ARG;
+  if (n_blocks == 0) return KVQ_OK;
+  if (!pool || !block_ids || !k_out || !v_out) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  const float c = (float)(1.0 / sqrt((double)g.d));
+  const float unrot_c = (float)(1.0 / ((double)g.d * (double)c));
+  return hip_status(launch_dequantize_blocks(g, (const uint8_t*)pool, block_ids, n_blocks, k_out, v_out, unrot_c,
+                                             (hipStream_t)stream));
+}
+
 int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k, const uint16_t* v,
                       const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* positions,
                       const uint8_t* prec, void* stream) {

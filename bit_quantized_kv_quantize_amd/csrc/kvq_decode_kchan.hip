@@ -60,8 +60,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][NGV][64 * kPP];
   __shared__ float s_wm[4][G], s_wl[4][G];
   __shared__ int s_tbl[kMaxSplitBlocks];
-  __shared__ int s_col[kMaxSplitBlocks];
-  __shared__ int s_ccnt[4];
+  __shared__ uint16_t s_col[kMaxSplitBlocks];
   static_assert(sizeof(float) * 4 * G * D <= sizeof(_Float16) * 4 * NGV * 64 * kPP, "s_wacc fits in s_p");
   float (*s_wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&s_p[0][0][0]);  // used after the token loop
 
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   // Blocks the cascade kernel took for every sequence are skipped here; its partials join the merge.
   const int n_pre = a.casc;
   const int nchunk = stage_columns(
-      max(b1 - b0, 0), tid, s_tbl, s_col, s_ccnt, [&](int i) { return n_pre == 0 || a.ws_cflag[b0 + i] == 0; },
+      max(b1 - b0, 0), tid, s_tbl, s_col, reinterpret_cast<int*>(&s_wm[0][0]), [&](int i) { return n_pre == 0 || a.ws_cflag[b0 + i] == 0; },
       [&](int i) { return a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i]; });
   const uint32_t* mask_row = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
   const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;

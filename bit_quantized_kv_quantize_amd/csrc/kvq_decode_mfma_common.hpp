@@ -73,9 +73,10 @@ constexpr int kMaxSplits = 64;        // splits per (sequence, KV head)
 constexpr float kTwo20 = 1048576.0f;
 
 // Stages into s_tbl, in order, the block-table entries phys(i) of the columns 0 <= i < n for which keep(i)
-// holds (both evaluated by thread i mod 256, all 256 threads taking part) and returns their number.
-template <class Keep, class Phys>
-__device__ int stage_columns(int n, int tid, int* s_tbl, int* s_idx, int* s_cnt, Keep keep, Phys phys) {
+// holds, and into s_idx their column indices (both evaluated by thread i mod 256, all 256 threads taking
+// part); returns their number. s_cnt: four ints of scratch.
+template <class Idx, class Keep, class Phys>
+__device__ int stage_columns(int n, int tid, int* s_tbl, Idx* s_idx, int* s_cnt, Keep keep, Phys phys) {
   const int w = tid >> 6, lane = tid & 63;
   int total = 0;
   for (int base = 0; base < n; base += 256) {
@@ -90,7 +91,7 @@ __device__ int stage_columns(int n, int tid, int* s_tbl, int* s_idx, int* s_cnt,
     if (k) {
       const int o = off + __builtin_popcountll(m & ((1ull << lane) - 1ull));
       s_tbl[o] = e;
-      s_idx[o] = i;
+      s_idx[o] = (Idx)i;
     }
     total += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
     __syncthreads();

@@ -284,6 +284,70 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
   return hipGetLastError();
 }
 
+// The cache restored as fp16 rows (QKVShare methodology, injection path): grid (n_blocks, H, 2), one
+// workgroup writes the 256 rows of tensor blockIdx.z (0 = K, 1 = V) of tile (block_ids[blockIdx.x],
+// blockIdx.y) as fp16 [n_blocks * 256][H][d], the input layout of quantize_rows_k. LPR = d / 8 lanes per row,
+// 8 channels each: value = fp32(code) * scale + zero (the product is exact), then for a rotated pool the
+// same butterflies as the rotation with the inverse scale 1 / (d c), then one rounding to fp16. Up to the
+// fp32 roundings of the sum and the butterflies this is the exact value rounded once.
+template <int LPR>
+__global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* __restrict__ pool,
+                                                   const int32_t* __restrict__ block_ids, uint16_t* __restrict__ k_out,
+                                                   uint16_t* __restrict__ v_out, float unrot_c) {
+  constexpr int RPP = 256 / LPR;  // rows per pass
+  const int h = blockIdx.y, which = blockIdx.z;
+  const uint8_t* tile = pool + ((size_t)block_ids[blockIdx.x] * g.H + h) * g.tile_bytes;
+  const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  uint16_t* out = which ? v_out : k_out;
+  const bool kchan = which == 0 && g.kg < 0;
+  const int grp = which ? g.vg : g.kg;
+  float cs[8], cz[8];  // per-channel K parameters of this lane's channels
+  if (kchan) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t pr = *reinterpret_cast<const uint32_t*>(tile + g.off_kch + 4 * (8 * li + i));
+      cs[i] = h2f(pr & 0xffffu);
+      cz[i] = h2f(pr >> 16);
+    }
+  }
+  for (int t = r0; t < kRows; t += RPP) {
+    const int bits = (g.mixed && ((tile[g.off_hdr + t / 8] >> (t % 8)) & 1)) ? 8 : 4;
+    const uint8_t* row = tile + (which ? g.vcode(t, bits) : g.kcode(t));
+    uint32_t code[8];
+    if (bits == 8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(row + li * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        code[i] = (w.x >> (8 * i)) & 255u;
+        code[4 + i] = (w.y >> (8 * i)) & 255u;
+      }
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(row + li * 4);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[i] = (w >> (4 * i)) & 15u;
+    }
+    float x[8];
+    if (kchan) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * cs[i] + cz[i];
+    } else {
+      // the lane's 8 channels lie in one group (groups are multiples of 8)
+      const uint32_t pr = *reinterpret_cast<const uint32_t*>(tile + (which ? g.vpar(t) : g.kpar(t)) +
+                                                             4 * ((8 * li) / grp));
+      const float s = h2f(pr & 0xffffu), z = h2f(pr >> 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * s + z;
+    }
+    if (g.rotate) rotate_row<LPR>(x, li, unrot_c);
+    uint4 o;
+    o.x = f2h(x[0]) | (f2h(x[1]) << 16);
+    o.y = f2h(x[2]) | (f2h(x[3]) << 16);
+    o.z = f2h(x[4]) | (f2h(x[5]) << 16);
+    o.w = f2h(x[6]) | (f2h(x[7]) << 16);
+    *reinterpret_cast<uint4*>(out + (((size_t)blockIdx.x * kRows + t) * g.H + h) * (8 * LPR) + 8 * li) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
@@ -314,6 +378,24 @@ hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, co
     case 256:
       hipLaunchKernelGGL(append_k<32>, grid, dim3(32), 0, stream, g, pool, k, v, block_table,
                          max_blocks_per_seq, positions, prec, rot_c);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_blocks(const TileGeom& g, const uint8_t* pool, const int32_t* block_ids, int n_blocks,
+                                    uint16_t* k_out, uint16_t* v_out, float unrot_c, hipStream_t stream) {
+  const dim3 grid(n_blocks, g.H, 2);
+  switch (g.d) {
+    case 64:
+      hipLaunchKernelGGL(dequantize_k<8>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
+      break;
+    case 128:
+      hipLaunchKernelGGL(dequantize_k<16>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
+      break;
+    case 256:
+      hipLaunchKernelGGL(dequantize_k<32>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
       break;
     default: return hipErrorInvalidValue;
   }

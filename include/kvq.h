@@ -147,6 +147,23 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
                       const int32_t* positions, const uint8_t* prec, void* stream);
 
 /*
+ * kvq_dequantize_blocks - the cache restored as fp16 rows, the unfused path of [QKV] methodology section
+ * (injection path: the quantised cache is rebuilt as fp16 key/value tensors before the forward pass),
+ * for callers that need plain fp16 K/V; decode attention itself never materialises them.
+ *   block_ids  device int32 [n_blocks]: physical blocks to restore, each < num_blocks.
+ *   k_out      device fp16 [n_blocks * 256][H_kv][d]: row t of block_ids[i], KV head h, at
+ *              ((i * 256 + t) * H_kv + h) * d - the layout kvq_quantize_blocks reads.
+ *   v_out      the same for V.
+ * Each value is code * scale + zero of its group (per-token or per-channel K groups, the row's own width
+ * in mixed pools), un-rotated by (1 / (d c)) H for rotated pools (the inverse of the rotation c H), rounded
+ * once to fp16 (round to nearest even). The arithmetic is fp32: a result may differ from the exact value
+ * rounded to fp16 by one fp16 ulp.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP.
+ */
+int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* block_ids, int32_t n_blocks,
+                          uint16_t* k_out, uint16_t* v_out, void* stream);
+
+/*
  * kvq_decode_attention - one decode query per sequence attending over its quantised cache, reading
  * the packed tiles directly and dequantising in registers ([AMB] 2.1 item 2, direct restore without a
  * dequantised copy; 2.1 item 3, many agents batched in one launch; 2.2, GQA; [UQ] technology section,

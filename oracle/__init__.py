@@ -78,6 +78,8 @@ def lib():
         L.orc_append_tokens.restype = ctypes.c_int
         L.orc_dequant_row.argtypes = [ctypes.POINTER(OrcLayout), P, i32, P, P]
         L.orc_dequant_row.restype = i32
+        L.orc_dequantize_blocks.argtypes = [ctypes.POINTER(OrcLayout), P, P, i32, P, P]
+        L.orc_dequantize_blocks.restype = ctypes.c_int
         L.orc_decode_attention.argtypes = [ctypes.POINTER(OrcLayout), P, P, i32, i32, P, i32, P, P, i32,
                                            ctypes.c_float, P, P, i32, i32]
         L.orc_decode_attention.restype = ctypes.c_int
@@ -165,6 +167,20 @@ def dequant_row(layout: OrcLayout, tile: np.ndarray, t: int):
     tile = _c(tile, np.uint8)
     bits = lib().orc_dequant_row(ctypes.byref(layout), _p(tile), t, _p(k), _p(v))
     return k, v, int(bits)
+
+
+def dequantize_blocks(layout: OrcLayout, pool: np.ndarray, block_ids):
+    """fp16 bits (uint16) k, v [n_blocks * 256, H, d]: the listed blocks restored (and un-rotated), one
+    rounding from the exact fp64 values."""
+    ids = _c(block_ids, np.int32)
+    n, H, d = ids.size, layout.num_kv_heads, layout.head_dim
+    k = np.zeros((n * 256, H, d), np.uint16)
+    v = np.zeros((n * 256, H, d), np.uint16)
+    pool = _c(pool, np.uint8)
+    st = lib().orc_dequantize_blocks(ctypes.byref(layout), _p(pool), _p(ids), n, _p(k), _p(v))
+    if st != 0:
+        raise ValueError("orc_dequantize_blocks: status %d" % st)
+    return k, v
 
 
 def decode_attention(layout: OrcLayout, pool: np.ndarray, q: np.ndarray, block_table, seq_lens,

@@ -418,6 +418,70 @@ int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, dou
   return bits;
 }
 
+/* fp64 -> IEEE binary16 bits, one rounding to nearest, ties to even (overflow to infinity). */
+static uint16_t f64_to_f16(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  double a = fabs(x);
+  if (isnan(a)) return 0x7e00u;
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u); /* at or above max + half an ulp */
+  if (a < ldexp(1.0, -14)) {                            /* subnormal range: quantum 2^-24 */
+    const double q = nearbyint(ldexp(a, 24));          /* may reach 1024, the smallest normal */
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int E = e - 1;
+  double q = nearbyint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+  if (q >= 2048.0) {
+    q = 1024.0;
+    E += 1;
+  }
+  if (E > 15) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+/* The cache restored as fp16 rows ([QKV] methodology section, injection path: the quantised cache
+ * rebuilt as fp16 key/value tensors before the forward pass). For every listed block b = block_ids[i],
+ * KV head h and row t: the row's K and V are dequantised exactly (orc_dequant_row), un-rotated for a
+ * rotated pool by (1 / (d c)) H in fp64 (the exact inverse of the rotation c H), and rounded once to
+ * fp16. Output layout is the input layout of orc_quantize_blocks: k_out / v_out [n_blocks * 256][H][d].
+ * Pinned by: test_oracle_dequant.py (grid-exact blocks restored bit for bit, the per-element error bound
+ * of the stored scales carried through the rotation, an explicit Hadamard matrix for the inverse). */
+int orc_dequantize_blocks(const orc_layout* L, const uint8_t* pool, const int32_t* block_ids, int32_t n_blocks,
+                          uint16_t* k_out, uint16_t* v_out) {
+  int st = orc_check_layout(L);
+  if (st != ORC_OK) return st;
+  if (n_blocks < 0) return ORC_ERR_ARG;
+  const int32_t H = L->num_kv_heads, d = L->head_dim;
+  const double unrot = 1.0 / ((double)d * (double)orc_rot_scale(d));
+  double* k = (double*)malloc(sizeof(double) * 2 * (size_t)d);
+  if (!k) return ORC_ERR_ARG;
+  double* v = k + d;
+  for (int32_t i = 0; i < n_blocks; ++i) {
+    for (int32_t h = 0; h < H; ++h) {
+      const uint8_t* tile = tile_ptr(L, (uint8_t*)pool, block_ids[i], h);
+      for (int32_t t = 0; t < ORC_ROWS; ++t) {
+        orc_dequant_row(L, tile, t, k, v);
+        if (L->rotate) {
+          fwht_f64(k, d);
+          fwht_f64(v, d);
+          for (int32_t c = 0; c < d; ++c) {
+            k[c] *= unrot;
+            v[c] *= unrot;
+          }
+        }
+        const size_t o = (((size_t)i * ORC_ROWS + t) * H + h) * d;
+        for (int32_t c = 0; c < d; ++c) {
+          k_out[o + c] = f64_to_f16(k[c]);
+          v_out[o + c] = f64_to_f16(v[c]);
+        }
+      }
+    }
+  }
+  free(k);
+  return ORC_OK;
+}
+
 /* Host-memory counterpart of kvq_decode_attention, in fp64, by the plain definition:
  *   for sequence s and query head j (KV head h = j / G): for every slot t < seq_lens[s], a sentinel
  *   slot has logit -1e4 and value 0; any other slot's K and V rows are dequantised exactly (and, for a

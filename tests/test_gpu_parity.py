@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import kvq_workloads as W
-from gpu_cases import TOL, gpu_run, host_inputs, oracle_run, rel_err
+from gpu_cases import TOL, gpu_run, host_inputs, oracle_run, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +177,48 @@ def test_cascade_shared_blocks(env, orc, name, cascade_mode):
     err = rel_err(got, ref)
     print("cascade %s [%s]: max rel err %.3g" % (name, cascade_mode, err))
     assert err <= TOL
+
+
+def _f16_ulps(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in fp16 ulps between bit patterns (order-preserving integer map; +0 and -0 coincide)."""
+    def key(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+DEQUANT_VARIANTS = [  # rotate, mixed, k_group, v_group, d
+    (0, 0, 64, 64, 128), (1, 0, -1, 32, 128), (1, 1, 64, 64, 128), (0, 1, 32, 64, 64), (1, 0, 64, 32, 256),
+    (0, 0, -1, 64, 64), (1, 0, 8, 256, 256)]
+
+
+@pytest.mark.parametrize("variant", DEQUANT_VARIANTS + W.CONFIG_ORDER)
+def test_dequantize_blocks_within_one_ulp(env, orc, variant):
+    # The restored fp16 rows of every quantised block (and, where the workload appends, the appended rows)
+    # against the oracle's exact values rounded once: at most one fp16 ulp apart, and equal almost everywhere.
+    kvq, torch = env
+    if isinstance(variant, str):
+        case = W.make_case(W.CONFIGS[variant], **SMALL[variant])
+    else:
+        rotate, mixed, kg, vg, d = variant
+        cfg = W.Config(9, "variant", d, 2, 2, 1, kg, vg, rotate, mixed, 3, 0, "perm", kg > 0, 3, 10.0, 1.0,
+                       top_fraction=0.3 if mixed else 0.0)
+        case = W.make_case(cfg, context=[700, 257, 1024])
+    inp = host_inputs(case)
+    ref_pool, _ = oracle_run(orc, case, inp, decode=False)
+    got_pool, _ = gpu_run(kvq, torch, case, inp, decode=False)
+    assert np.array_equal(got_pool, ref_pool)
+    ids = np.unique(case.block_table[case.block_table >= 0]).astype(np.int32)
+    ids = ids[ids < case.num_blocks][::-1].copy()  # reversed: output order follows the id list
+    lay_o = orc.make_layout(**case.cfg.layout())
+    kr, vr = orc.dequantize_blocks(lay_o, ref_pool, ids)
+    lay = kvq.Layout(**case.cfg.layout())
+    kg_, vg_ = kvq.dequantize_blocks(lay, to_dev(got_pool, torch), to_dev(ids, torch))
+    torch.cuda.synchronize()
+    for got, ref in ((kg_, kr), (vg_, vr)):
+        g = got.cpu().numpy().view(np.uint16)
+        u = _f16_ulps(g, ref)
+        print("dequantize %s: %d values, %d differ by one ulp, max %d" % (variant, u.size, int((u == 1).sum()),
+                                                                          int(u.max())))
+        assert u.max() <= 1
+        assert (u > 0).mean() < 1e-3
