@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "kvq_internal.hpp"
 
 namespace kvq {
@@ -95,8 +97,19 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   SplitPlan p = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
   size_t ns = (size_t)(n_seqs > 0 ? n_seqs : 0);
-  size_t parts = ns * num_q_heads * p.stride;
+  // The partial slots actually used, ns * num_q_heads * p.stride, shrink or grow with the split plan; the
+  // regions are sized by a bound that never decreases with n_seqs or max_seq_len, so that a workspace
+  // sized for one call serves every smaller one. With G = num_q_heads / H, units = n_seqs * H and
+  // c = ceil(blocks / 512): both per-sequence plans give at most G * max(512, units * c) + n_seqs *
+  // num_q_heads slots, and the cascade at most 8192 + n_seqs * num_q_heads * c more (its row groups hold
+  // 32 rows, so n_seqs * num_q_heads * 256 / (row groups * H) <= 8192).
+  const size_t G = g.H > 0 ? (size_t)(num_q_heads / g.H) : 1;
+  const size_t c512 = (size_t)(p.max_blocks + 511) / 512;
+  const size_t rows = ns * (size_t)num_q_heads;
+  size_t parts = G * std::max((size_t)512, ns * g.H * c512) + rows;
+  if (p.casc > 0) parts += (size_t)256 * kCascRows + rows * c512;
   WorkspaceLayout w{};
+  w.parts = parts;
   w.ctr = 0;
   w.ml = up(ns * g.H * sizeof(unsigned));
   w.acc = w.ml + up(parts * 2 * sizeof(float));
@@ -229,6 +242,7 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.out = out;
   a.plan = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
   const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
+  if ((size_t)n_seqs * num_q_heads * a.plan.stride > wl.parts) return KVQ_ERR_UNSUPPORTED;  // never, by the bound
   uint8_t* ws = (uint8_t*)workspace;
   a.ws_ctr = (unsigned*)(ws + wl.ctr);
   a.ws_ml = (float*)(ws + wl.ml);

@@ -101,6 +101,7 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
 // counts, row lists) for a call of this size; `total` is the size.
 struct WorkspaceLayout {
   size_t ctr, ml, acc, cnt, list, bcnt, cflag, total;
+  size_t parts;  // partial slots the ml / acc regions hold
   int list_cap;
   int bcnt_blocks;  // blocks per sequence in the per-block live-row counts
 };

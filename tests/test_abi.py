@@ -96,3 +96,20 @@ def test_host_argument_errors_return_before_launch(kvq):
                                     0.1, P(256), P(257), 1 << 20, None) == kvq.KVQ_ERR_WORKSPACE  # misaligned
     assert lib.kvq_decode_attention(ctypes.byref(lay), P(256), P(256), 0, 16, P(256), 4, P(256), 1000, None, 0,
                                     0.1, None, None, 0, None) == kvq.KVQ_OK                 # nothing to do
+
+
+def test_workspace_bytes_never_shrink_with_size(kvq):
+    # A workspace sized for (n_seqs, max_seq_len) serves every call with no more sequences and no longer
+    # maximum length (include/kvq.h), across the split plans of every decode kernel.
+    layouts = [kvq.Layout(128, 8, 64, 64), kvq.Layout(128, 8, -1, 32, 1, 0), kvq.Layout(256, 8, 64, 64),
+               kvq.Layout(128, 8, 64, 64, 0, 1), kvq.Layout(128, 2, -1, 64), kvq.Layout(64, 4, 32, 32)]
+    lens = [0, 1, 255, 256, 1000, 4096, 8193, 32768, 100000, 300000]
+    seqs = [1, 2, 3, 5, 12, 40, 64, 128, 300, 1000]
+    for lay in layouts:
+        for g in (1, 2, 4, 5, 8):
+            nqh = lay.num_kv_heads * g
+            tab = {(s, n): kvq.decode_workspace_bytes(lay, s, nqh, n) for s in seqs for n in lens}
+            for (s, n), b in tab.items():
+                for (s2, n2), b2 in tab.items():
+                    if s2 <= s and n2 <= n:
+                        assert b2 <= b, (lay.as_dict(), nqh, (s, n, b), (s2, n2, b2))
