@@ -43,6 +43,10 @@ if not os.path.exists(LIB_PATH):
     raise ImportError("libkvq.so is not built (%s); run `python -m bit_quantized_kv_quantize_amd._build` "
                       "(or __graft_entry__.build())" % LIB_PATH)
 
+# torch first: it carries its own HIP runtime, and libkvq.so must bind to that same runtime (loaded first,
+# it would pull in the system one as well, and the two would not share streams or device memory).
+import torch as _torch_runtime  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -61,6 +65,8 @@ _lib.kvq_quantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P, _P]
 _lib.kvq_quantize_blocks.restype = ctypes.c_int
 _lib.kvq_dequantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P]
 _lib.kvq_dequantize_blocks.restype = ctypes.c_int
+_lib.kvq_copy_blocks.argtypes = [_LP, _P, _P, _P, _P, _I, _P]
+_lib.kvq_copy_blocks.restype = ctypes.c_int
 _lib.kvq_append_tokens.argtypes = [_LP, _P, _I, _P, _P, _P, _I, _P, _P, _P]
 _lib.kvq_append_tokens.restype = ctypes.c_int
 _lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
@@ -68,8 +74,8 @@ _lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _
 _lib.kvq_decode_attention.restype = ctypes.c_int
 
 EXPORTS = ("kvq_check_layout", "kvq_tile_bytes", "kvq_pool_bytes", "kvq_decode_workspace_bytes",
-           "kvq_status_string", "kvq_quantize_blocks", "kvq_dequantize_blocks", "kvq_append_tokens",
-           "kvq_decode_attention")
+           "kvq_status_string", "kvq_quantize_blocks", "kvq_dequantize_blocks", "kvq_copy_blocks",
+           "kvq_append_tokens", "kvq_decode_attention")
 
 
 def lib():
@@ -186,6 +192,18 @@ def dequantize_blocks(layout: Layout, pool, block_ids, k_out=None, v_out=None, s
                                     _stream(stream))
     _check("kvq_dequantize_blocks", st)
     return k_out, v_out
+
+
+def copy_blocks(layout: Layout, src_pool, src_ids, dst_pool, dst_ids, stream=None) -> None:
+    """Block src_ids[i] of src_pool -> block dst_ids[i] of dst_pool (all KV heads); int32 id tensors."""
+    torch = _torch()
+    n = int(src_ids.numel())
+    if int(dst_ids.numel()) != n:
+        raise ValueError("src_ids and dst_ids differ in length")
+    st = _lib.kvq_copy_blocks(ctypes.byref(layout), _ptr(src_pool, "src_pool", (torch.uint8,), 16),
+                              _ptr(src_ids, "src_ids", (torch.int32,)), _ptr(dst_pool, "dst_pool", (torch.uint8,), 16),
+                              _ptr(dst_ids, "dst_ids", (torch.int32,)), n, _stream(stream))
+    _check("kvq_copy_blocks", st)
 
 
 def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None, stream=None) -> None:

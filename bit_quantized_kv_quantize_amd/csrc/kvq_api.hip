@@ -197,6 +197,19 @@ int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* 
                                              (hipStream_t)stream));
 }
 
+int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* src_ids, void* dst_pool,
+                    const int32_t* dst_ids, int32_t n_blocks, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (n_blocks < 0) return KVQ_ERR_ARG;
+  if (n_blocks == 0) return KVQ_OK;
+  if (!src_pool || !src_ids || !dst_pool || !dst_ids) return KVQ_ERR_ARG;
+  if (((uintptr_t)src_pool & 15u) || ((uintptr_t)dst_pool & 15u)) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  return hip_status(launch_copy_blocks(g, (const uint8_t*)src_pool, src_ids, (uint8_t*)dst_pool, dst_ids, n_blocks,
+                                       (hipStream_t)stream));
+}
+
 int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k, const uint16_t* v,
                       const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* positions,
                       const uint8_t* prec, void* stream) {

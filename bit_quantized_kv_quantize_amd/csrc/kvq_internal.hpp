@@ -113,6 +113,8 @@ hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_
                                   float rot_c, hipStream_t stream);
 hipError_t launch_dequantize_blocks(const TileGeom& g, const uint8_t* pool, const int32_t* block_ids, int n_blocks,
                                     uint16_t* k_out, uint16_t* v_out, float unrot_c, hipStream_t stream);
+hipError_t launch_copy_blocks(const TileGeom& g, const uint8_t* src, const int32_t* src_ids, uint8_t* dst,
+                              const int32_t* dst_ids, int n_blocks, hipStream_t stream);
 hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, const uint16_t* k,
                                 const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
                                 const int32_t* positions, const uint8_t* prec, float rot_c,

@@ -164,6 +164,19 @@ int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* 
                           uint16_t* k_out, uint16_t* v_out, void* stream);
 
 /*
+ * kvq_copy_blocks - copy whole blocks (all H_kv tiles of each) from one pool to another, or within one pool
+ * when source and destination tiles do not overlap: the device side of persisting and restoring quantised
+ * blocks ([AMB] 2.1: blocks saved and reloaded in their stored form; [QKV] methodology section, the
+ * CacheCard passed between agents). A tile holds only its own rows, so a copy is valid at any block id.
+ *   src_pool, dst_pool  device pools of the same layout, 16-byte aligned.
+ *   src_ids, dst_ids    device int32 [n_blocks]; block src_ids[i] of src_pool goes to block dst_ids[i] of
+ *                       dst_pool. Destination ids must be distinct.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP.
+ */
+int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* src_ids, void* dst_pool,
+                    const int32_t* dst_ids, int32_t n_blocks, void* stream);
+
+/*
  * kvq_decode_attention - one decode query per sequence attending over its quantised cache, reading
  * the packed tiles directly and dequantising in registers ([AMB] 2.1 item 2, direct restore without a
  * dequantised copy; 2.1 item 3, many agents batched in one launch; 2.2, GQA; [UQ] technology section,

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(kvq):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     dyn = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", dyn))
     assert set(names) <= exported, set(names) - exported
@@ -81,6 +81,9 @@ def test_host_argument_errors_return_before_launch(kvq):
     assert lib.kvq_dequantize_blocks(ctypes.byref(lay), None, None, 0, None, None, None) == kvq.KVQ_OK
     assert lib.kvq_dequantize_blocks(ctypes.byref(lay), P(256), P(256), -1, P(256), P(256), None) == kvq.KVQ_ERR_ARG
     assert lib.kvq_dequantize_blocks(ctypes.byref(lay), P(256), P(256), 3, None, P(256), None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_copy_blocks(ctypes.byref(lay), None, None, None, None, 0, None) == kvq.KVQ_OK
+    assert lib.kvq_copy_blocks(ctypes.byref(lay), P(256), P(256), P(256), None, 2, None) == kvq.KVQ_ERR_ARG
+    assert lib.kvq_copy_blocks(ctypes.byref(lay), P(264), P(256), P(256), P(256), 2, None) == kvq.KVQ_ERR_ARG
     chan = kvq.Layout(128, 8, -1, 32, 1, 0)
     assert lib.kvq_append_tokens(ctypes.byref(chan), P(256), 1, P(256), P(256), P(256), 1, P(256), None,
                                  None) == kvq.KVQ_ERR_UNSUPPORTED

@@ -222,3 +222,40 @@ def test_dequantize_blocks_within_one_ulp(env, orc, variant):
                                                                           int(u.max())))
         assert u.max() <= 1
         assert (u > 0).mean() < 1e-3
+
+
+@pytest.mark.parametrize("name", ["qwen25_14b_prefix_32k", "mixed_sentinel_32k", "llama31_8b_pool_8k"])
+def test_card_save_load_round_trip(env, orc, tmp_path, name):
+    # Blocks saved from a GPU pool to a card file (kvq_copy_blocks gathers them) and loaded into another pool
+    # at shuffled ids (kvq_copy_blocks scatters them): the card's tiles equal the oracle's bytes, and decode
+    # over the reloaded pool equals decode over the original pool bit for bit.
+    kvq, torch = env
+    from bit_quantized_kv_quantize_amd import cachecard
+    from safetensors.numpy import load_file
+
+    case = W.make_case(W.CONFIGS[name], **SMALL[name])
+    inp = host_inputs(case)
+    ref_pool, _ = oracle_run(orc, case, inp, decode=False)
+    cfg = case.cfg
+    lay = kvq.Layout(**cfg.layout())
+    pool = to_dev(gpu_run(kvq, torch, case, inp, decode=False)[0], torch)
+    table = to_dev(case.block_table, torch)
+    lens = to_dev(case.seq_lens, torch)
+    q = to_dev(inp["q"], torch, torch.float16)
+    mask = None if case.sentinel_mask is None else to_dev(case.sentinel_mask.view(np.int32), torch)
+    out1 = kvq.decode_attention(lay, pool, q, table, lens, case.max_seq_len, mask)
+    path = str(tmp_path / "card.safetensors")
+    n = cachecard.save(path, lay, pool, table, lens, model_id=name)
+    tb = kvq.tile_bytes(lay)
+    used = cachecard.used_blocks(case.block_table, case.seq_lens)
+    assert n == used.size
+    tiles = load_file(path)["tiles"]
+    assert np.array_equal(tiles, ref_pool.reshape(case.num_blocks, cfg.num_kv_heads, tb)[used])
+    pool2 = kvq.new_pool(lay, n + 7)
+    ids = torch.from_numpy((np.random.default_rng(2).permutation(n) + 7).astype(np.int32)).cuda()
+    card = cachecard.load(path, lay, pool2, ids)
+    assert card["model_id"] == name
+    t2 = card["block_table"].clamp(min=0).contiguous()
+    out2 = kvq.decode_attention(lay, pool2, q, t2, lens, case.max_seq_len, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
