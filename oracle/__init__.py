@@ -25,15 +25,16 @@ ORC_ERR_UNSUPPORTED = -2
 
 class OrcLayout(ctypes.Structure):
     """Same field order as the library's layout struct (head_dim, num_kv_heads, block_tokens, k_group,
-    v_group, rotate, mixed, reserved)."""
+    v_group, rotate, mixed, format)."""
 
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed",
-                 "reserved")]
+                 "format")]
 
 
-def make_layout(head_dim, num_kv_heads, k_group, v_group, rotate=0, mixed=0, block_tokens=256):
-    return OrcLayout(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed), 0)
+def make_layout(head_dim, num_kv_heads, k_group, v_group, rotate=0, mixed=0, block_tokens=256, format=0):
+    return OrcLayout(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed),
+                     int(format))
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +63,10 @@ def lib():
         L.orc_f32_to_f16.restype = ctypes.c_uint16
         L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_e4m3.argtypes = [ctypes.c_float]
+        L.orc_f32_to_e4m3.restype = ctypes.c_uint8
+        L.orc_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_f32.restype = ctypes.c_float
         L.orc_fwht_f32.argtypes = [P, i32]
         L.orc_fwht_f32.restype = None
         L.orc_rot_scale.argtypes = [i32]
@@ -103,6 +108,14 @@ def f32_to_f16_bits(x: float) -> int:
 
 def f16_bits_to_f32(h: int) -> float:
     return float(lib().orc_f16_to_f32(int(h)))
+
+
+def f32_to_e4m3(x: float) -> int:
+    return int(lib().orc_f32_to_e4m3(float(x)))
+
+
+def e4m3_to_f32(b: int) -> float:
+    return float(lib().orc_e4m3_to_f32(int(b)))
 
 
 def fwht_f32(x: np.ndarray) -> np.ndarray:

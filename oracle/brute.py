@@ -23,6 +23,23 @@ def hadamard(n: int) -> np.ndarray:
     return np.where(pop % 2 == 0, 1.0, -1.0)
 
 
+def e4m3_values() -> np.ndarray:
+    """fp64 value of each of the 256 FP8 E4M3 ("fn") bytes: sign bit 7, exponent bits 6..3 (bias 7), mantissa
+    bits 2..0; exponent 0 is subnormal (m * 2^-9); 0x7F and 0xFF are NaN."""
+    b = np.arange(256)
+    e, m = (b >> 3) & 15, (b & 7).astype(np.float64)
+    v = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    v = np.where((b & 0x7F) == 0x7F, np.nan, v)
+    return np.where(b & 0x80, -v, v)
+
+
+def _fp8_tile(tile: np.ndarray, d):
+    rows = 256
+    rec = tile[: rows * 2 * d].reshape(rows, 2 * d)
+    vals = e4m3_values()
+    return vals[rec[:, :d]], vals[rec[:, d:]]
+
+
 def _layout_offsets(d, k_group, v_group, mixed):
     """Byte geometry of a tile: row records (K codes then V codes of the row's width, 2 * slot bytes), the per-channel K
     parameters (if K is grouped per channel), per-row parameter records (K groups then V groups), header."""
@@ -55,8 +72,10 @@ def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed):
-    """-> (K [256][d], V [256][d]) fp64 in the stored (rotated) domain."""
+def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
+    """-> (K [256][d], V [256][d]) fp64 in the stored (rotated) domain. fmt 1: FP8 E4M3 records."""
+    if fmt == 1:
+        return _fp8_tile(tile, d)
     slot, off_par, off_prow, prow, kpr, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
     rows = 256
     if mixed:
@@ -86,9 +105,9 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed):
 
 
 def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed, q_bits: np.ndarray,
-                     block_table, seq_lens, sentinel_mask=None, softmax_scale=None) -> np.ndarray:
+                     block_table, seq_lens, sentinel_mask=None, softmax_scale=None, fmt=0) -> np.ndarray:
     """Dense fp64 attention of every query head over its sequence's dequantised cache."""
-    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[6]
+    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[6] if fmt == 0 else (256 * 2 * d + 255) // 256 * 256
     q = q_bits.view(np.float16).astype(np.float64)
     n_seqs, hq, _ = q.shape
     g = hq // h_kv
@@ -113,7 +132,7 @@ def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed,
             for lb in range((n + 255) // 256):
                 blk = int(block_table[s][lb])
                 base = (blk * h_kv + h) * tile_bytes
-                Kt, Vt = dequant_tile(pool[base: base + tile_bytes], d, k_group, v_group, mixed)
+                Kt, Vt = dequant_tile(pool[base: base + tile_bytes], d, k_group, v_group, mixed, fmt)
                 m = min(256, n - lb * 256)
                 K[lb * 256: lb * 256 + m] = Kt[:m]
                 V[lb * 256: lb * 256 + m] = Vt[:m]

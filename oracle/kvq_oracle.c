@@ -54,7 +54,7 @@ typedef struct orc_layout {
   int32_t v_group;
   int32_t rotate;
   int32_t mixed;
-  int32_t reserved;
+  int32_t format; /* 0: group-wise integer codes; 1: FP8 E4M3 per element */
 } orc_layout;
 
 /* ---------------------------------------------------------------- fp16 <-> fp32 (IEEE binary16) */
@@ -150,6 +150,44 @@ static void rotate_row(float* x, int32_t n) {
   for (int32_t i = 0; i < n; ++i) x[i] = x[i] * c;
 }
 
+/* ---------------------------------------------------------------- FP8 E4M3 */
+
+/* OCP FP8 E4M3 ("fn": no infinities): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0
+ * holds subnormals m * 2^-9; S.1111.111 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+ * fp32 -> E4M3: round to nearest, ties to even, magnitudes of 448 and more saturate to 448, NaN -> 0x7F.
+ * Pinned by: test_oracle_fp8.py (every code's value from the format definition, code -> value -> code,
+ * ties between neighbours, saturation, torch's own E4M3 conversion inside the range). */
+uint8_t orc_f32_to_e4m3(float f) {
+  const uint8_t sign = signbit(f) ? 0x80u : 0u;
+  double a = fabs((double)f);
+  if (isnan(a)) return 0x7Fu;
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  if (a < ldexp(1.0, -6)) { /* subnormal: quantum 2^-9 (a result of 8 is the smallest normal) */
+    const double q = nearbyint(ldexp(a, 9));
+    return (uint8_t)(sign | (uint8_t)q);
+  }
+  int e;
+  frexp(a, &e);
+  int E = e - 1; /* a in [2^E, 2^(E+1)), E in -6 .. 8 */
+  double q = nearbyint(ldexp(a, 3 - E)); /* in [8, 16] */
+  if (q >= 16.0) {
+    q = 8.0;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && q > 14.0)) return (uint8_t)(sign | 0x7Eu);
+  return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(q - 8.0));
+}
+
+/* E4M3 -> fp32, exact. */
+float orc_e4m3_to_f32(uint8_t b) {
+  const int e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(8.0 + m, e - 10);
+  return (float)((b & 0x80u) ? -v : v);
+}
+
 /* ---------------------------------------------------------------- one quantisation group */
 
 /* Quantise the n values x[i * stride] with L = 2^bits - 1 levels ([AMB] 2.1 item 2, affine form):
@@ -199,7 +237,14 @@ int orc_check_layout(const orc_layout* L) {
   if (!L) return ORC_ERR_ARG;
   int32_t d = L->head_dim;
   if (d <= 0 || d % 8 != 0 || d > 4096) return ORC_ERR_ARG;
-  if (L->num_kv_heads <= 0 || L->block_tokens != ORC_ROWS || L->reserved != 0) return ORC_ERR_ARG;
+  if (L->num_kv_heads <= 0 || L->block_tokens != ORC_ROWS) return ORC_ERR_ARG;
+  if (L->format == 1) { /* FP8: one byte per element, no groups, no per-token widths */
+    if (L->k_group != 0 || L->v_group != 0 || L->mixed != 0) return ORC_ERR_ARG;
+    if (L->rotate != 0 && L->rotate != 1) return ORC_ERR_ARG;
+    if (L->rotate && !is_pow2(d)) return ORC_ERR_UNSUPPORTED;
+    return ORC_OK;
+  }
+  if (L->format != 0) return ORC_ERR_ARG;
   if (!(L->k_group == -1 || (L->k_group > 0 && L->k_group % 8 == 0 && d % L->k_group == 0)))
     return ORC_ERR_ARG;
   if (!(L->v_group > 0 && L->v_group % 8 == 0 && d % L->v_group == 0)) return ORC_ERR_ARG;
@@ -221,7 +266,9 @@ int orc_check_layout(const orc_layout* L) {
  *   zero padding to a multiple of 256 bytes.
  * The pages fix only the content (codes and a 16-bit scale and bias per group); this arrangement keeps a
  * row's K and V codes in one record so a row is one contiguous read. */
-static size_t row_slot_bytes(const orc_layout* L) { return (size_t)L->head_dim * (L->mixed ? 8 : 4) / 8; }
+static size_t row_slot_bytes(const orc_layout* L) {
+  return (size_t)L->head_dim * ((L->mixed || L->format == 1) ? 8 : 4) / 8;
+}
 static size_t kcodes_off(const orc_layout* L, int32_t t) { return (size_t)t * 2 * row_slot_bytes(L); }
 static size_t vcodes_off(const orc_layout* L, int32_t t, int32_t bits) {
   return kcodes_off(L, t) + (size_t)L->head_dim * bits / 8;
@@ -229,10 +276,11 @@ static size_t vcodes_off(const orc_layout* L, int32_t t, int32_t bits) {
 static size_t off_params(const orc_layout* L) { return (size_t)ORC_ROWS * 2 * row_slot_bytes(L); }
 static size_t kparams_per_row(const orc_layout* L) { return L->k_group > 0 ? (size_t)(L->head_dim / L->k_group) : 0; }
 static size_t prow_bytes(const orc_layout* L) {
+  if (L->format == 1) return 0;
   return (kparams_per_row(L) + (size_t)(L->head_dim / L->v_group)) * 4;
 }
 static size_t off_prows(const orc_layout* L) {
-  return off_params(L) + (L->k_group > 0 ? 0 : (size_t)L->head_dim * 4);
+  return off_params(L) + ((L->k_group > 0 || L->format == 1) ? 0 : (size_t)L->head_dim * 4);
 }
 static size_t kparams_off(const orc_layout* L, int32_t t) { return off_prows(L) + (size_t)t * prow_bytes(L); }
 static size_t vparams_off(const orc_layout* L, int32_t t) { return kparams_off(L, t) + kparams_per_row(L) * 4; }
@@ -301,6 +349,18 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
       rotate_row(xk + (size_t)t * d, d);
       rotate_row(xv + (size_t)t * d, d);
     }
+  }
+  if (L->format == 1) { /* FP8: K bytes then V bytes of each row record */
+    for (int32_t t = 0; t < ORC_ROWS; ++t) {
+      uint8_t* rec = tile + kcodes_off(L, t);
+      for (int32_t c = 0; c < d; ++c) {
+        rec[c] = orc_f32_to_e4m3(xk[(size_t)t * d + c]);
+        rec[d + c] = orc_f32_to_e4m3(xv[(size_t)t * d + c]);
+      }
+    }
+    free(xk);
+    free(xv);
+    return;
   }
   /* K */
   if (L->k_group > 0) {
@@ -381,6 +441,11 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
         const uint16_t* src = (which == 0 ? k : v) + ((size_t)s * H + h) * d;
         for (int32_t c = 0; c < d; ++c) x[c] = orc_f16_to_f32(src[c]);
         if (L->rotate) rotate_row(x, d);
+        if (L->format == 1) {
+          uint8_t* rec = tile + kcodes_off(L, row) + (size_t)which * d;
+          for (int32_t c = 0; c < d; ++c) rec[c] = orc_f32_to_e4m3(x[c]);
+          continue;
+        }
         int32_t g = which == 0 ? L->k_group : L->v_group;
         size_t code_off = which == 0 ? kcodes_off(L, row) : vcodes_off(L, row, bits);
         size_t par_off = which == 0 ? kparams_off(L, row) : vparams_off(L, row);
@@ -402,6 +467,14 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
  * value = code * scale + zero, exact in fp64. Returns the row's bit width. */
 int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, double* k_out, double* v_out) {
   const int32_t d = L->head_dim;
+  if (L->format == 1) {
+    const uint8_t* rec = tile + kcodes_off(L, t);
+    for (int32_t c = 0; c < d; ++c) {
+      k_out[c] = (double)orc_e4m3_to_f32(rec[c]);
+      v_out[c] = (double)orc_e4m3_to_f32(rec[d + c]);
+    }
+    return 8;
+  }
   int32_t bits = 4;
   if (L->mixed) bits = ((tile[off_header(L) + t / 8] >> (t % 8)) & 1u) ? 8 : 4;
   const uint8_t* kr = tile + kcodes_off(L, t);
