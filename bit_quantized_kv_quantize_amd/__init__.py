@@ -29,14 +29,15 @@ class Layout(ctypes.Structure):
 
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed",
-                 "reserved")]
+                 "format")]
 
     def __init__(self, head_dim, num_kv_heads, k_group=64, v_group=64, rotate=0, mixed=0,
-                 block_tokens=BLOCK_TOKENS):
-        super().__init__(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed), 0)
+                 block_tokens=BLOCK_TOKENS, format=0):
+        super().__init__(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed),
+                         int(format))
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 if not os.path.exists(LIB_PATH):

@@ -24,7 +24,7 @@ import numpy as np
 
 FORMAT = "kvq-cachecard"
 VERSION = "1"
-_LAYOUT_FIELDS = ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed")
+_LAYOUT_FIELDS = ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed", "format")
 
 
 def _host_i32(a) -> np.ndarray:
@@ -48,8 +48,8 @@ def pack(layout_fields: dict, tiles: np.ndarray, block_table, seq_lens, model_id
         nb = _n_blocks(int(lens[s]), int(layout_fields["block_tokens"]))
         local[s, :nb] = [index[int(b)] for b in bt[s, :nb]]
     po = np.zeros(lens.size, np.int32) if position_offsets is None else _host_i32(position_offsets)
-    meta = {k: str(int(layout_fields[k])) for k in _LAYOUT_FIELDS}
-    meta.update(format=FORMAT, version=VERSION, model_id=str(model_id), tile_bytes=str(tiles.shape[2]))
+    meta = {k: str(int(layout_fields.get(k, 0))) for k in _LAYOUT_FIELDS}
+    meta.update(card_format=FORMAT, card_version=VERSION, model_id=str(model_id), tile_bytes=str(tiles.shape[2]))
     tensors = {"tiles": np.ascontiguousarray(tiles, dtype=np.uint8), "block_table": local, "seq_lens": lens,
                "position_offsets": po}
     return tensors, meta
@@ -58,11 +58,11 @@ def pack(layout_fields: dict, tiles: np.ndarray, block_table, seq_lens, model_id
 def unpack(tensors: dict, meta: dict, layout_fields: Optional[dict] = None):
     """(tensors, metadata) of a card -> dict with tiles, block_table (card indices), seq_lens,
     position_offsets, model_id and layout. With ``layout_fields`` the card's layout must equal it."""
-    if meta.get("format") != FORMAT or meta.get("version") != VERSION:
+    if meta.get("card_format") != FORMAT or meta.get("card_version") != VERSION:
         raise ValueError("not a %s v%s file" % (FORMAT, VERSION))
     layout = {k: int(meta[k]) for k in _LAYOUT_FIELDS}
     if layout_fields is not None:
-        want = {k: int(layout_fields[k]) for k in _LAYOUT_FIELDS}
+        want = {k: int(layout_fields.get(k, 0)) for k in _LAYOUT_FIELDS}
         if want != layout:
             raise ValueError("card layout %s differs from %s" % (json.dumps(layout), json.dumps(want)))
     tiles = tensors["tiles"]

@@ -17,7 +17,13 @@ int check_layout(const kvq_layout* L) {
   if (!L) return KVQ_ERR_ARG;
   if (!(L->head_dim == 64 || L->head_dim == 128 || L->head_dim == 256)) return KVQ_ERR_ARG;
   if (L->num_kv_heads <= 0 || L->num_kv_heads > 4096) return KVQ_ERR_ARG;
-  if (L->block_tokens != kRows || L->reserved != 0) return KVQ_ERR_ARG;
+  if (L->block_tokens != kRows) return KVQ_ERR_ARG;
+  if (L->format == 1) {  // FP8 E4M3 per element
+    if (L->k_group != 0 || L->v_group != 0 || L->mixed != 0) return KVQ_ERR_ARG;
+    if (L->rotate != 0 && L->rotate != 1) return KVQ_ERR_ARG;
+    return KVQ_OK;
+  }
+  if (L->format != 0) return KVQ_ERR_ARG;
   if (!(L->k_group == -1 || is_group(L->k_group, L->head_dim))) return KVQ_ERR_ARG;
   if (!is_group(L->v_group, L->head_dim)) return KVQ_ERR_ARG;
   if ((L->rotate != 0 && L->rotate != 1) || (L->mixed != 0 && L->mixed != 1)) return KVQ_ERR_ARG;
@@ -33,13 +39,14 @@ TileGeom make_geom(const kvq_layout* L) {
   g.vg = L->v_group;
   g.rotate = L->rotate;
   g.mixed = L->mixed;
-  g.slot = g.d * (g.mixed ? 8 : 4) / 8;
+  g.fp8 = L->format == 1;
+  g.slot = g.d * ((g.mixed || g.fp8) ? 8 : 4) / 8;
   g.rec = 2 * g.slot;
   g.kpr = g.kg > 0 ? g.d / g.kg : 0;
-  g.vpr = g.d / g.vg;
+  g.vpr = g.fp8 ? 0 : g.d / g.vg;
   g.prow = (g.kpr + g.vpr) * 4;
   g.off_kch = (uint32_t)(kRows * g.rec);
-  g.off_prow = g.off_kch + (g.kg > 0 ? 0u : (uint32_t)(g.d * 4));
+  g.off_prow = g.off_kch + ((g.kg > 0 || g.fp8) ? 0u : (uint32_t)(g.d * 4));
   g.off_hdr = g.off_prow + (uint32_t)(kRows * g.prow);
   uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
   g.tile_bytes = (end + 255u) / 256u * 256u;

@@ -39,6 +39,19 @@ __device__ __forceinline__ void codes8(const uint8_t* row, int c0, int bits, flo
   }
 }
 
+// Values of 8 consecutive channels starting at channel c0 of an FP8 E4M3 row (exact in fp32).
+__device__ __forceinline__ void fp8x8(const uint8_t* row, int c0, float (&c)[8]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(row + c0);
+  c[0] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 0);
+  c[1] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 1);
+  c[2] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 2);
+  c[3] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 3);
+  c[4] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 0);
+  c[5] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 1);
+  c[6] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 2);
+  c[7] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 3);
+}
+
 // Grid (n_splits, H_kv, n_seqs), 256 threads. Thread t scores token t of each block against the G query
 // heads of its KV head; for the value pass thread (cl, tg) owns channels cl*8 .. cl*8+7 and the tokens
 // t = tg (mod TG). Writes (m, l, acc[d]) per query head and split.
@@ -147,7 +160,17 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     for (int j = 0; j < GMAX; ++j) score[j] = 0.0f;
     if (live) {
       const uint8_t* krow = tile + g.kcode(tid);
-      if (g.kg > 0) {
+      if (g.fp8) {
+        for (int c0 = 0; c0 < D; c0 += 8) {
+          float c[8];
+          fp8x8(krow, c0, c);
+#pragma unroll
+          for (int j = 0; j < GMAX; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) score[j] += c[e] * s_q[j][c0 + e];
+          }
+        }
+      } else if (g.kg > 0) {
         const uint32_t* kpar = reinterpret_cast<const uint32_t*>(tile + g.kpar(tid));
         float part[GMAX];
 #pragma unroll
@@ -217,12 +240,23 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] *= alpha[j];
     }
-    const int vgi = (cl * 8) / g.vg;
+    const int vgi = g.fp8 ? 0 : (cl * 8) / g.vg;
     for (int t = tg; t < kRows; t += TG) {
       bool any = false;
 #pragma unroll
       for (int j = 0; j < GMAX; ++j) any |= s_p[j][t] != 0.0f;
       if (!any) continue;
+      if (g.fp8) {
+        float c[8];
+        fp8x8(tile + g.vcode(t, 8), cl * 8, c);
+#pragma unroll
+        for (int j = 0; j < GMAX; ++j) {
+          const float pj = s_p[j][t];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[j][e] += pj * c[e];
+        }
+        continue;
+      }
       const int vbits = (g.mixed && ((hdr[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
       float c[8];
       codes8(tile + g.vcode(t, vbits), cl * 8, vbits, c);

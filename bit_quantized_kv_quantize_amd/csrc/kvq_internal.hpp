@@ -23,6 +23,7 @@ struct TileGeom {
   int vg;           // V group (channels)
   int rotate;       // Walsh-Hadamard rotation applied before quantisation
   int mixed;        // per-token 4/8-bit rows, 32-byte bitmap at off_hdr
+  int fp8;          // FP8 E4M3 per element: records of d K bytes then d V bytes, no parameters
   int slot;         // code bytes of one row of K (or V): d/2, or d in mixed pools
   int rec;          // bytes of one row record (2 * slot)
   int kpr;          // K param entries per row (d / kg), 0 for per-channel K

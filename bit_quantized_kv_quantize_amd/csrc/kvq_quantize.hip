@@ -116,6 +116,26 @@ __device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_row_b
   }
 }
 
+// FP8 E4M3 bytes of a lane's 8 values (the FP8 pool format): the hardware conversion rounds to nearest
+// even; clamping to +-448 first makes larger magnitudes saturate to the largest finite value.
+__device__ __forceinline__ uint2 to_e4m3x8(const float (&x)[8]) {
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(x[i], -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  return uint2{(uint32_t)lo, (uint32_t)hi};
+}
+
+// One FP8 row of one tensor: optional rotation, then one byte per channel.
+template <int LPR>
+__device__ __forceinline__ void fp8_token_row(const TileGeom& g, float (&x)[8], int li, uint8_t* row, float rot_c) {
+  if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+  *reinterpret_cast<uint2*>(row + li * 8) = to_e4m3x8(x);
+}
+
 // One row of one tensor (K or V) with per-token groups of grp channels.
 template <int LPR>
 __device__ __forceinline__ void quantize_token_row(const TileGeom& g, float (&x)[8], int li, int grp, int bits,
@@ -150,6 +170,10 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
   for (int t = r0; t < kRows; t += kRowsPerPass) {
     float x[8];
     load8(src + (size_t)t * g.H * D, x);
+    if (g.fp8) {
+      fp8_token_row<LPR>(g, x, li, tile + (kv ? g.vcode(t, 8) : g.kcode(t)), rot_c);
+      continue;
+    }
     const int bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
     quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
                             tile + (kv ? g.vcode(t, bits) : g.kcode(t)), tile + (kv ? g.vpar(t) : g.kpar(t)),
@@ -257,6 +281,10 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
   const int grp = kv ? g.vg : g.kg;
   float x[8];
   load8((kv ? v : k) + ((size_t)s * g.H + h) * D + li * 8, x);
+  if (g.fp8) {
+    fp8_token_row<LPR>(g, x, li, tile + (kv ? g.vcode(row, 8) : g.kcode(row)), rot_c);
+    return;
+  }
   quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
                           tile + (kv ? g.vcode(row, bits) : g.kcode(row)), tile + (kv ? g.vpar(row) : g.kpar(row)),
                           rot_c);
@@ -272,7 +300,7 @@ template <int LPR>
 hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                              const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, float rot_c,
                              hipStream_t stream) {
-  if (g.kg > 0) {
+  if (g.kg > 0 || g.fp8) {
     hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, 2), dim3(256), 0, stream, g, pool, block_ids,
                        k, v, prec_bits, rot_c, 0);
   } else {
@@ -311,32 +339,44 @@ __global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* _
     }
   }
   for (int t = r0; t < kRows; t += RPP) {
-    const int bits = (g.mixed && ((tile[g.off_hdr + t / 8] >> (t % 8)) & 1)) ? 8 : 4;
-    const uint8_t* row = tile + (which ? g.vcode(t, bits) : g.kcode(t));
-    uint32_t code[8];
-    if (bits == 8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(row + li * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        code[i] = (w.x >> (8 * i)) & 255u;
-        code[4 + i] = (w.y >> (8 * i)) & 255u;
-      }
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(row + li * 4);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) code[i] = (w >> (4 * i)) & 15u;
-    }
     float x[8];
-    if (kchan) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * cs[i] + cz[i];
+    if (g.fp8) {  // E4M3 -> fp32 is exact
+      const uint2 w = *reinterpret_cast<const uint2*>(tile + (which ? g.vcode(t, 8) : g.kcode(t)) + li * 8);
+      x[0] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 0);
+      x[1] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 1);
+      x[2] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 2);
+      x[3] = __builtin_amdgcn_cvt_f32_fp8((int)w.x, 3);
+      x[4] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 0);
+      x[5] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 1);
+      x[6] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 2);
+      x[7] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 3);
     } else {
-      // the lane's 8 channels lie in one group (groups are multiples of 8)
-      const uint32_t pr = *reinterpret_cast<const uint32_t*>(tile + (which ? g.vpar(t) : g.kpar(t)) +
-                                                             4 * ((8 * li) / grp));
-      const float s = h2f(pr & 0xffffu), z = h2f(pr >> 16);
+      const int bits = (g.mixed && ((tile[g.off_hdr + t / 8] >> (t % 8)) & 1)) ? 8 : 4;
+      const uint8_t* row = tile + (which ? g.vcode(t, bits) : g.kcode(t));
+      uint32_t code[8];
+      if (bits == 8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(row + li * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * s + z;
+        for (int i = 0; i < 4; ++i) {
+          code[i] = (w.x >> (8 * i)) & 255u;
+          code[4 + i] = (w.y >> (8 * i)) & 255u;
+        }
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + li * 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = (w >> (4 * i)) & 15u;
+      }
+      if (kchan) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * cs[i] + cz[i];
+      } else {
+        // the lane's 8 channels lie in one group (groups are multiples of 8)
+        const uint32_t pr = *reinterpret_cast<const uint32_t*>(tile + (which ? g.vpar(t) : g.kpar(t)) +
+                                                               4 * ((8 * li) / grp));
+        const float s = h2f(pr & 0xffffu), z = h2f(pr >> 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * s + z;
+      }
     }
     if (g.rotate) rotate_row<LPR>(x, li, unrot_c);
     uint4 o;

@@ -83,7 +83,12 @@ typedef struct kvq_layout {
   int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of every K and V row before quantisation */
   int32_t mixed;        /* 0 or 1: each token row is 4-bit or 8-bit, chosen per token ([QKV] methodology);
                            requires per-token K groups */
-  int32_t reserved;     /* must be 0 */
+  int32_t format;       /* 0: the group-wise integer codes described above (the Q4 cache);
+                           1: FP8 E4M3 per element, the FP8 cache the [UQ] technology section compares the
+                           4-bit cache against. Requires k_group = v_group = 0 and mixed = 0; a tile is 256
+                           records of d K bytes then d V bytes (no parameters), padded to 256 bytes; each
+                           (optionally rotated) fp32 value becomes E4M3 ("fn": bias 7, no infinities) by
+                           rounding to nearest even, magnitudes of 448 and more saturating to 448. */
 } kvq_layout;
 
 /* KVQ_OK if the layout is one this library can store and process, else the status explaining why. */

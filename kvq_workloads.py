@@ -62,10 +62,12 @@ class Config:
     shared_prefix: int = 0  # shared_prefix tables: tokens of the common prefix
     dead_fraction: float = 0.0  # fraction of cached slots remapped to the sentinel
     top_fraction: float = 0.0   # mixed pools: fraction of tokens (largest K norm) stored 8-bit
+    fmt: int = 0                # pool format: 0 group-wise codes, 1 FP8 E4M3 per element
 
     def layout(self) -> Dict[str, int]:
         return dict(head_dim=self.head_dim, num_kv_heads=self.num_kv_heads, block_tokens=BLOCK,
-                    k_group=self.k_group, v_group=self.v_group, rotate=self.rotate, mixed=self.mixed)
+                    k_group=self.k_group, v_group=self.v_group, rotate=self.rotate, mixed=self.mixed,
+                    format=self.fmt)
 
 
 CONFIGS: Dict[str, Config] = {
@@ -80,6 +82,13 @@ CONFIGS: Dict[str, Config] = {
     ]
 }
 CONFIG_ORDER: List[str] = [n for n, _ in sorted(CONFIGS.items(), key=lambda kv: kv[1].index)]
+
+
+def fp8_variant(cfg: Config) -> Config:
+    """The same workload (same seeds, shapes and tables) stored as an FP8 E4M3 pool, the baseline the
+    UltraQuant article compares the 4-bit cache against: no groups, no per-token widths."""
+    return dataclasses.replace(cfg, name=cfg.name + "_fp8", k_group=0, v_group=0, mixed=0, fmt=1,
+                               top_fraction=0.0)
 
 
 def _rng(cfg: Config, layer: int, stream: int, index: int = 0) -> np.random.Generator:

@@ -38,7 +38,7 @@ def test_card_round_trip_reproduces_decode(orc, tmp_path, name, kw):
     with safe_open(path, framework="numpy") as f:
         meta2 = f.metadata()
     card = cachecard.unpack(load_file(path), meta2, fields)
-    assert card["model_id"] == "model-x" and card["layout"] == {k: int(v) for k, v in fields.items()}
+    assert card["model_id"] == "model-x" and card["layout"] == dict({k: int(v) for k, v in fields.items()}, format=0)
     assert np.array_equal(card["seq_lens"], case.seq_lens) and np.array_equal(card["position_offsets"], offs)
     if cfg.table == "shared_prefix":  # the shared prefix is stored once
         n_pref = kw["shared_prefix"] // 256
@@ -66,4 +66,4 @@ def test_card_rejects_other_layouts_and_bad_tables(orc):
     with pytest.raises(ValueError):
         cachecard.unpack(bad, meta, fields)
     with pytest.raises(ValueError):
-        cachecard.unpack(tensors, dict(meta, format="other"), fields)
+        cachecard.unpack(tensors, dict(meta, card_format="other"), fields)

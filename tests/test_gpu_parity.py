@@ -259,3 +259,53 @@ def test_card_save_load_round_trip(env, orc, tmp_path, name):
     out2 = kvq.decode_attention(lay, pool2, q, t2, lens, case.max_seq_len, mask)
     torch.cuda.synchronize()
     assert torch.equal(out1, out2)
+
+
+def test_fp8_quantize_every_fp16_value_bit_exact(env, orc):
+    # Every finite fp16 bit pattern once in K and once (reversed) in V of an FP8 pool: the hardware conversion
+    # after the clamp to +-448 gives the oracle's E4M3 rounding (nearest even, saturating) for all of them.
+    kvq, torch = env
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    bits = np.where(np.isfinite(vals), bits, np.uint16(0))
+    k = bits.reshape(2 * 256, 2, 64)
+    v = bits[::-1].copy().reshape(2 * 256, 2, 64)
+    for rotate in (0, 1):
+        lay_o = orc.make_layout(64, 2, 0, 0, rotate, 0, format=1)
+        ref = np.zeros(orc.tile_bytes(lay_o) * 2 * 2, np.uint8)
+        ids = np.array([1, 0], np.int32)
+        kk, vv = (k, v) if not rotate else (np.clip(vals.reshape(k.shape), -8, 8).astype(np.float16).view(np.uint16),
+                                            np.clip(vals[::-1].reshape(k.shape), -8, 8).astype(np.float16).view(np.uint16))
+        kk = np.where(np.isfinite(kk.view(np.float16)), kk, np.uint16(0))
+        vv = np.where(np.isfinite(vv.view(np.float16)), vv, np.uint16(0))
+        orc.quantize_blocks(lay_o, ref, ids, kk, vv)
+        lay = kvq.Layout(64, 2, 0, 0, rotate, 0, format=1)
+        pool = kvq.new_pool(lay, 2)
+        kvq.quantize_blocks(lay, pool, to_dev(ids, torch), to_dev(kk, torch, torch.float16),
+                            to_dev(vv, torch, torch.float16))
+        got = pool.cpu().numpy()
+        diff = np.nonzero(got != ref)[0]
+        assert diff.size == 0, (rotate, diff[:8], got[diff[:8]], ref[diff[:8]])
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_fp8_pool_decode_and_restore(env, orc, name):
+    # The workloads stored as FP8 pools (same seeded data and tables): pool bytes (quantise and append)
+    # bit-exact, decode attention within tolerance, and the restored fp16 rows exact (unrotated pools) or
+    # within one fp16 ulp (rotated).
+    kvq, torch = env
+    cfg = W.fp8_variant(W.CONFIGS[name])
+    case = W.make_case(cfg, **SMALL[name])
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    assert np.array_equal(got_pool, ref_pool)
+    err = rel_err(got, ref)
+    print("fp8 %s: max rel err %.3g" % (name, err))
+    assert err <= TOL
+    ids = np.unique(case.prefill_blocks).astype(np.int32)
+    kr, vr = orc.dequantize_blocks(orc.make_layout(**cfg.layout()), ref_pool, ids)
+    kg_, vg_ = kvq.dequantize_blocks(kvq.Layout(**cfg.layout()), to_dev(got_pool, torch), to_dev(ids, torch))
+    for g_, r_ in ((kg_, kr), (vg_, vr)):
+        u = _f16_ulps(g_.cpu().numpy().view(np.uint16), r_)
+        assert u.max() <= (1 if cfg.rotate else 0)
