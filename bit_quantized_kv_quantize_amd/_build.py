@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_rows.hip", "kvq_decode_kchan.hip",
-           "kvq_decode_cascade.hip", "kvq_tiles.hip"]
+           "kvq_decode_cascade.hip", "kvq_tiles.hip", "kvq_decode_fp8.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

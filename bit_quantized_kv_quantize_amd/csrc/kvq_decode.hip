@@ -335,6 +335,7 @@ hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t str
     return launch_decode_kchan(g, a, stream);
   }
   if (!generic && decode_mfma_supported(g, a.G)) return launch_decode_mfma(g, a, stream);
+  if (!generic && !a.mask && decode_fp8_supported(g, a.G)) return launch_decode_fp8(g, a, stream);
   return launch_decode_generic(g, a, stream);
 }
 

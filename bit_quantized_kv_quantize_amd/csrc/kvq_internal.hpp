@@ -158,6 +158,9 @@ hipError_t launch_decode_kchan(const TileGeom& g, const DecodeArgs& a, hipStream
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_mfma_supported(const TileGeom& g, int G);
+// FP8 pools (matrix-core kernel for head_dim 128, G <= 8, calls without a sentinel mask).
+bool decode_fp8_supported(const TileGeom& g, int G);
+hipError_t launch_decode_fp8(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 // Cascade kernel for blocks shared by all sequences: layouts of the per-channel-K kernel; the caller then
 // runs that kernel with a.casc set.
 bool decode_cascade_supported(const TileGeom& g, int G);

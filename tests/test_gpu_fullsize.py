@@ -110,11 +110,14 @@ def oracle_sample(orc, case, layer, seqs):
     return ids, pool.reshape(ids.size, -1), out
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+@pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8"])
 def test_full_size_sampled(env, orc, name):
+    # (the last case: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against)
     kvq, torch = env
-    layers, seqs = FULL[name]
-    case = W.make_case(W.CONFIGS[name])
+    fp8 = name.endswith("_fp8")
+    base = name[:-4] if fp8 else name
+    layers, seqs = FULL[base]
+    case = W.make_case(W.fp8_variant(W.CONFIGS[base]) if fp8 else W.CONFIGS[base])
     for layer in layers:
         print("[fullsize] %s layer %d: %d seqs, %d blocks" % (name, layer, case.n_seqs, case.num_blocks), flush=True)
         _, pool, out = build_on_gpu(kvq, torch, case, layer)
