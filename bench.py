@@ -87,8 +87,10 @@ def decode_bytes(cfg: W.Config, case: W.Case, n4: np.ndarray, n8: np.ndarray, un
     and width bitmaps of the tiles touched, q, out, block tables, lengths and masks."""
     d, H = cfg.head_dim, cfg.num_kv_heads
     kpar = (d // cfg.k_group) * 4 if cfg.k_group > 0 else 0
-    vpar = (d // cfg.v_group) * 4
+    vpar = (d // cfg.v_group) * 4 if cfg.v_group > 0 else 0
     row4, row8 = d + kpar + vpar, 2 * d + kpar + vpar
+    if cfg.fmt == 1:  # FP8 E4M3: one byte per K and V element, no parameters
+        row4 = row8 = 2 * d
     if unique and cfg.table == "shared_prefix":
         # every physical block read once: its live rows are the rows below the longest sequence using it
         rows = 0
@@ -100,7 +102,7 @@ def decode_bytes(cfg: W.Config, case: W.Case, n4: np.ndarray, n8: np.ndarray, un
     else:
         b = int((n4 * row4 + n8 * row8).sum()) * H
         tiles = int(np.ceil(case.seq_lens / W.BLOCK).sum())
-    if cfg.k_group < 0:
+    if cfg.k_group < 0 and cfg.fmt == 0:
         b += tiles * H * d * 4
     if cfg.mixed:
         b += tiles * H * 32
@@ -307,12 +309,23 @@ def main():
         del pools, aks, avs, qs, outs
         torch.cuda.empty_cache()
         workloads = {}
-        for name in W.CONFIG_ORDER:
+        for name in W.CONFIG_ORDER + [FP8_BASELINE]:
             if name != cfg.name:
                 workloads[name] = measure_workload(kvq, torch, name)
         workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
                                "GBps": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
                                "pool_instances": layers, "append_us": None}
+
+    # ---------------------------------------------------------------- baselines of the pages' comparisons
+    baselines = None
+    if workloads is not None and FP8_BASELINE in workloads:
+        f8 = workloads[FP8_BASELINE]
+        baselines = {
+            "fp8_e4m3_cache": {"workload": FP8_BASELINE, "decode_us": f8["decode_us"], "bytes": f8["bytes"],
+                               "GBps": f8["GBps"], "q4_speedup": round(f8["decode_us"] / (kern_s * 1e6), 3),
+                               "q4_byte_ratio": round(f8["bytes"] / dec_b, 3)},
+            "restore_fp16": measure_restore(kvq, torch, cfg.name),
+        }
 
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
     cpu = None
@@ -347,6 +360,7 @@ def main():
                      "kernel_sources": digest},
         "cpu_baseline": cpu,
         "workloads": workloads,
+        "baselines": baselines,
     }
     print(json.dumps(line), flush=True)
 
@@ -355,13 +369,63 @@ def main():
 # the working set exceeds the 256 MB Infinity Cache (the multi-layer workloads use their layer count).
 INSTANCES = {"tiny_1k": 1, "gemma3_12b_4k": 48, "llama31_8b_pool_8k": 32, "qwen25_14b_prefix_32k": 16,
              "mixed_sentinel_32k": 1}
+# The 12 x 8K pool stored as FP8 E4M3: the cache the 4-bit one is compared against (UltraQuant, technology section).
+FP8_BASELINE = "llama31_8b_pool_8k_fp8"
+
+
+def workload_config(name):
+    return W.fp8_variant(W.CONFIGS[name[:-4]]) if name.endswith("_fp8") else W.CONFIGS[name]
+
+
+def measure_restore(kvq, torch, name, launches=4):
+    """The unfused path of QKVShare's injection step: every block of the workload's pool restored to fp16
+    K/V rows (kvq_dequantize_blocks), timed in a graph between events."""
+    cfg = W.CONFIGS[name]
+    case = W.make_case(cfg)
+    lay = kvq.Layout(**cfg.layout())
+    pool = kvq.new_pool(lay, case.num_blocks)
+    for ids, k, v, bm in W.prefill_chunks(case, 0, max_blocks=2048, threads=16):
+        kvq.quantize_blocks(lay, pool, torch.from_numpy(ids).cuda(), torch.from_numpy(k).view(torch.float16).cuda(),
+                            torch.from_numpy(v).view(torch.float16).cuda())
+    ids = torch.arange(case.num_blocks, dtype=torch.int32, device="cuda")
+    ko, vo = kvq.dequantize_blocks(lay, pool, ids)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kvq.dequantize_blocks(lay, pool, ids, ko, vo)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for _ in range(launches):
+            kvq.dequantize_blocks(lay, pool, ids, ko, vo)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / launches)
+    us = float(np.median(ts))
+    moved = pool.numel() + 2 * ko.numel() * 2
+    log("restore fp16 %s: %.1f us for %d blocks, %.0f GB/s (read + write)" % (name, us, case.num_blocks,
+                                                                             moved / us / 1e3))
+    del pool, ko, vo
+    torch.cuda.empty_cache()
+    return {"workload": name, "blocks": case.num_blocks, "us": round(us, 2), "bytes_moved": moved,
+            "GBps": round(moved / us / 1e3, 1)}
 
 
 def measure_workload(kvq, torch, name, launches=16):
     """One workload at full size: its layer quantised on the GPU (copied to INSTANCES pools), the append
     where the workload appends, then decode kernels captured back to back in a HIP graph (cycling the
     pools) and timed between events on the launch stream. Returns per-launch times and algorithmic bytes."""
-    cfg = W.CONFIGS[name]
+    cfg = workload_config(name)
     case = W.make_case(cfg)
     lay = kvq.Layout(**cfg.layout())
     pool = kvq.new_pool(lay, case.num_blocks)
@@ -387,7 +451,7 @@ def measure_workload(kvq, torch, name, launches=16):
         app = (torch.from_numpy(ak).view(torch.float16).cuda(), torch.from_numpy(av).view(torch.float16).cuda(),
                None if prec is None else torch.from_numpy(prec).cuda())
         kvq.append_tokens(lay, pool, app[0], app[1], table, positions, app[2])
-    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name, 1) - 1)]
+    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name.replace("_fp8", ""), 1) - 1)]
     torch.cuda.synchronize()
 
     def timed(fn):
