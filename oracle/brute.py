@@ -44,19 +44,19 @@ def _layout_offsets(d, k_group, v_group, mixed):
     """Byte geometry of a tile: row records (K codes then V codes of the row's width, 2 * slot bytes), the per-channel K
     parameters (if K is grouped per channel), per-row parameter records (K groups then V groups), header."""
     rows = 256
-    slot = d * (8 if mixed else 4) // 8
+    slot = d * (16 if mixed == 2 else 8 if mixed else 4) // 8
     off_par = rows * 2 * slot
     kpr = d // k_group if k_group > 0 else 0
     prow = (kpr + d // v_group) * 4
     off_prow = off_par + (0 if k_group > 0 else d * 4)
     off_hdr = off_prow + rows * prow
-    end = off_hdr + (32 if mixed else 0)
+    end = off_hdr + (64 if mixed == 2 else 32 if mixed else 0)
     tile = (end + 255) // 256 * 256
     return slot, off_par, off_prow, prow, kpr, off_hdr, tile
 
 
 def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
-    """rows_bytes: uint8 [n][slot]; bits: [n] 4 or 8 -> integer codes [n][d]."""
+    """rows_bytes: uint8 [n][slot]; bits: [n] 2, 4 or 8 -> integer codes [n][d]."""
     n = rows_bytes.shape[0]
     out = np.zeros((n, d), np.int64)
     lo = rows_bytes[:, : d // 2] & 0xF
@@ -64,11 +64,14 @@ def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
     four = np.empty((n, d), np.int64)
     four[:, 0::2] = lo
     four[:, 1::2] = hi
+    two = np.empty((n, d), np.int64)
+    for k in range(4):
+        two[:, k::4] = (rows_bytes[:, : d // 4] >> (2 * k)) & 3
     eight = rows_bytes[:, :d].astype(np.int64) if rows_bytes.shape[1] >= d else four
-    sel = bits == 8
-    out[~sel] = four[~sel]
-    if sel.any():
-        out[sel] = eight[sel]
+    for b, src in ((4, four), (2, two), (8, eight)):
+        sel = bits == b
+        if sel.any():
+            out[sel] = src[sel]
     return out
 
 
@@ -78,17 +81,23 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
         return _fp8_tile(tile, d)
     slot, off_par, off_prow, prow, kpr, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
     rows = 256
-    if mixed:
+    t = np.arange(rows)
+    if mixed == 2:
+        hdr = tile[off_hdr: off_hdr + 64]
+        bits = 2 << ((hdr[t // 4] >> (2 * (t % 4))) & 3).astype(np.int64)
+    elif mixed:
         hdr = tile[off_hdr: off_hdr + 32]
-        bits = np.where((hdr[np.arange(rows) // 8] >> (np.arange(rows) % 8)) & 1, 8, 4)
+        bits = np.where((hdr[t // 8] >> (t % 8)) & 1, 8, 4)
     else:
         bits = np.full(rows, 4)
     rec = tile[: rows * 2 * slot].reshape(rows, 2 * slot)
-    kc = _codes(rec[:, :slot], d, bits)
-    # V codes follow the row's own K codes: d/2 bytes in for 4-bit rows, d for 8-bit rows
-    vc = _codes(rec[:, d // 2: d], d, np.full(rows, 4))
-    if mixed:
-        vc = np.where((bits == 8)[:, None], _codes(rec[:, d: 2 * d], d, np.full(rows, 8)), vc)
+    kc = _codes(rec[:, :slot], d, np.where(bits == 16, 4, bits))
+    # V codes follow the row's own K codes: d * bits / 8 bytes in
+    vc = np.zeros((rows, d), np.int64)
+    for b in (2, 4, 8):
+        sel = bits == b
+        if sel.any():
+            vc[sel] = _codes(rec[sel, d * b // 8: d * b // 8 + d], d, np.full(int(sel.sum()), b))
     par = tile[off_prow: off_prow + rows * prow].reshape(rows, prow)
     if k_group > 0:
         kp = par[:, : kpr * 4].copy().view(np.float16).reshape(rows, kpr, 2)
@@ -101,7 +110,12 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
     vp = par[:, kpr * 4:].copy().view(np.float16).reshape(rows, d // v_group, 2)
     vs = np.repeat(vp[:, :, 0].astype(np.float64), v_group, axis=1)
     vz = np.repeat(vp[:, :, 1].astype(np.float64), v_group, axis=1)
-    return kc * ks + kz, vc * vs + vz
+    K, V = kc * ks + kz, vc * vs + vz
+    f16 = bits == 16  # FP16 rows: raw values, K then V
+    if f16.any():
+        K[f16] = rec[f16, : 2 * d].copy().view(np.float16).astype(np.float64)
+        V[f16] = rec[f16, 2 * d: 4 * d].copy().view(np.float16).astype(np.float64)
+    return K, V
 
 
 def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed, q_bits: np.ndarray,

@@ -249,7 +249,7 @@ int orc_check_layout(const orc_layout* L) {
     return ORC_ERR_ARG;
   if (!(L->v_group > 0 && L->v_group % 8 == 0 && d % L->v_group == 0)) return ORC_ERR_ARG;
   if (L->rotate != 0 && L->rotate != 1) return ORC_ERR_ARG;
-  if (L->mixed != 0 && L->mixed != 1) return ORC_ERR_ARG;
+  if (L->mixed < 0 || L->mixed > 2) return ORC_ERR_ARG;
   if (L->rotate && !is_pow2(d)) return ORC_ERR_UNSUPPORTED;
   if (L->mixed && L->k_group < 0) return ORC_ERR_UNSUPPORTED;
   return ORC_OK;
@@ -266,9 +266,14 @@ int orc_check_layout(const orc_layout* L) {
  *   zero padding to a multiple of 256 bytes.
  * The pages fix only the content (codes and a 16-bit scale and bias per group); this arrangement keeps a
  * row's K and V codes in one record so a row is one contiguous read. */
+/* Bytes of one row's K (or V) slot: the widest width the pool allows (FP16 in pools with widths
+ * {2, 4, 8, FP16}, 8 bits in 4/8-bit pools and FP8 pools, else 4 bits). */
 static size_t row_slot_bytes(const orc_layout* L) {
-  return (size_t)L->head_dim * ((L->mixed || L->format == 1) ? 8 : 4) / 8;
+  const int32_t wmax = L->mixed == 2 ? 16 : ((L->mixed || L->format == 1) ? 8 : 4);
+  return (size_t)L->head_dim * wmax / 8;
 }
+/* Header bytes: mixed 1 = one width bit per row; mixed 2 = a 2-bit width code per row. */
+static size_t header_bytes(const orc_layout* L) { return L->mixed == 2 ? 64 : (L->mixed ? 32 : 0); }
 static size_t kcodes_off(const orc_layout* L, int32_t t) { return (size_t)t * 2 * row_slot_bytes(L); }
 static size_t vcodes_off(const orc_layout* L, int32_t t, int32_t bits) {
   return kcodes_off(L, t) + (size_t)L->head_dim * bits / 8;
@@ -289,7 +294,7 @@ static size_t off_header(const orc_layout* L) { return off_prows(L) + (size_t)OR
 
 size_t orc_tile_bytes(const orc_layout* L) {
   if (orc_check_layout(L) != ORC_OK) return 0;
-  size_t end = off_header(L) + (L->mixed ? 32 : 0);
+  size_t end = off_header(L) + header_bytes(L);
   return (end + 255) / 256 * 256;
 }
 
@@ -301,18 +306,21 @@ static void put_u16(uint8_t* p, uint16_t v) { p[0] = (uint8_t)(v & 0xff); p[1] =
 static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 
 /* Pack one row's codes (d * bits / 8 bytes): 4-bit rows two per byte, low nibble first; 8-bit rows one
- * per byte. */
+ * per byte; 2-bit rows four per byte, lowest bits first. */
 static void pack_row(const uint8_t* codes, int32_t d, int32_t bits, uint8_t* dst) {
   memset(dst, 0, (size_t)d * bits / 8);
   if (bits == 8) {
     for (int32_t j = 0; j < d; ++j) dst[j] = codes[j];
-  } else {
+  } else if (bits == 4) {
     for (int32_t j = 0; j < d; ++j) dst[j / 2] |= (uint8_t)((codes[j] & 0xf) << (4 * (j % 2)));
+  } else {
+    for (int32_t j = 0; j < d; ++j) dst[j / 4] |= (uint8_t)((codes[j] & 0x3) << (2 * (j % 4)));
   }
 }
 
 static uint8_t unpack_code(const uint8_t* row, int32_t j, int32_t bits) {
   if (bits == 8) return row[j];
+  if (bits == 2) return (uint8_t)((row[j / 4] >> (2 * (j % 4))) & 0x3);
   return (uint8_t)((row[j / 2] >> (4 * (j % 2))) & 0xf);
 }
 
@@ -329,8 +337,19 @@ static void quantize_row_groups(const float* x, int32_t d, int32_t g, int32_t bi
   pack_row(codes, d, bits, code_dst);
 }
 
-static int row_bits(const uint32_t* bitmap, int32_t t) {
+/* Width of row t from the caller's width words: mixed 1 = bit t % 32 of word t / 32 (set = 8-bit, else
+ * 4-bit); mixed 2 = the 2-bit code at bits 2 (t % 16) of word t / 16 (0, 1, 2, 3 = 2, 4, 8, 16 bits; 4 bits
+ * without words). */
+static int row_bits(const orc_layout* L, const uint32_t* bitmap, int32_t t) {
+  if (L->mixed == 2) {
+    const uint32_t c = bitmap ? (bitmap[t / 16] >> (2 * (t % 16))) & 3u : 1u;
+    return 2 << c;
+  }
   return (bitmap && ((bitmap[t / 32] >> (t % 32)) & 1u)) ? 8 : 4;
+}
+/* A row stored at FP16 width: the (rotated) fp32 values rounded to fp16, no parameters. */
+static void store_f16_row(const float* x, int32_t d, uint8_t* dst) {
+  for (int32_t c = 0; c < d; ++c) put_u16(dst + 2 * c, orc_f32_to_f16(x[c]));
 }
 
 /* Quantise one tile from its 256 fp16 rows: k_rows/v_rows give row t at k_rows + t * row_stride. */
@@ -364,9 +383,13 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
   }
   /* K */
   if (L->k_group > 0) {
-    for (int32_t t = 0; t < ORC_ROWS; ++t)
-      quantize_row_groups(xk + (size_t)t * d, d, L->k_group, row_bits(bitmap, t), tile + kcodes_off(L, t),
-                          tile + kparams_off(L, t));
+    for (int32_t t = 0; t < ORC_ROWS; ++t) {
+      const int32_t b = row_bits(L, bitmap, t);
+      if (b == 16)
+        store_f16_row(xk + (size_t)t * d, d, tile + kcodes_off(L, t));
+      else
+        quantize_row_groups(xk + (size_t)t * d, d, L->k_group, b, tile + kcodes_off(L, t), tile + kparams_off(L, t));
+    }
   } else {
     /* one group per channel over the 256 rows of the block; always 4-bit (mixed is rejected) */
     uint8_t* codes = (uint8_t*)malloc((size_t)ORC_ROWS * d);
@@ -382,12 +405,16 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
     free(codes);
   }
   /* V */
-  for (int32_t t = 0; t < ORC_ROWS; ++t)
-    quantize_row_groups(xv + (size_t)t * d, d, L->v_group, row_bits(bitmap, t),
-                        tile + vcodes_off(L, t, row_bits(bitmap, t)), tile + vparams_off(L, t));
+  for (int32_t t = 0; t < ORC_ROWS; ++t) {
+    const int32_t b = row_bits(L, bitmap, t);
+    if (b == 16)
+      store_f16_row(xv + (size_t)t * d, d, tile + vcodes_off(L, t, b));
+    else
+      quantize_row_groups(xv + (size_t)t * d, d, L->v_group, b, tile + vcodes_off(L, t, b), tile + vparams_off(L, t));
+  }
   if (L->mixed) {
     uint8_t* hdr = tile + off_header(L);
-    for (int32_t w = 0; w < 8; ++w) {
+    for (int32_t w = 0; w < (int32_t)header_bytes(L) / 4; ++w) {
       uint32_t word = bitmap ? bitmap[w] : 0u;
       for (int32_t b = 0; b < 4; ++b) hdr[4 * w + b] = (uint8_t)((word >> (8 * b)) & 0xff);
     }
@@ -410,7 +437,7 @@ int orc_quantize_blocks(const orc_layout* L, uint8_t* pool, const int32_t* block
     for (int32_t h = 0; h < H; ++h) {
       const size_t base = ((size_t)i * ORC_ROWS * H + h) * d;
       quantize_tile(L, tile_ptr(L, pool, block_ids[i], h), k + base, v + base, (size_t)H * d,
-                    prec_bits ? prec_bits + (size_t)i * 8 : NULL);
+                    prec_bits ? prec_bits + (size_t)i * (header_bytes(L) / 4) : NULL);
     }
   }
   return ORC_OK;
@@ -434,6 +461,10 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
     int32_t blk = block_table[(size_t)s * max_blocks_per_seq + p / ORC_ROWS];
     int32_t row = p % ORC_ROWS;
     int32_t bits = (prec && prec[s] == 8) ? 8 : 4;
+    if (L->mixed == 2) {
+      bits = prec ? prec[s] : 4;
+      if (bits != 2 && bits != 4 && bits != 8 && bits != 16) return ORC_ERR_ARG;
+    }
     for (int32_t h = 0; h < H; ++h) {
       uint8_t* tile = tile_ptr(L, pool, blk, h);
       memset(tile + kcodes_off(L, row), 0, 2 * slot); /* the whole record: a wider row may have been here */
@@ -449,12 +480,21 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
         int32_t g = which == 0 ? L->k_group : L->v_group;
         size_t code_off = which == 0 ? kcodes_off(L, row) : vcodes_off(L, row, bits);
         size_t par_off = which == 0 ? kparams_off(L, row) : vparams_off(L, row);
-        quantize_row_groups(x, d, g, bits, tile + code_off, tile + par_off);
+        if (bits == 16) {
+          store_f16_row(x, d, tile + code_off);
+          memset(tile + par_off, 0, (size_t)(d / g) * 4); /* an FP16 row has no parameters */
+        } else {
+          quantize_row_groups(x, d, g, bits, tile + code_off, tile + par_off);
+        }
       }
-      if (L->mixed) {
+      if (L->mixed == 1) {
         uint8_t* byte = tile + off_header(L) + row / 8;
         if (bits == 8) *byte |= (uint8_t)(1u << (row % 8));
         else *byte &= (uint8_t)~(1u << (row % 8));
+      } else if (L->mixed == 2) {
+        uint8_t* byte = tile + off_header(L) + row / 4;
+        const uint32_t code = bits == 2 ? 0u : bits == 4 ? 1u : bits == 8 ? 2u : 3u;
+        *byte = (uint8_t)((*byte & ~(3u << (2 * (row % 4)))) | (code << (2 * (row % 4))));
       }
     }
   }
@@ -476,9 +516,17 @@ int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, dou
     return 8;
   }
   int32_t bits = 4;
-  if (L->mixed) bits = ((tile[off_header(L) + t / 8] >> (t % 8)) & 1u) ? 8 : 4;
+  if (L->mixed == 1) bits = ((tile[off_header(L) + t / 8] >> (t % 8)) & 1u) ? 8 : 4;
+  if (L->mixed == 2) bits = 2 << ((tile[off_header(L) + t / 4] >> (2 * (t % 4))) & 3u);
   const uint8_t* kr = tile + kcodes_off(L, t);
   const uint8_t* vr = tile + vcodes_off(L, t, bits);
+  if (bits == 16) {
+    for (int32_t c = 0; c < d; ++c) {
+      k_out[c] = (double)orc_f16_to_f32(get_u16(kr + 2 * c));
+      v_out[c] = (double)orc_f16_to_f32(get_u16(vr + 2 * c));
+    }
+    return bits;
+  }
   for (int32_t c = 0; c < d; ++c) {
     const uint8_t* kp = L->k_group > 0 ? tile + kparams_off(L, t) + (size_t)(c / L->k_group) * 4
                                        : tile + kchan_off(L, c);
