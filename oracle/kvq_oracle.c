@@ -415,7 +415,8 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
   if (L->mixed) {
     uint8_t* hdr = tile + off_header(L);
     for (int32_t w = 0; w < (int32_t)header_bytes(L) / 4; ++w) {
-      uint32_t word = bitmap ? bitmap[w] : 0u;
+      /* without width words every row is 4-bit: code 1 in each 2-bit field of a mixed-2 header */
+      uint32_t word = bitmap ? bitmap[w] : (L->mixed == 2 ? 0x55555555u : 0u);
       for (int32_t b = 0; b < 4; ++b) hdr[4 * w + b] = (uint8_t)((word >> (8 * b)) & 0xff);
     }
   }

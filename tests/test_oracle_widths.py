@@ -70,6 +70,28 @@ def test_tile_bytes_and_positions(orc):
             assert not tile[256 * rec + t * prow: 256 * rec + (t + 1) * prow].any()
 
 
+def test_blocks_without_width_words_are_four_bit(orc):
+    # No width words: every row is 4-bit, and each row's codes and parameters are those of a pool with a
+    # single width (mixed = 0) fed the same input; the header says 4 bits for every row.
+    d, H = 64, 2
+    lay = _lay(orc, d, H, 32, 32)
+    one = orc.make_layout(d, H, 32, 32, 0, 0)
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((256, H, d)).astype(np.float16)
+    v = rng.standard_normal((256, H, d)).astype(np.float16)
+    pool = np.zeros(orc.tile_bytes(lay) * H, np.uint8)
+    ref = np.zeros(orc.tile_bytes(one) * H, np.uint8)
+    orc.quantize_blocks(lay, pool, np.array([0], np.int32), k.view(np.uint16), v.view(np.uint16))
+    orc.quantize_blocks(one, ref, np.array([0], np.int32), k.view(np.uint16), v.view(np.uint16))
+    tb, tr = orc.tile_bytes(lay), orc.tile_bytes(one)
+    for h in range(H):
+        for t in (0, 1, 77, 255):
+            a = orc.dequant_row(lay, pool[h * tb:(h + 1) * tb], t)
+            b = orc.dequant_row(one, ref[h * tr:(h + 1) * tr], t)
+            assert a[2] == b[2] == 4
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 @pytest.mark.parametrize("rotate", [0, 1])
 def test_append_equals_row_of_whole_block(orc, rotate):
     d, H = 64, 2
