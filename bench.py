@@ -55,57 +55,63 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def live_rows(case: W.Case, wide_bits=None, appended_prec=None):
-    """(live 4-bit rows, live 8-bit rows) per sequence of one decode call: slots below seq_len whose
-    sentinel bit is clear; a row is 8-bit when its block's width bitmap (``wide_bits``: physical block ->
-    uint32[8]) or, for the appended slot, ``appended_prec`` says so."""
-    n4 = np.zeros(case.n_seqs, np.int64)
-    n8 = np.zeros(case.n_seqs, np.int64)
+def live_rows(case: W.Case, width_words=None, appended_prec=None):
+    """Live rows of one decode call per sequence and width: int64 [n_seqs, 4], columns 2, 4, 8 and 16 bits.
+    A row is live when it lies below seq_len and its sentinel bit is clear; its width comes from its block's
+    width words (``width_words``: physical block -> uint32 words in the pool header's encoding) or, for the
+    appended slot, from ``appended_prec``; rows of blocks without words are 4-bit."""
+    mixed = case.cfg.mixed
+    counts = np.zeros((case.n_seqs, 4), np.int64)
     for s in range(case.n_seqs):
         L = int(case.seq_lens[s])
         t = np.arange(L)
         live = np.ones(L, bool)
         if case.sentinel_mask is not None:
             live = ~((case.sentinel_mask[s][t // 32] >> (t % 32).astype(np.uint32)) & 1).astype(bool)
-        wide = np.zeros(L, bool)
-        if wide_bits is not None:
+        code = np.ones(L, np.int64)  # width codes 0..3 = 2, 4, 8, 16 bits
+        if width_words is not None:
             for bi in range((L + W.BLOCK - 1) // W.BLOCK):
-                words = wide_bits.get(int(case.block_table[s, bi]))
-                if words is not None:
-                    tt = np.arange(min(W.BLOCK, L - bi * W.BLOCK))
-                    wide[bi * W.BLOCK: bi * W.BLOCK + tt.size] = (words[tt // 32] >> (tt % 32).astype(np.uint32)) & 1
-            if case.append and appended_prec is not None and appended_prec[s] == 8:
-                wide[L - 1] = True
-        n4[s] = int((live & ~wide).sum())
-        n8[s] = int((live & wide).sum())
-    return n4, n8
+                words = width_words.get(int(case.block_table[s, bi]))
+                if words is None:
+                    continue
+                tt = np.arange(min(W.BLOCK, L - bi * W.BLOCK))
+                if mixed == 2:
+                    c = (words[tt // 16] >> (2 * (tt % 16)).astype(np.uint32)) & 3
+                else:
+                    c = np.where((words[tt // 32] >> (tt % 32).astype(np.uint32)) & 1, 2, 1)
+                code[bi * W.BLOCK: bi * W.BLOCK + tt.size] = c
+            if case.append and appended_prec is not None and L:
+                code[L - 1] = {2: 0, 8: 2, 16: 3}.get(int(appended_prec[s]), 1)
+        counts[s] = np.bincount(code[live], minlength=4)
+    return counts
 
 
-def decode_bytes(cfg: W.Config, case: W.Case, n4: np.ndarray, n8: np.ndarray, unique: bool = True) -> int:
+def decode_bytes(cfg: W.Config, case: W.Case, counts: np.ndarray, unique: bool = True) -> int:
     """Algorithmic bytes of one decode-attention call: every live row's K and V codes and parameters once
-    (a block shared by several block tables counted once when ``unique``), the per-channel K parameters
-    and width bitmaps of the tiles touched, q, out, block tables, lengths and masks."""
+    (a block shared by several block tables counted once when ``unique``; an FP16 row has no parameters),
+    the per-channel K parameters and width headers of the tiles touched, q, out, block tables, lengths and
+    masks. ``counts``: live rows per sequence and width (2, 4, 8, 16 bits), as from live_rows."""
     d, H = cfg.head_dim, cfg.num_kv_heads
     kpar = (d // cfg.k_group) * 4 if cfg.k_group > 0 else 0
     vpar = (d // cfg.v_group) * 4 if cfg.v_group > 0 else 0
-    row4, row8 = d + kpar + vpar, 2 * d + kpar + vpar
+    row = np.array([2 * d * bits // 8 + kpar + vpar for bits in (2, 4, 8)] + [4 * d], np.int64)
     if cfg.fmt == 1:  # FP8 E4M3: one byte per K and V element, no parameters
-        row4 = row8 = 2 * d
+        row[:] = 2 * d
     if unique and cfg.table == "shared_prefix":
         # every physical block read once: its live rows are the rows below the longest sequence using it
         rows = 0
         for b in np.unique(case.block_table[case.block_table >= 0]):
             hits = np.argwhere(case.block_table == b)
             rows += max(min(W.BLOCK, int(case.seq_lens[s]) - int(j) * W.BLOCK) for s, j in hits)
-        b = rows * H * row4
+        b = rows * H * int(row[1])
         tiles = np.unique(case.block_table).size
     else:
-        b = int((n4 * row4 + n8 * row8).sum()) * H
+        b = int((counts * row).sum()) * H
         tiles = int(np.ceil(case.seq_lens / W.BLOCK).sum())
     if cfg.k_group < 0 and cfg.fmt == 0:
         b += tiles * H * d * 4
     if cfg.mixed:
-        b += tiles * H * 32
+        b += tiles * H * (64 if cfg.mixed == 2 else 32)
     b += case.n_seqs * cfg.num_q_heads * d * (2 + 4)                 # q fp16 in, out fp32
     b += case.block_table.size * 4 + case.n_seqs * 4
     if case.sentinel_mask is not None:
@@ -249,8 +255,7 @@ def main():
         run()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t_start) / args.steps
-    n4, n8 = live_rows(case)
-    dec_b = decode_bytes(cfg, case, n4, n8)
+    dec_b = decode_bytes(cfg, case, live_rows(case))
     app_b = append_bytes(cfg, case.n_seqs)
     step_bytes = (dec_b + app_b) * layers
     value = step_bytes / step_s / 1e9
@@ -309,7 +314,7 @@ def main():
         del pools, aks, avs, qs, outs
         torch.cuda.empty_cache()
         workloads = {}
-        for name in W.CONFIG_ORDER + [FP8_BASELINE]:
+        for name in W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL]:
             if name != cfg.name:
                 workloads[name] = measure_workload(kvq, torch, name)
         workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
@@ -371,10 +376,16 @@ INSTANCES = {"tiny_1k": 1, "gemma3_12b_4k": 48, "llama31_8b_pool_8k": 32, "qwen2
              "mixed_sentinel_32k": 1}
 # The 12 x 8K pool stored as FP8 E4M3: the cache the 4-bit one is compared against (UltraQuant, technology section).
 FP8_BASELINE = "llama31_8b_pool_8k_fp8"
+# The 12 x 8K pool with per-token widths {2, 4, 8, FP16} (QKVShare, methodology section).
+WIDTHS_POOL = "llama31_8b_pool_8k_widths"
 
 
 def workload_config(name):
-    return W.fp8_variant(W.CONFIGS[name[:-4]]) if name.endswith("_fp8") else W.CONFIGS[name]
+    if name.endswith("_fp8"):
+        return W.fp8_variant(W.CONFIGS[name[:-4]])
+    if name.endswith("_widths"):
+        return W.widths_variant(W.CONFIGS[name[:-7]])
+    return W.CONFIGS[name]
 
 
 def measure_restore(kvq, torch, name, launches=4):
@@ -451,7 +462,8 @@ def measure_workload(kvq, torch, name, launches=16):
         app = (torch.from_numpy(ak).view(torch.float16).cuda(), torch.from_numpy(av).view(torch.float16).cuda(),
                None if prec is None else torch.from_numpy(prec).cuda())
         kvq.append_tokens(lay, pool, app[0], app[1], table, positions, app[2])
-    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name.replace("_fp8", ""), 1) - 1)]
+    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name.replace("_fp8", "").replace("_widths", ""),
+                                                                    1) - 1)]
     torch.cuda.synchronize()
 
     def timed(fn):
@@ -485,12 +497,12 @@ def measure_workload(kvq, torch, name, launches=16):
     if app is not None:
         app_us = timed(lambda i: kvq.append_tokens(lay, pools[i % len(pools)], app[0], app[1], table, positions,
                                                    app[2]))
-    n4, n8 = live_rows(case, wide, prec)
-    b = decode_bytes(cfg, case, n4, n8, unique=True)
+    counts = live_rows(case, wide, prec)
+    b = decode_bytes(cfg, case, counts, unique=True)
     res = {"decode_us": round(dec_us, 2), "bytes": b, "GBps": round(b / dec_us / 1e3, 1),
            "frac_of_hbm_peak": round(b / dec_us / 1e3 / HBM_PEAK_GBPS, 4), "pool_instances": len(pools),
            "append_us": None if app_us is None else round(app_us, 2)}
-    b_log = decode_bytes(cfg, case, n4, n8, unique=False)
+    b_log = decode_bytes(cfg, case, counts, unique=False)
     if b_log != b:
         res["logical_bytes"] = b_log
         res["logical_GBps"] = round(b_log / dec_us / 1e3, 1)

@@ -164,9 +164,13 @@ def new_workspace(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: in
 
 
 def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, stream=None) -> None:
-    """k, v: fp16 [n_blocks*256, H_kv, d]; block_ids int32 [n_blocks]; prec_bits int32/uint32 [n_blocks, 8]."""
+    """k, v: fp16 [n_blocks*256, H_kv, d]; block_ids int32 [n_blocks]; prec_bits int32/uint32 [n_blocks, W]:
+    the rows' width words, W = 8 (mixed = 1: one bit per row, set = 8-bit) or 16 (mixed = 2: a 2-bit code per
+    row, 0..3 = 2, 4, 8, 16 bits), or None (every row 4-bit)."""
     torch = _torch()
     n_blocks = int(block_ids.numel())
+    if prec_bits is not None and int(prec_bits.numel()) != n_blocks * (16 if layout.mixed == 2 else 8):
+        raise ValueError("prec_bits must hold %d words per block" % (16 if layout.mixed == 2 else 8))
     st = _lib.kvq_quantize_blocks(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256),
                                   _ptr(block_ids, "block_ids", (torch.int32,)), n_blocks,
                                   _ptr(k, "k", _f16(), 16), _ptr(v, "v", _f16(), 16),
@@ -209,7 +213,8 @@ def copy_blocks(layout: Layout, src_pool, src_ids, dst_pool, dst_ids, stream=Non
 
 def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None, stream=None) -> None:
     """k, v: fp16 [n_seqs, H_kv, d]; block_table int32 [n_seqs, max_blocks]; positions int32 [n_seqs];
-    prec uint8 [n_seqs] (4 or 8) or None."""
+    prec uint8 [n_seqs]: each row's width (4 or 8 in a mixed = 1 pool; 2, 4, 8 or 16 in a mixed = 2 pool)
+    or None (all 4-bit)."""
     torch = _torch()
     n = int(positions.numel())
     st = _lib.kvq_append_tokens(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256), n,

@@ -26,7 +26,7 @@ int check_layout(const kvq_layout* L) {
   if (L->format != 0) return KVQ_ERR_ARG;
   if (!(L->k_group == -1 || is_group(L->k_group, L->head_dim))) return KVQ_ERR_ARG;
   if (!is_group(L->v_group, L->head_dim)) return KVQ_ERR_ARG;
-  if ((L->rotate != 0 && L->rotate != 1) || (L->mixed != 0 && L->mixed != 1)) return KVQ_ERR_ARG;
+  if ((L->rotate != 0 && L->rotate != 1) || L->mixed < 0 || L->mixed > 2) return KVQ_ERR_ARG;
   if (L->mixed && L->k_group < 0) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -40,7 +40,7 @@ TileGeom make_geom(const kvq_layout* L) {
   g.rotate = L->rotate;
   g.mixed = L->mixed;
   g.fp8 = L->format == 1;
-  g.slot = g.d * ((g.mixed || g.fp8) ? 8 : 4) / 8;
+  g.slot = g.d * (g.mixed == 2 ? 16 : (g.mixed || g.fp8) ? 8 : 4) / 8;
   g.rec = 2 * g.slot;
   g.kpr = g.kg > 0 ? g.d / g.kg : 0;
   g.vpr = g.fp8 ? 0 : g.d / g.vg;
@@ -48,7 +48,7 @@ TileGeom make_geom(const kvq_layout* L) {
   g.off_kch = (uint32_t)(kRows * g.rec);
   g.off_prow = g.off_kch + ((g.kg > 0 || g.fp8) ? 0u : (uint32_t)(g.d * 4));
   g.off_hdr = g.off_prow + (uint32_t)(kRows * g.prow);
-  uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
+  uint32_t end = g.off_hdr + g.header_bytes();
   g.tile_bytes = (end + 255u) / 256u * 256u;
   return g;
 }

@@ -32,11 +32,29 @@ __device__ __forceinline__ void codes8(const uint8_t* row, int c0, int bits, flo
       c[e] = (float)((w.x >> (8 * e)) & 0xffu);
       c[4 + e] = (float)((w.y >> (8 * e)) & 0xffu);
     }
-  } else {
+  } else if (bits == 4) {
     uint32_t w = *reinterpret_cast<const uint32_t*>(row + c0 / 2);
 #pragma unroll
     for (int e = 0; e < 8; ++e) c[e] = (float)((w >> (4 * e)) & 0xfu);
+  } else if (bits == 2) {
+    uint32_t w = *reinterpret_cast<const uint16_t*>(row + c0 / 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = (float)((w >> (2 * e)) & 0x3u);
+  } else {  // 16: the values themselves, fp16
+    const uint4 w = *reinterpret_cast<const uint4*>(row + 2 * c0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[2 * e] = h2f(ww[e] & 0xffffu);
+      c[2 * e + 1] = h2f(ww[e] >> 16);
+    }
   }
+}
+
+// Scale and zero of a group from its stored word; a 16-bit row carries its values as they are.
+__device__ __forceinline__ void group_params(uint32_t p, int bits, float& sc, float& zc) {
+  sc = bits == 16 ? 1.0f : h2f(p & 0xffffu);
+  zc = bits == 16 ? 0.0f : h2f(p >> 16);
 }
 
 // Values of 8 consecutive channels starting at channel c0 of an FP8 E4M3 row (exact in fp32).
@@ -133,7 +151,6 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
   for (int lb = b0; lb < b1; ++lb) {
     const int phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + lb];
     const uint8_t* tile = a.pool + ((size_t)phys * g.H + h) * g.tile_bytes;
-    const uint32_t* hdr = reinterpret_cast<const uint32_t*>(tile + g.off_hdr);
 
     if (g.kg < 0) {
       // per-channel K: fold scale into q and the zero into a per-head constant for this block
@@ -154,7 +171,7 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     // scores of token tid
     const int pos = lb * kRows + tid;
     const bool live = pos < len && !is_sentinel(mask_row, pos);
-    const int bits = (g.mixed && ((hdr[tid >> 5] >> (tid & 31)) & 1u)) ? 8 : 4;
+    const int bits = g.row_bits(tile, tid);
     float score[GMAX];
 #pragma unroll
     for (int j = 0; j < GMAX; ++j) score[j] = 0.0f;
@@ -187,8 +204,8 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
           }
           if (((c0 + 8) % g.kg) == 0) {
             const int gi = c0 / g.kg;
-            const uint32_t p = kpar[gi];
-            const float sc = h2f(p & 0xffffu), zc = h2f(p >> 16);
+            float sc, zc;
+            group_params(kpar[gi], bits, sc, zc);
 #pragma unroll
             for (int j = 0; j < GMAX; ++j) {
               score[j] += sc * part[j] + zc * s_qsum[j][gi];
@@ -257,11 +274,11 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
         }
         continue;
       }
-      const int vbits = (g.mixed && ((hdr[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
+      const int vbits = g.row_bits(tile, t);
       float c[8];
       codes8(tile + g.vcode(t, vbits), cl * 8, vbits, c);
-      const uint32_t p = reinterpret_cast<const uint32_t*>(tile + g.vpar(t))[vgi];
-      const float sc = h2f(p & 0xffffu), zc = h2f(p >> 16);
+      float sc, zc;
+      group_params(reinterpret_cast<const uint32_t*>(tile + g.vpar(t))[vgi], vbits, sc, zc);
 #pragma unroll
       for (int j = 0; j < GMAX; ++j) {
         const float pj = s_p[j][t];

@@ -22,7 +22,8 @@ struct TileGeom {
   int kg;           // K group (channels) or -1 for one group per channel over the block
   int vg;           // V group (channels)
   int rotate;       // Walsh-Hadamard rotation applied before quantisation
-  int mixed;        // per-token 4/8-bit rows, 32-byte bitmap at off_hdr
+  int mixed;        // 1: per-token 4/8-bit rows, 32-byte bitmap at off_hdr; 2: per-token widths 2/4/8/16,
+                    // a 2-bit width code per row in a 64-byte header at off_hdr
   int fp8;          // FP8 E4M3 per element: records of d K bytes then d V bytes, no parameters
   int slot;         // code bytes of one row of K (or V): d/2, or d in mixed pools
   int rec;          // bytes of one row record (2 * slot)
@@ -37,6 +38,13 @@ struct TileGeom {
   // a row's V codes follow its K codes: d/2 bytes in for a 4-bit row, d for an 8-bit row
   __host__ __device__ uint32_t vcode(int t, int bits) const { return kcode(t) + (uint32_t)(d * bits / 8); }
   __host__ __device__ uint32_t kpar(int t) const { return off_prow + (uint32_t)t * (uint32_t)prow; }
+  __host__ __device__ uint32_t header_bytes() const { return mixed == 2 ? 64u : (mixed ? 32u : 0u); }
+  // width in bits of row t of a tile (4 outside mixed pools; FP8 pools are handled apart)
+  __device__ int row_bits(const uint8_t* tile, int t) const {
+    if (mixed == 2) return 2 << ((tile[off_hdr + t / 4] >> (2 * (t % 4))) & 3);
+    if (mixed) return ((tile[off_hdr + t / 8] >> (t % 8)) & 1) ? 8 : 4;
+    return 4;
+  }
   __host__ __device__ uint32_t vpar(int t) const { return off_prow + (uint32_t)t * (uint32_t)prow + (uint32_t)kpr * 4u; }
 };
 

@@ -76,7 +76,7 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
   }
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
-  const float L = bits == 8 ? 255.0f : 15.0f;
+  const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
   const float s32 = (mx - mn) / L;
   const uint32_t sh = f2h(s32), zh = f2h(mn);
   param = sh | (zh << 16);
@@ -97,22 +97,31 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
   }
 }
 
-// Store one lane's share of a code row: 4-bit codes as one uint32 (low nibble first), 8-bit codes as
-// two. With zero_tail (the V row of a 4-bit row in a mixed pool) the lane also zeroes its share of the
-// d bytes after the row, the unused rest of the record.
-__device__ __forceinline__ void store_codes(uint8_t* row, int li, int half_row_bytes, int bits, bool zero_tail,
+// Store one lane's share of a code row (8 codes): 2-bit codes as one uint16 (lowest bits first), 4-bit codes
+// as one uint32 (low nibble first), 8-bit codes as two. With tail > 0 (the V row of a row narrower than the
+// pool's widest) the lane also zeroes its share (tail / lpr bytes) of the record after the row.
+__device__ __forceinline__ void store_codes(uint8_t* row, int li, int lpr, int bits, int tail,
                                             const uint32_t (&code)[8]) {
   if (bits == 8) {
     uint2 w;
     w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
     w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
     *reinterpret_cast<uint2*>(row + li * 8) = w;
-  } else {
+  } else if (bits == 4) {
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
     *reinterpret_cast<uint32_t*>(row + li * 4) = w;
-    if (zero_tail) *reinterpret_cast<uint2*>(row + half_row_bytes + li * 8) = uint2{0u, 0u};
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= code[i] << (2 * i);
+    *reinterpret_cast<uint16_t*>(row + li * 2) = (uint16_t)w;
+  }
+  if (tail > 0) {
+    const int share = tail / lpr;  // a multiple of 4 bytes
+    uint32_t* z = reinterpret_cast<uint32_t*>(row + lpr * bits + li * share);
+    for (int k = 0; k < share / 4; ++k) z[k] = 0u;
   }
 }
 
@@ -136,17 +145,28 @@ __device__ __forceinline__ void fp8_token_row(const TileGeom& g, float (&x)[8], 
   *reinterpret_cast<uint2*>(row + li * 8) = to_e4m3x8(x);
 }
 
-// One row of one tensor (K or V) with per-token groups of grp channels.
+// One row of one tensor (K or V) with per-token groups of grp channels, at width bits (2, 4, 8 or 16; a
+// 16-bit row is the fp16 rounding of its values, with zero parameters); tail as for store_codes.
 template <int LPR>
 __device__ __forceinline__ void quantize_token_row(const TileGeom& g, float (&x)[8], int li, int grp, int bits,
-                                                   bool zero_tail, uint8_t* code_row, uint8_t* param_row,
+                                                   int tail, uint8_t* code_row, uint8_t* param_row,
                                                    float rot_c) {
   if (g.rotate) rotate_row<LPR>(x, li, rot_c);
   const int gl = grp / 8;
+  if (bits == 16) {
+    uint4 o;
+    o.x = f2h(x[0]) | (f2h(x[1]) << 16);
+    o.y = f2h(x[2]) | (f2h(x[3]) << 16);
+    o.z = f2h(x[4]) | (f2h(x[5]) << 16);
+    o.w = f2h(x[6]) | (f2h(x[7]) << 16);
+    *reinterpret_cast<uint4*>(code_row + li * 16) = o;
+    if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(param_row)[li / gl] = 0u;
+    return;
+  }
   uint32_t code[8];
   uint32_t param;
   quantize8(x, gl, bits, code, param);
-  store_codes(code_row, li, LPR * 4, bits, zero_tail, code);
+  store_codes(code_row, li, LPR, bits, tail, code);
   if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(param_row)[li / gl] = param;
 }
 
@@ -166,7 +186,7 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
   uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
   const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 8;
   const int grp = kv ? g.vg : g.kg;
-  const uint32_t* bitmap = prec_bits ? prec_bits + (size_t)i * 8 : nullptr;
+  const uint32_t* bitmap = prec_bits ? prec_bits + (size_t)i * (g.header_bytes() / 4) : nullptr;
   for (int t = r0; t < kRows; t += kRowsPerPass) {
     float x[8];
     load8(src + (size_t)t * g.H * D, x);
@@ -174,18 +194,21 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
       fp8_token_row<LPR>(g, x, li, tile + (kv ? g.vcode(t, 8) : g.kcode(t)), rot_c);
       continue;
     }
-    const int bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
-    quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
+    const int bits = g.mixed == 2 ? (2 << (bitmap ? (bitmap[t >> 4] >> (2 * (t & 15))) & 3u : 1u))
+                                  : (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
+    quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - 2 * D * bits / 8 : 0,
                             tile + (kv ? g.vcode(t, bits) : g.kcode(t)), tile + (kv ? g.vpar(t) : g.kpar(t)),
                             rot_c);
   }
   if (kv == 1) {
     // zero the tail padding (and write the width bitmap of mixed pools)
-    const uint32_t end = g.off_hdr + (g.mixed ? 32u : 0u);
+    const uint32_t end = g.off_hdr + g.header_bytes();
     for (uint32_t o = end + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
       *reinterpret_cast<uint32_t*>(tile + o) = 0u;
-    if (g.mixed && threadIdx.x < 8)
-      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[threadIdx.x] = bitmap ? bitmap[threadIdx.x] : 0u;
+    // width words (without them a mixed-2 pool's rows are 4-bit: code 1 in every field)
+    if (g.mixed && threadIdx.x < g.header_bytes() / 4)
+      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[threadIdx.x] =
+          bitmap ? bitmap[threadIdx.x] : (g.mixed == 2 ? 0x55555555u : 0u);
   }
 }
 
@@ -277,7 +300,8 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
   const int row = p % kRows;
   const int blk = block_table[(size_t)s * max_blocks_per_seq + p / kRows];
   uint8_t* tile = pool + ((size_t)blk * g.H + h) * g.tile_bytes;
-  const int bits = (prec && prec[s] == 8) ? 8 : 4;
+  const int pb = prec ? (int)prec[s] : 4;  // widths the pool does not hold are stored as 4-bit rows
+  const int bits = (pb == 8 && g.mixed) || (g.mixed == 2 && (pb == 2 || pb == 16)) ? pb : 4;
   const int grp = kv ? g.vg : g.kg;
   float x[8];
   load8((kv ? v : k) + ((size_t)s * g.H + h) * D + li * 8, x);
@@ -285,14 +309,21 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
     fp8_token_row<LPR>(g, x, li, tile + (kv ? g.vcode(row, 8) : g.kcode(row)), rot_c);
     return;
   }
-  quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed && bits == 4,
+  quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - 2 * D * bits / 8 : 0,
                           tile + (kv ? g.vcode(row, bits) : g.kcode(row)), tile + (kv ? g.vpar(row) : g.kpar(row)),
                           rot_c);
-  if (g.mixed && kv == 0 && li == 0) {
+  if (g.mixed == 1 && kv == 0 && li == 0) {
     uint32_t* word = reinterpret_cast<uint32_t*>(tile + g.off_hdr) + (row >> 5);
     const uint32_t bit = 1u << (row & 31);
     if (bits == 8) atomicOr(word, bit);
     else atomicAnd(word, ~bit);
+  }
+  if (g.mixed == 2 && kv == 0 && li == 0) {  // this row's 2-bit width code
+    uint32_t* word = reinterpret_cast<uint32_t*>(tile + g.off_hdr) + (row >> 4);
+    const int sh = 2 * (row & 15);
+    const uint32_t code = bits == 2 ? 0u : bits == 4 ? 1u : bits == 8 ? 2u : 3u;
+    atomicAnd(word, ~(3u << sh));
+    atomicOr(word, code << sh);
   }
 }
 
@@ -351,22 +382,37 @@ __global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* _
       x[6] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 2);
       x[7] = __builtin_amdgcn_cvt_f32_fp8((int)w.y, 3);
     } else {
-      const int bits = (g.mixed && ((tile[g.off_hdr + t / 8] >> (t % 8)) & 1)) ? 8 : 4;
+      const int bits = g.row_bits(tile, t);
       const uint8_t* row = tile + (which ? g.vcode(t, bits) : g.kcode(t));
       uint32_t code[8];
-      if (bits == 8) {
+      if (bits == 16) {  // stored fp16: exact in fp32
+        const uint4 w = *reinterpret_cast<const uint4*>(row + li * 16);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          code[2 * i] = ww[i] & 0xffffu;
+          code[2 * i + 1] = ww[i] >> 16;
+        }
+      } else if (bits == 8) {
         const uint2 w = *reinterpret_cast<const uint2*>(row + li * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           code[i] = (w.x >> (8 * i)) & 255u;
           code[4 + i] = (w.y >> (8 * i)) & 255u;
         }
-      } else {
+      } else if (bits == 4) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(row + li * 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i) code[i] = (w >> (4 * i)) & 15u;
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(row + li * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = (w >> (2 * i)) & 3u;
       }
-      if (kchan) {
+      if (bits == 16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = h2f(code[i]);
+      } else if (kchan) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = (float)code[i] * cs[i] + cz[i];
       } else {

@@ -26,23 +26,27 @@
  * Pool layout (the block pool of [AMB] 2.1 item 1 with the Q4 format of [AMB] 2.1 item 2)
  *   A pool holds num_blocks * H_kv tiles; tile (b, h) starts at byte (b * H_kv + h) * kvq_tile_bytes().
  *   A tile holds the 256 token rows of one KV head of one block, in this order (R = 256, d = head_dim,
- *   S = d/2, or d in mixed pools):
+ *   S = d/2; d in mixed = 1 pools; 2d in mixed = 2 pools):
  *     row records   R x 2S bytes: record t at t * 2S holds row t's K codes (d * b / 8 bytes, b = the row's
- *                   width, 4 or 8) immediately followed by its V codes (d * b / 8 bytes); in a mixed pool
- *                   the last d bytes of a 4-bit row's record are zero
+ *                   width: 4; 4 or 8; 2, 4, 8 or 16) immediately followed by its V codes (d * b / 8
+ *                   bytes); the rest of a narrower row's record is zero. A 16-bit row holds the (rotated)
+ *                   values themselves as fp16, and its parameter record is zero
  *     K per channel when k_group == -1: d x 4 bytes, [c] {scale, zero}
  *     param records R x P bytes, P = 4 * (d / k_group + d / v_group) (4 * d / v_group when K is grouped
  *                   per channel): record t holds row t's K params [group] {scale, zero}, then its V params
- *     header        mixed pools only: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes
+ *     header        mixed = 1: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes;
+ *                   mixed = 2: 16 x uint32, bits 2 (t % 16) .. 2 (t % 16) + 1 of word t / 16 = row t's width
+ *                   code (0, 1, 2, 3 = 2, 4, 8, 16 bits)
  *     padding       zero bytes up to the next multiple of 256
  *   A 4-bit row's K and V codes are one contiguous d-byte span, so a decode that gathers live rows reads
  *   each row's codes as one piece (one 128-byte line at d = 128).
  *   4-bit codes: element j of a row sits in bits 4*(j % 8) of little-endian uint32 word j / 8 (byte i holds
- *   elements 2i in its low nibble and 2i+1 in its high nibble). 8-bit codes: one byte per element.
+ *   elements 2i in its low nibble and 2i+1 in its high nibble). 8-bit codes: one byte per element. 2-bit
+ *   codes: element j in bits 2 (j % 4) of byte j / 4.
  *   A parameter entry is {fp16 scale, fp16 zero} (scale at byte 0, zero at byte 2); the pages store a
  *   16-bit scale and bias per group, this library stores them as IEEE fp16.
  *
- * Codec (one group G of fp32 values x; L = 15 for 4-bit rows, 255 for 8-bit rows)
+ * Codec (one group G of fp32 values x; L = 2^b - 1: 3, 15 or 255 for rows of b = 2, 4 or 8 bits)
  *   If layout.rotate: each fp16 row is first mapped to fp32 and rotated, y = c * H * x, H the natural
  *   (Sylvester) Hadamard matrix applied as butterflies with stage strides 1, 2, 4, ..., d/2, each pair
  *   (a, b) -> (a + b, a - b) in fp32, then one multiply by c = fp32(1/sqrt(d)) ([UQ] technology section).
@@ -81,8 +85,9 @@ typedef struct kvq_layout {
                            (asymmetric K/V grouping, [UQ] technology section) */
   int32_t v_group;      /* > 0: V groups are v_group consecutive channels of one token (32, 64 or 128) */
   int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of every K and V row before quantisation */
-  int32_t mixed;        /* 0 or 1: each token row is 4-bit or 8-bit, chosen per token ([QKV] methodology);
-                           requires per-token K groups */
+  int32_t mixed;        /* 0: every row 4-bit; 1: each token row is 4-bit or 8-bit; 2: each token row is
+                           2-, 4-, 8-bit or FP16 - the per-token widths of [QKV] methodology section.
+                           Requires per-token K groups */
   int32_t format;       /* 0: the group-wise integer codes described above (the Q4 cache);
                            1: FP8 E4M3 per element, the FP8 cache the [UQ] technology section compares the
                            4-bit cache against. Requires k_group = v_group = 0 and mixed = 0; a tile is 256
@@ -120,9 +125,11 @@ const char* kvq_status_string(int status);
  *   n_blocks   >= 0 (0 is a no-op).
  *   k, v       device fp16 [n_blocks * 256][H_kv][d], token-major: row t of input block i for head h
  *              starts at element ((i * 256 + t) * H_kv + h) * d.
- *   prec_bits  device uint32 [n_blocks][8] or NULL. Bit (t % 32) of word t / 32 set = token t of block
- *              i is stored with 8-bit codes (K and V, every head). Must be NULL unless L->mixed; NULL
- *              in a mixed pool means every token is 4-bit.
+ *   prec_bits  device uint32 [n_blocks][W] or NULL, the widths of each block's rows (K and V, every head)
+ *              in the header's own encoding: mixed = 1, W = 8, bit (t % 32) of word t / 32 set = token t
+ *              of block i is 8-bit; mixed = 2, W = 16, bits 2 (t % 16) of word t / 16 = token t's width
+ *              code (0, 1, 2, 3 = 2, 4, 8, 16 bits). Must be NULL unless L->mixed; NULL means every token
+ *              is 4-bit.
  * Errors: KVQ_ERR_ARG (null pool/k/v/block_ids with n_blocks > 0, prec_bits for a non-mixed layout,
  * invalid layout), KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP.
  */
@@ -141,8 +148,10 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
  *   positions    device int32 [n_seqs]: slot of the new token (usually the old sequence length). The
  *                row written is positions[s] % 256 of block block_table[s][positions[s] / 256], which
  *                the caller must have allocated (trusted). Other rows are untouched.
- *   prec         device uint8 [n_seqs] holding 4 or 8, or NULL (all 4-bit). Must be NULL unless
- *                L->mixed. In mixed pools the row's header bit is set or cleared accordingly.
+ *   prec         device uint8 [n_seqs]: the row's width - 4 or 8 (mixed = 1), 2, 4, 8 or 16 (mixed =
+ *                2); any other value stores a 4-bit row - or NULL (all 4-bit). Must be NULL unless
+ *                L->mixed. The row's header field is rewritten and the whole record cleared first, so a
+ *                slot may be rewritten at another width.
  * The caller advances its own seq_lens afterwards; this call does not touch them.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (per-channel K groups: a partial block has no defined
  * channel statistics), KVQ_ERR_HIP.

@@ -30,7 +30,7 @@ from __future__ import annotations
 
 import dataclasses
 from concurrent.futures import ThreadPoolExecutor
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -63,6 +63,8 @@ class Config:
     dead_fraction: float = 0.0  # fraction of cached slots remapped to the sentinel
     top_fraction: float = 0.0   # mixed pools: fraction of tokens (largest K norm) stored 8-bit
     fmt: int = 0                # pool format: 0 group-wise codes, 1 FP8 E4M3 per element
+    width_fracs: Tuple[float, float, float] = (0.0, 0.0, 0.0)  # mixed = 2 pools: fractions of tokens
+    # stored FP16 (largest K norms), 8-bit (the next largest) and 2-bit (the smallest); the rest are 4-bit
 
     def layout(self) -> Dict[str, int]:
         return dict(head_dim=self.head_dim, num_kv_heads=self.num_kv_heads, block_tokens=BLOCK,
@@ -89,6 +91,13 @@ def fp8_variant(cfg: Config) -> Config:
     UltraQuant article compares the 4-bit cache against: no groups, no per-token widths."""
     return dataclasses.replace(cfg, name=cfg.name + "_fp8", k_group=0, v_group=0, mixed=0, fmt=1,
                                top_fraction=0.0)
+
+
+def widths_variant(cfg: Config, fracs: Tuple[float, float, float] = (0.05, 0.15, 0.30)) -> Config:
+    """The same workload with per-token widths {2, 4, 8, FP16} (a mixed = 2 pool): each sequence's tokens
+    ranked by K norm, the largest ``fracs[0]`` stored FP16, the next ``fracs[1]`` 8-bit, the smallest
+    ``fracs[2]`` 2-bit, the rest 4-bit. Per-token K groups only."""
+    return dataclasses.replace(cfg, name=cfg.name + "_widths", mixed=2, top_fraction=0.0, width_fracs=fracs)
 
 
 def _rng(cfg: Config, layer: int, stream: int, index: int = 0) -> np.random.Generator:
@@ -272,6 +281,62 @@ def appended_is_8bit(norms_sq_cached: np.ndarray, norm_sq_new: float, top_fracti
     return bool(norm_sq_new >= kth)
 
 
+def width_codes(norms_sq: np.ndarray, fracs) -> np.ndarray:
+    """uint8 [n] width codes (0, 1, 2, 3 = 2, 4, 8, 16 bits) of tokens ranked by K norm (ties to the lower
+    index): floor(fracs[0] n) largest -> 3, the next floor(fracs[1] n) -> 2, floor(fracs[2] n) smallest
+    -> 0 (never one already given 3 or 2), the rest -> 1."""
+    n = norms_sq.size
+    order = np.argsort(-norms_sq, kind="stable")
+    n16, n8 = int(np.floor(fracs[0] * n)), int(np.floor(fracs[1] * n))
+    n2 = min(int(np.floor(fracs[2] * n)), n - n16 - n8)
+    codes = np.ones(n, np.uint8)
+    codes[order[:n16]] = 3
+    codes[order[n16:n16 + n8]] = 2
+    if n2:
+        codes[order[n - n2:]] = 0
+    return codes
+
+
+def appended_width(norms_sq_cached: np.ndarray, norm_sq_new: float, fracs) -> int:
+    """Width in bits of an appended token: 16 or 8 if its norm reaches the smallest norm of the cached
+    FP16 or FP16 + 8-bit set, 2 if it is below the largest norm of the cached 2-bit set, else 4."""
+    codes = width_codes(norms_sq_cached, fracs)
+    for c, bits in ((3, 16), (2, 8)):
+        if (codes >= c).any() and norm_sq_new >= norms_sq_cached[codes >= c].min():
+            return bits
+    if (codes == 0).any() and norm_sq_new < norms_sq_cached[codes == 0].max():
+        return 2
+    return 4
+
+
+def width_words(codes_rows: np.ndarray) -> np.ndarray:
+    """uint8 [n_blocks * 256] width codes -> uint32 [n_blocks][16] (code of row t at bits 2 (t % 16) of
+    word t / 16)."""
+    nb = codes_rows.size // BLOCK
+    c = codes_rows.reshape(nb, 16, 16).astype(np.uint64)
+    w = (c << (2 * np.arange(16, dtype=np.uint64))).sum(axis=2)
+    return w.astype(np.uint32)
+
+
+def _block_words(cfg: Config, ns: np.ndarray, nb: int) -> np.ndarray:
+    """Width words of one sequence's nb blocks from the K norms of its ns.size cached tokens; slots past
+    the cached tokens get the 4-bit code (mixed = 2) or a clear bit."""
+    n = ns.size
+    if cfg.mixed == 2:
+        codes = np.ones(nb * BLOCK, np.uint8)
+        codes[:n] = width_codes(ns, cfg.width_fracs)
+        return width_words(codes)
+    sel = np.zeros(nb * BLOCK, bool)
+    sel[:n] = precision_map(ns, cfg.top_fraction)
+    return bits_words(sel)
+
+
+def _append_prec(cfg: Config, ns: np.ndarray, norm_sq_new: float) -> int:
+    if cfg.mixed == 2:
+        return appended_width(ns, norm_sq_new, cfg.width_fracs)
+    return 8 if appended_is_8bit(ns, norm_sq_new, cfg.top_fraction) else 4
+
+
 def bits_words(sel_rows: np.ndarray) -> np.ndarray:
     """bool [n_blocks * 256] -> uint32 [n_blocks][8] bitmap (bit t % 32 of word t / 32)."""
     nb = sel_rows.size // BLOCK
@@ -291,7 +356,7 @@ def prefill_chunks(case: Case, layer: int, max_blocks: int = 2048, threads: int 
     each chunk at most ``max_blocks`` blocks (one sequence more for mixed pools), so a full-size pool can
     be filled without holding all of its fp16 source at once.
 
-    For mixed pools ``bitmaps`` is the uint32 [n][8] precision bitmap of the chunk's blocks (the same
+    For mixed pools ``bitmaps`` is the uint32 [n][W] width words of the chunk's blocks (the same
     per-sequence ranking as ``mixed_precision_inputs``) and, if ``prec_out`` is given, the width of each
     sequence's appended token is written into it; otherwise ``bitmaps`` is None."""
     cfg = case.cfg
@@ -332,29 +397,27 @@ def prefill_chunks(case: Case, layer: int, max_blocks: int = 2048, threads: int 
         else:
             for i in range(n_blk):
                 one(i)
-        bitmaps = np.empty((n_blk, 8), np.uint32)
+        bitmaps = np.empty((n_blk, 16 if cfg.mixed == 2 else 8), np.uint32)
         off = 0
         for s in seqs:
             nb = sequence_blocks(case, s).size
             n = int(case.context[s])
             ns = norms[off * BLOCK: off * BLOCK + n]
-            sel = np.zeros(nb * BLOCK, bool)
-            sel[:n] = precision_map(ns, cfg.top_fraction)
-            bitmaps[off: off + nb] = bits_words(sel)
+            bitmaps[off: off + nb] = _block_words(cfg, ns, nb)
             if ak is not None and nb:
-                prec_out[s] = 8 if appended_is_8bit(ns, float(k_norms_sq(ak[s:s + 1])[0]), cfg.top_fraction) else 4
+                prec_out[s] = _append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
             off += nb
         yield ids, k, v, bitmaps
 
 
 def mixed_precision_inputs(case: Case, layer: int, threads: int = 8):
-    """For a mixed pool: per prefill block the uint32[8] precision bitmap (aligned with
-    case.prefill_blocks) and per sequence the 4/8 width of its appended token.
+    """For a mixed pool: per prefill block the uint32 [W] width words (W = 8 for mixed = 1, 16 for mixed = 2;
+    aligned with case.prefill_blocks) and per sequence the width in bits of its appended token.
 
     Each sequence ranks its own cached tokens by K norm; blocks must not be shared between sequences."""
     cfg = case.cfg
     pos = {int(b): i for i, b in enumerate(case.prefill_blocks)}
-    bitmaps = np.zeros((case.prefill_blocks.size, 8), np.uint32)
+    bitmaps = np.zeros((case.prefill_blocks.size, 16 if cfg.mixed == 2 else 8), np.uint32)
     prec = np.full(case.n_seqs, 4, np.uint8)
     ak, _ = append_kv(cfg, layer, case.n_seqs)
     for s in range(case.n_seqs):
@@ -362,11 +425,9 @@ def mixed_precision_inputs(case: Case, layer: int, threads: int = 8):
         k, _ = blocks_kv(cfg, layer, blocks, threads)
         n = int(case.context[s])
         ns = k_norms_sq(k[:n])
-        sel = np.zeros(blocks.size * BLOCK, bool)
-        sel[:n] = precision_map(ns, cfg.top_fraction)
-        words = bits_words(sel)
+        words = _block_words(cfg, ns, blocks.size)
         for i, b in enumerate(blocks):
             bitmaps[pos[int(b)]] = words[i]
-        if case.append and appended_is_8bit(ns, float(k_norms_sq(ak[s:s + 1])[0]), cfg.top_fraction):
-            prec[s] = 8
+        if case.append and blocks.size:
+            prec[s] = _append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
     return bitmaps, prec

@@ -444,8 +444,9 @@ int orc_quantize_blocks(const orc_layout* L, uint8_t* pool, const int32_t* block
   return ORC_OK;
 }
 
-/* Host-memory counterpart of kvq_append_tokens. Pinned by: test_oracle_codec.py (an appended row
- * equals the same row inside a whole quantised block). */
+/* Host-memory counterpart of kvq_append_tokens. prec[s] is the row's width: 8 in a mixed pool, 2, 8 or 16
+ * in a mixed-2 pool; any other value (or no prec) stores a 4-bit row. Pinned by: test_oracle_codec.py and
+ * test_oracle_widths.py (an appended row equals the same row inside a whole quantised block). */
 int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const uint16_t* k,
                       const uint16_t* v, const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* positions, const uint8_t* prec) {
@@ -462,10 +463,7 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
     int32_t blk = block_table[(size_t)s * max_blocks_per_seq + p / ORC_ROWS];
     int32_t row = p % ORC_ROWS;
     int32_t bits = (prec && prec[s] == 8) ? 8 : 4;
-    if (L->mixed == 2) {
-      bits = prec ? prec[s] : 4;
-      if (bits != 2 && bits != 4 && bits != 8 && bits != 16) return ORC_ERR_ARG;
-    }
+    if (L->mixed == 2 && prec && (prec[s] == 2 || prec[s] == 16)) bits = prec[s]; /* any other value: 4 */
     for (int32_t h = 0; h < H; ++h) {
       uint8_t* tile = tile_ptr(L, pool, blk, h);
       memset(tile + kcodes_off(L, row), 0, 2 * slot); /* the whole record: a wider row may have been here */

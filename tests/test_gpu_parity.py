@@ -73,14 +73,16 @@ def test_decode_within_tolerance(env, orc, name, decode_path):
     (1, 0, -1, 32, 5, 256), (1, 1, 32, 64, 2, 64), (0, 0, 128, 16, 4, 128), (0, 0, 8, 256, 2, 256),
     (1, 0, 64, 64, 8, 128), (0, 0, 64, 64, 2, 128), (1, 0, 64, 64, 4, 256), (0, 0, 64, 64, 1, 256),
     (1, 0, -1, 32, 5, 128), (0, 0, -1, 64, 8, 128), (1, 0, -1, 32, 3, 128), (0, 0, -1, 32, 1, 128),
-    (0, 1, 64, 64, 4, 128), (1, 1, 64, 64, 2, 128)])
+    (0, 1, 64, 64, 4, 128), (1, 1, 64, 64, 2, 128), (0, 2, 64, 64, 4, 128), (1, 2, 32, 64, 2, 64),
+    (1, 2, 64, 32, 8, 256), (0, 2, 16, 128, 1, 128)])
 def test_layout_variants(env, orc, rotate, mixed, kg, vg, G, d, decode_path):
     # Generic layouts beyond the five workloads: group sizes, widths, rotation, G up to 16, ragged
     # lengths (0, 1, 255, 256, 257, long) and sentinel masks (one sequence entirely sentinel).
     kvq, torch = env
     H = 2
     cfg = W.Config(9, "variant", d, H * G, H, 1, kg, vg, rotate, mixed, 6, 0, "perm", kg > 0, 3, 10.0, 1.0,
-                   dead_fraction=0.5, top_fraction=0.2 if mixed else 0.0)
+                   dead_fraction=0.5, top_fraction=0.2 if mixed == 1 else 0.0,
+                   width_fracs=(0.1, 0.2, 0.3) if mixed == 2 else (0.0, 0.0, 0.0))
     case = W.make_case(cfg, context=[0, 1, 255, 256, 700, 1500] if kg > 0 else [1, 255, 256, 257, 700, 1500])
     case.sentinel_mask[4] = 0xFFFFFFFF
     if kg > 0:
@@ -189,7 +191,7 @@ def _f16_ulps(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
 
 DEQUANT_VARIANTS = [  # rotate, mixed, k_group, v_group, d
     (0, 0, 64, 64, 128), (1, 0, -1, 32, 128), (1, 1, 64, 64, 128), (0, 1, 32, 64, 64), (1, 0, 64, 32, 256),
-    (0, 0, -1, 64, 64), (1, 0, 8, 256, 256)]
+    (0, 0, -1, 64, 64), (1, 0, 8, 256, 256), (0, 2, 64, 64, 128), (1, 2, 32, 16, 64), (1, 2, 64, 64, 256)]
 
 
 @pytest.mark.parametrize("variant", DEQUANT_VARIANTS + W.CONFIG_ORDER)
@@ -202,7 +204,8 @@ def test_dequantize_blocks_within_one_ulp(env, orc, variant):
     else:
         rotate, mixed, kg, vg, d = variant
         cfg = W.Config(9, "variant", d, 2, 2, 1, kg, vg, rotate, mixed, 3, 0, "perm", kg > 0, 3, 10.0, 1.0,
-                       top_fraction=0.3 if mixed else 0.0)
+                       top_fraction=0.3 if mixed == 1 else 0.0,
+                       width_fracs=(0.1, 0.2, 0.3) if mixed == 2 else (0.0, 0.0, 0.0))
         case = W.make_case(cfg, context=[700, 257, 1024])
     inp = host_inputs(case)
     ref_pool, _ = oracle_run(orc, case, inp, decode=False)
@@ -309,3 +312,61 @@ def test_fp8_pool_decode_and_restore(env, orc, name):
     for g_, r_ in ((kg_, kr), (vg_, vr)):
         u = _f16_ulps(g_.cpu().numpy().view(np.uint16), r_)
         assert u.max() <= (1 if cfg.rotate else 0)
+
+
+WIDTH_WORKLOADS = ["tiny_1k", "gemma3_12b_4k", "llama31_8b_pool_8k", "mixed_sentinel_32k"]
+
+
+@pytest.mark.parametrize("name", WIDTH_WORKLOADS)
+def test_widths_pool_decode_and_restore(env, orc, name):
+    # The workloads with per-token K groups stored with widths {2, 4, 8, FP16} (same seeded data and tables;
+    # widths by K-norm rank): pool bytes (quantise and append) bit-exact, decode attention within
+    # tolerance, and the restored fp16 rows within one fp16 ulp of the oracle's.
+    kvq, torch = env
+    cfg = W.widths_variant(W.CONFIGS[name])
+    case = W.make_case(cfg, **SMALL[name])
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    diff = np.nonzero(got_pool != ref_pool)[0]
+    assert diff.size == 0, "first differing bytes at %s" % diff[:16]
+    err = rel_err(got, ref)
+    print("widths %s: max rel err %.3g" % (name, err))
+    assert err <= TOL
+    ids = np.unique(case.prefill_blocks).astype(np.int32)
+    kr, vr = orc.dequantize_blocks(orc.make_layout(**cfg.layout()), ref_pool, ids)
+    kg_, vg_ = kvq.dequantize_blocks(kvq.Layout(**cfg.layout()), to_dev(got_pool, torch), to_dev(ids, torch))
+    for g_, r_ in ((kg_, kr), (vg_, vr)):
+        u = _f16_ulps(g_.cpu().numpy().view(np.uint16), r_)
+        assert u.max() <= 1 and (u > 0).mean() < 1e-3
+
+
+def test_widths_append_rewrites_record_at_another_width(env, orc):
+    # Each slot appended twice, the second time at another width (and once at a width the pool does not
+    # hold, stored 4-bit): the record, the parameters and the header field end up as the oracle's.
+    kvq, torch = env
+    d, H = 128, 4
+    rng = np.random.default_rng(21)
+    n = 40
+    table = np.array([[i % 3] for i in range(n)], np.int32)
+    pos = rng.choice(256 * 3, n, replace=False) % 256
+    pos = np.unique(pos)[:n].astype(np.int32)
+    n = pos.size
+    table = table[:n]
+    k = rng.standard_normal((2, n, H, d)).astype(np.float16)
+    v = rng.standard_normal((2, n, H, d)).astype(np.float16)
+    first = rng.choice(np.array([2, 4, 8, 16, 5], np.uint8), n)
+    second = rng.choice(np.array([2, 4, 8, 16, 7], np.uint8), n)
+    for rotate in (0, 1):
+        lay_o = orc.make_layout(d, H, 64, 32, rotate, 2)
+        ref = np.zeros(orc.tile_bytes(lay_o) * H * 3, np.uint8)
+        lay = kvq.Layout(d, H, 64, 32, rotate, 2)
+        pool = kvq.new_pool(lay, 3)
+        for step, prec in ((0, first), (1, second)):
+            assert orc.append_tokens(lay_o, ref, k[step].view(np.uint16), v[step].view(np.uint16), table, pos,
+                                     prec) == 0
+            kvq.append_tokens(lay, pool, to_dev(k[step], torch), to_dev(v[step], torch), to_dev(table, torch),
+                              to_dev(pos, torch), to_dev(prec, torch))
+        got = pool.cpu().numpy()
+        diff = np.nonzero(got != ref)[0]
+        assert diff.size == 0, (rotate, diff[:16])

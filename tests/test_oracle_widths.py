@@ -114,6 +114,13 @@ def test_append_equals_row_of_whole_block(orc, rotate):
     assert orc.append_tokens(lay, built, k[rows].view(np.uint16), v[rows].view(np.uint16), table, pos, wrong) == 0
     assert orc.append_tokens(lay, built, k[rows].view(np.uint16), v[rows].view(np.uint16), table, pos, prec) == 0
     tb = orc.tile_bytes(lay)
+    # a width the pool does not hold stores the row at 4 bits, as if 4 had been given
+    odd = np.zeros_like(whole)
+    four = np.zeros_like(whole)
+    for buf, w in ((odd, 5), (four, 4)):
+        assert orc.append_tokens(lay, buf, k[rows].view(np.uint16), v[rows].view(np.uint16), table, pos,
+                                 np.full(len(rows), w, np.uint8)) == 0
+    assert np.array_equal(odd, four)
     for h in range(H):
         for r in rows:
             a = orc.dequant_row(lay, whole[h * tb:(h + 1) * tb], r)

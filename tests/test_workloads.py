@@ -56,9 +56,11 @@ def test_sentinel_mask_exact_count_and_precision_map():
 
 
 def test_prefill_chunks_cover_every_block_once():
-    for name, kw in [("llama31_8b_pool_8k", dict(n_seqs=3, context=[1000, 513, 0])),
-                     ("mixed_sentinel_32k", dict(n_seqs=4, context=[1024, 600, 0, 333]))]:
-        case = W.make_case(W.CONFIGS[name], **kw)
+    for name, kw, widths in [("llama31_8b_pool_8k", dict(n_seqs=3, context=[1000, 513, 0]), False),
+                             ("mixed_sentinel_32k", dict(n_seqs=4, context=[1024, 600, 0, 333]), False),
+                             ("llama31_8b_pool_8k", dict(n_seqs=4, context=[1000, 513, 0, 300]), True)]:
+        cfg = W.widths_variant(W.CONFIGS[name]) if widths else W.CONFIGS[name]
+        case = W.make_case(cfg, **kw)
         prec = np.zeros(case.n_seqs, np.uint8)
         ids, ks, bms = [], [], []
         for chunk, k, v, bm in W.prefill_chunks(case, 0, max_blocks=3, threads=2, prec_out=prec):
@@ -77,3 +79,20 @@ def test_prefill_chunks_cover_every_block_once():
             assert np.array_equal(prec, prec_ref)
         else:
             assert all(b is None for b in bms)
+
+
+def test_width_codes_and_words():
+    norms = np.arange(100, dtype=np.float64)[::-1].copy()   # token i has the (100 - i)-th norm
+    codes = W.width_codes(norms, (0.05, 0.15, 0.3))
+    assert (codes[:5] == 3).all() and (codes[5:20] == 2).all() and (codes[20:70] == 1).all()
+    assert (codes[70:] == 0).all()
+    assert W.appended_width(norms, norms[4], (0.05, 0.15, 0.3)) == 16
+    assert W.appended_width(norms, norms[10], (0.05, 0.15, 0.3)) == 8
+    assert W.appended_width(norms, norms[40], (0.05, 0.15, 0.3)) == 4
+    assert W.appended_width(norms, norms[80], (0.05, 0.15, 0.3)) == 2
+    assert W.appended_width(norms[:0], 1.0, (0.05, 0.15, 0.3)) == 4
+    rows = np.arange(512) % 4
+    words = W.width_words(rows.astype(np.uint8))
+    assert words.shape == (2, 16)
+    for t in (0, 1, 2, 3, 17, 255, 300, 511):
+        assert (words[t // 256, (t % 256) // 16] >> (2 * (t % 16))) & 3 == rows[t]
