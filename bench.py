@@ -381,11 +381,7 @@ WIDTHS_POOL = "llama31_8b_pool_8k_widths"
 
 
 def workload_config(name):
-    if name.endswith("_fp8"):
-        return W.fp8_variant(W.CONFIGS[name[:-4]])
-    if name.endswith("_widths"):
-        return W.widths_variant(W.CONFIGS[name[:-7]])
-    return W.CONFIGS[name]
+    return W.named_config(name)
 
 
 def measure_restore(kvq, torch, name, launches=4):

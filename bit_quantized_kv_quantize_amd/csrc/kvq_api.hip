@@ -120,14 +120,16 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   w.ctr = 0;
   w.ml = up(ns * g.H * sizeof(unsigned));
   w.acc = w.ml + up(parts * 2 * sizeof(float));
+  // row lists only for layouts the row-list kernel reads: one list per width (4 and 8 bits, and 2 and 16
+  // in pools of four widths)
+  const size_t nwd = g.mixed == 2 ? 4 : 2;
   w.cnt = w.acc + up(parts * g.d * sizeof(float));
-  w.list = w.cnt + up(ns * 2 * sizeof(int));
-  // row lists only for layouts the row-list kernel reads
+  w.list = w.cnt + up(ns * nwd * sizeof(int));
   w.list_cap = decode_rows_supported(g, num_q_heads / g.H) ? (max_seq_len + 63) / 64 * 64 : 0;
-  w.bcnt = w.list + up(ns * 2 * (size_t)w.list_cap * sizeof(uint32_t));
+  w.bcnt = w.list + up(ns * nwd * (size_t)w.list_cap * sizeof(uint32_t));
   // at least one block per sequence, so the count kernels always have a grid
   w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
-  w.cflag = w.bcnt + up(ns * 2 * (size_t)w.bcnt_blocks * sizeof(int));
+  w.cflag = w.bcnt + up(ns * nwd * (size_t)w.bcnt_blocks * sizeof(int));
   w.total = w.cflag + up(p.casc > 0 ? (size_t)p.max_blocks * sizeof(int) : 0);
   return w;
 }

@@ -3,11 +3,12 @@
 // Memory Below the Prompt", technical summary 2.1-2.2, with the sentinel slots of the IntentKV article and
 // the per-token bit widths of QKVShare's methodology).
 //
-// Work unit: a chunk of live rows of one (sequence, KV head) - 64 rows of 4-bit codes or 32 rows of 8-bit
-// codes, about 4 KB of codes either way. Pure 4-bit pools without sentinel slots are read block by block
-// (each wave takes 64 rows of every block of its split). Pools with sentinel slots or mixed widths are read
-// as compacted row lists built by compact_rows_k: per sequence, the live 4-bit rows and the live 8-bit rows
-// in slot order, so every chunk is of one width and sentinel rows are never fetched.
+// Work unit: a chunk of live rows of one (sequence, KV head) - 64 rows of 4-bit codes, 32 rows of 8-bit
+// codes, 64 rows of 2-bit codes or 16 FP16 rows (8 KB of K and V, 4 KB for 2-bit chunks). Pure 4-bit pools
+// without sentinel slots are read block by block (each wave takes 64 rows of every block of its split).
+// Pools with sentinel slots or per-token widths are read as compacted row lists built by compact_rows_k:
+// per sequence, the live rows of each width in slot order, so every chunk is of one width and sentinel
+// rows are never fetched.
 //
 // Matrix-core layout (v_mfma_f32_16x16x32_f16 throughout):
 // * MFMA row r = 4 h + 2 gamma + part: query head h, K (or V) group gamma, part 0/1 = fp16 hi/lo of the
@@ -15,11 +16,12 @@
 //   16-token slice of K costs one MFMA per 32 channels.
 // * QK: B = K codes of 16 tokens (lane = token), unpacked without arithmetic: masking a packed word with
 //   0x000F000F leaves two nibbles as fp16 subnormals n * 2^-24 (0x00F000F0 gives 16 n * 2^-24); 8-bit codes
-//   are paired with byte permutes (bytes are exact subnormals too). The 2^24 and 1/16 factors fold into the
-//   group scales and the query.
-// * PV: V rows are staged in LDS as loaded (lane = token) and read back transposed with the gfx950 LDS
-//   transpose loads (16 nibbles or 8 bytes per lane, one output channel per lane), so the B operand of
-//   32 tokens x 16 channels needs no per-element shuffling. The A operand (p * v_scale as hi/lo, one row per
+//   are paired with byte permutes (bytes are exact subnormals too); 2-bit codes are masked field by field
+//   (4^p n * 2^-24 for field p); FP16 rows are the operand as stored. The 2^24 and 1/16 (1/4^p) factors
+//   fold into the group scales and the query.
+// * PV: V rows are staged in LDS as loaded (lane = token; 2-bit codes widened to nibbles) and read back
+//   transposed with the gfx950 LDS transpose loads (16 nibbles, 8 bytes or 4 halves per lane, one output
+//   channel per lane), so the B operand of 32 tokens x 16 channels needs no per-element shuffling. The A operand (p * v_scale as hi/lo, one row per
 //   (head, V group, part)) is written position-major and read with the 16-bit transpose load.
 // Online softmax per wave (16-lane DPP reductions), the four waves merge at the end, and the split-K merge
 // runs in the split that arrives last (splitk_arrive).
@@ -56,31 +58,49 @@ __device__ __forceinline__ uint32_t pair_sel(int m) {
 constexpr int kD = 128;
 constexpr int kVP = 80;     // LDS row pitch (bytes) of staged 4-bit V rows
 constexpr int kVP8 = 144;   // LDS row pitch (bytes) of staged 8-bit V rows
+constexpr int kVP16 = 288;  // LDS row pitch (bytes) of staged FP16 V rows
 constexpr int kPP = 20;     // halves per position of the position-major p * v_scale tile (16 rows + pad)
 
 // ------------------------------------------------------------------------------------- row compaction
-// Per sequence, the live 4-bit rows then the live 8-bit rows as (physical block << 8 | row) in slot
-// order, and their counts. A slot is live when it is below seq_len and its sentinel bit is clear; its
-// width comes from the mixed-pool bitmap (KV head 0's tile: every head of a block holds the same
+// Per sequence and width, the live rows in slot order as (physical block << 8 | row), and their counts:
+// NWD = 2 lists (4-bit, 8-bit) for 4-bit pools and pools of 4- and 8-bit rows, NWD = 4 lists (4-bit, 8-bit,
+// 2-bit, FP16) for pools of four widths. A slot is live when it is below seq_len and its sentinel bit is
+// clear; its width comes from the pool header (KV head 0's tile: every head of a block holds the same
 // per-token widths). Grid (n_seqs), 1024 threads. A wave takes 8 logical blocks at a time, 8 lanes per
-// block and 32 rows per lane (one word of the sentinel mask and of the width bitmap): the waves count
-// every block's live rows, the counts are scanned in the workspace, and the waves write each block's
-// entries at its offsets.
+// block and 32 rows per lane (one word of the sentinel mask): the waves count every block's live rows per
+// width, the counts are scanned in the workspace, and the waves write each block's entries at its offsets.
 constexpr int kCompactThreads = 1024;
 
+template <int NWD>
 struct RowBits {
-  int b, phys;     // logical block (or -1 past the end), physical block
-  uint32_t w4, w8;  // rows 32k .. 32k + 31 of the block (k = lane & 7): live 4-bit, live 8-bit
+  int b, phys;        // logical block (or -1 past the end), physical block
+  uint32_t m[NWD];    // rows 32k .. 32k + 31 of the block (k = lane & 7), live and in width list i
 };
-__device__ __forceinline__ RowBits row_bits(const TileGeom& g, const DecodeArgs& a, int seq, int bb, int nblk, int len,
-                                            int l) {
-  RowBits r;
+
+// Bit j of the result set where 2-bit field j of the 64-bit (h1:h0) equals c.
+__device__ __forceinline__ uint32_t fields_equal(uint32_t h0, uint32_t h1, uint32_t c) {
+  auto one = [c](uint32_t h) {
+    const uint32_t x = h ^ (c * 0x55555555u);  // equal fields become 00
+    uint32_t z = ~(x | (x >> 1)) & 0x55555555u;
+    z = (z | (z >> 1)) & 0x33333333u;            // gather the even bits into the low 16
+    z = (z | (z >> 2)) & 0x0F0F0F0Fu;
+    z = (z | (z >> 4)) & 0x00FF00FFu;
+    return (z | (z >> 8)) & 0x0000FFFFu;
+  };
+  return one(h0) | (one(h1) << 16);
+}
+
+template <int NWD>
+__device__ __forceinline__ RowBits<NWD> row_bits(const TileGeom& g, const DecodeArgs& a, int seq, int bb, int nblk,
+                                                 int len, int l) {
+  RowBits<NWD> r;
   const int k = l & 7;
   r.b = bb + (l >> 3);
   if (r.b >= nblk) {
     r.b = -1;
     r.phys = 0;
-    r.w4 = r.w8 = 0u;
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) r.m[i] = 0u;
     return r;
   }
   r.phys = a.block_table[(size_t)seq * a.max_blocks_per_seq + r.b];
@@ -88,106 +108,111 @@ __device__ __forceinline__ RowBits row_bits(const TileGeom& g, const DecodeArgs&
   const int nvalid = min(max(len - t0, 0), 32);
   uint32_t live = nvalid >= 32 ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
   if (a.mask) live &= ~a.mask[(size_t)seq * a.mask_words + (t0 >> 5)];
-  const uint32_t wide =
-      g.mixed ? reinterpret_cast<const uint32_t*>(a.pool + (size_t)r.phys * g.H * g.tile_bytes + g.off_hdr)[k] : 0u;
-  r.w4 = live & ~wide;
-  r.w8 = live & wide;
+  const uint32_t* hdr = reinterpret_cast<const uint32_t*>(a.pool + (size_t)r.phys * g.H * g.tile_bytes + g.off_hdr);
+  if constexpr (NWD == 2) {
+    const uint32_t wide = g.mixed ? hdr[k] : 0u;
+    r.m[0] = live & ~wide;
+    r.m[1] = live & wide;
+  } else {  // width codes 0, 1, 2, 3 = 2, 4, 8, 16 bits -> lists 2, 0, 1, 3
+    const uint32_t h0 = hdr[2 * k], h1 = hdr[2 * k + 1];
+    r.m[0] = live & fields_equal(h0, h1, 1u);
+    r.m[1] = live & fields_equal(h0, h1, 2u);
+    r.m[2] = live & fields_equal(h0, h1, 0u);
+    r.m[3] = live & fields_equal(h0, h1, 3u);
+  }
   return r;
 }
 
+template <int NWD>
 __global__ __launch_bounds__(kCompactThreads) void compact_rows_k(TileGeom g, DecodeArgs a) {
   constexpr int NW = kCompactThreads / 64;
-  __shared__ int s_tot[NW][2];
-  __shared__ int s_carry[2];
+  __shared__ int s_tot[NW][NWD];
+  __shared__ int s_carry[NWD];
   const int seq = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int len = a.seq_lens[seq];
   const int nblk = (len + kRows - 1) / kRows;
-  int* cnt = a.ws_bcnt + (size_t)seq * a.bcnt_blocks * 2;
+  int* cnt = a.ws_bcnt + (size_t)seq * a.bcnt_blocks * NWD;
   // counts of each block (the 8 lanes of a block add theirs up)
   for (int bb = 8 * w; bb < nblk; bb += 8 * NW) {
-    const RowBits r = row_bits(g, a, seq, bb, nblk, len, l);
-    int c4 = __popc(r.w4), c8 = __popc(r.w8);
+    const RowBits<NWD> r = row_bits<NWD>(g, a, seq, bb, nblk, len, l);
 #pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      c4 += __shfl_xor(c4, m);
-      c8 += __shfl_xor(c8, m);
-    }
-    if ((l & 7) == 0 && r.b >= 0) {
-      cnt[2 * r.b] = c4;
-      cnt[2 * r.b + 1] = c8;
+    for (int i = 0; i < NWD; ++i) {
+      int c = __popc(r.m[i]);
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) c += __shfl_xor(c, m);
+      if ((l & 7) == 0 && r.b >= 0) cnt[NWD * r.b + i] = c;
     }
   }
   __syncthreads();
   // exclusive scan of the counts, kCompactThreads blocks at a time (thread = block)
-  if (tid == 0) {
-    s_carry[0] = 0;
-    s_carry[1] = 0;
-  }
+  if (tid < NWD) s_carry[tid] = 0;
   __syncthreads();
   for (int b0 = 0; b0 < nblk; b0 += kCompactThreads) {
     const int b = b0 + tid;
-    const int c4 = b < nblk ? cnt[2 * b] : 0, c8 = b < nblk ? cnt[2 * b + 1] : 0;
-    int i4 = c4, i8 = c8;  // inclusive scan within the wave
+    int c[NWD], x[NWD];
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) {
+      c[i] = b < nblk ? cnt[NWD * b + i] : 0;
+      x[i] = c[i];  // inclusive scan within the wave
+    }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
-      const int u4 = __shfl_up(i4, m), u8 = __shfl_up(i8, m);
-      if (l >= m) {
-        i4 += u4;
-        i8 += u8;
+#pragma unroll
+      for (int i = 0; i < NWD; ++i) {
+        const int u = __shfl_up(x[i], m);
+        if (l >= m) x[i] += u;
       }
     }
     if (l == 63) {
-      s_tot[w][0] = i4;
-      s_tot[w][1] = i8;
+#pragma unroll
+      for (int i = 0; i < NWD; ++i) s_tot[w][i] = x[i];
     }
     __syncthreads();
-    int o4 = s_carry[0] + i4 - c4, o8 = s_carry[1] + i8 - c8;
-    for (int j = 0; j < w; ++j) {
-      o4 += s_tot[j][0];
-      o8 += s_tot[j][1];
+    int o[NWD];
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) {
+      o[i] = s_carry[i] + x[i] - c[i];
+      for (int j = 0; j < w; ++j) o[i] += s_tot[j][i];
     }
     __syncthreads();
     if (b < nblk) {
-      cnt[2 * b] = o4;
-      cnt[2 * b + 1] = o8;
+#pragma unroll
+      for (int i = 0; i < NWD; ++i) cnt[NWD * b + i] = o[i];
     }
     if (tid == kCompactThreads - 1) {
-      s_carry[0] = o4 + c4;
-      s_carry[1] = o8 + c8;
+#pragma unroll
+      for (int i = 0; i < NWD; ++i) s_carry[i] = o[i] + c[i];
     }
     __syncthreads();
   }
-  if (tid == 0) {
-    a.ws_cnt[2 * seq] = s_carry[0];
-    a.ws_cnt[2 * seq + 1] = s_carry[1];
-  }
+  if (tid < NWD) a.ws_cnt[NWD * seq + tid] = s_carry[tid];
   // entries of each block at its offsets: lane k of a block starts after the live rows of lanes 0 .. k-1
-  uint32_t* l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
-  uint32_t* l8 = l4 + a.list_cap;
+  uint32_t* lists = a.ws_list + (size_t)seq * NWD * a.list_cap;
   for (int bb = 8 * w; bb < nblk; bb += 8 * NW) {
-    const RowBits r = row_bits(g, a, seq, bb, nblk, len, l);
-    const int c4 = __popc(r.w4), c8 = __popc(r.w8);
-    int i4 = c4, i8 = c8;  // inclusive scan over the block's 8 lanes
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      const int u4 = __shfl_up(i4, m), u8 = __shfl_up(i8, m);
-      if ((l & 7) >= m) {
-        i4 += u4;
-        i8 += u8;
-      }
-    }
-    if (r.b < 0) continue;
-    int o4 = cnt[2 * r.b] + i4 - c4, o8 = cnt[2 * r.b + 1] + i8 - c8;
+    const RowBits<NWD> r = row_bits<NWD>(g, a, seq, bb, nblk, len, l);
     const uint32_t hi = ((uint32_t)r.phys << 8) | (uint32_t)(32 * (l & 7));
-    for (uint32_t m = r.w4; m; m &= m - 1u) l4[o4++] = hi | (uint32_t)(__ffs(m) - 1);
-    for (uint32_t m = r.w8; m; m &= m - 1u) l8[o8++] = hi | (uint32_t)(__ffs(m) - 1);
+#pragma unroll
+    for (int i = 0; i < NWD; ++i) {
+      const int c = __popc(r.m[i]);
+      int x = c;  // inclusive scan over the block's 8 lanes
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        const int u = __shfl_up(x, m);
+        if ((l & 7) >= m) x += u;
+      }
+      if (r.b < 0) continue;
+      int o = cnt[NWD * r.b + i] + x - c;
+      uint32_t* li = lists + (size_t)i * a.list_cap;
+      for (uint32_t m = r.m[i]; m; m &= m - 1u) li[o++] = hi | (uint32_t)(__ffs(m) - 1);
+    }
   }
 }
 
 // ------------------------------------------------------------------------------------- decode
-// Raw codes and parameters of one chunk for one lane. 4-bit chunks: tokens 16c + lj (c = 0..3), 16 bytes
-// each of K and V (channels 32 la .. 32 la + 31). 8-bit chunks: tokens 16c + lj (c = 0, 1), 32 bytes each
-// (k[2c], k[2c + 1]).
+// Raw codes and parameters of one chunk for one lane (channels 32 la .. 32 la + 31 of K and of V). 4-bit
+// chunks: tokens 16c + lj (c = 0..3), 16 bytes each of K and V. 8-bit chunks: tokens 16c + lj (c = 0, 1),
+// 32 bytes each (k[2c], k[2c + 1]). 2-bit chunks: tokens 16c + lj (c = 0..3), 8 bytes each (k[c].x, .y).
+// FP16 chunks: token lj, 64 bytes each (k[0..3]).
 struct Raw {
   u32x4 k[4];
   u32x4 v[4];
@@ -195,10 +220,25 @@ struct Raw {
   uint32_t valid;  // bit c: token 16c + lj of the chunk exists
 };
 
-template <int G, bool GATHER>
+// Chunk kinds, in the order of the row lists: 4-bit chunks of 64 rows, 8-bit chunks of 32 rows, and in
+// pools of four widths 2-bit chunks of 64 rows and FP16 chunks of 16 rows.
+constexpr int kK4 = 0, kK8 = 1, kK2 = 2, kK16 = 3;
+template <int K>
+using Kind = std::integral_constant<int, K>;
+
+// 16 two-bit codes (8 in each 16-bit half) -> the same codes as nibbles, in order (8 per word).
+__device__ __forceinline__ uint32_t spread2(uint32_t w, uint32_t sel) {
+  uint32_t x = __builtin_amdgcn_perm(0u, w, sel);  // the half's two bytes at bytes 0 and 2
+  x = ((x << 4) | x) & 0x0F0F0F0Fu;
+  return ((x << 2) | x) & 0x33333333u;
+}
+
+template <int G, bool GATHER, bool MIX2>
 __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a) {
   static_assert(G == 1 || G == 2 || G == 4, "GQA ratio 1, 2 or 4");
+  static_assert(GATHER || !MIX2, "pools of four widths are read through the row lists");
   constexpr int D = kD;
+  constexpr int NWD = MIX2 ? 4 : 2;  // row lists per sequence
   __shared__ float s_q[G][D];
   __shared__ float s_qsum[G][2];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][64 * kVP];   // staged V rows, per wave
@@ -229,7 +269,13 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     const int i = min(tid + 256 * k, G * D - 1);  // unconditional loads: no branch waits for them
     qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D];
   }
-  int b0 = 0, ntbl = 0, nchunk = 0, n4 = 0, n8 = 0, nc4 = 0, c0 = 0;
+  // rows per chunk of each kind, and the kind of chunk ci (wave-uniform)
+  auto chunk_rows = [](int kind) __attribute__((always_inline)) {
+    return kind == kK8 ? 32 : kind == kK16 ? 16 : 64;
+  };
+  int b0 = 0, ntbl = 0, nchunk = 0, c0 = 0;
+  int nrow[NWD] = {};     // gather: live rows per list
+  int cend[NWD] = {};     // gather: end of each kind's chunks in the chunk order
   int tb0 = 0, tb1 = 0;
   if (!GATHER) {
     int b1;
@@ -239,20 +285,25 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     tb0 = bt[min(tid, ntbl - 1)];
     if (ntbl > 256) tb1 = bt[min(tid + 256, ntbl - 1)];
   }
+  auto kind_of = [&](int ci) __attribute__((always_inline)) {
+    if (!MIX2) return ci >= cend[0] ? kK8 : kK4;
+    return ci < cend[0] ? kK4 : ci < cend[1] ? kK8 : ci < cend[2] ? kK2 : kK16;
+  };
   bool wg_empty;
-  const uint32_t* l4 = nullptr;
-  const uint32_t* l8 = nullptr;
+  const uint32_t* lists = nullptr;
   if (GATHER) {
-    n4 = a.ws_cnt[2 * seq];
-    n8 = a.ws_cnt[2 * seq + 1];
-    nc4 = (n4 + 63) / 64;
-    const int nc = nc4 + (n8 + 31) / 32;
+    int nc = 0;
+#pragma unroll
+    for (int k = 0; k < NWD; ++k) {
+      nrow[k] = a.ws_cnt[NWD * seq + k];
+      nc += (nrow[k] + chunk_rows(k) - 1) / chunk_rows(k);
+      cend[k] = nc;
+    }
     c0 = (int)(((long)split * nc) / ns);
     const int c1 = (int)(((long)(split + 1) * nc) / ns);
     nchunk = c1 - c0 > w ? (c1 - c0 - w + 3) / 4 : 0;
     wg_empty = c1 <= c0;
-    l4 = a.ws_list + (size_t)seq * 2 * a.list_cap;
-    l8 = l4 + a.list_cap;
+    lists = a.ws_list + (size_t)seq * NWD * a.list_cap;
   } else {
     nchunk = min(b0 + ntbl, (len + kRows - 1) / kRows) - b0;
     wg_empty = nchunk <= 0;
@@ -293,15 +344,22 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   auto fetch = [&](Ent& en, int i) __attribute__((always_inline)) {
     if (GATHER) {
       const int ci = c0 + w + 4 * i;
-      const bool w8 = ci >= nc4;
-      const uint32_t* lst = w8 ? l8 : l4;
-      const int n = w8 ? n8 : n4;
-      const int e0 = w8 ? (ci - nc4) * 32 : ci * 64;
+      const int kind = kind_of(ci);
+      const uint32_t* lst = lists + (size_t)kind * a.list_cap;
+      const int rpc = chunk_rows(kind);
+      // register selects rather than indexing the arrays with a run-time kind
+      int start = 0, n = nrow[0];
+#pragma unroll
+      for (int k = 1; k < NWD; ++k) {
+        start = kind == k ? cend[k - 1] : start;
+        n = kind == k ? nrow[k] : n;
+      }
+      const int e0 = (ci - start) * rpc;
       uint32_t valid = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         int idx = e0 + 16 * c + lj;
-        const bool ok = idx < n && (c < 2 || !w8);
+        const bool ok = idx < n && 16 * c < rpc;
         valid |= ok ? (1u << c) : 0u;
         en.e[c] = lst[ok ? idx : e0];  // the chunk's first row always exists
       }
@@ -317,9 +375,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   auto load = [&](Raw& r, const Ent& en, int i) __attribute__((always_inline)) {
     const uint8_t* tile[4];
     uint32_t row[4];
-    bool w8 = false;
+    int kind = kK4;
     if (GATHER) {
-      w8 = (c0 + w + 4 * i) >= nc4;
+      kind = kind_of(c0 + w + 4 * i);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         tile[c] = pool_h + (size_t)(en.e[c] >> 8) * tstride;
@@ -337,12 +395,28 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
     }
     r.valid = en.valid;
-    if (!w8) {
+    if (kind == kK4) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint8_t* rp = tile[c] + (row[c] * R + la * 16);
         r.k[c] = *reinterpret_cast<const u32x4*>(rp);
         r.v[c] = *reinterpret_cast<const u32x4*>(rp + kD / 2);  // V codes follow the row's 4-bit K codes
+      }
+    } else if (MIX2 && kind == kK2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint8_t* rp = tile[c] + (row[c] * R + la * 8);
+        const uint2 kk = *reinterpret_cast<const uint2*>(rp);
+        const uint2 vv = *reinterpret_cast<const uint2*>(rp + kD / 4);  // V codes follow the 2-bit K codes
+        r.k[c] = u32x4{kk.x, kk.y, 0u, 0u};
+        r.v[c] = u32x4{vv.x, vv.y, 0u, 0u};
+      }
+    } else if (MIX2 && kind == kK16) {
+      const uint8_t* rp = tile[0] + (row[0] * R + la * 64);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        r.k[c] = *reinterpret_cast<const u32x4*>(rp + 16 * c);
+        r.v[c] = *reinterpret_cast<const u32x4*>(rp + 2 * kD + 16 * c);  // V values follow the K values
       }
     } else {
 #pragma unroll
@@ -411,10 +485,14 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   lds_barrier();
 
   // QK A operand for k-step s: row lj = 4 hq + 2 gam + part; lane group la supplies channels
-  // 32 la + 8 s + nib(e), e = 0..7, nib = 0,4,1,5,2,6,3,7 (the unpacking order of both widths); 4-bit
-  // chunks see the odd-position nibbles multiplied by 16, so their query entries are divided by 16.
+  // 32 la + ch(s, e), e = 0..7 = 2 p + k, in the unpacking order of the chunk's width:
+  // * 4- and 8-bit: ch = 8 s + p + 4 k (nibbles 0,4,1,5,2,6,3,7); 4-bit chunks see the odd-p nibbles
+  //   multiplied by 16, so their query entries are divided by 16;
+  // * 2-bit: ch = 16 (s >> 1) + 4 (s & 1) + p + 8 k, the code field p of each 16-bit half, seen multiplied
+  //   by 4^p, so the query entry is divided by 4^p;
+  // * FP16: ch = 8 s + e, the values as stored.
   u32x4 qa[4];
-  auto build_qa = [&](bool w8) __attribute__((always_inline)) {
+  auto build_qa = [&](int kind) __attribute__((always_inline)) {
     const int hq = lj >> 2, gam = (lj >> 1) & 1, part = lj & 1;
     const bool in_group = hq < G && (la >> 1) == gam;
 #pragma unroll
@@ -424,10 +502,15 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         _Float16 x[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-          const int e = 2 * p + k;
-          const int nib = (e >> 1) + 4 * (e & 1);
-          const float f = (!w8 && (e & 2)) ? 0.0625f : 1.0f;
-          const float v = in_group ? s_q[hq][32 * la + 8 * s + nib] * f : 0.0f;
+          int ch = 8 * s + p + 4 * k;
+          float f = (kind == kK4 && (p & 1)) ? 0.0625f : 1.0f;
+          if (MIX2 && kind == kK2) {
+            ch = 16 * (s >> 1) + 4 * (s & 1) + p + 8 * k;
+            f = p == 0 ? 1.0f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
+          } else if (MIX2 && kind == kK16) {
+            ch = 8 * s + 2 * p + k;
+          }
+          const float v = in_group ? s_q[hq][32 * la + ch] * f : 0.0f;
           const _Float16 hi = (_Float16)v;
           x[k] = part ? (_Float16)(v - (float)hi) : hi;
         }
@@ -435,8 +518,8 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
     }
   };
-  build_qa(false);
-  bool cur8 = false;
+  build_qa(kK4);
+  int cur_kind = kK4;
   const bool head_ok = la < G;
   const float qs0 = head_ok ? s_qsum[la][0] : 0.0f, qs1 = head_ok ? s_qsum[la][1] : 0.0f;
 
@@ -448,19 +531,31 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   uint8_t* sv = s_v[w];
   _Float16* sp = s_p[w];
 
-  auto process = [&](const Raw& r, auto w8c) __attribute__((always_inline)) {
-    constexpr bool W8 = decltype(w8c)::value;
-    constexpr int NC = W8 ? 2 : 4;  // 16-token slices
+  auto process = [&](const Raw& r, auto kc) __attribute__((always_inline)) {
+    constexpr int KIND = decltype(kc)::value;
+    constexpr bool W8 = KIND == kK8, F16 = KIND == kK16;
+    constexpr int NC = W8 ? 2 : F16 ? 1 : 4;  // 16-token slices
     // ---------------------------------------------------------- stage V rows (lane = token) in LDS
-    if (!W8) {
+    // (2-bit codes widened to nibbles, so the value pass of 2-bit chunks is the 4-bit one)
+    if constexpr (KIND == kK4) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP + la * 16) = r.v[c];
-    } else {
+    } else if constexpr (KIND == kK2) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 nib = {spread2(r.v[c][0], 0x0C010C00u), spread2(r.v[c][0], 0x0C030C02u),
+                           spread2(r.v[c][1], 0x0C010C00u), spread2(r.v[c][1], 0x0C030C02u)};
+        *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP + la * 16) = nib;
+      }
+    } else if constexpr (W8) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP8 + la * 32) = r.v[2 * c];
         *reinterpret_cast<u32x4*>(sv + (16 * c + lj) * kVP8 + la * 32 + 16) = r.v[2 * c + 1];
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(sv + lj * kVP16 + la * 64 + 16 * c) = r.v[c];
     }
     // ---------------------------------------------------------- logits: QK on the matrix cores
     floatx4 acc[NC];
@@ -471,13 +566,19 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         u32x4 b;
-        if (!W8) {
+        if constexpr (KIND == kK4) {
           const uint32_t wd = r.k[c][s], w8 = wd >> 8;
           b = u32x4{wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
-        } else {
+        } else if constexpr (KIND == kK2) {
+          // field p of each 16-bit half as an fp16 subnormal (code * 4^p) * 2^-24
+          const uint32_t wd = r.k[c][s >> 1] >> (8 * (s & 1));
+          b = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
+        } else if constexpr (W8) {
           const uint32_t lo = r.k[2 * c + (s >> 1)][2 * (s & 1)], hi = r.k[2 * c + (s >> 1)][2 * (s & 1) + 1];
           b = u32x4{__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
                     __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
+        } else {
+          b = r.k[s];  // fp16 values as stored
         }
         acc[c] = mfma16(qa[s], b, acc[c]);
       }
@@ -485,10 +586,14 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const bool live = head_ok && ((r.valid >> c) & 1u);
-      const float dot = h2f(r.kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
-                        h2f(r.kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
-      const float zq = h2f(r.kp[c][0] >> 16) * qs0 + h2f(r.kp[c][1] >> 16) * qs1;
-      sc[c] = live ? dot * kTwo24 + zq : kNegInf;
+      if constexpr (F16) {
+        sc[c] = live ? (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]) : kNegInf;
+      } else {
+        const float dot = h2f(r.kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
+                          h2f(r.kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
+        const float zq = h2f(r.kp[c][0] >> 16) * qs0 + h2f(r.kp[c][1] >> 16) * qs1;
+        sc[c] = live ? dot * kTwo24 + zq : kNegInf;
+      }
     }
     // ---------------------------------------------------------- online softmax (head la, 16-lane rows)
     float mx = sc[0];
@@ -514,39 +619,52 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     }
     // ---------------------------------------------------------- p * v_scale (hi, lo) to LDS
     // Position of token t: (t & ~7) | sinv(t & 7), sinv(u) = 2 (u & 3) + (u >> 2), the inverse of the
-    // token order 0,4,1,5,2,6,3,7 of the V operand; odd tokens of 4-bit chunks are divided by 16. The
-    // chunk's operands carry the wave-uniform scale of chunk_pv_scale (undone when the chunk is added).
+    // token order 0,4,1,5,2,6,3,7 of the V operand; odd tokens of 4-bit (and widened 2-bit) chunks are
+    // divided by 16. The chunk's operands carry the wave-uniform scale of chunk_pv_scale (undone when the
+    // chunk is added).
     // Odd tokens (u odd) enter the MFMA as -p * v_scale times the complemented code (L - code, L = 15 or
     // 255) and add p * (v_zero + L * v_scale) to the zero-point term, which is the same value: the
     // products then carry both signs, so the matrix core's rounding of long all-positive sums does not
     // bias the code term (which cancels against the zero-point term down to the much smaller output).
-    float vmax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      vmax = fmaxf(vmax, fmaxf(h2f(r.vp[c][0] & 0xffffu), h2f(r.vp[c][1] & 0xffffu)));
+    // FP16 chunks: token t at position t, the weight p itself (scale 2^14) in the rows of both V groups.
     float pv_inv;
-    const float pv_scale = chunk_pv_scale(vmax, pv_inv);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int t = 16 * c + lj, u = lj & 7;
-      const int pos = (t & ~7) | (((u & 3) << 1) | (u >> 2));
-      const float pp = p[c];
-      const bool on = pp != 0.0f;
-      const bool odd = u & 1;
-      const float f = odd ? (W8 ? -pv_scale : -0.0625f * pv_scale) : pv_scale;
-      const float Lc = odd ? (W8 ? 255.0f : 15.0f) : 0.0f;
-      const float vs0 = on ? h2f(r.vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(r.vp[c][0] >> 16) : 0.0f;
-      const float vs1 = on ? h2f(r.vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(r.vp[c][1] >> 16) : 0.0f;
-      zacc0 += pp * (vz0 + Lc * vs0);
-      zacc1 += pp * (vz1 + Lc * vs1);
-      const float pv0 = (pp * f) * vs0, pv1 = (pp * f) * vs1;
-      const _Float16 h0 = (_Float16)pv0, h1 = (_Float16)pv1;
-      const _Float16 e0 = (_Float16)(pv0 - (float)h0), e1 = (_Float16)(pv1 - (float)h1);
+    if constexpr (F16) {
+      pv_inv = 1.0f / (16384.0f * kTwo24);  // the values are not codes * 2^-24: undo that factor too
+      const float pv = p[0] * 16384.0f;
+      const _Float16 h0 = (_Float16)pv;
+      const _Float16 e0 = (_Float16)(pv - (float)h0);
       if (head_ok) {
-        uint2 wv;
-        wv.x = pack_h2(h0, e0);
-        wv.y = pack_h2(h1, e1);
-        *reinterpret_cast<uint2*>(sp + pos * kPP + la * 4) = wv;
+        const uint32_t x = pack_h2(h0, e0);
+        *reinterpret_cast<uint2*>(sp + lj * kPP + la * 4) = uint2{x, x};
+      }
+    } else {
+      float vmax = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        vmax = fmaxf(vmax, fmaxf(h2f(r.vp[c][0] & 0xffffu), h2f(r.vp[c][1] & 0xffffu)));
+      const float pv_scale = chunk_pv_scale(vmax, pv_inv);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int t = 16 * c + lj, u = lj & 7;
+        const int pos = (t & ~7) | (((u & 3) << 1) | (u >> 2));
+        const float pp = p[c];
+        const bool on = pp != 0.0f;
+        const bool odd = u & 1;
+        const float f = odd ? (W8 ? -pv_scale : -0.0625f * pv_scale) : pv_scale;
+        const float Lc = odd ? (W8 ? 255.0f : 15.0f) : 0.0f;
+        const float vs0 = on ? h2f(r.vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(r.vp[c][0] >> 16) : 0.0f;
+        const float vs1 = on ? h2f(r.vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(r.vp[c][1] >> 16) : 0.0f;
+        zacc0 += pp * (vz0 + Lc * vs0);
+        zacc1 += pp * (vz1 + Lc * vs1);
+        const float pv0 = (pp * f) * vs0, pv1 = (pp * f) * vs1;
+        const _Float16 h0 = (_Float16)pv0, h1 = (_Float16)pv1;
+        const _Float16 e0 = (_Float16)(pv0 - (float)h0), e1 = (_Float16)(pv1 - (float)h1);
+        if (head_ok) {
+          uint2 wv;
+          wv.x = pack_h2(h0, e0);
+          wv.y = pack_h2(h1, e1);
+          *reinterpret_cast<uint2*>(sp + pos * kPP + la * 4) = wv;
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -559,7 +677,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     floatx4 ob[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ob[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    constexpr int NKB = W8 ? 1 : 2;  // 32-token k-blocks
+    constexpr int NKB = W8 || F16 ? 1 : 2;  // 32-token k-blocks
     u32x4 pa[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -568,7 +686,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       const v2i x1 = lds_tr16(sp + (base + 4) * kPP + (lj & 3) * 4);
       pa[kb] = u32x4{(uint32_t)x0.x, (uint32_t)x0.y, (uint32_t)x1.x, (uint32_t)x1.y};
     }
-    if (!W8) {
+    if constexpr (!W8 && !F16) {
       const int tok = lj < 8 ? 8 * la + lj : 32 + 8 * la + (lj - 8);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -581,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
           ob[t] = mfma16(pa[kb], b, ob[t]);
         }
       }
-    } else {
+    } else if constexpr (W8) {
       const int tok = 8 * la + (lj >> 1);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -594,6 +712,20 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
                          __builtin_amdgcn_perm(hi, lo, pair_sel(3)) ^ 0x00FF00FFu};
         ob[t] = mfma16(pa[0], b, ob[t]);
       }
+    } else {
+      // B: V values of tokens 8 la + e at channel 16 t + lj (16-bit transpose read of the token-major rows).
+      // The chunk has 16 tokens: lanes with la >= 2 (tokens 16..31) read rows of la - 2 and contribute zero.
+      const bool hi_half = la >= 2;
+      if (hi_half) pa[0] = u32x4{0u, 0u, 0u, 0u};
+      const int row = 8 * (la & 1) + (lj >> 2);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const v2i x0 = lds_tr16(sv + row * kVP16 + 2 * (16 * t + 4 * (lj & 3)));
+        const v2i x1 = lds_tr16(sv + (row + 4) * kVP16 + 2 * (16 * t + 4 * (lj & 3)));
+        u32x4 b = {(uint32_t)x0.x, (uint32_t)x0.y, (uint32_t)x1.x, (uint32_t)x1.y};
+        if (hi_half) b = u32x4{0u, 0u, 0u, 0u};
+        ob[t] = mfma16(pa[0], b, ob[t]);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] += ob[t] * pv_inv;
@@ -601,17 +733,27 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   };
   auto run = [&](const Raw& r, int i) __attribute__((always_inline)) {
     if (GATHER) {
-      const bool w8 = (c0 + w + 4 * i) >= nc4;
-      if (w8 != cur8) {
-        build_qa(w8);
-        cur8 = w8;
+      const int kind = kind_of(c0 + w + 4 * i);
+      if (kind != cur_kind) {
+        build_qa(kind);
+        cur_kind = kind;
       }
-      if (w8) {
-        process(r, std::true_type{});
+      if (kind == kK8) {
+        process(r, Kind<kK8>{});
         return;
       }
+      if constexpr (MIX2) {
+        if (kind == kK2) {
+          process(r, Kind<kK2>{});
+          return;
+        }
+        if (kind == kK16) {
+          process(r, Kind<kK16>{});
+          return;
+        }
+      }
     }
-    process(r, std::false_type{});
+    process(r, Kind<kK4>{});
   };
 
   // sched_barrier keeps a chunk's loads (and the list entries of the one after) ahead of the arithmetic
@@ -719,21 +861,24 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 template <int G>
 hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.plan.wgs);
-  if (a.mask || g.mixed) {
-    hipLaunchKernelGGL(compact_rows_k, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
-    hipLaunchKernelGGL((decode_rows_k<G, true>), grid, dim3(256), 0, stream, g, a);
+  if (g.mixed == 2) {
+    hipLaunchKernelGGL(compact_rows_k<4>, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, true, true>), grid, dim3(256), 0, stream, g, a);
+  } else if (a.mask || g.mixed) {
+    hipLaunchKernelGGL(compact_rows_k<2>, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, true, false>), grid, dim3(256), 0, stream, g, a);
   } else {
-    hipLaunchKernelGGL((decode_rows_k<G, false>), grid, dim3(256), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, false, false>), grid, dim3(256), 0, stream, g, a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Layouts with this kernel: head_dim 128, per-token K and V groups of 64, 4-bit pools or pools of 4- and
-// 8-bit rows, G = 1, 2, 4.
+// Layouts with this kernel: head_dim 128, per-token K and V groups of 64, 4-bit pools and pools of per-token
+// widths, G = 1, 2, 4.
 bool decode_rows_supported(const TileGeom& g, int G) {
-  return g.d == 128 && g.kg == 64 && g.vg == 64 && g.mixed <= 1 && (G == 1 || G == 2 || G == 4);
+  return g.d == 128 && g.kg == 64 && g.vg == 64 && !g.fp8 && (G == 1 || G == 2 || G == 4);
 }
 
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {

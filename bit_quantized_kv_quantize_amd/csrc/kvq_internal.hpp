@@ -139,10 +139,11 @@ struct DecodeArgs {
   unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernel); zero between calls
   float* ws_ml;   // [n_seqs][H_q][plan.stride] x {m, l} (the generic kernel: [plan.n_splits])
   float* ws_acc;  // [n_seqs][H_q][plan.stride][d]
-  int* ws_cnt;       // [n_seqs][2] live 4-bit / 8-bit rows (row-list kernel)
-  uint32_t* ws_list; // [n_seqs][2][list_cap] live rows as (physical block << 8 | row)
+  int* ws_cnt;       // [n_seqs][W] live rows per width list (row-list kernel; W = 2: 4-bit, 8-bit; W = 4
+                     // in pools of four widths: 4-bit, 8-bit, 2-bit, FP16)
+  uint32_t* ws_list; // [n_seqs][W][list_cap] live rows as (physical block << 8 | row)
   int list_cap;
-  int* ws_bcnt;      // [n_seqs][bcnt_blocks][2] live 4-bit / 8-bit rows of each logical block
+  int* ws_bcnt;      // [n_seqs][bcnt_blocks][W] live rows per width list of each logical block
   int bcnt_blocks;
   int* ws_cflag;     // [plan.max_blocks] 1 where the cascade kernel took the logical block for every sequence
   int casc;          // cascade partial slots merged by the per-sequence kernel in this call (0 or plan.casc)

@@ -100,6 +100,15 @@ def widths_variant(cfg: Config, fracs: Tuple[float, float, float] = (0.05, 0.15,
     return dataclasses.replace(cfg, name=cfg.name + "_widths", mixed=2, top_fraction=0.0, width_fracs=fracs)
 
 
+def named_config(name: str) -> Config:
+    """A workload by name; the suffixes _fp8 and _widths name its FP8 and per-token-width variants."""
+    if name.endswith("_fp8"):
+        return fp8_variant(CONFIGS[name[:-len("_fp8")]])
+    if name.endswith("_widths"):
+        return widths_variant(CONFIGS[name[:-len("_widths")]])
+    return CONFIGS[name]
+
+
 def _rng(cfg: Config, layer: int, stream: int, index: int = 0) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.index, layer, stream, index])))
 
@@ -318,7 +327,7 @@ def width_words(codes_rows: np.ndarray) -> np.ndarray:
     return w.astype(np.uint32)
 
 
-def _block_words(cfg: Config, ns: np.ndarray, nb: int) -> np.ndarray:
+def block_width_words(cfg: Config, ns: np.ndarray, nb: int) -> np.ndarray:
     """Width words of one sequence's nb blocks from the K norms of its ns.size cached tokens; slots past
     the cached tokens get the 4-bit code (mixed = 2) or a clear bit."""
     n = ns.size
@@ -331,7 +340,7 @@ def _block_words(cfg: Config, ns: np.ndarray, nb: int) -> np.ndarray:
     return bits_words(sel)
 
 
-def _append_prec(cfg: Config, ns: np.ndarray, norm_sq_new: float) -> int:
+def append_prec(cfg: Config, ns: np.ndarray, norm_sq_new: float) -> int:
     if cfg.mixed == 2:
         return appended_width(ns, norm_sq_new, cfg.width_fracs)
     return 8 if appended_is_8bit(ns, norm_sq_new, cfg.top_fraction) else 4
@@ -403,9 +412,9 @@ def prefill_chunks(case: Case, layer: int, max_blocks: int = 2048, threads: int 
             nb = sequence_blocks(case, s).size
             n = int(case.context[s])
             ns = norms[off * BLOCK: off * BLOCK + n]
-            bitmaps[off: off + nb] = _block_words(cfg, ns, nb)
+            bitmaps[off: off + nb] = block_width_words(cfg, ns, nb)
             if ak is not None and nb:
-                prec_out[s] = _append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
+                prec_out[s] = append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
             off += nb
         yield ids, k, v, bitmaps
 
@@ -425,9 +434,9 @@ def mixed_precision_inputs(case: Case, layer: int, threads: int = 8):
         k, _ = blocks_kv(cfg, layer, blocks, threads)
         n = int(case.context[s])
         ns = k_norms_sq(k[:n])
-        words = _block_words(cfg, ns, blocks.size)
+        words = block_width_words(cfg, ns, blocks.size)
         for i, b in enumerate(blocks):
             bitmaps[pos[int(b)]] = words[i]
         if case.append and blocks.size:
-            prec[s] = _append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
+            prec[s] = append_prec(cfg, ns, float(k_norms_sq(ak[s:s + 1])[0]))
     return bitmaps, prec

@@ -92,12 +92,10 @@ def oracle_sample(orc, case, layer, seqs):
             k, _ = W.blocks_kv(cfg, layer, blocks, threads=16)
             n = int(case.context[s])
             ns = W.k_norms_sq(k[:n])
-            sel = np.zeros(blocks.size * W.BLOCK, bool)
-            sel[:n] = W.precision_map(ns, cfg.top_fraction)
-            for i, words in enumerate(W.bits_words(sel)):
+            for i, words in enumerate(W.block_width_words(cfg, ns, blocks.size)):
                 bm[int(blocks[i])] = words
-            if case.append and W.appended_is_8bit(ns, float(W.k_norms_sq(ak[r:r + 1])[0]), cfg.top_fraction):
-                prec[r] = 8
+            if case.append and blocks.size:
+                prec[r] = W.append_prec(cfg, ns, float(W.k_norms_sq(ak[r:r + 1])[0]))
         bitmaps = np.stack([bm[int(b)] for b in prefill])
     k, v = W.blocks_kv(cfg, layer, prefill, threads=16)
     orc.quantize_blocks(lay, pool, np.array([compact[int(b)] for b in prefill], np.int32), k, v, bitmaps)
@@ -110,14 +108,15 @@ def oracle_sample(orc, case, layer, seqs):
     return ids, pool.reshape(ids.size, -1), out
 
 
-@pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8"])
+@pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8", "llama31_8b_pool_8k_widths",
+                                                   "mixed_sentinel_32k_widths"])
 def test_full_size_sampled(env, orc, name):
-    # (the last case: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against)
+    # (the last cases: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against,
+    # and two workloads stored with per-token widths {2, 4, 8, FP16})
     kvq, torch = env
-    fp8 = name.endswith("_fp8")
-    base = name[:-4] if fp8 else name
+    base = name.replace("_fp8", "").replace("_widths", "")
     layers, seqs = FULL[base]
-    case = W.make_case(W.fp8_variant(W.CONFIGS[base]) if fp8 else W.CONFIGS[base])
+    case = W.make_case(W.named_config(name))
     for layer in layers:
         print("[fullsize] %s layer %d: %d seqs, %d blocks" % (name, layer, case.n_seqs, case.num_blocks), flush=True)
         _, pool, out = build_on_gpu(kvq, torch, case, layer)

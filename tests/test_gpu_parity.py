@@ -74,7 +74,7 @@ def test_decode_within_tolerance(env, orc, name, decode_path):
     (1, 0, 64, 64, 8, 128), (0, 0, 64, 64, 2, 128), (1, 0, 64, 64, 4, 256), (0, 0, 64, 64, 1, 256),
     (1, 0, -1, 32, 5, 128), (0, 0, -1, 64, 8, 128), (1, 0, -1, 32, 3, 128), (0, 0, -1, 32, 1, 128),
     (0, 1, 64, 64, 4, 128), (1, 1, 64, 64, 2, 128), (0, 2, 64, 64, 4, 128), (1, 2, 32, 64, 2, 64),
-    (1, 2, 64, 32, 8, 256), (0, 2, 16, 128, 1, 128)])
+    (1, 2, 64, 32, 8, 256), (0, 2, 16, 128, 1, 128), (1, 2, 64, 64, 2, 128), (0, 2, 64, 64, 1, 128)])
 def test_layout_variants(env, orc, rotate, mixed, kg, vg, G, d, decode_path):
     # Generic layouts beyond the five workloads: group sizes, widths, rotation, G up to 16, ragged
     # lengths (0, 1, 255, 256, 257, long) and sentinel masks (one sequence entirely sentinel).
@@ -370,3 +370,21 @@ def test_widths_append_rewrites_record_at_another_width(env, orc):
         got = pool.cpu().numpy()
         diff = np.nonzero(got != ref)[0]
         assert diff.size == 0, (rotate, diff[:16])
+
+
+@pytest.mark.parametrize("mixed", [1, 2])
+def test_row_lists_of_a_sequence_past_256k_slots(env, orc, mixed):
+    # One sequence of 270,000 slots (1055 blocks, more than the compaction kernel's 1024 threads scan in one
+    # pass) with sentinel slots and per-token widths: row lists of 100K+ entries per width.
+    kvq, torch = env
+    cfg = W.Config(9, "long", 128, 4, 1, 1, 64, 64, 1, mixed, 1, 270000, "perm", True, 3, 10.0, 1.0,
+                   dead_fraction=0.4, top_fraction=0.2 if mixed == 1 else 0.0,
+                   width_fracs=(0.05, 0.15, 0.3) if mixed == 2 else (0.0, 0.0, 0.0))
+    case = W.make_case(cfg)
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp, n_threads=8)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    assert np.array_equal(got_pool, ref_pool)
+    err = rel_err(got, ref)
+    print("long sequence mixed=%d: max rel err %.3g" % (mixed, err))
+    assert err <= TOL
