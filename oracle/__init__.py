@@ -25,16 +25,22 @@ ORC_ERR_UNSUPPORTED = -2
 
 class OrcLayout(ctypes.Structure):
     """Same field order as the library's layout struct (head_dim, num_kv_heads, block_tokens, k_group,
-    v_group, rotate, mixed, format)."""
+    v_group, rotate, mixed, format, v_head_dim)."""
 
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed",
-                 "format")]
+                 "format", "v_head_dim")]
 
 
-def make_layout(head_dim, num_kv_heads, k_group, v_group, rotate=0, mixed=0, block_tokens=256, format=0):
+def make_layout(head_dim, num_kv_heads, k_group, v_group, rotate=0, mixed=0, block_tokens=256, format=0,
+                v_head_dim=0):
     return OrcLayout(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed),
-                     int(format))
+                     int(format), int(v_head_dim))
+
+
+def v_dim(layout: OrcLayout) -> int:
+    """V's head dim (the K head dim unless the layout gives another)."""
+    return layout.v_head_dim if layout.v_head_dim > 0 else layout.head_dim
 
 
 def build(force: bool = True) -> str:
@@ -149,7 +155,7 @@ def tile_bytes(layout: OrcLayout) -> int:
 
 def quantize_blocks(layout: OrcLayout, pool: np.ndarray, block_ids, k: np.ndarray, v: np.ndarray,
                     prec_bits: Optional[np.ndarray] = None) -> None:
-    """In-place on ``pool`` (uint8, host). k, v: uint16 fp16 bits [n_blocks*256][H_kv][d]."""
+    """In-place on ``pool`` (uint8, host). k, v: uint16 fp16 bits [n_blocks*256][H_kv][d] and [..][dv]."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     block_ids = _c(block_ids, np.int32)
     k = _c(k, np.uint16)
@@ -174,21 +180,20 @@ def append_tokens(layout: OrcLayout, pool: np.ndarray, k: np.ndarray, v: np.ndar
 
 def dequant_row(layout: OrcLayout, tile: np.ndarray, t: int):
     """Rotated-domain fp64 (k, v) of row t of one tile, plus the row's bit width."""
-    d = layout.head_dim
-    k = np.zeros(d, np.float64)
-    v = np.zeros(d, np.float64)
+    k = np.zeros(layout.head_dim, np.float64)
+    v = np.zeros(v_dim(layout), np.float64)
     tile = _c(tile, np.uint8)
     bits = lib().orc_dequant_row(ctypes.byref(layout), _p(tile), t, _p(k), _p(v))
     return k, v, int(bits)
 
 
 def dequantize_blocks(layout: OrcLayout, pool: np.ndarray, block_ids):
-    """fp16 bits (uint16) k, v [n_blocks * 256, H, d]: the listed blocks restored (and un-rotated), one
-    rounding from the exact fp64 values."""
+    """fp16 bits (uint16) k [n_blocks * 256, H, d], v [.., dv]: the listed blocks restored (and un-rotated),
+    one rounding from the exact fp64 values."""
     ids = _c(block_ids, np.int32)
     n, H, d = ids.size, layout.num_kv_heads, layout.head_dim
     k = np.zeros((n * 256, H, d), np.uint16)
-    v = np.zeros((n * 256, H, d), np.uint16)
+    v = np.zeros((n * 256, H, v_dim(layout)), np.uint16)
     pool = _c(pool, np.uint8)
     st = lib().orc_dequantize_blocks(ctypes.byref(layout), _p(pool), _p(ids), n, _p(k), _p(v))
     if st != 0:
@@ -199,7 +204,8 @@ def dequantize_blocks(layout: OrcLayout, pool: np.ndarray, block_ids):
 def decode_attention(layout: OrcLayout, pool: np.ndarray, q: np.ndarray, block_table, seq_lens,
                      sentinel_mask=None, softmax_scale: float = None, want_weights: bool = False,
                      n_threads: int = 0):
-    """fp64 attention output [n_seqs][H_q][d] (and optionally the softmax weights)."""
+    """fp64 attention output [n_seqs][H_q][dv] for queries [n_seqs][H_q][d] (and optionally the softmax
+    weights)."""
     q = _c(q, np.uint16)
     n_seqs, hq, d = q.shape
     bt = _c(block_table, np.int32)
@@ -209,7 +215,7 @@ def decode_attention(layout: OrcLayout, pool: np.ndarray, q: np.ndarray, block_t
     mask = None if sentinel_mask is None else _c(sentinel_mask, np.uint32)
     words = 0 if mask is None else mask.shape[1]
     max_len = int(max(1, sl.max() if sl.size else 1))
-    out = np.zeros((n_seqs, hq, d), np.float64)
+    out = np.zeros((n_seqs, hq, v_dim(layout)), np.float64)
     w = np.zeros((n_seqs, hq, max_len), np.float64) if want_weights else None
     st = lib().orc_decode_attention(ctypes.byref(layout), _p(pool), _p(q), n_seqs, hq, _p(bt), bt.shape[1],
                                     _p(sl), _p(mask), words, float(softmax_scale), _p(out), _p(w), max_len,

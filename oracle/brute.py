@@ -33,26 +33,28 @@ def e4m3_values() -> np.ndarray:
     return np.where(b & 0x80, -v, v)
 
 
-def _fp8_tile(tile: np.ndarray, d):
+def _fp8_tile(tile: np.ndarray, d, dv):
     rows = 256
-    rec = tile[: rows * 2 * d].reshape(rows, 2 * d)
+    rec = tile[: rows * (d + dv)].reshape(rows, d + dv)
     vals = e4m3_values()
     return vals[rec[:, :d]], vals[rec[:, d:]]
 
 
-def _layout_offsets(d, k_group, v_group, mixed):
-    """Byte geometry of a tile: row records (K codes then V codes of the row's width, 2 * slot bytes), the per-channel K
-    parameters (if K is grouped per channel), per-row parameter records (K groups then V groups), header."""
+def _layout_offsets(d, k_group, v_group, mixed, dv=None):
+    """Byte geometry of a tile (K head dim d, V head dim dv): row records (K codes then V codes of the row's
+    width, rec bytes = K and V at the pool's widest width), the per-channel K parameters (if K is grouped per
+    channel), per-row parameter records (K groups then V groups), header."""
+    dv = d if dv is None else dv
     rows = 256
-    slot = d * (16 if mixed == 2 else 8 if mixed else 4) // 8
-    off_par = rows * 2 * slot
+    rec = (d + dv) * (16 if mixed == 2 else 8 if mixed else 4) // 8
+    off_par = rows * rec
     kpr = d // k_group if k_group > 0 else 0
-    prow = (kpr + d // v_group) * 4
+    prow = (kpr + dv // v_group) * 4
     off_prow = off_par + (0 if k_group > 0 else d * 4)
     off_hdr = off_prow + rows * prow
     end = off_hdr + (64 if mixed == 2 else 32 if mixed else 0)
     tile = (end + 255) // 256 * 256
-    return slot, off_par, off_prow, prow, kpr, off_hdr, tile
+    return rec, off_par, off_prow, prow, kpr, off_hdr, tile
 
 
 def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
@@ -75,11 +77,12 @@ def _codes(rows_bytes: np.ndarray, d: int, bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
-    """-> (K [256][d], V [256][d]) fp64 in the stored (rotated) domain. fmt 1: FP8 E4M3 records."""
+def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0, dv=None):
+    """-> (K [256][d], V [256][dv]) fp64 in the stored (rotated) domain. fmt 1: FP8 E4M3 records."""
+    dv = d if dv is None else dv
     if fmt == 1:
-        return _fp8_tile(tile, d)
-    slot, off_par, off_prow, prow, kpr, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed)
+        return _fp8_tile(tile, d, dv)
+    recb, off_par, off_prow, prow, kpr, off_hdr, _ = _layout_offsets(d, k_group, v_group, mixed, dv)
     rows = 256
     t = np.arange(rows)
     if mixed == 2:
@@ -90,14 +93,14 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
         bits = np.where((hdr[t // 8] >> (t % 8)) & 1, 8, 4)
     else:
         bits = np.full(rows, 4)
-    rec = tile[: rows * 2 * slot].reshape(rows, 2 * slot)
-    kc = _codes(rec[:, :slot], d, np.where(bits == 16, 4, bits))
+    rec = tile[: rows * recb].reshape(rows, recb)
+    kc = _codes(rec[:, :d], d, np.where(bits == 16, 4, bits))
     # V codes follow the row's own K codes: d * bits / 8 bytes in
-    vc = np.zeros((rows, d), np.int64)
+    vc = np.zeros((rows, dv), np.int64)
     for b in (2, 4, 8):
         sel = bits == b
         if sel.any():
-            vc[sel] = _codes(rec[sel, d * b // 8: d * b // 8 + d], d, np.full(int(sel.sum()), b))
+            vc[sel] = _codes(rec[sel, d * b // 8: d * b // 8 + dv], dv, np.full(int(sel.sum()), b))
     par = tile[off_prow: off_prow + rows * prow].reshape(rows, prow)
     if k_group > 0:
         kp = par[:, : kpr * 4].copy().view(np.float16).reshape(rows, kpr, 2)
@@ -107,30 +110,33 @@ def dequant_tile(tile: np.ndarray, d, k_group, v_group, mixed, fmt=0):
         kp = tile[off_par: off_par + d * 4].view(np.float16).reshape(d, 2)
         ks = np.broadcast_to(kp[:, 0].astype(np.float64), (rows, d))
         kz = np.broadcast_to(kp[:, 1].astype(np.float64), (rows, d))
-    vp = par[:, kpr * 4:].copy().view(np.float16).reshape(rows, d // v_group, 2)
+    vp = par[:, kpr * 4:].copy().view(np.float16).reshape(rows, dv // v_group, 2)
     vs = np.repeat(vp[:, :, 0].astype(np.float64), v_group, axis=1)
     vz = np.repeat(vp[:, :, 1].astype(np.float64), v_group, axis=1)
     K, V = kc * ks + kz, vc * vs + vz
     f16 = bits == 16  # FP16 rows: raw values, K then V
     if f16.any():
         K[f16] = rec[f16, : 2 * d].copy().view(np.float16).astype(np.float64)
-        V[f16] = rec[f16, 2 * d: 4 * d].copy().view(np.float16).astype(np.float64)
+        V[f16] = rec[f16, 2 * d: 2 * d + 2 * dv].copy().view(np.float16).astype(np.float64)
     return K, V
 
 
 def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed, q_bits: np.ndarray,
-                     block_table, seq_lens, sentinel_mask=None, softmax_scale=None, fmt=0) -> np.ndarray:
-    """Dense fp64 attention of every query head over its sequence's dequantised cache."""
-    tile_bytes = _layout_offsets(d, k_group, v_group, mixed)[6] if fmt == 0 else (256 * 2 * d + 255) // 256 * 256
+                     block_table, seq_lens, sentinel_mask=None, softmax_scale=None, fmt=0, dv=None) -> np.ndarray:
+    """Dense fp64 attention of every query head over its sequence's dequantised cache (queries of K's head
+    dim d, outputs of V's head dim dv)."""
+    dv = d if dv is None else dv
+    tile_bytes = (_layout_offsets(d, k_group, v_group, mixed, dv)[6] if fmt == 0
+                  else (256 * (d + dv) + 255) // 256 * 256)
     q = q_bits.view(np.float16).astype(np.float64)
     n_seqs, hq, _ = q.shape
     g = hq // h_kv
     # the scale crosses the C ABI as fp32
     scale = float(np.float32(1.0 / np.sqrt(d) if softmax_scale is None else softmax_scale))
     if rotate:
-        c = float(np.float32(1.0 / np.sqrt(d)))
-        unrot = hadamard(d) / (d * c)
-    out = np.zeros((n_seqs, hq, d))
+        unrot_k = hadamard(d) / (d * float(np.float32(1.0 / np.sqrt(d))))
+        unrot_v = hadamard(dv) / (dv * float(np.float32(1.0 / np.sqrt(dv))))
+    out = np.zeros((n_seqs, hq, dv))
     for s in range(n_seqs):
         n = int(seq_lens[s])
         if n == 0:
@@ -142,17 +148,17 @@ def decode_attention(pool: np.ndarray, d, h_kv, k_group, v_group, rotate, mixed,
             sent = np.zeros(n, bool)
         for h in range(h_kv):
             K = np.zeros((n, d))
-            V = np.zeros((n, d))
+            V = np.zeros((n, dv))
             for lb in range((n + 255) // 256):
                 blk = int(block_table[s][lb])
                 base = (blk * h_kv + h) * tile_bytes
-                Kt, Vt = dequant_tile(pool[base: base + tile_bytes], d, k_group, v_group, mixed, fmt)
+                Kt, Vt = dequant_tile(pool[base: base + tile_bytes], d, k_group, v_group, mixed, fmt, dv)
                 m = min(256, n - lb * 256)
                 K[lb * 256: lb * 256 + m] = Kt[:m]
                 V[lb * 256: lb * 256 + m] = Vt[:m]
             if rotate:
-                K = K @ unrot.T
-                V = V @ unrot.T
+                K = K @ unrot_k.T
+                V = V @ unrot_v.T
             V[sent] = 0.0
             Q = q[s, h * g: (h + 1) * g]
             logits = scale * (Q @ K.T)

@@ -55,6 +55,7 @@ typedef struct orc_layout {
   int32_t rotate;
   int32_t mixed;
   int32_t format; /* 0: group-wise integer codes; 1: FP8 E4M3 per element */
+  int32_t v_head_dim; /* V's head dim when it differs from K's (MLA); 0 = head_dim */
 } orc_layout;
 
 /* ---------------------------------------------------------------- fp16 <-> fp32 (IEEE binary16) */
@@ -231,34 +232,38 @@ void orc_quantize_group(const float* x, int32_t n, int32_t stride, int32_t bits,
 
 static int is_pow2(int32_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-/* Which layouts the oracle can express: any head_dim that is a multiple of 8 (a power of two when
- * rotated), groups that are multiples of 8 dividing head_dim, 256-row blocks. */
+/* V's head dim: head_dim unless the layout gives another (MLA, [AMB] 2.2: K and V dims differ). */
+static int32_t vdim(const orc_layout* L) { return L->v_head_dim > 0 ? L->v_head_dim : L->head_dim; }
+
+/* Which layouts the oracle can express: K and V head dims that are multiples of 8 (powers of two when
+ * rotated), groups that are multiples of 8 dividing their tensor's head dim, 256-row blocks. */
 int orc_check_layout(const orc_layout* L) {
   if (!L) return ORC_ERR_ARG;
-  int32_t d = L->head_dim;
+  int32_t d = L->head_dim, dv = vdim(L);
   if (d <= 0 || d % 8 != 0 || d > 4096) return ORC_ERR_ARG;
+  if (L->v_head_dim < 0 || dv % 8 != 0 || dv > 4096) return ORC_ERR_ARG;
   if (L->num_kv_heads <= 0 || L->block_tokens != ORC_ROWS) return ORC_ERR_ARG;
   if (L->format == 1) { /* FP8: one byte per element, no groups, no per-token widths */
     if (L->k_group != 0 || L->v_group != 0 || L->mixed != 0) return ORC_ERR_ARG;
     if (L->rotate != 0 && L->rotate != 1) return ORC_ERR_ARG;
-    if (L->rotate && !is_pow2(d)) return ORC_ERR_UNSUPPORTED;
+    if (L->rotate && !(is_pow2(d) && is_pow2(dv))) return ORC_ERR_UNSUPPORTED;
     return ORC_OK;
   }
   if (L->format != 0) return ORC_ERR_ARG;
   if (!(L->k_group == -1 || (L->k_group > 0 && L->k_group % 8 == 0 && d % L->k_group == 0)))
     return ORC_ERR_ARG;
-  if (!(L->v_group > 0 && L->v_group % 8 == 0 && d % L->v_group == 0)) return ORC_ERR_ARG;
+  if (!(L->v_group > 0 && L->v_group % 8 == 0 && dv % L->v_group == 0)) return ORC_ERR_ARG;
   if (L->rotate != 0 && L->rotate != 1) return ORC_ERR_ARG;
   if (L->mixed < 0 || L->mixed > 2) return ORC_ERR_ARG;
-  if (L->rotate && !is_pow2(d)) return ORC_ERR_UNSUPPORTED;
+  if (L->rotate && !(is_pow2(d) && is_pow2(dv))) return ORC_ERR_UNSUPPORTED;
   if (L->mixed && L->k_group < 0) return ORC_ERR_UNSUPPORTED;
   return ORC_OK;
 }
 
-/* Tile layout (one block of 256 rows, one KV head):
- *   row records       256 x (2 * slot) bytes (slot = d/2, or d in mixed pools): record t at t * 2 * slot
- *                     holds the row's K codes (d * b / 8 bytes, b its width) immediately followed by its
- *                     V codes (d * b / 8 bytes); in mixed pools the rest of a 4-bit row's record is zero;
+/* Tile layout (one block of 256 rows, one KV head; d = K's head dim, dv = V's):
+ *   row records       256 x rec bytes (rec = (d + dv) * w / 8, w the widest width the pool allows):
+ *                     record t holds the row's K codes (d * b / 8 bytes, b its width) immediately followed
+ *                     by its V codes (dv * b / 8 bytes); the rest of a narrower row's record is zero;
  *   per-channel K     K grouped per channel: d x {fp16 scale, fp16 zero};
  *   parameter records 256 x prow bytes: record t holds K params [group] {scale, zero} (per-token K
  *                     groups only) then V params [group] {scale, zero};
@@ -266,23 +271,23 @@ int orc_check_layout(const orc_layout* L) {
  *   zero padding to a multiple of 256 bytes.
  * The pages fix only the content (codes and a 16-bit scale and bias per group); this arrangement keeps a
  * row's K and V codes in one record so a row is one contiguous read. */
-/* Bytes of one row's K (or V) slot: the widest width the pool allows (FP16 in pools with widths
+/* Bytes of one row record: K and V at the widest width the pool allows (FP16 in pools with widths
  * {2, 4, 8, FP16}, 8 bits in 4/8-bit pools and FP8 pools, else 4 bits). */
-static size_t row_slot_bytes(const orc_layout* L) {
+static size_t row_rec_bytes(const orc_layout* L) {
   const int32_t wmax = L->mixed == 2 ? 16 : ((L->mixed || L->format == 1) ? 8 : 4);
-  return (size_t)L->head_dim * wmax / 8;
+  return (size_t)(L->head_dim + vdim(L)) * wmax / 8;
 }
 /* Header bytes: mixed 1 = one width bit per row; mixed 2 = a 2-bit width code per row. */
 static size_t header_bytes(const orc_layout* L) { return L->mixed == 2 ? 64 : (L->mixed ? 32 : 0); }
-static size_t kcodes_off(const orc_layout* L, int32_t t) { return (size_t)t * 2 * row_slot_bytes(L); }
+static size_t kcodes_off(const orc_layout* L, int32_t t) { return (size_t)t * row_rec_bytes(L); }
 static size_t vcodes_off(const orc_layout* L, int32_t t, int32_t bits) {
   return kcodes_off(L, t) + (size_t)L->head_dim * bits / 8;
 }
-static size_t off_params(const orc_layout* L) { return (size_t)ORC_ROWS * 2 * row_slot_bytes(L); }
+static size_t off_params(const orc_layout* L) { return (size_t)ORC_ROWS * row_rec_bytes(L); }
 static size_t kparams_per_row(const orc_layout* L) { return L->k_group > 0 ? (size_t)(L->head_dim / L->k_group) : 0; }
 static size_t prow_bytes(const orc_layout* L) {
   if (L->format == 1) return 0;
-  return (kparams_per_row(L) + (size_t)(L->head_dim / L->v_group)) * 4;
+  return (kparams_per_row(L) + (size_t)(vdim(L) / L->v_group)) * 4;
 }
 static size_t off_prows(const orc_layout* L) {
   return off_params(L) + ((L->k_group > 0 || L->format == 1) ? 0 : (size_t)L->head_dim * 4);
@@ -352,30 +357,27 @@ static void store_f16_row(const float* x, int32_t d, uint8_t* dst) {
   for (int32_t c = 0; c < d; ++c) put_u16(dst + 2 * c, orc_f32_to_f16(x[c]));
 }
 
-/* Quantise one tile from its 256 fp16 rows: k_rows/v_rows give row t at k_rows + t * row_stride. */
-static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_rows,
-                          const uint16_t* v_rows, size_t row_stride, const uint32_t* bitmap) {
-  const int32_t d = L->head_dim;
+/* Quantise one tile from its 256 fp16 rows: row t of K at k_rows + t * k_stride (d values), of V at
+ * v_rows + t * v_stride (dv values). */
+static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_rows, size_t k_stride,
+                          const uint16_t* v_rows, size_t v_stride, const uint32_t* bitmap) {
+  const int32_t d = L->head_dim, dv = vdim(L);
   memset(tile, 0, orc_tile_bytes(L));
   float* xk = (float*)malloc(sizeof(float) * ORC_ROWS * d);
-  float* xv = (float*)malloc(sizeof(float) * ORC_ROWS * d);
+  float* xv = (float*)malloc(sizeof(float) * ORC_ROWS * dv);
   for (int32_t t = 0; t < ORC_ROWS; ++t) {
-    for (int32_t c = 0; c < d; ++c) {
-      xk[(size_t)t * d + c] = orc_f16_to_f32(k_rows[(size_t)t * row_stride + c]);
-      xv[(size_t)t * d + c] = orc_f16_to_f32(v_rows[(size_t)t * row_stride + c]);
-    }
+    for (int32_t c = 0; c < d; ++c) xk[(size_t)t * d + c] = orc_f16_to_f32(k_rows[(size_t)t * k_stride + c]);
+    for (int32_t c = 0; c < dv; ++c) xv[(size_t)t * dv + c] = orc_f16_to_f32(v_rows[(size_t)t * v_stride + c]);
     if (L->rotate) {
       rotate_row(xk + (size_t)t * d, d);
-      rotate_row(xv + (size_t)t * d, d);
+      rotate_row(xv + (size_t)t * dv, dv);
     }
   }
   if (L->format == 1) { /* FP8: K bytes then V bytes of each row record */
     for (int32_t t = 0; t < ORC_ROWS; ++t) {
       uint8_t* rec = tile + kcodes_off(L, t);
-      for (int32_t c = 0; c < d; ++c) {
-        rec[c] = orc_f32_to_e4m3(xk[(size_t)t * d + c]);
-        rec[d + c] = orc_f32_to_e4m3(xv[(size_t)t * d + c]);
-      }
+      for (int32_t c = 0; c < d; ++c) rec[c] = orc_f32_to_e4m3(xk[(size_t)t * d + c]);
+      for (int32_t c = 0; c < dv; ++c) rec[d + c] = orc_f32_to_e4m3(xv[(size_t)t * dv + c]);
     }
     free(xk);
     free(xv);
@@ -408,9 +410,9 @@ static void quantize_tile(const orc_layout* L, uint8_t* tile, const uint16_t* k_
   for (int32_t t = 0; t < ORC_ROWS; ++t) {
     const int32_t b = row_bits(L, bitmap, t);
     if (b == 16)
-      store_f16_row(xv + (size_t)t * d, d, tile + vcodes_off(L, t, b));
+      store_f16_row(xv + (size_t)t * dv, dv, tile + vcodes_off(L, t, b));
     else
-      quantize_row_groups(xv + (size_t)t * d, d, L->v_group, b, tile + vcodes_off(L, t, b), tile + vparams_off(L, t));
+      quantize_row_groups(xv + (size_t)t * dv, dv, L->v_group, b, tile + vcodes_off(L, t, b), tile + vparams_off(L, t));
   }
   if (L->mixed) {
     uint8_t* hdr = tile + off_header(L);
@@ -433,11 +435,11 @@ int orc_quantize_blocks(const orc_layout* L, uint8_t* pool, const int32_t* block
   if (st != ORC_OK) return st;
   if (n_blocks < 0) return ORC_ERR_ARG;
   if (prec_bits && !L->mixed) return ORC_ERR_ARG;
-  const int32_t H = L->num_kv_heads, d = L->head_dim;
+  const int32_t H = L->num_kv_heads, d = L->head_dim, dv = vdim(L);
   for (int32_t i = 0; i < n_blocks; ++i) {
     for (int32_t h = 0; h < H; ++h) {
-      const size_t base = ((size_t)i * ORC_ROWS * H + h) * d;
-      quantize_tile(L, tile_ptr(L, pool, block_ids[i], h), k + base, v + base, (size_t)H * d,
+      const size_t row0 = (size_t)i * ORC_ROWS * H + h;
+      quantize_tile(L, tile_ptr(L, pool, block_ids[i], h), k + row0 * d, (size_t)H * d, v + row0 * dv, (size_t)H * dv,
                     prec_bits ? prec_bits + (size_t)i * (header_bytes(L) / 4) : NULL);
     }
   }
@@ -455,8 +457,8 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
   if (L->k_group < 0) return ORC_ERR_UNSUPPORTED;
   if (n_seqs < 0 || max_blocks_per_seq <= 0) return ORC_ERR_ARG;
   if (prec && !L->mixed) return ORC_ERR_ARG;
-  const int32_t H = L->num_kv_heads, d = L->head_dim;
-  const size_t slot = row_slot_bytes(L);
+  const int32_t H = L->num_kv_heads, d = L->head_dim, dv = vdim(L);
+  const size_t rec_bytes = row_rec_bytes(L);
   float x[4096];
   for (int32_t s = 0; s < n_seqs; ++s) {
     int32_t p = positions[s];
@@ -466,24 +468,25 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
     if (L->mixed == 2 && prec && (prec[s] == 2 || prec[s] == 16)) bits = prec[s]; /* any other value: 4 */
     for (int32_t h = 0; h < H; ++h) {
       uint8_t* tile = tile_ptr(L, pool, blk, h);
-      memset(tile + kcodes_off(L, row), 0, 2 * slot); /* the whole record: a wider row may have been here */
+      memset(tile + kcodes_off(L, row), 0, rec_bytes); /* the whole record: a wider row may have been here */
       for (int32_t which = 0; which < 2; ++which) {
-        const uint16_t* src = (which == 0 ? k : v) + ((size_t)s * H + h) * d;
-        for (int32_t c = 0; c < d; ++c) x[c] = orc_f16_to_f32(src[c]);
-        if (L->rotate) rotate_row(x, d);
+        const int32_t n = which == 0 ? d : dv;
+        const uint16_t* src = which == 0 ? k + ((size_t)s * H + h) * d : v + ((size_t)s * H + h) * dv;
+        for (int32_t c = 0; c < n; ++c) x[c] = orc_f16_to_f32(src[c]);
+        if (L->rotate) rotate_row(x, n);
         if (L->format == 1) {
           uint8_t* rec = tile + kcodes_off(L, row) + (size_t)which * d;
-          for (int32_t c = 0; c < d; ++c) rec[c] = orc_f32_to_e4m3(x[c]);
+          for (int32_t c = 0; c < n; ++c) rec[c] = orc_f32_to_e4m3(x[c]);
           continue;
         }
         int32_t g = which == 0 ? L->k_group : L->v_group;
         size_t code_off = which == 0 ? kcodes_off(L, row) : vcodes_off(L, row, bits);
         size_t par_off = which == 0 ? kparams_off(L, row) : vparams_off(L, row);
         if (bits == 16) {
-          store_f16_row(x, d, tile + code_off);
-          memset(tile + par_off, 0, (size_t)(d / g) * 4); /* an FP16 row has no parameters */
+          store_f16_row(x, n, tile + code_off);
+          memset(tile + par_off, 0, (size_t)(n / g) * 4); /* an FP16 row has no parameters */
         } else {
-          quantize_row_groups(x, d, g, bits, tile + code_off, tile + par_off);
+          quantize_row_groups(x, n, g, bits, tile + code_off, tile + par_off);
         }
       }
       if (L->mixed == 1) {
@@ -502,16 +505,14 @@ int orc_append_tokens(const orc_layout* L, uint8_t* pool, int32_t n_seqs, const 
 
 /* ---------------------------------------------------------------- decoding */
 
-/* Dequantise row t of one tile into fp64 (rotated domain, no inverse rotation): k_out[d], v_out[d]:
+/* Dequantise row t of one tile into fp64 (rotated domain, no inverse rotation): k_out[d], v_out[dv]:
  * value = code * scale + zero, exact in fp64. Returns the row's bit width. */
 int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, double* k_out, double* v_out) {
-  const int32_t d = L->head_dim;
+  const int32_t d = L->head_dim, dv = vdim(L);
   if (L->format == 1) {
     const uint8_t* rec = tile + kcodes_off(L, t);
-    for (int32_t c = 0; c < d; ++c) {
-      k_out[c] = (double)orc_e4m3_to_f32(rec[c]);
-      v_out[c] = (double)orc_e4m3_to_f32(rec[d + c]);
-    }
+    for (int32_t c = 0; c < d; ++c) k_out[c] = (double)orc_e4m3_to_f32(rec[c]);
+    for (int32_t c = 0; c < dv; ++c) v_out[c] = (double)orc_e4m3_to_f32(rec[d + c]);
     return 8;
   }
   int32_t bits = 4;
@@ -520,18 +521,18 @@ int32_t orc_dequant_row(const orc_layout* L, const uint8_t* tile, int32_t t, dou
   const uint8_t* kr = tile + kcodes_off(L, t);
   const uint8_t* vr = tile + vcodes_off(L, t, bits);
   if (bits == 16) {
-    for (int32_t c = 0; c < d; ++c) {
-      k_out[c] = (double)orc_f16_to_f32(get_u16(kr + 2 * c));
-      v_out[c] = (double)orc_f16_to_f32(get_u16(vr + 2 * c));
-    }
+    for (int32_t c = 0; c < d; ++c) k_out[c] = (double)orc_f16_to_f32(get_u16(kr + 2 * c));
+    for (int32_t c = 0; c < dv; ++c) v_out[c] = (double)orc_f16_to_f32(get_u16(vr + 2 * c));
     return bits;
   }
   for (int32_t c = 0; c < d; ++c) {
     const uint8_t* kp = L->k_group > 0 ? tile + kparams_off(L, t) + (size_t)(c / L->k_group) * 4
                                        : tile + kchan_off(L, c);
-    const uint8_t* vp = tile + vparams_off(L, t) + (size_t)(c / L->v_group) * 4;
     k_out[c] = (double)unpack_code(kr, c, bits) * (double)orc_f16_to_f32(get_u16(kp)) +
                (double)orc_f16_to_f32(get_u16(kp + 2));
+  }
+  for (int32_t c = 0; c < dv; ++c) {
+    const uint8_t* vp = tile + vparams_off(L, t) + (size_t)(c / L->v_group) * 4;
     v_out[c] = (double)unpack_code(vr, c, bits) * (double)orc_f16_to_f32(get_u16(vp)) +
                (double)orc_f16_to_f32(get_u16(vp + 2));
   }
@@ -563,8 +564,9 @@ static uint16_t f64_to_f16(double x) {
 /* The cache restored as fp16 rows ([QKV] methodology section, injection path: the quantised cache
  * rebuilt as fp16 key/value tensors before the forward pass). For every listed block b = block_ids[i],
  * KV head h and row t: the row's K and V are dequantised exactly (orc_dequant_row), un-rotated for a
- * rotated pool by (1 / (d c)) H in fp64 (the exact inverse of the rotation c H), and rounded once to
- * fp16. Output layout is the input layout of orc_quantize_blocks: k_out / v_out [n_blocks * 256][H][d].
+ * rotated pool by (1 / (n c)) H in fp64 (the exact inverse of the rotation c H at length n = d or dv), and
+ * rounded once to fp16. Output layout is the input layout of orc_quantize_blocks: k_out [n_blocks * 256][H][d],
+ * v_out [n_blocks * 256][H][dv].
  * Pinned by: test_oracle_dequant.py (grid-exact blocks restored bit for bit, the per-element error bound
  * of the stored scales carried through the rotation, an explicit Hadamard matrix for the inverse). */
 int orc_dequantize_blocks(const orc_layout* L, const uint8_t* pool, const int32_t* block_ids, int32_t n_blocks,
@@ -572,9 +574,10 @@ int orc_dequantize_blocks(const orc_layout* L, const uint8_t* pool, const int32_
   int st = orc_check_layout(L);
   if (st != ORC_OK) return st;
   if (n_blocks < 0) return ORC_ERR_ARG;
-  const int32_t H = L->num_kv_heads, d = L->head_dim;
-  const double unrot = 1.0 / ((double)d * (double)orc_rot_scale(d));
-  double* k = (double*)malloc(sizeof(double) * 2 * (size_t)d);
+  const int32_t H = L->num_kv_heads, d = L->head_dim, dv = vdim(L);
+  const double unrot_k = 1.0 / ((double)d * (double)orc_rot_scale(d));
+  const double unrot_v = 1.0 / ((double)dv * (double)orc_rot_scale(dv));
+  double* k = (double*)malloc(sizeof(double) * ((size_t)d + (size_t)dv));
   if (!k) return ORC_ERR_ARG;
   double* v = k + d;
   for (int32_t i = 0; i < n_blocks; ++i) {
@@ -584,17 +587,13 @@ int orc_dequantize_blocks(const orc_layout* L, const uint8_t* pool, const int32_
         orc_dequant_row(L, tile, t, k, v);
         if (L->rotate) {
           fwht_f64(k, d);
-          fwht_f64(v, d);
-          for (int32_t c = 0; c < d; ++c) {
-            k[c] *= unrot;
-            v[c] *= unrot;
-          }
+          fwht_f64(v, dv);
+          for (int32_t c = 0; c < d; ++c) k[c] *= unrot_k;
+          for (int32_t c = 0; c < dv; ++c) v[c] *= unrot_v;
         }
-        const size_t o = (((size_t)i * ORC_ROWS + t) * H + h) * d;
-        for (int32_t c = 0; c < d; ++c) {
-          k_out[o + c] = f64_to_f16(k[c]);
-          v_out[o + c] = f64_to_f16(v[c]);
-        }
+        const size_t row = ((size_t)i * ORC_ROWS + t) * H + h;
+        for (int32_t c = 0; c < d; ++c) k_out[row * d + c] = f64_to_f16(k[c]);
+        for (int32_t c = 0; c < dv; ++c) v_out[row * dv + c] = f64_to_f16(v[c]);
       }
     }
   }
@@ -605,8 +604,9 @@ int orc_dequantize_blocks(const orc_layout* L, const uint8_t* pool, const int32_
 /* Host-memory counterpart of kvq_decode_attention, in fp64, by the plain definition:
  *   for sequence s and query head j (KV head h = j / G): for every slot t < seq_lens[s], a sentinel
  *   slot has logit -1e4 and value 0; any other slot's K and V rows are dequantised exactly (and, for a
- *   rotated pool, un-rotated by (1 / (d c)) H, the exact inverse of c H), logit = scale * (q . k);
- *   out = sum_t softmax(logits)_t * v_t. A sequence with no slot gives 0.
+ *   rotated pool, un-rotated by (1 / (n c)) H, the exact inverse of c H at length n = d or dv),
+ *   logit = scale * (q . k); out = sum_t softmax(logits)_t * v_t. A sequence with no slot gives 0.
+ *   q is [n_seqs][num_q_heads][d], out [n_seqs][num_q_heads][dv].
  * weights (optional, may be NULL): fp64 [n_seqs][num_q_heads][max_seq_len] softmax weights.
  * n_threads > 0 sets the OpenMP thread count (one (s, h) pair per iteration).
  * Pinned by: test_oracle_attention.py (numpy dense brute force with an explicit Hadamard matrix,
@@ -618,10 +618,11 @@ int orc_decode_attention(const orc_layout* L, const uint8_t* pool, const uint16_
                          int32_t max_seq_len, int32_t n_threads) {
   int st = orc_check_layout(L);
   if (st != ORC_OK) return st;
-  const int32_t H = L->num_kv_heads, d = L->head_dim;
+  const int32_t H = L->num_kv_heads, d = L->head_dim, dv = vdim(L);
   if (n_seqs < 0 || num_q_heads <= 0 || num_q_heads % H != 0) return ORC_ERR_ARG;
   const int32_t G = num_q_heads / H;
-  const double unrot = 1.0 / ((double)d * (double)orc_rot_scale(d));
+  const double unrot_k = 1.0 / ((double)d * (double)orc_rot_scale(d));
+  const double unrot_v = 1.0 / ((double)dv * (double)orc_rot_scale(dv));
 #ifdef _OPENMP
   if (n_threads > 0) omp_set_num_threads(n_threads);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -631,25 +632,27 @@ int orc_decode_attention(const orc_layout* L, const uint8_t* pool, const uint16_
     const int32_t n = seq_lens[s];
     if (n <= 0) {
       for (int32_t jj = 0; jj < G; ++jj)
-        for (int32_t c = 0; c < d; ++c) out[((size_t)s * num_q_heads + h * G + jj) * d + c] = 0.0;
+        for (int32_t c = 0; c < dv; ++c) out[((size_t)s * num_q_heads + h * G + jj) * dv + c] = 0.0;
       continue;
     }
     double* kt = (double*)malloc(sizeof(double) * (size_t)n * d);
-    double* vt = (double*)malloc(sizeof(double) * (size_t)n * d);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)n * dv);
     char* sent = (char*)malloc((size_t)n);
     for (int32_t t = 0; t < n; ++t) {
       sent[t] = sentinel_mask && ((sentinel_mask[(size_t)s * mask_words_per_seq + t / 32] >> (t % 32)) & 1u);
       if (sent[t]) {
-        for (int32_t c = 0; c < d; ++c) { kt[(size_t)t * d + c] = 0.0; vt[(size_t)t * d + c] = 0.0; }
+        for (int32_t c = 0; c < d; ++c) kt[(size_t)t * d + c] = 0.0;
+        for (int32_t c = 0; c < dv; ++c) vt[(size_t)t * dv + c] = 0.0;
         continue;
       }
       int32_t blk = block_table[(size_t)s * max_blocks_per_seq + t / ORC_ROWS];
       const uint8_t* tile = pool + ((size_t)blk * H + h) * orc_tile_bytes(L);
-      orc_dequant_row(L, tile, t % ORC_ROWS, kt + (size_t)t * d, vt + (size_t)t * d);
+      orc_dequant_row(L, tile, t % ORC_ROWS, kt + (size_t)t * d, vt + (size_t)t * dv);
       if (L->rotate) {
         fwht_f64(kt + (size_t)t * d, d);
-        fwht_f64(vt + (size_t)t * d, d);
-        for (int32_t c = 0; c < d; ++c) { kt[(size_t)t * d + c] *= unrot; vt[(size_t)t * d + c] *= unrot; }
+        fwht_f64(vt + (size_t)t * dv, dv);
+        for (int32_t c = 0; c < d; ++c) kt[(size_t)t * d + c] *= unrot_k;
+        for (int32_t c = 0; c < dv; ++c) vt[(size_t)t * dv + c] *= unrot_v;
       }
     }
     double* logit = (double*)malloc(sizeof(double) * (size_t)n);
@@ -669,12 +672,12 @@ int orc_decode_attention(const orc_layout* L, const uint8_t* pool, const uint16_
       }
       double denom = 0.0;
       for (int32_t t = 0; t < n; ++t) denom += exp(logit[t] - m);
-      double* o = out + ((size_t)s * num_q_heads + j) * d;
-      for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+      double* o = out + ((size_t)s * num_q_heads + j) * dv;
+      for (int32_t c = 0; c < dv; ++c) o[c] = 0.0;
       for (int32_t t = 0; t < n; ++t) {
         double w = exp(logit[t] - m) / denom;
         if (weights) weights[((size_t)s * num_q_heads + j) * max_seq_len + t] = w;
-        for (int32_t c = 0; c < d; ++c) o[c] += w * vt[(size_t)t * d + c];
+        for (int32_t c = 0; c < dv; ++c) o[c] += w * vt[(size_t)t * dv + c];
       }
     }
     free(logit);

@@ -82,7 +82,7 @@ def test_restored_rows_within_stored_scale_bound(orc, rotate, kg, mixed):
     for i in range(n):
         for h in range(H):
             tile = pool[(i * H + h) * tb:(i * H + h + 1) * tb]
-            slot, off_par, off_prow, prow, kpr, off_hdr, _ = brute._layout_offsets(d, kg, vg, mixed)
+            _, off_par, off_prow, prow, kpr, off_hdr, _ = brute._layout_offsets(d, kg, vg, mixed)
             bits = np.full(256, 4)
             if mixed:
                 hdr = tile[off_hdr:off_hdr + 32]
