@@ -91,12 +91,12 @@ def decode_bytes(cfg: W.Config, case: W.Case, counts: np.ndarray, unique: bool =
     (a block shared by several block tables counted once when ``unique``; an FP16 row has no parameters),
     the per-channel K parameters and width headers of the tiles touched, q, out, block tables, lengths and
     masks. ``counts``: live rows per sequence and width (2, 4, 8, 16 bits), as from live_rows."""
-    d, H = cfg.head_dim, cfg.num_kv_heads
+    d, dv, H = cfg.head_dim, cfg.dv, cfg.num_kv_heads
     kpar = (d // cfg.k_group) * 4 if cfg.k_group > 0 else 0
-    vpar = (d // cfg.v_group) * 4 if cfg.v_group > 0 else 0
-    row = np.array([2 * d * bits // 8 + kpar + vpar for bits in (2, 4, 8)] + [4 * d], np.int64)
+    vpar = (dv // cfg.v_group) * 4 if cfg.v_group > 0 else 0
+    row = np.array([(d + dv) * bits // 8 + kpar + vpar for bits in (2, 4, 8)] + [2 * (d + dv)], np.int64)
     if cfg.fmt == 1:  # FP8 E4M3: one byte per K and V element, no parameters
-        row[:] = 2 * d
+        row[:] = d + dv
     if unique and cfg.table == "shared_prefix":
         # every physical block read once: its live rows are the rows below the longest sequence using it
         rows = 0
@@ -112,7 +112,7 @@ def decode_bytes(cfg: W.Config, case: W.Case, counts: np.ndarray, unique: bool =
         b += tiles * H * d * 4
     if cfg.mixed:
         b += tiles * H * (64 if cfg.mixed == 2 else 32)
-    b += case.n_seqs * cfg.num_q_heads * d * (2 + 4)                 # q fp16 in, out fp32
+    b += case.n_seqs * cfg.num_q_heads * (d * 2 + dv * 4)             # q fp16 in, out fp32
     b += case.block_table.size * 4 + case.n_seqs * 4
     if case.sentinel_mask is not None:
         b += case.sentinel_mask.size * 4
@@ -120,14 +120,14 @@ def decode_bytes(cfg: W.Config, case: W.Case, counts: np.ndarray, unique: bool =
 
 
 def append_bytes(cfg: W.Config, n_seqs: int) -> int:
-    d, H = cfg.head_dim, cfg.num_kv_heads
+    d, dv, H = cfg.head_dim, cfg.dv, cfg.num_kv_heads
     kpar = (d // cfg.k_group) * 4
-    row_out = 2 * (d // 2) + kpar + (d // cfg.v_group) * 4
-    return n_seqs * H * (2 * d * 2 + row_out) + n_seqs * 4 * 2
+    row_out = (d + dv) // 2 + kpar + (dv // cfg.v_group) * 4
+    return n_seqs * H * ((d + dv) * 2 + row_out) + n_seqs * 4 * 2
 
 
 def quantize_bytes(cfg: W.Config, n_blocks: int, tile_bytes: int) -> int:
-    return n_blocks * W.BLOCK * cfg.num_kv_heads * cfg.head_dim * 2 * 2 + n_blocks * cfg.num_kv_heads * tile_bytes
+    return n_blocks * W.BLOCK * cfg.num_kv_heads * (cfg.head_dim + cfg.dv) * 2 + n_blocks * cfg.num_kv_heads * tile_bytes
 
 
 def kernel_source_digest() -> str:
@@ -190,7 +190,7 @@ def main():
         avs.append(torch.from_numpy(av).view(torch.float16).to(dev))
         qs.append(torch.from_numpy(W.queries(cfg, l, case.n_seqs)).view(torch.float16).to(dev))
         pools.append(kvq.new_pool(lay, case.num_blocks))
-        outs.append(torch.empty((case.n_seqs, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device=dev))
+        outs.append(torch.empty((case.n_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device=dev))
         if l % 8 == 7:
             log("generated layer %d/%d (%.1f s)" % (l + 1, layers, time.time() - t0))
     block_ids = torch.from_numpy(case.prefill_blocks).to(dev)
@@ -314,7 +314,7 @@ def main():
         del pools, aks, avs, qs, outs
         torch.cuda.empty_cache()
         workloads = {}
-        for name in W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL]:
+        for name in W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL, MLA_POOL]:
             if name != cfg.name:
                 workloads[name] = measure_workload(kvq, torch, name)
         workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
@@ -373,11 +373,13 @@ def main():
 # Pool instances cycled through when one workload's decode is timed on its own: enough distinct copies that
 # the working set exceeds the 256 MB Infinity Cache (the multi-layer workloads use their layer count).
 INSTANCES = {"tiny_1k": 1, "gemma3_12b_4k": 48, "llama31_8b_pool_8k": 32, "qwen25_14b_prefix_32k": 16,
-             "mixed_sentinel_32k": 1}
+             "mixed_sentinel_32k": 1, "deepseek_v2_lite_mla_8k": 8}
 # The 12 x 8K pool stored as FP8 E4M3: the cache the 4-bit one is compared against (UltraQuant, technology section).
 FP8_BASELINE = "llama31_8b_pool_8k_fp8"
 # The 12 x 8K pool with per-token widths {2, 4, 8, FP16} (QKVShare, methodology section).
 WIDTHS_POOL = "llama31_8b_pool_8k_widths"
+# 12 agents x 8K of an MLA model: K head dim 192, V 128 ("Agent Memory Below the Prompt", 2.2).
+MLA_POOL = "deepseek_v2_lite_mla_8k"
 
 
 def workload_config(name):
@@ -450,7 +452,7 @@ def measure_workload(kvq, torch, name, launches=16):
     seq_lens = torch.from_numpy(case.seq_lens).cuda()
     mask = None if case.sentinel_mask is None else torch.from_numpy(case.sentinel_mask.view(np.int32)).cuda()
     q = torch.from_numpy(W.queries(cfg, 0, case.n_seqs)).view(torch.float16).cuda()
-    out = torch.empty((case.n_seqs, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    out = torch.empty((case.n_seqs, cfg.num_q_heads, cfg.dv), dtype=torch.float32, device="cuda")
     ws = kvq.new_workspace(lay, case.n_seqs, cfg.num_q_heads, case.max_seq_len)
     app = None
     if case.append:

@@ -29,12 +29,17 @@ class Layout(ctypes.Structure):
 
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed",
-                 "format")]
+                 "format", "v_head_dim")]
 
     def __init__(self, head_dim, num_kv_heads, k_group=64, v_group=64, rotate=0, mixed=0,
-                 block_tokens=BLOCK_TOKENS, format=0):
+                 block_tokens=BLOCK_TOKENS, format=0, v_head_dim=0):
         super().__init__(head_dim, num_kv_heads, block_tokens, k_group, v_group, int(rotate), int(mixed),
-                         int(format))
+                         int(format), int(v_head_dim))
+
+    @property
+    def dv(self) -> int:
+        """V's head dim (the K head dim unless v_head_dim gives another)."""
+        return self.v_head_dim if self.v_head_dim > 0 else self.head_dim
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -164,7 +169,7 @@ def new_workspace(layout: Layout, n_seqs: int, num_q_heads: int, max_seq_len: in
 
 
 def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, stream=None) -> None:
-    """k, v: fp16 [n_blocks*256, H_kv, d]; block_ids int32 [n_blocks]; prec_bits int32/uint32 [n_blocks, W]:
+    """k fp16 [n_blocks*256, H_kv, d], v [.., dv]; block_ids int32 [n_blocks]; prec_bits int32/uint32 [n_blocks, W]:
     the rows' width words, W = 8 (mixed = 1: one bit per row, set = 8-bit) or 16 (mixed = 2: a 2-bit code per
     row, 0..3 = 2, 4, 8, 16 bits), or None (every row 4-bit)."""
     torch = _torch()
@@ -180,17 +185,18 @@ def quantize_blocks(layout: Layout, pool, block_ids, k, v, prec_bits=None, strea
 
 
 def dequantize_blocks(layout: Layout, pool, block_ids, k_out=None, v_out=None, stream=None):
-    """fp16 k, v [n_blocks*256, H_kv, d] of the listed blocks (un-rotated for rotated pools); allocated
-    here unless given."""
+    """fp16 k [n_blocks*256, H_kv, d], v [.., dv] of the listed blocks (un-rotated for rotated pools);
+    allocated here unless given."""
     torch = _torch()
     n_blocks = int(block_ids.numel())
     shape = (n_blocks * 256, layout.num_kv_heads, layout.head_dim)
+    vshape = shape[:2] + (layout.dv,)
     if k_out is None:
         k_out = torch.empty(shape, dtype=torch.float16, device=pool.device)
     if v_out is None:
-        v_out = torch.empty(shape, dtype=torch.float16, device=pool.device)
-    if tuple(k_out.shape) != shape or tuple(v_out.shape) != shape:
-        raise ValueError("k_out and v_out must have shape %s" % (shape,))
+        v_out = torch.empty(vshape, dtype=torch.float16, device=pool.device)
+    if tuple(k_out.shape) != shape or tuple(v_out.shape) != vshape:
+        raise ValueError("k_out and v_out must have shapes %s and %s" % (shape, vshape))
     st = _lib.kvq_dequantize_blocks(ctypes.byref(layout), _ptr(pool, "pool", (torch.uint8,), 256),
                                     _ptr(block_ids, "block_ids", (torch.int32,)), n_blocks,
                                     _ptr(k_out, "k_out", _f16(), 16), _ptr(v_out, "v_out", _f16(), 16),
@@ -212,7 +218,7 @@ def copy_blocks(layout: Layout, src_pool, src_ids, dst_pool, dst_ids, stream=Non
 
 
 def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None, stream=None) -> None:
-    """k, v: fp16 [n_seqs, H_kv, d]; block_table int32 [n_seqs, max_blocks]; positions int32 [n_seqs];
+    """k fp16 [n_seqs, H_kv, d], v [n_seqs, H_kv, dv]; block_table int32 [n_seqs, max_blocks]; positions int32 [n_seqs];
     prec uint8 [n_seqs]: each row's width (4 or 8 in a mixed = 1 pool; 2, 4, 8 or 16 in a mixed = 2 pool)
     or None (all 4-bit)."""
     torch = _torch()
@@ -227,14 +233,18 @@ def append_tokens(layout: Layout, pool, k, v, block_table, positions, prec=None,
 
 def decode_attention(layout: Layout, pool, q, block_table, seq_lens, max_seq_len: int, sentinel_mask=None,
                      softmax_scale: Optional[float] = None, out=None, workspace=None, stream=None):
-    """q fp16 [n_seqs, H_q, d] -> fp32 [n_seqs, H_q, d]. ``max_seq_len`` must bound every seq_lens
+    """q fp16 [n_seqs, H_q, d] -> fp32 [n_seqs, H_q, dv]. ``max_seq_len`` must bound every seq_lens
     entry (it sizes the split plan); sentinel_mask int32/uint32 [n_seqs, words] or None."""
     torch = _torch()
     n_seqs, hq, d = (int(x) for x in q.shape)
+    if d != layout.head_dim:
+        raise ValueError("q has head dim %d, the layout %d" % (d, layout.head_dim))
     if softmax_scale is None:
         softmax_scale = d ** -0.5
     if out is None:
-        out = torch.empty((n_seqs, hq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((n_seqs, hq, layout.dv), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (n_seqs, hq, layout.dv):
+        raise ValueError("out must have shape %s" % ((n_seqs, hq, layout.dv),))
     need = decode_workspace_bytes(layout, n_seqs, hq, max_seq_len)
     if workspace is None:
         workspace = new_workspace(layout, n_seqs, hq, max_seq_len, q.device)

@@ -24,7 +24,8 @@ import numpy as np
 
 FORMAT = "kvq-cachecard"
 VERSION = "1"
-_LAYOUT_FIELDS = ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed", "format")
+_LAYOUT_FIELDS = ("head_dim", "num_kv_heads", "block_tokens", "k_group", "v_group", "rotate", "mixed", "format",
+                  "v_head_dim")
 
 
 def _host_i32(a) -> np.ndarray:
@@ -60,7 +61,7 @@ def unpack(tensors: dict, meta: dict, layout_fields: Optional[dict] = None):
     position_offsets, model_id and layout. With ``layout_fields`` the card's layout must equal it."""
     if meta.get("card_format") != FORMAT or meta.get("card_version") != VERSION:
         raise ValueError("not a %s v%s file" % (FORMAT, VERSION))
-    layout = {k: int(meta[k]) for k in _LAYOUT_FIELDS}
+    layout = {k: int(meta.get(k, "0")) for k in _LAYOUT_FIELDS}
     if layout_fields is not None:
         want = {k: int(layout_fields.get(k, 0)) for k in _LAYOUT_FIELDS}
         if want != layout:

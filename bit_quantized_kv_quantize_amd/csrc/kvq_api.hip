@@ -10,40 +10,50 @@
 namespace kvq {
 
 static bool is_group(int g, int d) {
-  return (g == 8 || g == 16 || g == 32 || g == 64 || g == 128 || g == 256) && g <= d;
+  return (g == 8 || g == 16 || g == 32 || g == 64 || g == 128 || g == 256) && g <= d && d % g == 0;
 }
+
+static int v_dim(const kvq_layout* L) { return L->v_head_dim > 0 ? L->v_head_dim : L->head_dim; }
 
 int check_layout(const kvq_layout* L) {
   if (!L) return KVQ_ERR_ARG;
-  if (!(L->head_dim == 64 || L->head_dim == 128 || L->head_dim == 256)) return KVQ_ERR_ARG;
+  const int d = L->head_dim, dv = v_dim(L);
+  if (!(d == 64 || d == 128 || d == 192 || d == 256) || L->v_head_dim < 0) return KVQ_ERR_ARG;
+  if (!(dv == 64 || dv == 128 || dv == 192 || dv == 256)) return KVQ_ERR_ARG;
   if (L->num_kv_heads <= 0 || L->num_kv_heads > 4096) return KVQ_ERR_ARG;
   if (L->block_tokens != kRows) return KVQ_ERR_ARG;
+  // unequal K and V head dims (MLA): K 192 or 256 with V 128, per-token K groups, integer codes
+  const bool unequal = dv != d;
+  if (unequal && !((d == 192 || d == 256) && dv == 128)) return KVQ_ERR_UNSUPPORTED;
+  if (d == 192 && !unequal) return KVQ_ERR_UNSUPPORTED;  // (dv = 192 is covered by the pair check above)
   if (L->format == 1) {  // FP8 E4M3 per element
     if (L->k_group != 0 || L->v_group != 0 || L->mixed != 0) return KVQ_ERR_ARG;
     if (L->rotate != 0 && L->rotate != 1) return KVQ_ERR_ARG;
-    return KVQ_OK;
+    return unequal ? KVQ_ERR_UNSUPPORTED : KVQ_OK;
   }
   if (L->format != 0) return KVQ_ERR_ARG;
-  if (!(L->k_group == -1 || is_group(L->k_group, L->head_dim))) return KVQ_ERR_ARG;
-  if (!is_group(L->v_group, L->head_dim)) return KVQ_ERR_ARG;
+  if (!(L->k_group == -1 || is_group(L->k_group, d))) return KVQ_ERR_ARG;
+  if (!is_group(L->v_group, dv)) return KVQ_ERR_ARG;
   if ((L->rotate != 0 && L->rotate != 1) || L->mixed < 0 || L->mixed > 2) return KVQ_ERR_ARG;
+  if (L->rotate && d == 192) return KVQ_ERR_UNSUPPORTED;  // the rotation needs power-of-two dims
   if (L->mixed && L->k_group < 0) return KVQ_ERR_UNSUPPORTED;
+  if (unequal && L->k_group < 0) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
 TileGeom make_geom(const kvq_layout* L) {
   TileGeom g{};
   g.d = L->head_dim;
+  g.dv = v_dim(L);
   g.H = L->num_kv_heads;
   g.kg = L->k_group;
   g.vg = L->v_group;
   g.rotate = L->rotate;
   g.mixed = L->mixed;
   g.fp8 = L->format == 1;
-  g.slot = g.d * (g.mixed == 2 ? 16 : (g.mixed || g.fp8) ? 8 : 4) / 8;
-  g.rec = 2 * g.slot;
+  g.rec = (g.d + g.dv) * (g.mixed == 2 ? 16 : (g.mixed || g.fp8) ? 8 : 4) / 8;
   g.kpr = g.kg > 0 ? g.d / g.kg : 0;
-  g.vpr = g.fp8 ? 0 : g.d / g.vg;
+  g.vpr = g.fp8 ? 0 : g.dv / g.vg;
   g.prow = (g.kpr + g.vpr) * 4;
   g.off_kch = (uint32_t)(kRows * g.rec);
   g.off_prow = g.off_kch + ((g.kg > 0 || g.fp8) ? 0u : (uint32_t)(g.d * 4));
@@ -119,11 +129,11 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   w.parts = parts;
   w.ctr = 0;
   w.ml = up(ns * g.H * sizeof(unsigned));
-  w.acc = w.ml + up(parts * 2 * sizeof(float));
+  w.acc = w.ml + up(parts * 2 * sizeof(float));  // accumulators of V's head dim
   // row lists only for layouts the row-list kernel reads: one list per width (4 and 8 bits, and 2 and 16
   // in pools of four widths)
   const size_t nwd = g.mixed == 2 ? 4 : 2;
-  w.cnt = w.acc + up(parts * g.d * sizeof(float));
+  w.cnt = w.acc + up(parts * g.dv * sizeof(float));
   w.list = w.cnt + up(ns * nwd * sizeof(int));
   w.list_cap = decode_rows_supported(g, num_q_heads / g.H) ? (max_seq_len + 63) / 64 * 64 : 0;
   w.bcnt = w.list + up(ns * nwd * (size_t)w.list_cap * sizeof(uint32_t));
@@ -139,6 +149,10 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// The rotation of an n-channel row is c H with c = fp32(1 / sqrt(n)); its inverse is (1 / (n c)) H.
+static float rot_scale(int n) { return (float)(1.0 / sqrt((double)n)); }
+static float unrot_scale(int n) { return (float)(1.0 / ((double)n * (double)rot_scale(n))); }
 
 }  // namespace kvq
 
@@ -187,9 +201,8 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
   if (n_blocks == 0) return KVQ_OK;
   if (!pool || !block_ids || !k || !v) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
-  float rot_c = (float)(1.0 / sqrt((double)g.d));
-  return hip_status(launch_quantize_blocks(g, (uint8_t*)pool, block_ids, n_blocks, k, v, prec_bits, rot_c,
-                                           (hipStream_t)stream));
+  return hip_status(launch_quantize_blocks(g, (uint8_t*)pool, block_ids, n_blocks, k, v, prec_bits, rot_scale(g.d),
+                                           rot_scale(g.dv), (hipStream_t)stream));
 }
 
 int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* block_ids, int32_t n_blocks,
@@ -200,10 +213,8 @@ int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* 
   if (n_blocks == 0) return KVQ_OK;
   if (!pool || !block_ids || !k_out || !v_out) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
-  const float c = (float)(1.0 / sqrt((double)g.d));
-  const float unrot_c = (float)(1.0 / ((double)g.d * (double)c));
-  return hip_status(launch_dequantize_blocks(g, (const uint8_t*)pool, block_ids, n_blocks, k_out, v_out, unrot_c,
-                                             (hipStream_t)stream));
+  return hip_status(launch_dequantize_blocks(g, (const uint8_t*)pool, block_ids, n_blocks, k_out, v_out,
+                                             unrot_scale(g.d), unrot_scale(g.dv), (hipStream_t)stream));
 }
 
 int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* src_ids, void* dst_pool,
@@ -230,9 +241,8 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
   if (n_seqs == 0) return KVQ_OK;
   if (!pool || !k || !v || !block_table || !positions) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
-  float rot_c = (float)(1.0 / sqrt((double)g.d));
   return hip_status(launch_append_tokens(g, (uint8_t*)pool, n_seqs, k, v, block_table, max_blocks_per_seq,
-                                         positions, prec, rot_c, (hipStream_t)stream));
+                                         positions, prec, rot_scale(g.d), rot_scale(g.dv), (hipStream_t)stream));
 }
 
 int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
@@ -282,8 +292,8 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.mask_words = sentinel_mask ? mask_words_per_seq : 0;
   a.q_scale = (float)((double)softmax_scale * 1.4426950408889634);
-  float c = (float)(1.0 / sqrt((double)g.d));
-  a.unrot_c = (float)(1.0 / ((double)g.d * (double)c));
+  a.unrot_c = unrot_scale(g.d);
+  a.unrot_cv = unrot_scale(g.dv);
   return hip_status(launch_decode(g, a, (hipStream_t)stream));
 }
 

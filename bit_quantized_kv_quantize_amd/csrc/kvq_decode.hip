@@ -72,11 +72,12 @@ __device__ __forceinline__ void fp8x8(const uint8_t* row, int c0, float (&c)[8])
 
 // Grid (n_splits, H_kv, n_seqs), 256 threads. Thread t scores token t of each block against the G query
 // heads of its KV head; for the value pass thread (cl, tg) owns channels cl*8 .. cl*8+7 and the tokens
-// t = tg (mod TG). Writes (m, l, acc[d]) per query head and split.
-template <int D, int GMAX>
+// t = tg (mod TG). Writes (m, l, acc[dv]) per query head and split. D = K's head dim (and the query's),
+// DV = V's.
+template <int D, int DV, int GMAX>
 __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
   constexpr int NT = 256;
-  constexpr int CL = D / 8;   // lanes per row in the value pass
+  constexpr int CL = DV / 8;  // lanes per row in the value pass
   constexpr int TG = NT / CL; // token groups in the value pass
   __shared__ float s_q[GMAX][D];
   __shared__ float s_qk[GMAX][D];   // q * scale per channel (per-channel K groups only)
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
   __shared__ float s_kconst[GMAX];
   __shared__ float s_p[GMAX][NT];
   __shared__ float s_red[GMAX][NT / 64];
-  __shared__ float s_acc[TG][D];
+  __shared__ float s_acc[TG][DV];
 
   const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x;
@@ -305,10 +306,10 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     for (int e = 0; e < 8; ++e) s_acc[tg][cl * 8 + e] = acc[j][e] + zacc[j];
     __syncthreads();
     const size_t pi = part0 + (size_t)j * a.plan.n_splits;
-    for (int c = tid; c < D; c += NT) {
+    for (int c = tid; c < DV; c += NT) {
       float sum = 0.0f;
       for (int r = 0; r < TG; ++r) sum += s_acc[r][c];
-      a.ws_acc[pi * D + c] = sum;
+      a.ws_acc[pi * DV + c] = sum;
     }
     if (tid == 0) {
       a.ws_ml[2 * pi] = m_run[j];
@@ -317,19 +318,19 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     __syncthreads();
   }
 }
-template <int D, int GMAX>
+template <int D, int DV, int GMAX>
 hipError_t launch_t(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_attn_k<D, GMAX>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
+  hipLaunchKernelGGL((decode_attn_k<D, DV, GMAX>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
                      g, a);
-  hipLaunchKernelGGL(decode_reduce_k<D>, dim3(a.num_q_heads, a.n_seqs), dim3(D), 0, stream, g, a);
+  hipLaunchKernelGGL(decode_reduce_k<DV>, dim3(a.num_q_heads, a.n_seqs), dim3(DV), 0, stream, g, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int DV>
 hipError_t launch_d(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  if (a.G <= 4) return launch_t<D, 4>(g, a, stream);
-  if (a.G <= 8) return launch_t<D, 8>(g, a, stream);
-  return launch_t<D, 16>(g, a, stream);
+  if (a.G <= 4) return launch_t<D, DV, 4>(g, a, stream);
+  if (a.G <= 8) return launch_t<D, DV, 8>(g, a, stream);
+  return launch_t<D, DV, 16>(g, a, stream);
 }
 
 }  // namespace
@@ -357,11 +358,15 @@ hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t str
 }
 
 hipError_t launch_decode_generic(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  switch (g.d) {
-    case 64: return launch_d<64>(g, a, stream);
-    case 128: return launch_d<128>(g, a, stream);
-    case 256: return launch_d<256>(g, a, stream);
+  if (g.dv == g.d) {
+    switch (g.d) {
+      case 64: return launch_d<64, 64>(g, a, stream);
+      case 128: return launch_d<128, 128>(g, a, stream);
+      case 256: return launch_d<256, 256>(g, a, stream);
+    }
   }
+  if (g.d == 192 && g.dv == 128) return launch_d<192, 128>(g, a, stream);
+  if (g.d == 256 && g.dv == 128) return launch_d<256, 128>(g, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, 1) void cascade_k(TileGeom g, DecodeArgs a) {
 
 // Layouts of the per-channel-K kernel with V groups of 32 or 64.
 bool decode_cascade_supported(const TileGeom& g, int G) {
-  return g.d == 128 && g.kg < 0 && !g.mixed && (g.vg == 32 || g.vg == 64) && G >= 1 && G <= 8;
+  return g.d == 128 && g.dv == 128 && g.kg < 0 && !g.mixed && (g.vg == 32 || g.vg == 64) && G >= 1 && G <= 8;
 }
 
 hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {

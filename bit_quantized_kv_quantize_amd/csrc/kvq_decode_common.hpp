@@ -54,8 +54,9 @@ __device__ int count_sentinels(const DecodeArgs& a, int seq, int len, int tid, i
 
 // Final output row of query head j: live slots contribute (M, L, o) (base-2 max, sum of exp2(logit - M),
 // sum of exp2(logit - M) * v; M = -inf and L = 0 when there are none), each of the n_sent sentinel slots
-// contributes logit -1e4 and value 0. Thread c < D holds o for channel c. For a rotated pool the row is
-// multiplied by (1 / (d c)) H, the inverse of the quantiser's rotation. All NT threads must call this.
+// contributes logit -1e4 and value 0. Thread c < D holds o for channel c (D = V's head dim). For a rotated
+// pool the row is multiplied by (1 / (D c)) H, the inverse of the quantiser's rotation of V rows. All NT
+// threads must call this.
 template <int D, int NT>
 __device__ void finalize_head(const TileGeom& g, const DecodeArgs& a, int seq, int j, int len, int n_sent,
                               float M, float L, float o, int tid, float* s_o) {
@@ -84,7 +85,7 @@ __device__ void finalize_head(const TileGeom& g, const DecodeArgs& a, int seq, i
       if (tid < D) s_o[tid] = r;
       __syncthreads();
     }
-    if (tid < D) o = s_o[tid] * a.unrot_c;
+    if (tid < D) o = s_o[tid] * a.unrot_cv;
   }
   if (tid < D) a.out[((size_t)seq * a.num_q_heads + j) * D + tid] = o;
 }

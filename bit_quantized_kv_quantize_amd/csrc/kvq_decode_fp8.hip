@@ -326,7 +326,9 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_k(TileGeom g, DecodeArgs a)
 }  // namespace
 
 // FP8 pools with head_dim 128 and G = 1..8, without a sentinel mask (masked FP8 calls take the generic kernel).
-bool decode_fp8_supported(const TileGeom& g, int G) { return g.fp8 && g.d == 128 && G >= 1 && G <= 8; }
+bool decode_fp8_supported(const TileGeom& g, int G) {
+  return g.fp8 && g.d == 128 && g.dv == 128 && G >= 1 && G <= 8;
+}
 
 hipError_t launch_decode_fp8(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.plan.n_splits, g.H, a.n_seqs);

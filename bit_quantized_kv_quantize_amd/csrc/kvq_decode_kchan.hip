@@ -449,7 +449,7 @@ hipError_t launch_vg(const TileGeom& g, const DecodeArgs& a, hipStream_t stream)
 
 // Layouts with this kernel: head_dim 128, K grouped per channel, V groups of 32 or 64, G = 1..8.
 bool decode_kchan_supported(const TileGeom& g, int G) {
-  return g.d == 128 && g.kg < 0 && (g.vg == 32 || g.vg == 64) && G >= 1 && G <= 8;
+  return g.d == 128 && g.dv == 128 && g.kg < 0 && (g.vg == 32 || g.vg == 64) && G >= 1 && G <= 8;
 }
 
 hipError_t launch_decode_kchan(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {

@@ -425,7 +425,7 @@ hipError_t launch_one(const TileGeom& g, const DecodeArgs& a, hipStream_t stream
 
 // Layouts with a compiled matrix-core kernel: 4-bit pools (not mixed) with per-token K and V groups.
 bool decode_mfma_supported(const TileGeom& g, int G) {
-  if (g.mixed || g.kg <= 0) return false;
+  if (g.mixed || g.kg <= 0 || g.dv != g.d) return false;
   if (g.d == 128 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4 || G == 8;
   if (g.d == 256 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4;
   return false;

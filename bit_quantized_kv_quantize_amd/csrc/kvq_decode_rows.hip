@@ -878,7 +878,7 @@ hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 // Layouts with this kernel: head_dim 128, per-token K and V groups of 64, 4-bit pools and pools of per-token
 // widths, G = 1, 2, 4.
 bool decode_rows_supported(const TileGeom& g, int G) {
-  return g.d == 128 && g.kg == 64 && g.vg == 64 && !g.fp8 && (G == 1 || G == 2 || G == 4);
+  return g.d == 128 && g.dv == 128 && g.kg == 64 && g.vg == 64 && !g.fp8 && (G == 1 || G == 2 || G == 4);
 }
 
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {

@@ -12,12 +12,13 @@ namespace kvq {
 constexpr int kRows = 256;  // tokens per block (the block pool of "Agent Memory Below the Prompt", 2.1)
 
 // Byte geometry of one tile, computed once on the host and passed to kernels by value. A tile holds 256
-// row records (the K codes of one token immediately followed by its V codes, d * width / 8 bytes each;
-// the rest of a 4-bit row's record in a mixed pool is zero), the per-channel K parameters when K is grouped per
-// channel, 256 parameter records (K groups then V groups of one token, each {fp16 scale, fp16 zero}),
-// the width bitmap of mixed pools, and zero padding to a multiple of 256 bytes.
+// row records (the K codes of one token, d * width / 8 bytes, immediately followed by its V codes,
+// dv * width / 8 bytes; the rest of a narrower row's record is zero), the per-channel K parameters when K
+// is grouped per channel, 256 parameter records (K groups then V groups of one token, each {fp16 scale,
+// fp16 zero}), the width header of pools with per-token widths, and zero padding to a multiple of 256 bytes.
 struct TileGeom {
-  int d;            // head_dim
+  int d;            // K's head dim (and the query's)
+  int dv;           // V's head dim (and the output's); d unless the layout gives another
   int H;            // KV heads
   int kg;           // K group (channels) or -1 for one group per channel over the block
   int vg;           // V group (channels)
@@ -25,10 +26,9 @@ struct TileGeom {
   int mixed;        // 1: per-token 4/8-bit rows, 32-byte bitmap at off_hdr; 2: per-token widths 2/4/8/16,
                     // a 2-bit width code per row in a 64-byte header at off_hdr
   int fp8;          // FP8 E4M3 per element: records of d K bytes then d V bytes, no parameters
-  int slot;         // code bytes of one row of K (or V): d/2, or d in mixed pools
-  int rec;          // bytes of one row record (2 * slot)
+  int rec;          // bytes of one row record: K and V at the pool's widest width, (d + dv) * w / 8
   int kpr;          // K param entries per row (d / kg), 0 for per-channel K
-  int vpr;          // V param entries per row (d / vg)
+  int vpr;          // V param entries per row (dv / vg)
   int prow;         // bytes of one parameter record ((kpr + vpr) * 4)
   uint32_t off_kch; // per-channel K params, d entries (kg < 0 only)
   uint32_t off_prow;// parameter record of row 0
@@ -117,16 +117,18 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 
 // Launchers (defined next to their kernels). They return hipSuccess or the launch error.
+// rot_c / unrot_c apply to K rows, rot_cv / unrot_cv to V rows (they differ when the head dims do).
 hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                                   const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
-                                  float rot_c, hipStream_t stream);
+                                  float rot_c, float rot_cv, hipStream_t stream);
 hipError_t launch_dequantize_blocks(const TileGeom& g, const uint8_t* pool, const int32_t* block_ids, int n_blocks,
-                                    uint16_t* k_out, uint16_t* v_out, float unrot_c, hipStream_t stream);
+                                    uint16_t* k_out, uint16_t* v_out, float unrot_c, float unrot_cv,
+                                    hipStream_t stream);
 hipError_t launch_copy_blocks(const TileGeom& g, const uint8_t* src, const int32_t* src_ids, uint8_t* dst,
                               const int32_t* dst_ids, int n_blocks, hipStream_t stream);
 hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, const uint16_t* k,
                                 const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
-                                const int32_t* positions, const uint8_t* prec, float rot_c,
+                                const int32_t* positions, const uint8_t* prec, float rot_c, float rot_cv,
                                 hipStream_t stream);
 
 struct DecodeArgs {
@@ -153,7 +155,8 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int mask_words;
   float q_scale;   // softmax_scale * log2(e): logits are kept in base-2 units
-  float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale
+  float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale of K rows
+  float unrot_cv;  // the same for V rows (dv in place of d)
   SplitPlan plan;
 };
 // Decode dispatch: the row-list matrix-core kernel (per-token K groups) or the per-channel-K matrix-core

@@ -12,6 +12,8 @@
 // FMA contraction is disabled for this file (contraction would change the rounding of those steps).
 #pragma clang fp contract(off)
 
+#include <type_traits>
+
 #include "kvq_internal.hpp"
 
 namespace kvq {
@@ -187,7 +189,8 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
   const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 8;
   const int grp = kv ? g.vg : g.kg;
   const uint32_t* bitmap = prec_bits ? prec_bits + (size_t)i * (g.header_bytes() / 4) : nullptr;
-  for (int t = r0; t < kRows; t += kRowsPerPass) {
+  // (with d = 192, 24 lanes per row, the last 16 threads hold no row)
+  for (int t = r0 < kRowsPerPass ? r0 : kRows; t < kRows; t += kRowsPerPass) {
     float x[8];
     load8(src + (size_t)t * g.H * D, x);
     if (g.fp8) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
     }
     const int bits = g.mixed == 2 ? (2 << (bitmap ? (bitmap[t >> 4] >> (2 * (t & 15))) & 3u : 1u))
                                   : (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
-    quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - 2 * D * bits / 8 : 0,
+    quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - (g.d + g.dv) * bits / 8 : 0,
                             tile + (kv ? g.vcode(t, bits) : g.kcode(t)), tile + (kv ? g.vpar(t) : g.kpar(t)),
                             rot_c);
   }
@@ -286,15 +289,16 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
   }
 }
 
-// Grid (n_seqs, H, 2), LPR threads: row positions[s] % 256 of block block_table[s][positions[s] / 256].
+// Grid (n_seqs, H, tensors), LPR threads: row positions[s] % 256 of block block_table[s][positions[s] / 256];
+// tensor kv_base + blockIdx.z (0 = K, 1 = V) of head dim D = 8 LPR.
 template <int LPR>
 __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict__ pool,
                                                 const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                 const int32_t* __restrict__ block_table, int max_blocks_per_seq,
                                                 const int32_t* __restrict__ positions,
-                                                const uint8_t* __restrict__ prec, float rot_c) {
+                                                const uint8_t* __restrict__ prec, float rot_c, int kv_base) {
   constexpr int D = LPR * 8;
-  const int s = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+  const int s = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
   const int li = threadIdx.x;
   const int p = positions[s];
   const int row = p % kRows;
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
     fp8_token_row<LPR>(g, x, li, tile + (kv ? g.vcode(row, 8) : g.kcode(row)), rot_c);
     return;
   }
-  quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - 2 * D * bits / 8 : 0,
+  quantize_token_row<LPR>(g, x, li, grp, bits, kv && g.mixed ? g.rec - (g.d + g.dv) * bits / 8 : 0,
                           tile + (kv ? g.vcode(row, bits) : g.kcode(row)), tile + (kv ? g.vpar(row) : g.kpar(row)),
                           rot_c);
   if (g.mixed == 1 && kv == 0 && li == 0) {
@@ -330,16 +334,16 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
 template <int LPR>
 hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                              const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, float rot_c,
-                             hipStream_t stream) {
-  if (g.kg > 0 || g.fp8) {
-    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, 2), dim3(256), 0, stream, g, pool, block_ids,
-                       k, v, prec_bits, rot_c, 0);
-  } else {
+                             int kv_base, int n_tensors, hipStream_t stream) {
+  if (kv_base == 0 && !(g.kg > 0 || g.fp8)) {  // per-channel K first, then the V rows
     hipLaunchKernelGGL(quantize_kchan_k<LPR>, dim3(n_blocks, g.H, 1), dim3(256), 0, stream, g, pool,
                        block_ids, k, rot_c);
-    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, 1), dim3(256), 0, stream, g, pool, block_ids,
-                       k, v, prec_bits, rot_c, 1);
+    kv_base = 1;
+    n_tensors -= 1;
   }
+  if (n_tensors > 0)
+    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
+                       block_ids, k, v, prec_bits, rot_c, kv_base);
   return hipGetLastError();
 }
 
@@ -352,9 +356,9 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
 template <int LPR>
 __global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* __restrict__ pool,
                                                    const int32_t* __restrict__ block_ids, uint16_t* __restrict__ k_out,
-                                                   uint16_t* __restrict__ v_out, float unrot_c) {
+                                                   uint16_t* __restrict__ v_out, float unrot_c, int which_base) {
   constexpr int RPP = 256 / LPR;  // rows per pass
-  const int h = blockIdx.y, which = blockIdx.z;
+  const int h = blockIdx.y, which = blockIdx.z + which_base;
   const uint8_t* tile = pool + ((size_t)block_ids[blockIdx.x] * g.H + h) * g.tile_bytes;
   const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
   uint16_t* out = which ? v_out : k_out;
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* _
       cz[i] = h2f(pr >> 16);
     }
   }
-  for (int t = r0; t < kRows; t += RPP) {
+  for (int t = r0 < RPP ? r0 : kRows; t < kRows; t += RPP) {  // (24 lanes per row at d = 192: 16 idle threads)
     float x[8];
     if (g.fp8) {  // E4M3 -> fp32 is exact
       const uint2 w = *reinterpret_cast<const uint2*>(tile + (which ? g.vcode(t, 8) : g.kcode(t)) + li * 8);
@@ -436,56 +440,53 @@ __global__ __launch_bounds__(256) void dequantize_k(TileGeom g, const uint8_t* _
 
 }  // namespace
 
+// One launch per tensor when K and V head dims differ (D = 8 LPR is the tensor's own), one for both otherwise.
+template <class F>
+static hipError_t per_tensor(const TileGeom& g, F&& launch) {
+  auto one = [&](int dim, int kv_base, int n_tensors) -> hipError_t {
+    switch (dim) {
+      case 64: return launch(std::integral_constant<int, 8>{}, kv_base, n_tensors);
+      case 128: return launch(std::integral_constant<int, 16>{}, kv_base, n_tensors);
+      case 192: return launch(std::integral_constant<int, 24>{}, kv_base, n_tensors);
+      case 256: return launch(std::integral_constant<int, 32>{}, kv_base, n_tensors);
+    }
+    return hipErrorInvalidValue;
+  };
+  if (g.dv == g.d) return one(g.d, 0, 2);
+  const hipError_t e = one(g.d, 0, 1);
+  return e != hipSuccess ? e : one(g.dv, 1, 1);
+}
+
 hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                                   const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
-                                  float rot_c, hipStream_t stream) {
-  switch (g.d) {
-    case 64: return launch_quantize_t<8>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
-    case 128: return launch_quantize_t<16>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
-    case 256: return launch_quantize_t<32>(g, pool, block_ids, n_blocks, k, v, prec_bits, rot_c, stream);
-  }
-  return hipErrorInvalidValue;
+                                  float rot_c, float rot_cv, hipStream_t stream) {
+  return per_tensor(g, [&](auto lpr, int kv_base, int n_tensors) {
+    return launch_quantize_t<decltype(lpr)::value>(g, pool, block_ids, n_blocks, k, v, prec_bits,
+                                                   kv_base ? rot_cv : rot_c, kv_base, n_tensors, stream);
+  });
 }
 
 hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, const uint16_t* k,
                                 const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
-                                const int32_t* positions, const uint8_t* prec, float rot_c,
+                                const int32_t* positions, const uint8_t* prec, float rot_c, float rot_cv,
                                 hipStream_t stream) {
-  dim3 grid(n_seqs, g.H, 2);
-  switch (g.d) {
-    case 64:
-      hipLaunchKernelGGL(append_k<8>, grid, dim3(8), 0, stream, g, pool, k, v, block_table, max_blocks_per_seq,
-                         positions, prec, rot_c);
-      break;
-    case 128:
-      hipLaunchKernelGGL(append_k<16>, grid, dim3(16), 0, stream, g, pool, k, v, block_table,
-                         max_blocks_per_seq, positions, prec, rot_c);
-      break;
-    case 256:
-      hipLaunchKernelGGL(append_k<32>, grid, dim3(32), 0, stream, g, pool, k, v, block_table,
-                         max_blocks_per_seq, positions, prec, rot_c);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return per_tensor(g, [&](auto lpr, int kv_base, int n_tensors) {
+    constexpr int LPR = decltype(lpr)::value;
+    hipLaunchKernelGGL(append_k<LPR>, dim3(n_seqs, g.H, n_tensors), dim3(LPR), 0, stream, g, pool, k, v,
+                       block_table, max_blocks_per_seq, positions, prec, kv_base ? rot_cv : rot_c, kv_base);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_dequantize_blocks(const TileGeom& g, const uint8_t* pool, const int32_t* block_ids, int n_blocks,
-                                    uint16_t* k_out, uint16_t* v_out, float unrot_c, hipStream_t stream) {
-  const dim3 grid(n_blocks, g.H, 2);
-  switch (g.d) {
-    case 64:
-      hipLaunchKernelGGL(dequantize_k<8>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
-      break;
-    case 128:
-      hipLaunchKernelGGL(dequantize_k<16>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
-      break;
-    case 256:
-      hipLaunchKernelGGL(dequantize_k<32>, grid, dim3(256), 0, stream, g, pool, block_ids, k_out, v_out, unrot_c);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+                                    uint16_t* k_out, uint16_t* v_out, float unrot_c, float unrot_cv,
+                                    hipStream_t stream) {
+  return per_tensor(g, [&](auto lpr, int kv_base, int n_tensors) {
+    constexpr int LPR = decltype(lpr)::value;
+    hipLaunchKernelGGL(dequantize_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool, block_ids,
+                       k_out, v_out, kv_base ? unrot_cv : unrot_c, kv_base);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace kvq

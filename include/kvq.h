@@ -26,13 +26,14 @@
  * Pool layout (the block pool of [AMB] 2.1 item 1 with the Q4 format of [AMB] 2.1 item 2)
  *   A pool holds num_blocks * H_kv tiles; tile (b, h) starts at byte (b * H_kv + h) * kvq_tile_bytes().
  *   A tile holds the 256 token rows of one KV head of one block, in this order (R = 256, d = head_dim,
- *   S = d/2; d in mixed = 1 pools; 2d in mixed = 2 pools):
- *     row records   R x 2S bytes: record t at t * 2S holds row t's K codes (d * b / 8 bytes, b = the row's
- *                   width: 4; 4 or 8; 2, 4, 8 or 16) immediately followed by its V codes (d * b / 8
- *                   bytes); the rest of a narrower row's record is zero. A 16-bit row holds the (rotated)
- *                   values themselves as fp16, and its parameter record is zero
+ *   dv = V's head dim (v_head_dim, else d), w = the pool's widest width: 4; 8 in mixed = 1 and FP8 pools;
+ *   16 in mixed = 2 pools):
+ *     row records   R x S bytes, S = (d + dv) * w / 8: record t at t * S holds row t's K codes (d * b / 8
+ *                   bytes, b = the row's width: 4; 4 or 8; 2, 4, 8 or 16) immediately followed by its V
+ *                   codes (dv * b / 8 bytes); the rest of a narrower row's record is zero. A 16-bit row
+ *                   holds the (rotated) values themselves as fp16, and its parameter record is zero
  *     K per channel when k_group == -1: d x 4 bytes, [c] {scale, zero}
- *     param records R x P bytes, P = 4 * (d / k_group + d / v_group) (4 * d / v_group when K is grouped
+ *     param records R x P bytes, P = 4 * (d / k_group + dv / v_group) (4 * dv / v_group when K is grouped
  *                   per channel): record t holds row t's K params [group] {scale, zero}, then its V params
  *     header        mixed = 1: 8 x uint32, bit (t % 32) of word (t / 32) set = row t holds 8-bit codes;
  *                   mixed = 2: 16 x uint32, bits 2 (t % 16) .. 2 (t % 16) + 1 of word t / 16 = row t's width
@@ -77,13 +78,14 @@ enum kvq_status {
 /* Geometry and codec options of one pool (the per-architecture cache shape of [AMB] 2.2).
  * Passed by pointer; the library copies it on every call. */
 typedef struct kvq_layout {
-  int32_t head_dim;     /* d: 64, 128 or 256 */
+  int32_t head_dim;     /* d, K's (and the query's) head dim: 64, 128 or 256; 192 with v_head_dim 128 */
   int32_t num_kv_heads; /* H_kv >= 1 */
   int32_t block_tokens; /* rows per block; must be 256 ([AMB] 2.1 item 1) */
-  int32_t k_group;      /* > 0: K groups are k_group consecutive channels of one token (32, 64 or 128,
-                           dividing d); -1: one K group per channel spanning the block's 256 rows
+  int32_t k_group;      /* > 0: K groups are k_group consecutive channels of one token (8 .. 256, a power
+                           of two dividing d); -1: one K group per channel spanning the block's 256 rows
                            (asymmetric K/V grouping, [UQ] technology section) */
-  int32_t v_group;      /* > 0: V groups are v_group consecutive channels of one token (32, 64 or 128) */
+  int32_t v_group;      /* > 0: V groups are v_group consecutive channels of one token (8 .. 256, a power
+                           of two dividing dv) */
   int32_t rotate;       /* 0 or 1: Walsh-Hadamard rotation of every K and V row before quantisation */
   int32_t mixed;        /* 0: every row 4-bit; 1: each token row is 4-bit or 8-bit; 2: each token row is
                            2-, 4-, 8-bit or FP16 - the per-token widths of [QKV] methodology section.
@@ -94,6 +96,11 @@ typedef struct kvq_layout {
                            records of d K bytes then d V bytes (no parameters), padded to 256 bytes; each
                            (optionally rotated) fp32 value becomes E4M3 ("fn": bias 7, no infinities) by
                            rounding to nearest even, magnitudes of 448 and more saturating to 448. */
+  int32_t v_head_dim;   /* dv, V's (and the output's) head dim when it differs from K's, as in MLA models
+                           ([AMB] 2.2: K and V head dims differ, e.g. DeepSeek-Coder-V2-Lite); 0 means
+                           head_dim. Unequal dims: head_dim 192 or 256 with v_head_dim 128, per-token K
+                           groups, format 0; rotation needs power-of-two dims (each tensor is rotated at
+                           its own length). Other pairs return KVQ_ERR_UNSUPPORTED. */
 } kvq_layout;
 
 /* KVQ_OK if the layout is one this library can store and process, else the status explaining why. */
@@ -123,8 +130,8 @@ const char* kvq_status_string(int status);
  *   block_ids  device int32 [n_blocks]: physical block receiving input block i. Ids must be distinct
  *              and < the pool's block count (trusted).
  *   n_blocks   >= 0 (0 is a no-op).
- *   k, v       device fp16 [n_blocks * 256][H_kv][d], token-major: row t of input block i for head h
- *              starts at element ((i * 256 + t) * H_kv + h) * d.
+ *   k, v       device fp16 k [n_blocks * 256][H_kv][d] and v [n_blocks * 256][H_kv][dv], token-major: row t
+ *              of input block i for head h starts at element ((i * 256 + t) * H_kv + h) * d (dv for v).
  *   prec_bits  device uint32 [n_blocks][W] or NULL, the widths of each block's rows (K and V, every head)
  *              in the header's own encoding: mixed = 1, W = 8, bit (t % 32) of word t / 32 set = token t
  *              of block i is 8-bit; mixed = 2, W = 16, bits 2 (t % 16) of word t / 16 = token t's width
@@ -143,7 +150,7 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
  * kvq_quantize_blocks on a single row.
  *
  *   n_seqs       >= 0.
- *   k, v         device fp16 [n_seqs][H_kv][d].
+ *   k, v         device fp16 k [n_seqs][H_kv][d], v [n_seqs][H_kv][dv].
  *   block_table  device int32 [n_seqs][max_blocks_per_seq]: logical block -> physical block.
  *   positions    device int32 [n_seqs]: slot of the new token (usually the old sequence length). The
  *                row written is positions[s] % 256 of block block_table[s][positions[s] / 256], which
@@ -167,9 +174,10 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
  *   block_ids  device int32 [n_blocks]: physical blocks to restore, each < num_blocks.
  *   k_out      device fp16 [n_blocks * 256][H_kv][d]: row t of block_ids[i], KV head h, at
  *              ((i * 256 + t) * H_kv + h) * d - the layout kvq_quantize_blocks reads.
- *   v_out      the same for V.
+ *   v_out      the same for V, with dv channels.
  * Each value is code * scale + zero of its group (per-token or per-channel K groups, the row's own width
- * in mixed pools), un-rotated by (1 / (d c)) H for rotated pools (the inverse of the rotation c H), rounded
+ * in mixed pools), un-rotated by (1 / (n c)) H for rotated pools (the inverse of the rotation c H at the
+ * tensor's length n = d or dv), rounded
  * once to fp16 (round to nearest even). The arithmetic is fp32: a result may differ from the exact value
  * rounded to fp16 by one fp16 ulp.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP.
@@ -209,7 +217,7 @@ int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* sr
  *                  -1e4 and its value row is 0, so its softmax weight underflows to zero while the
  *                  surviving slots keep their positions. mask_words_per_seq >= ceil(max_seq_len / 32).
  *   softmax_scale  logit = softmax_scale * (q . k) for live slots (usually 1/sqrt(d)).
- *   out            device fp32 [n_seqs][num_q_heads][d]: softmax-weighted sum of the dequantised (and,
+ *   out            device fp32 [n_seqs][num_q_heads][dv]: softmax-weighted sum of the dequantised (and,
  *                  for rotated pools, un-rotated) V rows. A sequence with seq_lens[s] == 0 gets zeros.
  *   workspace      device scratch of at least kvq_decode_workspace_bytes(L, n_seqs, num_q_heads,
  *                  max_seq_len) bytes, 256-byte aligned: split-K partials and, in its first

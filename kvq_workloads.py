@@ -25,6 +25,13 @@ in the IntentKV article, per-token bit widths in QKVShare):
   mixed_sentinel_32k   128 seqs x 32768 slots, 32 q / 8 KV heads, d 128, groups of 64, top 20% of tokens
                        by K norm stored 8-bit, 24576 of 32768 slots per sequence remapped to the
                        sentinel (8192 live), then one appended token per sequence.
+
+One more workload for the MLA models "Agent Memory Below the Prompt" lists (technical summary 2.2,
+DeepSeek-Coder-V2-Lite: K and V head dims differ):
+
+  deepseek_v2_lite_mla_8k  12 agents x 8192 tokens, 16 q = 16 KV heads, K head dim 192 (128 + 64 rotary),
+                       V head dim 128, 27 layers, one pool of blocks (permuted tables), groups of 64, no
+                       rotation (192 is not a power of two).
 """
 from __future__ import annotations
 
@@ -65,11 +72,16 @@ class Config:
     fmt: int = 0                # pool format: 0 group-wise codes, 1 FP8 E4M3 per element
     width_fracs: Tuple[float, float, float] = (0.0, 0.0, 0.0)  # mixed = 2 pools: fractions of tokens
     # stored FP16 (largest K norms), 8-bit (the next largest) and 2-bit (the smallest); the rest are 4-bit
+    v_head_dim: int = 0         # V's head dim when it differs from K's (MLA); 0 = head_dim
+
+    @property
+    def dv(self) -> int:
+        return self.v_head_dim or self.head_dim
 
     def layout(self) -> Dict[str, int]:
         return dict(head_dim=self.head_dim, num_kv_heads=self.num_kv_heads, block_tokens=BLOCK,
                     k_group=self.k_group, v_group=self.v_group, rotate=self.rotate, mixed=self.mixed,
-                    format=self.fmt)
+                    format=self.fmt, v_head_dim=self.v_head_dim)
 
 
 CONFIGS: Dict[str, Config] = {
@@ -84,6 +96,13 @@ CONFIGS: Dict[str, Config] = {
     ]
 }
 CONFIG_ORDER: List[str] = [n for n, _ in sorted(CONFIGS.items(), key=lambda kv: kv[1].index)]
+
+EXTRA: Dict[str, Config] = {
+    c.name: c for c in [
+        Config(10, "deepseek_v2_lite_mla_8k", 192, 16, 16, 27, 64, 64, 0, 0, 12, 8192, "perm", True, 4, 10.0,
+               1.0, v_head_dim=128),
+    ]
+}
 
 
 def fp8_variant(cfg: Config) -> Config:
@@ -106,7 +125,7 @@ def named_config(name: str) -> Config:
         return fp8_variant(CONFIGS[name[:-len("_fp8")]])
     if name.endswith("_widths"):
         return widths_variant(CONFIGS[name[:-len("_widths")]])
-    return CONFIGS[name]
+    return CONFIGS[name] if name in CONFIGS else EXTRA[name]
 
 
 def _rng(cfg: Config, layer: int, stream: int, index: int = 0) -> np.random.Generator:
@@ -126,26 +145,26 @@ def _draw_rows(cfg: Config, layer: int, stream_k: int, stream_v: int, index: int
     k = _rng(cfg, layer, stream_k, index).standard_normal(shape, dtype=np.float32)
     for h in range(cfg.num_kv_heads):
         k[:, h, outliers[h]] *= np.float32(cfg.outlier_scale)
-    v = _rng(cfg, layer, stream_v, index).standard_normal(shape, dtype=np.float32)
+    v = _rng(cfg, layer, stream_v, index).standard_normal((n_rows, cfg.num_kv_heads, cfg.dv), dtype=np.float32)
     if cfg.v_std != 1.0:
         v *= np.float32(cfg.v_std)
     return k.astype(np.float16).view(np.uint16), v.astype(np.float16).view(np.uint16)
 
 
 def block_kv(cfg: Config, layer: int, block_id: int, outliers: Optional[np.ndarray] = None):
-    """fp16 bits (K, V), each [256][H_kv][d], of physical block ``block_id`` in ``layer``."""
+    """fp16 bits (K [256][H_kv][d], V [256][H_kv][dv]) of physical block ``block_id`` in ``layer``."""
     if outliers is None:
         outliers = outlier_channels(cfg, layer)
     return _draw_rows(cfg, layer, STREAM_K, STREAM_V, block_id, BLOCK, outliers)
 
 
 def blocks_kv(cfg: Config, layer: int, block_ids: Sequence[int], threads: int = 8):
-    """(K, V) for several physical blocks, concatenated token-major: [len(block_ids) * 256][H_kv][d]."""
+    """(K, V) for several physical blocks, concatenated token-major: [len(block_ids) * 256][H_kv][d or dv]."""
     outl = outlier_channels(cfg, layer)
     ids = [int(b) for b in block_ids]
     n = len(ids)
     k = np.empty((n * BLOCK, cfg.num_kv_heads, cfg.head_dim), np.uint16)
-    v = np.empty_like(k)
+    v = np.empty((n * BLOCK, cfg.num_kv_heads, cfg.dv), np.uint16)
 
     def one(i):
         kb, vb = block_kv(cfg, layer, ids[i], outl)
@@ -162,7 +181,8 @@ def blocks_kv(cfg: Config, layer: int, block_ids: Sequence[int], threads: int = 
 
 
 def append_kv(cfg: Config, layer: int, n_seqs: int, step: int = 0):
-    """fp16 bits (K, V) [n_seqs][H_kv][d] of the token each sequence appends at decode step ``step``."""
+    """fp16 bits (K [n_seqs][H_kv][d], V [n_seqs][H_kv][dv]) of the token each sequence appends at decode
+    step ``step``."""
     k, v = _draw_rows(cfg, layer, STREAM_APPEND, STREAM_APPEND + 100, step, n_seqs,
                       outlier_channels(cfg, layer))
     return k, v
@@ -391,7 +411,7 @@ def prefill_chunks(case: Case, layer: int, max_blocks: int = 2048, threads: int 
             continue
         ids = np.concatenate([sequence_blocks(case, s) for s in seqs]).astype(np.int32)
         k = np.empty((n_blk * BLOCK, cfg.num_kv_heads, cfg.head_dim), np.uint16)
-        v = np.empty_like(k)
+        v = np.empty((n_blk * BLOCK, cfg.num_kv_heads, cfg.dv), np.uint16)
         norms = np.empty(n_blk * BLOCK, np.float64)
 
         def one(i):

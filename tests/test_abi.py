@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(kvq):
 def test_layout_helpers_match_oracle(kvq, orc):
     import kvq_workloads as W
 
-    for cfg in W.CONFIGS.values():
+    for cfg in list(W.CONFIGS.values()) + list(W.EXTRA.values()):
         lay = kvq.Layout(**cfg.layout())
         assert kvq.check_layout(lay) == 0
         olay = orc.make_layout(**cfg.layout())
@@ -61,6 +61,16 @@ def test_layout_validation_and_status(kvq):
     assert kvq.check_layout(kvq.Layout(128, 8, -1, 32, 0, 1)) == kvq.KVQ_ERR_UNSUPPORTED
     assert kvq.check_layout(kvq.Layout(128, 0)) == kvq.KVQ_ERR_ARG
     assert kvq.check_layout(kvq.Layout(128, 8, block_tokens=128)) == kvq.KVQ_ERR_ARG
+    # unequal K and V head dims: K 192 or 256 with V 128, per-token K groups, no rotation at 192
+    assert kvq.check_layout(kvq.Layout(192, 16, 64, 64, v_head_dim=128)) == kvq.KVQ_OK
+    assert kvq.check_layout(kvq.Layout(256, 8, 64, 32, 1, v_head_dim=128)) == kvq.KVQ_OK
+    assert kvq.check_layout(kvq.Layout(192, 16, 64, 64, 1, v_head_dim=128)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(192, 16, 64, 64)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(128, 8, 64, 32, v_head_dim=192)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(192, 16, -1, 32, v_head_dim=128)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(192, 16, 128, 64, v_head_dim=128)) == kvq.KVQ_ERR_ARG  # 128 does not divide 192
+    assert kvq.check_layout(kvq.Layout(192, 16, 0, 0, format=1, v_head_dim=128)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.check_layout(kvq.Layout(128, 8, v_head_dim=-1)) == kvq.KVQ_ERR_ARG
     assert kvq.tile_bytes(kvq.Layout(96, 8)) == 0
     assert kvq.decode_workspace_bytes(kvq.Layout(128, 8), 4, 12, 100) == 0   # 12 % 8 != 0
     for st in (0, -1, -2, -3, -4, -99):
@@ -105,7 +115,8 @@ def test_workspace_bytes_never_shrink_with_size(kvq):
     # A workspace sized for (n_seqs, max_seq_len) serves every call with no more sequences and no longer
     # maximum length (include/kvq.h), across the split plans of every decode kernel.
     layouts = [kvq.Layout(128, 8, 64, 64), kvq.Layout(128, 8, -1, 32, 1, 0), kvq.Layout(256, 8, 64, 64),
-               kvq.Layout(128, 8, 64, 64, 0, 1), kvq.Layout(128, 2, -1, 64), kvq.Layout(64, 4, 32, 32)]
+               kvq.Layout(128, 8, 64, 64, 0, 1), kvq.Layout(128, 2, -1, 64), kvq.Layout(64, 4, 32, 32),
+               kvq.Layout(128, 8, 64, 64, 0, 2), kvq.Layout(192, 16, 64, 64, v_head_dim=128)]
     lens = [0, 1, 255, 256, 1000, 4096, 8193, 32768, 100000, 300000]
     seqs = [1, 2, 3, 5, 12, 40, 64, 128, 300, 1000]
     for lay in layouts:

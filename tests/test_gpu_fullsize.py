@@ -26,6 +26,7 @@ FULL = {
     "llama31_8b_pool_8k": ([0, 31], [0, 5, 11]),
     "qwen25_14b_prefix_32k": ([0], [0, 37, 63]),
     "mixed_sentinel_32k": ([0], [0, 77, 127]),
+    "deepseek_v2_lite_mla_8k": ([0, 26], [0, 5, 11]),
 }
 
 
@@ -109,10 +110,11 @@ def oracle_sample(orc, case, layer, seqs):
 
 
 @pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8", "llama31_8b_pool_8k_widths",
-                                                   "mixed_sentinel_32k_widths"])
+                                                   "mixed_sentinel_32k_widths", "deepseek_v2_lite_mla_8k"])
 def test_full_size_sampled(env, orc, name):
     # (the last cases: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against,
-    # and two workloads stored with per-token widths {2, 4, 8, FP16})
+    # two workloads stored with per-token widths {2, 4, 8, FP16}, and an MLA model's pool: K head dim 192,
+    # V head dim 128)
     kvq, torch = env
     base = name.replace("_fp8", "").replace("_widths", "")
     layers, seqs = FULL[base]

@@ -388,3 +388,38 @@ def test_row_lists_of_a_sequence_past_256k_slots(env, orc, mixed):
     err = rel_err(got, ref)
     print("long sequence mixed=%d: max rel err %.3g" % (mixed, err))
     assert err <= TOL
+
+
+MLA_VARIANTS = [  # K head dim, rotate, mixed, k_group, v_group, G (V head dim 128)
+    (192, 0, 0, 64, 64, 1), (192, 0, 2, 64, 32, 2), (256, 1, 0, 64, 32, 4), (256, 1, 1, 32, 64, 1),
+    (192, 0, 1, 32, 128, 16), (192, 0, 0, 8, 16, 3)]
+
+
+@pytest.mark.parametrize("variant", MLA_VARIANTS)
+def test_unequal_head_dims(env, orc, variant):
+    # MLA layouts (K and V head dims differ): pool bytes (quantise and append) bit-exact, decode within
+    # tolerance over ragged lengths with sentinel slots (one sequence all sentinel), restore within one ulp.
+    kvq, torch = env
+    d, rotate, mixed, kg, vg, G = variant
+    H = 2
+    cfg = W.Config(9, "mla", d, H * G, H, 1, kg, vg, rotate, mixed, 6, 0, "perm", True, 3, 10.0, 1.0,
+                   dead_fraction=0.5, top_fraction=0.2 if mixed == 1 else 0.0,
+                   width_fracs=(0.1, 0.2, 0.3) if mixed == 2 else (0.0, 0.0, 0.0), v_head_dim=128)
+    case = W.make_case(cfg, context=[0, 1, 255, 256, 700, 1500])
+    case.sentinel_mask[4] = 0xFFFFFFFF
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    diff = np.nonzero(got_pool != ref_pool)[0]
+    assert diff.size == 0, "first differing bytes at %s" % diff[:16]
+    assert got.shape == (6, H * G, 128)
+    err = rel_err(got, ref)
+    print("mla d=%d rotate=%d mixed=%d kg=%d vg=%d G=%d: max rel err %.3g" % (d, rotate, mixed, kg, vg, G, err))
+    assert err <= TOL
+    assert not got[4].any()                                  # every slot remapped to the sentinel
+    ids = np.unique(case.prefill_blocks).astype(np.int32)
+    kr, vr = orc.dequantize_blocks(orc.make_layout(**cfg.layout()), ref_pool, ids)
+    kg_, vg_ = kvq.dequantize_blocks(kvq.Layout(**cfg.layout()), to_dev(got_pool, torch), to_dev(ids, torch))
+    for g_, r_ in ((kg_, kr), (vg_, vr)):
+        u = _f16_ulps(g_.cpu().numpy().view(np.uint16), r_)
+        assert u.max() <= 1 and (u > 0).mean() < 1e-3
