@@ -27,23 +27,25 @@ namespace {
 using namespace dec;
 
 // Grid (n_splits, H_kv, n_seqs), 256 threads = 4 waves; wave w owns rows 64w .. 64w+63 of each block.
-template <int D, int G, int KG, int VG>
-__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom g, DecodeArgs a) {
+// D = K's head dim (and the query's), DV = V's (and the output's): 128/128, 256/256 or, for MLA pools,
+// 192/128.
+template <int D, int DV, int G, int KG, int VG>
+__global__ __launch_bounds__(256, D >= 192 ? 1 : 2) void decode_mfma_k(TileGeom g, DecodeArgs a) {
   constexpr int NGK = D / KG;      // K groups per row
-  constexpr int NGV = D / VG;      // V groups per row
+  constexpr int NGV = DV / VG;     // V groups per row
   constexpr int HPL = (G + 3) / 4; // query heads per 16-lane row group
   static_assert(HPL * NGK <= 4 && HPL * NGV <= 4, "MFMA rows: heads x groups per lane group <= 4");
   constexpr int KW = D / 32;       // K words per lane per row = QK k-steps
-  constexpr int VW = D / 128;      // V words per lane per row
+  constexpr int VW = DV / 128;     // V words per lane per row
   constexpr int NTILE = 8 * VW;    // PV output tiles of 16 channels
   constexpr int PSTR = 72;         // LDS row stride (halves) of the p * v_scale tiles
-  static_assert(D == 128 || D == 256, "head_dim 128 or 256");
+  static_assert((D == 128 || D == 192 || D == 256) && (DV == 128 || DV == 256), "head dims");
 
   __shared__ float s_q[G][D];
   __shared__ float s_qsum[G][NGK];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][2][16][PSTR];  // [wave][hi, lo][row][token]
   __shared__ float s_wm[4][G], s_wl[4][G];
-  __shared__ float s_wacc[4][G][D];
+  __shared__ float s_wacc[4][G][DV];
   __shared__ int s_tbl[kMaxSplitBlocks];
   __shared__ uint32_t s_mask[kMaxSplitBlocks * (kRows / 32)];
 
@@ -61,16 +63,16 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
       __shared__ int s_cnt0[4];
       const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt0);
       for (int jj = 0; jj < G; ++jj)
-        finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, kNegInf, 0.0f, 0.0f, tid, &s_wacc[0][0][0]);
+        finalize_head<DV, 256>(g, a, seq, h * G + jj, len, n_sent, kNegInf, 0.0f, 0.0f, tid, &s_wacc[0][0][0]);
     } else {
       if (tid < G) {
         s_wm[0][tid] = kNegInf;
         s_wl[0][tid] = 0.0f;
       }
-      for (int i = tid; i < G * D; i += 256) s_wacc[1][i / D][i % D] = 0.0f;
+      for (int i = tid; i < G * DV; i += 256) s_wacc[1][i / DV][i % DV] = 0.0f;
       __syncthreads();
-      splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
-                          &s_wacc[0][0][0]);
+      splitk_arrive<DV, G>(g, a, seq, h, split, ns, len, tid, &s_wm[0][0], &s_wl[0][0], &s_wacc[1][0][0],
+                           &s_wacc[0][0][0]);
     }
     return;
   }
@@ -92,14 +94,24 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int row = r0 + 16 * c + lj;
-      const uint4* kp = reinterpret_cast<const uint4*>(tile + g.kcode(row) + la * KW * 4);
+      if constexpr (KW % 4 == 0) {
+        const uint4* kp = reinterpret_cast<const uint4*>(tile + g.kcode(row) + la * KW * 4);
 #pragma unroll
-      for (int q4 = 0; q4 < KW / 4; ++q4) {
-        const uint4 v4 = kp[q4];
-        r.kraw[c][4 * q4 + 0] = v4.x;
-        r.kraw[c][4 * q4 + 1] = v4.y;
-        r.kraw[c][4 * q4 + 2] = v4.z;
-        r.kraw[c][4 * q4 + 3] = v4.w;
+        for (int q4 = 0; q4 < KW / 4; ++q4) {
+          const uint4 v4 = kp[q4];
+          r.kraw[c][4 * q4 + 0] = v4.x;
+          r.kraw[c][4 * q4 + 1] = v4.y;
+          r.kraw[c][4 * q4 + 2] = v4.z;
+          r.kraw[c][4 * q4 + 3] = v4.w;
+        }
+      } else {  // 6 words (K head dim 192): three 8-byte loads
+        const uint2* kp = reinterpret_cast<const uint2*>(tile + g.kcode(row) + la * KW * 4);
+#pragma unroll
+        for (int q2 = 0; q2 < KW / 2; ++q2) {
+          const uint2 v2 = kp[q2];
+          r.kraw[c][2 * q2 + 0] = v2.x;
+          r.kraw[c][2 * q2 + 1] = v2.y;
+        }
       }
       const uint32_t* kpp = reinterpret_cast<const uint32_t*>(tile + g.kpar(row));
       const uint32_t* vpp = reinterpret_cast<const uint32_t*>(tile + g.vpar(row));
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
   if (ns == 1) {
     // the whole sequence was this workgroup's: finalise the rows here
     __shared__ int s_cnt[4];
-    __shared__ float s_o[D];
+    __shared__ float s_o[DV];
     const int n_sent = count_sentinels<256>(a, seq, len, tid, s_cnt);
     for (int jj = 0; jj < G; ++jj) {
       float M = kNegInf;
@@ -378,19 +390,19 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
           const float sc_w = exp2f(s_wm[ww][jj] - M);
-          if (tid < D) acc += s_wacc[ww][jj][tid] * sc_w;
+          if (tid < DV) acc += s_wacc[ww][jj][tid] * sc_w;
           L += s_wl[ww][jj] * sc_w;
         }
       }
-      finalize_head<D, 256>(g, a, seq, h * G + jj, len, n_sent, M, L, acc, tid, s_o);
+      finalize_head<DV, 256>(g, a, seq, h * G + jj, len, n_sent, M, L, acc, tid, s_o);
     }
     return;
   }
   // merge the four waves into this split's partials (staged in LDS), then arrive
   __shared__ float s_pm[G], s_pl[G];
-  __shared__ float s_pacc[G][D];
-  for (int i = tid; i < G * D; i += 256) {
-    const int jj = i / D, c = i % D;
+  __shared__ float s_pacc[G][DV];
+  for (int i = tid; i < G * DV; i += 256) {
+    const int jj = i / DV, c = i % DV;
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, s_wm[ww][jj]);
@@ -410,40 +422,47 @@ __global__ __launch_bounds__(256, D == 256 ? 1 : 2) void decode_mfma_k(TileGeom 
     }
   }
   __syncthreads();
-  splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
+  splitk_arrive<DV, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 
-template <int D, int G, int KG, int VG>
+template <int D, int DV, int G, int KG, int VG>
 hipError_t launch_one(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mfma_k<D, G, KG, VG>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0, stream,
-                     g, a);
-
+  hipLaunchKernelGGL((decode_mfma_k<D, DV, G, KG, VG>), dim3(a.plan.n_splits, g.H, a.n_seqs), dim3(256), 0,
+                     stream, g, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Layouts with a compiled matrix-core kernel: 4-bit pools (not mixed) with per-token K and V groups.
+// Layouts with a compiled matrix-core kernel: 4-bit pools (not mixed) with per-token K and V groups of 64;
+// head dims 128, 256, or K 192 with V 128 (MLA).
 bool decode_mfma_supported(const TileGeom& g, int G) {
-  if (g.mixed || g.kg <= 0 || g.dv != g.d) return false;
-  if (g.d == 128 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4 || G == 8;
-  if (g.d == 256 && g.kg == 64 && g.vg == 64) return G == 1 || G == 2 || G == 4;
+  if (g.mixed || g.kg != 64 || g.vg != 64) return false;
+  if (g.d == 128 && g.dv == 128) return G == 1 || G == 2 || G == 4 || G == 8;
+  if (g.d == 256 && g.dv == 256) return G == 1 || G == 2 || G == 4;
+  if (g.d == 192 && g.dv == 128) return G == 1 || G == 2 || G == 4;
   return false;
 }
 
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   if (g.d == 128) {
     switch (a.G) {
-      case 1: return launch_one<128, 1, 64, 64>(g, a, stream);
-      case 2: return launch_one<128, 2, 64, 64>(g, a, stream);
-      case 4: return launch_one<128, 4, 64, 64>(g, a, stream);
-      case 8: return launch_one<128, 8, 64, 64>(g, a, stream);
+      case 1: return launch_one<128, 128, 1, 64, 64>(g, a, stream);
+      case 2: return launch_one<128, 128, 2, 64, 64>(g, a, stream);
+      case 4: return launch_one<128, 128, 4, 64, 64>(g, a, stream);
+      case 8: return launch_one<128, 128, 8, 64, 64>(g, a, stream);
     }
   } else if (g.d == 256) {
     switch (a.G) {
-      case 1: return launch_one<256, 1, 64, 64>(g, a, stream);
-      case 2: return launch_one<256, 2, 64, 64>(g, a, stream);
-      case 4: return launch_one<256, 4, 64, 64>(g, a, stream);
+      case 1: return launch_one<256, 256, 1, 64, 64>(g, a, stream);
+      case 2: return launch_one<256, 256, 2, 64, 64>(g, a, stream);
+      case 4: return launch_one<256, 256, 4, 64, 64>(g, a, stream);
+    }
+  } else if (g.d == 192) {
+    switch (a.G) {
+      case 1: return launch_one<192, 128, 1, 64, 64>(g, a, stream);
+      case 2: return launch_one<192, 128, 2, 64, 64>(g, a, stream);
+      case 4: return launch_one<192, 128, 4, 64, 64>(g, a, stream);
     }
   }
   return hipErrorInvalidValue;

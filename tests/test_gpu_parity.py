@@ -391,12 +391,12 @@ def test_row_lists_of_a_sequence_past_256k_slots(env, orc, mixed):
 
 
 MLA_VARIANTS = [  # K head dim, rotate, mixed, k_group, v_group, G (V head dim 128)
-    (192, 0, 0, 64, 64, 1), (192, 0, 2, 64, 32, 2), (256, 1, 0, 64, 32, 4), (256, 1, 1, 32, 64, 1),
-    (192, 0, 1, 32, 128, 16), (192, 0, 0, 8, 16, 3)]
+    (192, 0, 0, 64, 64, 1), (192, 0, 0, 64, 64, 2), (192, 0, 0, 64, 64, 4), (192, 0, 2, 64, 32, 2),
+    (256, 1, 0, 64, 32, 4), (256, 1, 1, 32, 64, 1), (192, 0, 1, 32, 128, 16), (192, 0, 0, 8, 16, 3)]
 
 
 @pytest.mark.parametrize("variant", MLA_VARIANTS)
-def test_unequal_head_dims(env, orc, variant):
+def test_unequal_head_dims(env, orc, variant, decode_path):
     # MLA layouts (K and V head dims differ): pool bytes (quantise and append) bit-exact, decode within
     # tolerance over ragged lengths with sentinel slots (one sequence all sentinel), restore within one ulp.
     kvq, torch = env
@@ -414,7 +414,8 @@ def test_unequal_head_dims(env, orc, variant):
     assert diff.size == 0, "first differing bytes at %s" % diff[:16]
     assert got.shape == (6, H * G, 128)
     err = rel_err(got, ref)
-    print("mla d=%d rotate=%d mixed=%d kg=%d vg=%d G=%d: max rel err %.3g" % (d, rotate, mixed, kg, vg, G, err))
+    print("mla d=%d rotate=%d mixed=%d kg=%d vg=%d G=%d [%s]: max rel err %.3g" % (d, rotate, mixed, kg, vg, G,
+                                                                              decode_path, err))
     assert err <= TOL
     assert not got[4].any()                                  # every slot remapped to the sentinel
     ids = np.unique(case.prefill_blocks).astype(np.int32)
