@@ -360,7 +360,7 @@ def main():
         "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "decode_rows_k<4, false>", "bytes_per_launch": dec_b,
+                     "kernel": "decode_rows_k<4, false, false>", "bytes_per_launch": dec_b,
                      "us_per_launch": round(kern_s * 1e6, 3),
                      "kernel_sources": digest},
         "cpu_baseline": cpu,
