@@ -62,12 +62,17 @@ struct RawS {
 // One-dimensional grid: workgroup wg -> unit u = (wg >> 3) / casc_rg * 8 + (wg & 7), row group
 // (wg >> 3) mod casc_rg, so every workgroup of KV head h (u mod H = h) and one block range shares an XCD.
 template <int VG>
-__global__ __launch_bounds__(256, 1) void cascade_k(TileGeom g, DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void cascade_k(TileGeom g, DecodeArgs a) {
   constexpr int D = kD, NT = kNT, NR = kCascRows, NQT = 2 * NT, NGV = D / VG;
   static_assert(NGV == 2 || NGV == 4, "V groups of 64 or 32");
-  __shared__ __attribute__((aligned(16))) uint32_t s_qa[2][NQT][4][64][4];  // QK A operands [buf][tile][k-step][lane]
+  // The loop's QK A operands [buf][tile][k-step][lane] and staged V rows [wave], and after the loop the
+  // waves' accumulators, share one buffer.
+  constexpr int kQaBytes = 2 * NQT * 4 * 64 * 4 * 4, kVBytes = 4 * 64 * kVP, kWaccBytes = 4 * 16 * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kQaBytes + kVBytes > kWaccBytes ? kQaBytes + kVBytes
+                                                                                       : kWaccBytes];
+  auto s_qa = reinterpret_cast<uint32_t (*)[NQT][4][64][4]>(&s_buf[0]);
+  auto s_v = reinterpret_cast<uint8_t (*)[64 * kVP]>(&s_buf[kQaBytes]);
   __shared__ float s_zq[2][NR];                                           // sum_c q_c z_c per row and block
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][64 * kVP];
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][NT][64 * kPP];
   // V parameters of each wave's 8-token groups as fp16 pairs of tokens (r, r + 4): [wave][k-block][group of
   // 8][V group][2 r + {scale, zero}]
@@ -76,9 +81,8 @@ __global__ __launch_bounds__(256, 1) void cascade_k(TileGeom g, DecodeArgs a) {
   __shared__ int s_bad[kMaxSplitBlocks];
   __shared__ int s_ccnt[4], s_minlen;
   __shared__ float s_wm[4][16], s_wl[4][16];
-  static_assert(sizeof(float) * 4 * 16 * D <= sizeof(s_qa), "wave merge fits in s_qa");
   static_assert(sizeof(float) * NR * D <= sizeof(s_p), "query set-up fits in s_p");
-  float (*s_wacc)[16][D] = reinterpret_cast<float (*)[16][D]>(&s_qa[0][0][0][0][0]);  // after the block loop
+  float (*s_wacc)[16][D] = reinterpret_cast<float (*)[16][D]>(&s_buf[0]);  // after the block loop
   float (*s_q)[D] = reinterpret_cast<float (*)[D]>(&s_p[0][0][0]);                    // during the set-up
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;

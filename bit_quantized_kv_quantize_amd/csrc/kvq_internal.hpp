@@ -176,7 +176,8 @@ hipError_t launch_decode_fp8(const TileGeom& g, const DecodeArgs& a, hipStream_t
 // Cascade kernel for blocks shared by all sequences: layouts of the per-channel-K kernel; the caller then
 // runs that kernel with a.casc set.
 bool decode_cascade_supported(const TileGeom& g, int G);
-constexpr int kCascRows = 32;  // (sequence, query head) rows of one cascade workgroup
+constexpr int kCascRows = 16;   // (sequence, query head) rows of one cascade workgroup
+constexpr int kCascUnits = 512; // cascade workgroups aimed for: two per CU
 hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 
