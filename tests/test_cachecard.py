@@ -12,7 +12,7 @@ from gpu_cases import host_inputs, oracle_run
 
 
 def _oracle_case(orc, name, **kw):
-    case = W.make_case(W.CONFIGS[name], **kw)
+    case = W.make_case(W.named_config(name), **kw)
     inp = host_inputs(case)
     pool, out = oracle_run(orc, case, inp)
     return case, inp, pool, out
@@ -21,6 +21,8 @@ def _oracle_case(orc, name, **kw):
 @pytest.mark.parametrize("name,kw", [
     ("qwen25_14b_prefix_32k", dict(n_seqs=3, shared_prefix=512, context=[768, 612, 1023])),
     ("mixed_sentinel_32k", dict(n_seqs=3, context=[1024, 600, 333])),
+    ("mixed_sentinel_32k_widths", dict(n_seqs=3, context=[1024, 600, 333])),
+    ("deepseek_v2_lite_mla_8k", dict(n_seqs=2, context=[700, 257])),
 ])
 def test_card_round_trip_reproduces_decode(orc, tmp_path, name, kw):
     case, inp, pool, ref = _oracle_case(orc, name, **kw)

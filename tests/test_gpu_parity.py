@@ -227,7 +227,8 @@ def test_dequantize_blocks_within_one_ulp(env, orc, variant):
         assert (u > 0).mean() < 1e-3
 
 
-@pytest.mark.parametrize("name", ["qwen25_14b_prefix_32k", "mixed_sentinel_32k", "llama31_8b_pool_8k"])
+@pytest.mark.parametrize("name", ["qwen25_14b_prefix_32k", "mixed_sentinel_32k", "llama31_8b_pool_8k",
+                                  "llama31_8b_pool_8k_widths", "deepseek_v2_lite_mla_8k"])
 def test_card_save_load_round_trip(env, orc, tmp_path, name):
     # Blocks saved from a GPU pool to a card file (kvq_copy_blocks gathers them) and loaded into another pool
     # at shuffled ids (kvq_copy_blocks scatters them): the card's tiles equal the oracle's bytes, and decode
@@ -236,7 +237,8 @@ def test_card_save_load_round_trip(env, orc, tmp_path, name):
     from bit_quantized_kv_quantize_amd import cachecard
     from safetensors.numpy import load_file
 
-    case = W.make_case(W.CONFIGS[name], **SMALL[name])
+    size = SMALL.get(name.replace("_widths", ""), dict(n_seqs=3, context=[1000, 300, 513]))
+    case = W.make_case(W.named_config(name), **size)
     inp = host_inputs(case)
     ref_pool, _ = oracle_run(orc, case, inp, decode=False)
     cfg = case.cfg
