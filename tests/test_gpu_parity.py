@@ -181,6 +181,33 @@ def test_cascade_shared_blocks(env, orc, name, cascade_mode):
     assert err <= TOL
 
 
+def _two_prefix_case(n_seqs, prefix_blocks, context):
+    """The prefix workload's layout with two shared prompts: sequences below n_seqs // 2 share prefix A (the
+    case's own), the others a second copy of it at other physical blocks (prefix B)."""
+    case = W.make_case(W.CONFIGS["qwen25_14b_prefix_32k"], n_seqs=n_seqs, shared_prefix=256 * prefix_blocks,
+                       context=context)
+    b_ids = np.arange(case.num_blocks, case.num_blocks + prefix_blocks, dtype=np.int32)
+    case.block_table[n_seqs // 2:, :prefix_blocks] = b_ids
+    case.num_blocks += prefix_blocks
+    case.prefill_blocks = np.array(sorted(set(case.prefill_blocks.tolist()) | set(b_ids.tolist())), np.int32)
+    return case
+
+
+@pytest.mark.parametrize("n_seqs", [8, 13])
+def test_cascade_groups_sharing_different_prefixes(env, orc, n_seqs, cascade_mode):
+    # Two prompts, each shared by half of the sequences: blocks aliased by several tables but not by all of
+    # them. The cascade takes only blocks every sequence shares, so here the per-sequence kernel reads each
+    # prompt block once per sequence; the output must not depend on which kernel took which block.
+    kvq, torch = env
+    case = _two_prefix_case(n_seqs, 4, [1024 + (211 * i) % 700 for i in range(n_seqs)])
+    inp = host_inputs(case)
+    _, ref = oracle_run(orc, case, inp)
+    _, got = gpu_run(kvq, torch, case, inp)
+    err = rel_err(got, ref)
+    print("two prefixes n_seqs=%d [%s]: max rel err %.3g" % (n_seqs, cascade_mode, err))
+    assert err <= TOL
+
+
 def _f16_ulps(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     """Distance in fp16 ulps between bit patterns (order-preserving integer map; +0 and -0 coincide)."""
     def key(x):
