@@ -453,3 +453,27 @@ def test_unequal_head_dims(env, orc, variant, decode_path):
     for g_, r_ in ((kg_, kr), (vg_, vr)):
         u = _f16_ulps(g_.cpu().numpy().view(np.uint16), r_)
         assert u.max() <= 1 and (u > 0).mean() < 1e-3
+
+
+@pytest.mark.parametrize("layout", ["rows", "rows_sentinel", "kchan", "generic_d64"])
+def test_many_short_sequences(env, orc, layout):
+    # 2000 sequences of 1..600 slots in one call (grids of thousands of (sequence, KV head) pairs, row lists
+    # of 2000 sequences): every output row against the oracle.
+    kvq, torch = env
+    n = 2000
+    ctx = [1 + (37 * i) % 600 for i in range(n)]
+    if layout == "kchan":
+        cfg = W.Config(9, "many", 128, 4, 2, 1, -1, 32, 1, 0, n, 0, "perm", False, 3, 10.0, 1.0)
+    elif layout == "generic_d64":
+        cfg = W.Config(9, "many", 64, 6, 2, 1, 32, 32, 0, 0, n, 0, "perm", True, 3, 10.0, 1.0)
+    else:
+        cfg = W.Config(9, "many", 128, 8, 2, 1, 64, 64, 0, 0, n, 0, "perm", True, 3, 10.0, 1.0,
+                       dead_fraction=0.3 if layout == "rows_sentinel" else 0.0)
+    case = W.make_case(cfg, context=ctx)
+    inp = host_inputs(case)
+    ref_pool, ref = oracle_run(orc, case, inp, n_threads=8)
+    got_pool, got = gpu_run(kvq, torch, case, inp)
+    assert np.array_equal(got_pool, ref_pool)
+    err = rel_err(got, ref)
+    print("many sequences [%s]: max rel err %.3g" % (layout, err))
+    assert err <= TOL
