@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (diagnostics only)")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload decode table")
+    ap.add_argument("--workload-table", default="",
+                    help="comma-separated workloads for the per-workload table (default: every workload)")
+    ap.add_argument("--workload-launches", type=int, default=16, help="decode launches per workload graph")
     return ap.parse_args()
 
 
@@ -314,9 +317,15 @@ def main():
         del pools, aks, avs, qs, outs
         torch.cuda.empty_cache()
         workloads = {}
-        for name in W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL, MLA_POOL]:
+        names = W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL, MLA_POOL]
+        if args.workload_table:
+            names = [n for n in args.workload_table.split(",") if n]
+            for n in names:
+                workload_config(n)  # unknown names fail here, before any timing
+        for name in names:
             if name != cfg.name:
-                workloads[name] = measure_workload(kvq, torch, name)
+                workloads[name] = measure_workload(kvq, torch, name, launches=args.workload_launches,
+                                                   graph=not args.no_graph)
         workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
                                "GBps": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
                                "pool_instances": layers, "append_us": None}
@@ -430,10 +439,11 @@ def measure_restore(kvq, torch, name, launches=4):
             "GBps": round(moved / us / 1e3, 1)}
 
 
-def measure_workload(kvq, torch, name, launches=16):
+def measure_workload(kvq, torch, name, launches=16, graph=True):
     """One workload at full size: its layer quantised on the GPU (copied to INSTANCES pools), the append
     where the workload appends, then decode kernels captured back to back in a HIP graph (cycling the
-    pools) and timed between events on the launch stream. Returns per-launch times and algorithmic bytes."""
+    pools) and timed between events on the launch stream (launched eagerly with graph=False). Returns
+    per-launch times and algorithmic bytes."""
     cfg = workload_config(name)
     case = W.make_case(cfg)
     lay = kvq.Layout(**cfg.layout())
@@ -472,18 +482,24 @@ def measure_workload(kvq, torch, name, launches=16):
                 fn(i)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(launches):
-                fn(i)
-        graph.replay()
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(launches):
+                    fn(i)
+            run = g.replay
+        else:
+            def run():
+                for i in range(launches):
+                    fn(i)
+        run()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         ts = []
         for _ in range(5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            graph.replay()
+            run()
             e1.record(stream)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3 / launches)
