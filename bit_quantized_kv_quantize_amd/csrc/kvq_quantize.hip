@@ -331,6 +331,74 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
   }
 }
 
+// Quantise this lane's 16 values at 4 bits as part of a group spanning gl lanes: the same fp32 operations
+// per value as quantize8, so the same codes and parameters. Codes are packed low nibble first.
+__device__ __forceinline__ void quantize16_q4(const float (&x)[16], int gl, uint2& codes, uint32_t& param) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  for (int m = 1; m < gl; m *= 2) {
+    mn = fminf(mn, __shfl_xor(mn, m));
+    mx = fmaxf(mx, __shfl_xor(mx, m));
+  }
+  mn = mn + 0.0f;  // a -0 extreme becomes +0
+  mx = mx + 0.0f;
+  const float s32 = (mx - mn) / 15.0f;
+  const uint32_t sh = f2h(s32), zh = f2h(mn);
+  param = sh | (zh << 16);
+  const float s = h2f(sh), z = h2f(zh);
+  uint32_t w[2] = {0u, 0u};
+  if (s != 0.0f) {
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float qv = __builtin_rintf((x[i] - z) * r);
+      qv = fminf(fmaxf(qv, 0.0f), 15.0f);
+      w[i >> 3] |= (uint32_t)qv << (4 * (i & 7));
+    }
+  }
+  codes = uint2{w[0], w[1]};
+}
+
+// quantize_rows_k for 4-bit pools without rotation whose groups span whole 16-channel lanes: LPR = d / 16
+// lanes per row with 16 values each, so the per-row work (group extremes, the two divisions, addressing)
+// is shared by twice as many values. Grid and output as quantize_rows_k.
+template <int LPR>
+__global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                         const int32_t* __restrict__ block_ids,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int kv_base) {
+  constexpr int D = LPR * 16;
+  constexpr int kRowsPerPass = 256 / LPR;
+  const int i = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
+  const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
+  const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 16;
+  const int gl = (kv ? g.vg : g.kg) / 16;
+  for (int t = r0; t < kRows; t += kRowsPerPass) {
+    float a[8], b[8], x[16];
+    load8(src + (size_t)t * g.H * D, a);
+    load8(src + (size_t)t * g.H * D + 8, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = a[e];
+      x[8 + e] = b[e];
+    }
+    uint2 codes;
+    uint32_t param;
+    quantize16_q4(x, gl, codes, param);
+    *reinterpret_cast<uint2*>(tile + (kv ? g.vcode(t, 4) : g.kcode(t)) + li * 8) = codes;
+    if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(tile + (kv ? g.vpar(t) : g.kpar(t)))[li / gl] = param;
+  }
+  if (kv == 1) {  // zero the tail padding
+    for (uint32_t o = g.off_hdr + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
+      *reinterpret_cast<uint32_t*>(tile + o) = 0u;
+  }
+}
+
 template <int LPR>
 hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                              const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, float rot_c,
@@ -341,9 +409,15 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
     kv_base = 1;
     n_tensors -= 1;
   }
-  if (n_tensors > 0)
-    hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
-                       block_ids, k, v, prec_bits, rot_c, kv_base);
+  if (n_tensors > 0) {
+    const bool k_lanes = kv_base > 0 || g.kg % 16 == 0;  // the K rows' groups span whole 16-channel lanes
+    if (LPR == 16 && !g.fp8 && !g.mixed && !g.rotate && g.dv == g.d && k_lanes && g.vg % 16 == 0)
+      hipLaunchKernelGGL(quantize_rows16_k<8>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
+                         block_ids, k, v, kv_base);
+    else
+      hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
+                         block_ids, k, v, prec_bits, rot_c, kv_base);
+  }
   return hipGetLastError();
 }
 
