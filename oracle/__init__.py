@@ -94,6 +94,8 @@ def lib():
         L.orc_decode_attention.argtypes = [ctypes.POINTER(OrcLayout), P, P, i32, i32, P, i32, P, P, i32,
                                            ctypes.c_float, P, P, i32, i32]
         L.orc_decode_attention.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = i32
         _lib = L
@@ -227,3 +229,8 @@ def decode_attention(layout: OrcLayout, pool: np.ndarray, q: np.ndarray, block_t
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the quantisation loop (and the default of every parallel loop); n <= 0 keeps the default."""
+    lib().orc_set_threads(int(n))

@@ -436,6 +436,8 @@ int orc_quantize_blocks(const orc_layout* L, uint8_t* pool, const int32_t* block
   if (n_blocks < 0) return ORC_ERR_ARG;
   if (prec_bits && !L->mixed) return ORC_ERR_ARG;
   const int32_t H = L->num_kv_heads, d = L->head_dim, dv = vdim(L);
+  /* tiles are independent (block ids are distinct): one (block, head) tile per iteration, in any order */
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
   for (int32_t i = 0; i < n_blocks; ++i) {
     for (int32_t h = 0; h < H; ++h) {
       const size_t row0 = (size_t)i * ORC_ROWS * H + h;
@@ -689,6 +691,11 @@ int orc_decode_attention(const orc_layout* L, const uint8_t* pool, const uint16_
 }
 
 /* Threads the OpenMP runtime will use for a parallel region (1 without OpenMP). */
+/* Threads of the parallel loops that take no thread count (quantisation); 0 keeps OpenMP's default. */
+void orc_set_threads(int32_t n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 int32_t orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
