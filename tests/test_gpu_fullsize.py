@@ -1,16 +1,18 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration of the full batch.
+"""GPU parity at the workloads' full sizes, in the launch configuration of the full batch, over every sequence.
 
-Each layer is built on the GPU the way the benchmark builds it: every prefill block quantised (in chunks
-of the seeded source), one token appended per sequence where the workload appends, then one decode call
-over all sequences - so the split plan, grid and workspace are those of the full-size call. The oracle
-then rebuilds, from the same seeded inputs, what it can compute in seconds:
+Each layer is built twice from the same seeded chunks of source rows (the generator module is the only
+code the two sides share): on the GPU the way the benchmark builds it - every prefill block quantised in
+chunks, one token appended per sequence where the workload appends, then one decode call over all
+sequences, so the split plan, grid and workspace are those of the full-size call - and by the oracle
+(quantisation parallel over tiles, decode parallel over (sequence, KV head)). Compared:
 
-* every tile of the sampled sequences' blocks (codes, fp16 scales/zeros, bitmaps, padding and the
-  appended rows), compared bit for bit with the GPU pool;
-* the decode output of the sampled sequences (all their query heads), within 2e-3 max relative error.
+* the whole pool, bit for bit: codes, fp16 scales/zeros, width headers, padding and the appended rows of
+  every block;
+* every output row - all sequences, all query heads - within 2e-3 max relative error.
 
-The oracle's pool for the sample holds only the sampled sequences' blocks (renumbered); nothing computed
-on the GPU feeds it."""
+Nothing computed on the GPU feeds the oracle."""
+import os
+
 import numpy as np
 import pytest
 
@@ -19,15 +21,16 @@ from gpu_cases import TOL, rel_err
 
 pytestmark = pytest.mark.gpu
 
-# workload -> (layers checked, sampled sequences)
+# workload -> layers checked
 FULL = {
-    "tiny_1k": ([0], [0]),
-    "gemma3_12b_4k": ([0, 47], [0]),
-    "llama31_8b_pool_8k": ([0, 31], [0, 5, 11]),
-    "qwen25_14b_prefix_32k": ([0], [0, 37, 63]),
-    "mixed_sentinel_32k": ([0], [0, 77, 127]),
-    "deepseek_v2_lite_mla_8k": ([0, 26], [0, 5, 11]),
+    "tiny_1k": [0],
+    "gemma3_12b_4k": [0, 47],
+    "llama31_8b_pool_8k": [0, 31],
+    "qwen25_14b_prefix_32k": [0],
+    "mixed_sentinel_32k": [0],
+    "deepseek_v2_lite_mla_8k": [0, 26],
 }
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 @pytest.fixture(scope="module")
@@ -40,16 +43,21 @@ def env():
     return kvq, torch
 
 
-def build_on_gpu(kvq, torch, case, layer):
-    """Full-size layer on the GPU: pool, appended tokens, decode output (host copy)."""
+def build_both(kvq, torch, orc, case, layer):
+    """The full-size layer on the GPU and in the oracle from the same chunks: (GPU pool as host bytes, oracle
+    pool, GPU decode output, oracle decode output)."""
     cfg = case.cfg
     lay = kvq.Layout(**cfg.layout())
+    lay_o = orc.make_layout(**cfg.layout())
     pool = kvq.new_pool(lay, case.num_blocks)
+    ref_pool = np.zeros(orc.tile_bytes(lay_o) * cfg.num_kv_heads * case.num_blocks, np.uint8)
     prec = np.full(case.n_seqs, 4, np.uint8) if cfg.mixed else None
-    for ids, k, v, bm in W.prefill_chunks(case, layer, max_blocks=2048, threads=16, prec_out=prec):
+    orc.set_threads(THREADS)
+    for ids, k, v, bm in W.prefill_chunks(case, layer, max_blocks=2048, threads=THREADS, prec_out=prec):
         kvq.quantize_blocks(lay, pool, torch.from_numpy(ids).cuda(), torch.from_numpy(k).view(torch.float16).cuda(),
                             torch.from_numpy(v).view(torch.float16).cuda(),
                             None if bm is None else torch.from_numpy(bm.view(np.int32)).cuda())
+        orc.quantize_blocks(lay_o, ref_pool, ids, k, v, bm)
         torch.cuda.synchronize()
     table = torch.from_numpy(case.block_table).cuda()
     if case.append:
@@ -58,77 +66,42 @@ def build_on_gpu(kvq, torch, case, layer):
                           torch.from_numpy(av).view(torch.float16).cuda(), table,
                           torch.from_numpy(case.positions).cuda(),
                           None if prec is None else torch.from_numpy(prec).cuda())
-    q = torch.from_numpy(W.queries(cfg, layer, case.n_seqs)).view(torch.float16).cuda()
+        assert orc.append_tokens(lay_o, ref_pool, ak, av, case.block_table, case.positions, prec) == 0
+    qh = W.queries(cfg, layer, case.n_seqs)
+    q = torch.from_numpy(qh).view(torch.float16).cuda()
     mask = None if case.sentinel_mask is None else torch.from_numpy(case.sentinel_mask.view(np.int32)).cuda()
     out = kvq.decode_attention(lay, pool, q, table, torch.from_numpy(case.seq_lens).cuda(), case.max_seq_len, mask)
     torch.cuda.synchronize()
-    return lay, pool, out.cpu().numpy()
+    got_pool = pool.cpu().numpy()
+    out = out.cpu().numpy()
+    del pool
+    torch.cuda.empty_cache()
+    ref_out = orc.decode_attention(lay_o, ref_pool, qh, case.block_table, case.seq_lens, case.sentinel_mask,
+                                   n_threads=THREADS)
+    return got_pool, ref_pool, out, ref_out
 
 
-def oracle_sample(orc, case, layer, seqs):
-    """The oracle on the sampled sequences only: (original block ids, their tiles, decode output)."""
-    cfg = case.cfg
-    n_used = (case.seq_lens[seqs] + W.BLOCK - 1) // W.BLOCK
-    ids = np.unique(np.concatenate([case.block_table[s, :n] for s, n in zip(seqs, n_used)])).astype(np.int32)
-    compact = {int(b): i for i, b in enumerate(ids)}
-    table = np.zeros((len(seqs), case.max_blocks_per_seq), np.int32)
-    for r, (s, n) in enumerate(zip(seqs, n_used)):
-        table[r, :n] = [compact[int(b)] for b in case.block_table[s, :n]]
-    prefill = np.array([b for b in ids if b in set(case.prefill_blocks.tolist())], np.int32)
-    lay = orc.make_layout(**cfg.layout())
-    tb = orc.tile_bytes(lay)
-    pool = np.zeros(tb * cfg.num_kv_heads * ids.size, np.uint8)
-    bitmaps = None
-    prec = None
-    ak = av = None
-    if case.append:
-        ak, av = W.append_kv(cfg, layer, case.n_seqs)
-        ak, av = ak[seqs], av[seqs]
-    if cfg.mixed:
-        # per-sequence ranking of cached tokens by K norm, as for the whole batch
-        bm = {}
-        prec = np.full(len(seqs), 4, np.uint8)
-        for r, s in enumerate(seqs):
-            blocks = W.sequence_blocks(case, s)
-            k, _ = W.blocks_kv(cfg, layer, blocks, threads=16)
-            n = int(case.context[s])
-            ns = W.k_norms_sq(k[:n])
-            for i, words in enumerate(W.block_width_words(cfg, ns, blocks.size)):
-                bm[int(blocks[i])] = words
-            if case.append and blocks.size:
-                prec[r] = W.append_prec(cfg, ns, float(W.k_norms_sq(ak[r:r + 1])[0]))
-        bitmaps = np.stack([bm[int(b)] for b in prefill])
-    k, v = W.blocks_kv(cfg, layer, prefill, threads=16)
-    orc.quantize_blocks(lay, pool, np.array([compact[int(b)] for b in prefill], np.int32), k, v, bitmaps)
-    pos = case.positions[seqs]
-    if case.append:
-        assert orc.append_tokens(lay, pool, ak, av, table, pos, prec) == 0
-    q = W.queries(cfg, layer, case.n_seqs)[seqs]
-    mask = None if case.sentinel_mask is None else np.ascontiguousarray(case.sentinel_mask[seqs])
-    out = orc.decode_attention(lay, pool, q, table, case.seq_lens[seqs], mask, n_threads=16)
-    return ids, pool.reshape(ids.size, -1), out
-
-
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8", "llama31_8b_pool_8k_widths",
                                                    "mixed_sentinel_32k_widths", "deepseek_v2_lite_mla_8k"])
-def test_full_size_sampled(env, orc, name):
+def test_full_size_every_sequence(env, orc, name):
     # (the last cases: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against,
     # two workloads stored with per-token widths {2, 4, 8, FP16}, and an MLA model's pool: K head dim 192,
     # V head dim 128)
     kvq, torch = env
     base = name.replace("_fp8", "").replace("_widths", "")
-    layers, seqs = FULL[base]
     case = W.make_case(W.named_config(name))
-    for layer in layers:
+    for layer in FULL[base]:
         print("[fullsize] %s layer %d: %d seqs, %d blocks" % (name, layer, case.n_seqs, case.num_blocks), flush=True)
-        _, pool, out = build_on_gpu(kvq, torch, case, layer)
-        ids, ref_tiles, ref_out = oracle_sample(orc, case, layer, seqs)
-        got_tiles = pool.view(case.num_blocks, -1)[torch.from_numpy(ids).long().cuda()].cpu().numpy()
-        diff = np.nonzero(got_tiles != ref_tiles)
-        assert diff[0].size == 0, "tiles differ: block %s byte %s" % (ids[diff[0][:4]], diff[1][:4])
-        err = rel_err(out[seqs], ref_out)
-        print("[fullsize] %s layer %d: max rel err %.3g over sequences %s" % (name, layer, err, seqs), flush=True)
-        assert err <= TOL
+        got_pool, ref_pool, out, ref_out = build_both(kvq, torch, orc, case, layer)
+        if not np.array_equal(got_pool, ref_pool):
+            tb = got_pool.size // case.num_blocks
+            diff = np.nonzero(got_pool != ref_pool)[0]
+            raise AssertionError("pool bytes differ: %d bytes, first in blocks %s (offsets %s)"
+                                 % (diff.size, np.unique(diff // tb)[:4], diff[:4] % tb))
+        err = rel_err(out, ref_out)
+        print("[fullsize] %s layer %d: pool bit-exact (%.2f GB), max rel err %.3g over all %d sequences"
+              % (name, layer, got_pool.size / 1e9, err, case.n_seqs), flush=True)
         assert np.isfinite(out).all()
-        del pool
-        torch.cuda.empty_cache()
+        assert err <= TOL
+        del got_pool, ref_pool
