@@ -53,31 +53,57 @@ if not os.path.exists(LIB_PATH):
 # it would pull in the system one as well, and the two would not share streams or device memory).
 import torch as _torch_runtime  # noqa: E402,F401
 
-_lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _LP = ctypes.POINTER(Layout)
-_lib.kvq_check_layout.argtypes = [_LP]
-_lib.kvq_check_layout.restype = ctypes.c_int
-_lib.kvq_tile_bytes.argtypes = [_LP]
-_lib.kvq_tile_bytes.restype = ctypes.c_size_t
-_lib.kvq_pool_bytes.argtypes = [_LP, _I]
-_lib.kvq_pool_bytes.restype = ctypes.c_size_t
-_lib.kvq_decode_workspace_bytes.argtypes = [_LP, _I, _I, _I]
-_lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.kvq_status_string.argtypes = [ctypes.c_int]
-_lib.kvq_status_string.restype = ctypes.c_char_p
-_lib.kvq_quantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P, _P]
-_lib.kvq_quantize_blocks.restype = ctypes.c_int
-_lib.kvq_dequantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P]
-_lib.kvq_dequantize_blocks.restype = ctypes.c_int
-_lib.kvq_copy_blocks.argtypes = [_LP, _P, _P, _P, _P, _I, _P]
-_lib.kvq_copy_blocks.restype = ctypes.c_int
-_lib.kvq_append_tokens.argtypes = [_LP, _P, _I, _P, _P, _P, _I, _P, _P, _P]
-_lib.kvq_append_tokens.restype = ctypes.c_int
-_lib.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
-                                      ctypes.c_size_t, _P]
-_lib.kvq_decode_attention.restype = ctypes.c_int
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    L.kvq_check_layout.argtypes = [_LP]
+    L.kvq_check_layout.restype = ctypes.c_int
+    L.kvq_tile_bytes.argtypes = [_LP]
+    L.kvq_tile_bytes.restype = ctypes.c_size_t
+    L.kvq_pool_bytes.argtypes = [_LP, _I]
+    L.kvq_pool_bytes.restype = ctypes.c_size_t
+    L.kvq_decode_workspace_bytes.argtypes = [_LP, _I, _I, _I]
+    L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kvq_status_string.argtypes = [ctypes.c_int]
+    L.kvq_status_string.restype = ctypes.c_char_p
+    L.kvq_quantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P, _P]
+    L.kvq_quantize_blocks.restype = ctypes.c_int
+    L.kvq_dequantize_blocks.argtypes = [_LP, _P, _P, _I, _P, _P, _P]
+    L.kvq_dequantize_blocks.restype = ctypes.c_int
+    L.kvq_copy_blocks.argtypes = [_LP, _P, _P, _P, _P, _I, _P]
+    L.kvq_copy_blocks.restype = ctypes.c_int
+    L.kvq_append_tokens.argtypes = [_LP, _P, _I, _P, _P, _P, _I, _P, _P, _P]
+    L.kvq_append_tokens.restype = ctypes.c_int
+    L.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
+                                       ctypes.c_size_t, _P]
+    L.kvq_decode_attention.restype = ctypes.c_int
+    return L
+
+
+_libs = {"release": _load(LIB_PATH)}
+_lib = _libs["release"]
+DEBUG_LIB_PATH = os.path.join(_HERE, "libkvq_debug.so")
+
+
+def use_library(which: str = "release"):
+    """Route every call of this module to the release library (default) or to its debug build
+    (``libkvq_debug.so``: device-resident ids, lengths and positions are checked on the host before any
+    launch, and the KVQ_DECODE_KERNEL environment variable may force a decode kernel - a test hook). Returns
+    the ctypes handle now in use."""
+    global _lib
+    if which not in ("release", "debug"):
+        raise ValueError("use_library: 'release' or 'debug'")
+    if which not in _libs:
+        if not os.path.exists(DEBUG_LIB_PATH):
+            raise ImportError("libkvq_debug.so is not built (%s)" % DEBUG_LIB_PATH)
+        _libs[which] = _load(DEBUG_LIB_PATH)
+    _lib = _libs[which]
+    return _lib
+
 
 EXPORTS = ("kvq_check_layout", "kvq_tile_bytes", "kvq_pool_bytes", "kvq_decode_workspace_bytes",
            "kvq_status_string", "kvq_quantize_blocks", "kvq_dequantize_blocks", "kvq_copy_blocks",

@@ -4,6 +4,11 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#ifdef KVQ_DEBUG
+#include <stdio.h>
+
+#include <vector>
+#endif
 
 #include "kvq_internal.hpp"
 
@@ -137,8 +142,7 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   if (p.casc > 0) parts += (size_t)2 * kCascUnits * kCascRows + rows * c512;
   WorkspaceLayout w{};
   w.parts = parts;
-  w.ctr = 0;
-  w.ml = up(ns * g.H * sizeof(unsigned));
+  w.ml = 0;
   w.acc = w.ml + up(parts * 2 * sizeof(float));  // accumulators of V's head dim
   // row lists only for layouts the row-list kernel reads: one list per width (4 and 8 bits, and 2 and 16
   // in pools of four widths)
@@ -150,8 +154,19 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   // at least one block per sequence, so the count kernels always have a grid
   w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
   w.cflag = w.bcnt + up(ns * nwd * (size_t)w.bcnt_blocks * sizeof(int));
-  w.total = w.cflag + up(p.casc > 0 ? (size_t)p.max_blocks * sizeof(int) : 0);
+  w.body = w.cflag + up(p.casc > 0 ? (size_t)p.max_blocks * sizeof(int) : 0);
+  // The split-K arrival counters sit at the end of the caller's workspace (ctr_offset), after every other
+  // region: the other regions grow with n_seqs and max_seq_len, so no smaller call sharing the workspace
+  // can write partials over a larger call's counters, and a smaller call's counters are a subset of the
+  // larger call's (all zero between calls).
+  w.ctr_bytes = ns * g.H * sizeof(unsigned);
+  w.total = w.body + up(w.ctr_bytes);
   return w;
+}
+
+size_t ctr_offset(const WorkspaceLayout& w, size_t workspace_bytes) {
+  // the last ctr_bytes below the 4-byte-aligned end; workspace_bytes >= w.total keeps this >= w.body
+  return workspace_bytes / 4 * 4 - w.ctr_bytes;
 }
 
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len) {
@@ -159,6 +174,62 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
 }
 
 static int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+#ifdef KVQ_DEBUG
+// Debug builds check the device-resident arguments on the host before any launch: the arrays are copied
+// back (a stream synchronisation per array), every block id must address a whole block inside the pool's
+// device allocation (hipMemGetAddressRange: the allocation that holds the pointer, so the bound is that
+// allocation's end), and lengths and positions must lie in their stated ranges. A violation returns
+// KVQ_ERR_ARG with a message on stderr and nothing is launched.
+static bool fetch_i32(const int32_t* dev, size_t n, std::vector<int32_t>& host, hipStream_t stream) {
+  host.resize(n);
+  if (n == 0) return true;
+  return hipMemcpyAsync(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream) == hipSuccess &&
+         hipStreamSynchronize(stream) == hipSuccess;
+}
+// Blocks of the pool that fit between `pool` and the end of its device allocation (-1 if unknown).
+static long pool_blocks(const TileGeom& g, const void* pool) {
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)pool) != hipSuccess || !base) return -1;
+  const size_t off = (size_t)((const uint8_t*)pool - (const uint8_t*)base);
+  if (off > size) return 0;
+  return (long)((size - off) / ((size_t)g.H * g.tile_bytes));
+}
+static int debug_fail(const char* fn, const char* what, long i, long v) {
+  fprintf(stderr, "%s: %s (index %ld, value %ld)\n", fn, what, i, v);
+  return KVQ_ERR_ARG;
+}
+static int check_ids(const char* fn, const TileGeom& g, const void* pool, const int32_t* ids, int n, bool distinct,
+                     hipStream_t stream) {
+  std::vector<int32_t> h;
+  if (!fetch_i32(ids, (size_t)n, h, stream)) return KVQ_ERR_HIP;
+  const long nb = pool_blocks(g, pool);
+  for (int i = 0; i < n; ++i)
+    if (h[i] < 0 || (nb >= 0 && h[i] >= nb)) return debug_fail(fn, "block id outside the pool", i, h[i]);
+  if (distinct) {
+    std::vector<int32_t> s(h);
+    std::sort(s.begin(), s.end());
+    for (size_t i = 1; i < s.size(); ++i)
+      if (s[i] == s[i - 1]) return debug_fail(fn, "block id repeated", (long)i, s[i]);
+  }
+  return KVQ_OK;
+}
+// Table entries of the blocks that slots [0, len) (or the one slot pos) use, for each sequence.
+static int check_table(const char* fn, const TileGeom& g, const void* pool, const int32_t* table, int n_seqs,
+                       int max_blocks, const std::vector<int32_t>& first, const std::vector<int32_t>& last,
+                       hipStream_t stream) {
+  std::vector<int32_t> t;
+  if (!fetch_i32(table, (size_t)n_seqs * max_blocks, t, stream)) return KVQ_ERR_HIP;
+  const long nb = pool_blocks(g, pool);
+  for (int s = 0; s < n_seqs; ++s)
+    for (int b = first[s]; b < last[s]; ++b) {
+      const int32_t id = t[(size_t)s * max_blocks + b];
+      if (id < 0 || (nb >= 0 && id >= nb)) return debug_fail(fn, "block table entry outside the pool", s, id);
+    }
+  return KVQ_OK;
+}
+#endif
 
 // The rotation of an n-channel row is c H with c = fp32(1 / sqrt(n)); its inverse is (1 / (n c)) H.
 static float rot_scale(int n) { return (float)(1.0 / sqrt((double)n)); }
@@ -211,6 +282,10 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
   if (n_blocks == 0) return KVQ_OK;
   if (!pool || !block_ids || !k || !v) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
+#ifdef KVQ_DEBUG
+  if ((st = check_ids("kvq_quantize_blocks", g, pool, block_ids, n_blocks, true, (hipStream_t)stream)) != KVQ_OK)
+    return st;
+#endif
   return hip_status(launch_quantize_blocks(g, (uint8_t*)pool, block_ids, n_blocks, k, v, prec_bits, rot_scale(g.d),
                                            rot_scale(g.dv), (hipStream_t)stream));
 }
@@ -223,6 +298,10 @@ int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* 
   if (n_blocks == 0) return KVQ_OK;
   if (!pool || !block_ids || !k_out || !v_out) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
+#ifdef KVQ_DEBUG
+  if ((st = check_ids("kvq_dequantize_blocks", g, pool, block_ids, n_blocks, false, (hipStream_t)stream)) != KVQ_OK)
+    return st;
+#endif
   return hip_status(launch_dequantize_blocks(g, (const uint8_t*)pool, block_ids, n_blocks, k_out, v_out,
                                              unrot_scale(g.d), unrot_scale(g.dv), (hipStream_t)stream));
 }
@@ -236,6 +315,11 @@ int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* sr
   if (!src_pool || !src_ids || !dst_pool || !dst_ids) return KVQ_ERR_ARG;
   if (((uintptr_t)src_pool & 15u) || ((uintptr_t)dst_pool & 15u)) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
+#ifdef KVQ_DEBUG
+  if ((st = check_ids("kvq_copy_blocks", g, src_pool, src_ids, n_blocks, false, (hipStream_t)stream)) != KVQ_OK ||
+      (st = check_ids("kvq_copy_blocks", g, dst_pool, dst_ids, n_blocks, true, (hipStream_t)stream)) != KVQ_OK)
+    return st;
+#endif
   return hip_status(launch_copy_blocks(g, (const uint8_t*)src_pool, src_ids, (uint8_t*)dst_pool, dst_ids, n_blocks,
                                        (hipStream_t)stream));
 }
@@ -251,6 +335,21 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
   if (n_seqs == 0) return KVQ_OK;
   if (!pool || !k || !v || !block_table || !positions) return KVQ_ERR_ARG;
   TileGeom g = make_geom(L);
+#ifdef KVQ_DEBUG
+  {
+    std::vector<int32_t> pos, first(n_seqs), last(n_seqs);
+    if (!fetch_i32(positions, (size_t)n_seqs, pos, (hipStream_t)stream)) return KVQ_ERR_HIP;
+    for (int s = 0; s < n_seqs; ++s) {
+      if (pos[s] < 0 || (long)pos[s] >= (long)max_blocks_per_seq * kRows)
+        return debug_fail("kvq_append_tokens", "position outside the block table", s, pos[s]);
+      first[s] = pos[s] / kRows;
+      last[s] = first[s] + 1;
+    }
+    if ((st = check_table("kvq_append_tokens", g, pool, block_table, n_seqs, max_blocks_per_seq, first, last,
+                          (hipStream_t)stream)) != KVQ_OK)
+      return st;
+  }
+#endif
   return hip_status(launch_append_tokens(g, (uint8_t*)pool, n_seqs, k, v, block_table, max_blocks_per_seq,
                                          positions, prec, rot_scale(g.d), rot_scale(g.dv), (hipStream_t)stream));
 }
@@ -273,6 +372,20 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   TileGeom g = make_geom(L);
   const int G = num_q_heads / g.H;
   if (G > 16) return KVQ_ERR_UNSUPPORTED;
+#ifdef KVQ_DEBUG
+  {
+    std::vector<int32_t> len, first(n_seqs, 0), last(n_seqs);
+    if (!fetch_i32(seq_lens, (size_t)n_seqs, len, (hipStream_t)stream)) return KVQ_ERR_HIP;
+    for (int s = 0; s < n_seqs; ++s) {
+      if (len[s] < 0 || len[s] > max_seq_len)
+        return debug_fail("kvq_decode_attention", "sequence length outside [0, max_seq_len]", s, len[s]);
+      last[s] = (len[s] + kRows - 1) / kRows;
+    }
+    if ((st = check_table("kvq_decode_attention", g, pool, block_table, n_seqs, max_blocks_per_seq, first, last,
+                          (hipStream_t)stream)) != KVQ_OK)
+      return st;
+  }
+#endif
   size_t need = decode_workspace_bytes(g, n_seqs, num_q_heads, max_seq_len);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVQ_ERR_WORKSPACE;
   DecodeArgs a{};
@@ -286,7 +399,7 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
   if ((size_t)n_seqs * num_q_heads * a.plan.stride > wl.parts) return KVQ_ERR_UNSUPPORTED;  // never, by the bound
   uint8_t* ws = (uint8_t*)workspace;
-  a.ws_ctr = (unsigned*)(ws + wl.ctr);
+  a.ws_ctr = (unsigned*)(ws + ctr_offset(wl, workspace_bytes));
   a.ws_ml = (float*)(ws + wl.ml);
   a.ws_acc = (float*)(ws + wl.acc);
   a.ws_cnt = (int*)(ws + wl.cnt);
@@ -301,7 +414,8 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
   a.G = G;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.mask_words = sentinel_mask ? mask_words_per_seq : 0;
-  a.q_scale = (float)((double)softmax_scale * 1.4426950408889634);
+  a.q_scale64 = (double)softmax_scale * 1.4426950408889634;  // log2(e)
+  a.q_scale = (float)a.q_scale64;
   a.unrot_c = unrot_scale(g.d);
   a.unrot_cv = unrot_scale(g.dv);
   return hip_status(launch_decode(g, a, (hipStream_t)stream));

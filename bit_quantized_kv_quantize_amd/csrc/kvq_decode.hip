@@ -17,6 +17,7 @@
 #include <string.h>
 
 #include "kvq_decode_common.hpp"
+#include "kvq_decode_precise.hpp"
 
 namespace kvq {
 namespace {
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
     float score[GMAX];
 #pragma unroll
     for (int j = 0; j < GMAX; ++j) score[j] = 0.0f;
+    float terms = 0.0f;  // largest sum of term magnitudes of this token's logits (per-token K groups)
     if (live) {
       const uint8_t* krow = tile + g.kcode(tid);
       if (g.fp8) {
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < GMAX; ++j) {
               score[j] += sc * part[j] + zc * s_qsum[j][gi];
+              terms = fmaxf(terms, fabsf(sc * part[j]) + fabsf(zc * s_qsum[j][gi]));
               part[j] = 0.0f;
             }
           }
@@ -225,7 +228,35 @@ __global__ __launch_bounds__(256) void decode_attn_k(TileGeom g, DecodeArgs a) {
           }
         }
 #pragma unroll
-        for (int j = 0; j < GMAX; ++j) score[j] += s_kconst[j];
+        for (int j = 0; j < GMAX; ++j) {
+          terms = fmaxf(terms, fabsf(score[j]) + fabsf(s_kconst[j]));
+          score[j] += s_kconst[j];
+        }
+      }
+      // Logits with terms beyond kPreciseAbove (base-2 units): this token's logits again in fp64, from the
+      // exactly dequantised K row (the plain definition; rare, so a per-thread branch).
+      bool big = terms > kPreciseAbove;
+#pragma unroll
+      for (int j = 0; j < GMAX; ++j) big |= j < G && fabsf(score[j]) > kPreciseAbove;
+      if (big) {
+        const int kbits = g.fp8 ? 8 : bits;
+        double dot[GMAX];
+#pragma unroll
+        for (int j = 0; j < GMAX; ++j) dot[j] = 0.0;
+        for (int c = 0; c < D; ++c) {
+          float ks, kz;
+          k_params(g, tile, tid, c, ks, kz);
+          const double kv = code_value(g, krow, kbits, c, ks, kz);
+#pragma unroll
+          for (int j = 0; j < GMAX; ++j) {
+            const double qc = g.rotate || j >= G
+                                  ? (double)s_q[j][c]
+                                  : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * D + c]) * a.q_scale64;
+            dot[j] += qc * kv;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < GMAX; ++j) score[j] = (float)dot[j];
       }
     }
     // block max per head
@@ -336,7 +367,12 @@ hipError_t launch_d(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 }  // namespace
 
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+#ifdef KVQ_DEBUG
+  // test hook of the debug build only: KVQ_DECODE_KERNEL=generic|mfma|nocascade (read on every call)
   const char* force = getenv("KVQ_DECODE_KERNEL");
+#else
+  const char* force = nullptr;
+#endif
   const bool generic = force && !strcmp(force, "generic");
   const bool mfma = force && !strcmp(force, "mfma");
   if (!generic && !mfma && decode_rows_supported(g, a.G)) return launch_decode_rows(g, a, stream);

@@ -16,6 +16,7 @@
 // merge runs in the split that arrives last (splitk_arrive). After the cascade kernel (a.casc > 0) the blocks
 // it flagged as shared by every sequence are skipped, and its partials join the merge.
 #include "kvq_decode_mfma_common.hpp"
+#include "kvq_decode_precise.hpp"
 
 namespace kvq {
 namespace {
@@ -351,7 +352,26 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   }
 
   // ---------------------------------------------------------------- merge the four waves
-  {
+  // A wave whose largest logit of some head lies beyond kPreciseAbove (base-2 units) redoes its rows with fp64
+  // logits (checked once, after the loop, which has no register to spare), writing its merge slots itself.
+  const bool big = (ok0 && m_run[0] != kNegInf && fabsf(m_run[0]) > kPreciseAbove) ||
+                   (ok1 && m_run[1] != kNegInf && fabsf(m_run[1]) > kPreciseAbove);
+  if (__builtin_amdgcn_ballot_w64(big) != 0) {
+    auto qv = [&](int j, int c) __attribute__((always_inline)) -> double {
+      return g.rotate ? (double)s_q[j][c]
+                      : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * D + c]) * a.q_scale64;
+    };
+    auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
+      tile = pool_h + (size_t)s_tbl[p] * tstride;
+      row = 64 * w + i;
+      const int pos = (b0 + s_col[p]) * kRows + row;
+      const uint32_t mw = (mask_row && pos < len) ? mask_row[pos >> 5] : 0u;
+      return pos < len && !((mw >> (row & 31)) & 1u);
+    };
+    // scratch: this wave's V staging area (s_p is aliased by the merge slots of other waves)
+    precise_wave_pass<D, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sv), &s_wm[w][0], &s_wl[w][0],
+                               &s_wacc[w][0][0]);
+  } else {
     const float lt0 = row_sum16(l_run[0]), lt1 = row_sum16(l_run[1]);
     float zt[2][NGV];
 #pragma unroll

@@ -20,6 +20,7 @@
 //   per (sequence, KV head) the workgroup finalises the output itself; otherwise the split that arrives
 //   last merges all splits' partials (splitk_arrive) - one kernel per call either way.
 #include "kvq_decode_mfma_common.hpp"
+#include "kvq_decode_precise.hpp"
 
 namespace kvq {
 namespace {
@@ -349,6 +350,29 @@ __global__ __launch_bounds__(256, D >= 192 ? 1 : 2) void decode_mfma_k(TileGeom 
   }
 
   // ---------------------------------------------------------------- merge the four waves
+  // A wave whose largest logit of some head lies beyond kPreciseAbove (base-2 units) redoes its rows with fp64
+  // logits. (This kernel checks the largest logit once, after its loop, rather than each logit's terms as the
+  // row-list kernel does: its block loop has no register to spare. Terms beyond the bound that cancel to a
+  // moderate logit are not caught here; the tokens that carry the weight have logits near the largest.)
+  bool big = false;
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) big |= m_run[u] != kNegInf && fabsf(m_run[u]) > kPreciseAbove;
+  const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
+  if (wave_big) {
+    // this wave's rows again with fp64 logits; the pass writes the wave's merge slots itself
+    auto qv = [&](int j, int c) __attribute__((always_inline)) -> double {
+      return g.rotate ? (double)s_q[j][c]
+                      : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * D + c]) * a.q_scale64;
+    };
+    auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
+      tile = a.pool + ((size_t)s_tbl[p] * g.H + h) * g.tile_bytes;
+      row = r0 + i;
+      const uint32_t mword = mask_row ? s_mask[p * (kRows / 32) + (row >> 5)] : 0u;
+      return (b0 + p) * kRows + row < len && !((mword >> (row & 31)) & 1u);
+    };
+    precise_wave_pass<D, DV, G>(g, b1 - b0, tok, qv, reinterpret_cast<float*>(&s_p[w][0][0][0]), &s_wm[w][0],
+                                &s_wl[w][0], &s_wacc[w][0][0]);
+  } else {
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
     const float lt = row_sum16(l_run[u]);
@@ -374,6 +398,7 @@ __global__ __launch_bounds__(256, D >= 192 ? 1 : 2) void decode_mfma_k(TileGeom 
           s_wacc[w][jj][c] = val;
         }
     }
+  }
   }
   __syncthreads();
   if (ns == 1) {

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "kvq_decode_mfma_common.hpp"
+#include "kvq_decode_precise.hpp"
 
 namespace kvq {
 namespace {
@@ -530,6 +531,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 
   uint8_t* sv = s_v[w];
   _Float16* sp = s_p[w];
+  // Set when a chunk of this wave had logit terms above kPreciseAbove: the wave's rows then go through the fp64
+  // pass (precise_wave_pass) after the main loop (wave-uniform).
+  bool wave_big = false;
 
   auto process = [&](const Raw& r, auto kc) __attribute__((always_inline)) {
     constexpr int KIND = decltype(kc)::value;
@@ -583,18 +587,24 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         acc[c] = mfma16(qa[s], b, acc[c]);
       }
     float sc[NC];
+    bool big = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const bool live = head_ok && ((r.valid >> c) & 1u);
       if constexpr (F16) {
-        sc[c] = live ? (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]) : kNegInf;
+        const float dk = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+        sc[c] = live ? dk : kNegInf;
+        big |= live && fabsf(dk) > kPreciseAbove;
       } else {
         const float dot = h2f(r.kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
                           h2f(r.kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
         const float zq = h2f(r.kp[c][0] >> 16) * qs0 + h2f(r.kp[c][1] >> 16) * qs1;
-        sc[c] = live ? dot * kTwo24 + zq : kNegInf;
+        const float dk = dot * kTwo24;
+        sc[c] = live ? dk + zq : kNegInf;
+        big |= live && fabsf(dk) + fabsf(zq) > kPreciseAbove;
       }
     }
+    wave_big |= __builtin_amdgcn_ballot_w64(big) != 0;
     // ---------------------------------------------------------- online softmax (head la, 16-lane rows)
     float mx = sc[0];
 #pragma unroll
@@ -794,7 +804,42 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   }
 
   // ---------------------------------------------------------------- merge the four waves
-  {
+  if (wave_big) {
+    // this wave's rows again with fp64 logits; the pass writes the wave's merge slots itself
+    auto qv = [&](int j, int c) __attribute__((always_inline)) -> double {
+      return g.rotate ? (double)s_q[j][c]
+                      : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * D + c]) * a.q_scale64;
+    };
+    if constexpr (GATHER) {
+      auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
+        const int ci = c0 + w + 4 * p;
+        const int kind = kind_of(ci);
+        const int rpc = chunk_rows(kind);
+        int start = 0, n = nrow[0];
+#pragma unroll
+        for (int k = 1; k < NWD; ++k) {
+          start = kind == k ? cend[k - 1] : start;
+          n = kind == k ? nrow[k] : n;
+        }
+        const int e0 = (ci - start) * rpc, idx = e0 + i;
+        const bool ok = i < rpc && idx < n;
+        const uint32_t e = lists[(size_t)kind * a.list_cap + (ok ? idx : e0)];
+        tile = pool_h + (size_t)(e >> 8) * tstride;
+        row = (int)(e & 255u);
+        return ok;
+      };
+      precise_wave_pass<D, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
+                                 &s_wacc[w][0][0]);
+    } else {
+      auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
+        tile = pool_h + (size_t)s_tbl[p] * tstride;
+        row = 64 * w + i;
+        return (b0 + p) * kRows + row < len;
+      };
+      precise_wave_pass<D, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
+                                 &s_wacc[w][0][0]);
+    }
+  } else {
     const float lt = row_sum16(l_run);
     const float zt0 = row_sum16(zacc0), zt1 = row_sum16(zacc1);
     if (head_ok) {

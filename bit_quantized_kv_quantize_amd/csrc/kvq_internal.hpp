@@ -106,15 +106,18 @@ __host__ __device__ inline void rows_work(const SplitPlan& p, int n_pairs, int w
 }
 SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
 size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
-// Byte offsets of the workspace regions (split-K counters, partial (m, l), partial accumulators, row
-// counts, row lists) for a call of this size; `total` is the size.
+// Byte offsets of the workspace regions (partial (m, l), partial accumulators, row counts, row lists,
+// cascade flags) for a call of this size, all below `body`; the split-K arrival counters (ctr_bytes) take
+// the end of the caller's workspace (ctr_offset). `total` is the size a call of this size needs.
 struct WorkspaceLayout {
-  size_t ctr, ml, acc, cnt, list, bcnt, cflag, total;
+  size_t ml, acc, cnt, list, bcnt, cflag, body, ctr_bytes, total;
   size_t parts;  // partial slots the ml / acc regions hold
   int list_cap;
   int bcnt_blocks;  // blocks per sequence in the per-block live-row counts
 };
 WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads, int max_seq_len);
+// Offset of the arrival counters in a workspace of workspace_bytes (>= w.total) bytes.
+size_t ctr_offset(const WorkspaceLayout& w, size_t workspace_bytes);
 
 // Launchers (defined next to their kernels). They return hipSuccess or the launch error.
 // rot_c / unrot_c apply to K rows, rot_cv / unrot_cv to V rows (they differ when the head dims do).
@@ -138,7 +141,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const uint32_t* mask;
   float* out;
-  unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernel); zero between calls
+  unsigned* ws_ctr; // [n_seqs][H_kv] split-K arrival counters (matrix-core kernels), at the workspace's end;
+                    // zero between calls
   float* ws_ml;   // [n_seqs][H_q][plan.stride] x {m, l} (the generic kernel: [plan.n_splits])
   float* ws_acc;  // [n_seqs][H_q][plan.stride][d]
   int* ws_cnt;       // [n_seqs][W] live rows per width list (row-list kernel; W = 2: 4-bit, 8-bit; W = 4
@@ -155,14 +159,16 @@ struct DecodeArgs {
   int max_blocks_per_seq;
   int mask_words;
   float q_scale;   // softmax_scale * log2(e): logits are kept in base-2 units
+  double q_scale64;  // the same in fp64, for logits recomputed in fp64
   float unrot_c;   // 1 / (d * fp32(1/sqrt(d))): inverse of the quantiser's rotation scale of K rows
   float unrot_cv;  // the same for V rows (dv in place of d)
   SplitPlan plan;
 };
 // Decode dispatch: the row-list matrix-core kernel (per-token K groups) or the per-channel-K matrix-core
 // kernel where their layouts are compiled, then the block matrix-core kernel, then the generic kernel.
-// The environment variable KVQ_DECODE_KERNEL (a test hook) may name "generic" or "mfma" to skip the
-// kernels before it, or "nocascade" to keep shared blocks in the per-sequence kernel.
+// In the debug build (KVQ_DEBUG) only, the environment variable KVQ_DECODE_KERNEL (a test hook) may name
+// "generic" or "mfma" to skip the kernels before it, or "nocascade" to keep shared blocks in the
+// per-sequence kernel.
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 bool decode_rows_supported(const TileGeom& g, int G);
 bool decode_kchan_supported(const TileGeom& g, int G);

@@ -62,6 +62,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point is exported from the shared library; the library's internal symbols are hidden. */
+#define KVQ_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -104,22 +107,23 @@ typedef struct kvq_layout {
 } kvq_layout;
 
 /* KVQ_OK if the layout is one this library can store and process, else the status explaining why. */
-int kvq_check_layout(const kvq_layout* L);
+KVQ_API int kvq_check_layout(const kvq_layout* L);
 
 /* Bytes of one tile (256 rows of one KV head), a multiple of 256; 0 if the layout is invalid. */
-size_t kvq_tile_bytes(const kvq_layout* L);
+KVQ_API size_t kvq_tile_bytes(const kvq_layout* L);
 
 /* Bytes of a pool of num_blocks blocks (num_blocks * H_kv tiles); 0 if invalid. */
-size_t kvq_pool_bytes(const kvq_layout* L, int32_t num_blocks);
+KVQ_API size_t kvq_pool_bytes(const kvq_layout* L, int32_t num_blocks);
 
 /* Bytes of device workspace kvq_decode_attention needs for these sizes; 0 if invalid. The value depends
- * only on the arguments, so a workspace sized here is valid for every call with the same or smaller
- * n_seqs and max_seq_len. */
-size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_seqs, int32_t num_q_heads,
+ * only on the arguments and never decreases as n_seqs or max_seq_len grow, so a workspace sized here is
+ * valid for every call with the same layout and num_q_heads and the same or smaller n_seqs and
+ * max_seq_len. */
+KVQ_API size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_seqs, int32_t num_q_heads,
                                   int32_t max_seq_len);
 
 /* Static, human-readable name of a status code. Never NULL. */
-const char* kvq_status_string(int status);
+KVQ_API const char* kvq_status_string(int status);
 
 /*
  * kvq_quantize_blocks - quantise whole 256-token blocks into the pool ([AMB] 2.1 items 1-2; rotation
@@ -140,7 +144,7 @@ const char* kvq_status_string(int status);
  * Errors: KVQ_ERR_ARG (null pool/k/v/block_ids with n_blocks > 0, prec_bits for a non-mixed layout,
  * invalid layout), KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP.
  */
-int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_ids, int32_t n_blocks,
+KVQ_API int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_ids, int32_t n_blocks,
                         const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
                         void* stream);
 
@@ -163,7 +167,7 @@ int kvq_quantize_blocks(const kvq_layout* L, void* pool, const int32_t* block_id
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (per-channel K groups: a partial block has no defined
  * channel statistics), KVQ_ERR_HIP.
  */
-int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k,
+KVQ_API int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uint16_t* k,
                       const uint16_t* v, const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* positions, const uint8_t* prec, void* stream);
 
@@ -182,7 +186,7 @@ int kvq_append_tokens(const kvq_layout* L, void* pool, int32_t n_seqs, const uin
  * rounded to fp16 by one fp16 ulp.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP.
  */
-int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* block_ids, int32_t n_blocks,
+KVQ_API int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* block_ids, int32_t n_blocks,
                           uint16_t* k_out, uint16_t* v_out, void* stream);
 
 /*
@@ -195,7 +199,7 @@ int kvq_dequantize_blocks(const kvq_layout* L, const void* pool, const int32_t* 
  *                       dst_pool. Destination ids must be distinct.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP.
  */
-int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* src_ids, void* dst_pool,
+KVQ_API int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* src_ids, void* dst_pool,
                     const int32_t* dst_ids, int32_t n_blocks, void* stream);
 
 /*
@@ -219,16 +223,19 @@ int kvq_copy_blocks(const kvq_layout* L, const void* src_pool, const int32_t* sr
  *   softmax_scale  logit = softmax_scale * (q . k) for live slots (usually 1/sqrt(d)).
  *   out            device fp32 [n_seqs][num_q_heads][dv]: softmax-weighted sum of the dequantised (and,
  *                  for rotated pools, un-rotated) V rows. A sequence with seq_lens[s] == 0 gets zeros.
- *   workspace      device scratch of at least kvq_decode_workspace_bytes(L, n_seqs, num_q_heads,
- *                  max_seq_len) bytes, 256-byte aligned: split-K partials and, in its first
- *                  n_seqs * H_kv * 4 bytes, per-(sequence, KV head) arrival counters. Zero-fill it once
- *                  before its first use; every completed call leaves the counters at zero again, so the
- *                  same workspace serves later calls of the same or smaller size without clearing.
- *                  Calls sharing one workspace must not overlap on the device.
+ *   workspace      device scratch of workspace_bytes >= kvq_decode_workspace_bytes(L, n_seqs,
+ *                  num_q_heads, max_seq_len) bytes, 256-byte aligned: split-K partials and live-row lists
+ *                  from its start, and per-(sequence, KV head) arrival counters (uint32) in its last
+ *                  n_seqs * H_kv * 4 bytes below workspace_bytes rounded down to a multiple of 4. Zero-fill
+ *                  it once before its first use; every completed call leaves the counters at zero again,
+ *                  and no call writes anything else into the counter span of a call of the same or larger
+ *                  size, so the same workspace serves later calls of the same or smaller size (same
+ *                  layout and num_q_heads) without clearing, provided every call passes the same
+ *                  workspace_bytes. Calls sharing one workspace must not overlap on the device.
  * Errors: KVQ_ERR_ARG (also n_seqs > 65535), KVQ_ERR_UNSUPPORTED (more than 16 query heads per
  * KV head), KVQ_ERR_WORKSPACE, KVQ_ERR_HIP.
  */
-int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+KVQ_API int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
                          int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
                          const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
                          int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,

@@ -11,14 +11,19 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
 LIB = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "libkvq.so")
+DEBUG_LIB = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "libkvq_debug.so")
 
 
 @pytest.fixture(scope="module")
 def kvq():
-    if not os.path.exists(LIB):
-        from bit_quantized_kv_quantize_amd import _build
+    if not (os.path.exists(LIB) and os.path.exists(DEBUG_LIB)):
+        import importlib.util
 
-        _build.build()
+        spec = importlib.util.spec_from_file_location(
+            "kvq_build", os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "_build.py"))
+        _build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(_build)
+        _build.build_all()
     import bit_quantized_kv_quantize_amd as kvq
 
     return kvq
@@ -30,14 +35,18 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
 
 
-def test_every_declared_symbol_is_exported(kvq):
+@pytest.mark.parametrize("path", [LIB, DEBUG_LIB])
+def test_every_declared_symbol_is_exported(kvq, path):
+    # the release library and its debug build export exactly the header's entry points (internal symbols
+    # are hidden)
     names = declared_functions()
     assert len(names) == 10, names
-    dyn = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r" T (kvq_\w+)", dyn))
+    dyn = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" [TW] (\S+)", dyn))
     assert set(names) <= exported, set(names) - exported
+    assert not {e for e in exported if e.startswith("_ZN3kvq")}, "internal symbols exported"
     assert set(kvq.EXPORTS) == set(names)
-    lib = ctypes.CDLL(LIB)
+    lib = ctypes.CDLL(path)
     for n in names:
         assert getattr(lib, n) is not None
 
