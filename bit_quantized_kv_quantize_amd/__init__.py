@@ -81,6 +81,8 @@ def _load(path):
     L.kvq_decode_attention.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P,
                                        ctypes.c_size_t, _P]
     L.kvq_decode_attention.restype = ctypes.c_int
+    L.kvq_decode_attention_static.argtypes = [_LP, _P, _P, _I, _I, _P, _I, _P, _I, _P, _I, ctypes.c_float, _P, _P]
+    L.kvq_decode_attention_static.restype = ctypes.c_int
     return L
 
 
@@ -107,7 +109,7 @@ def use_library(which: str = "release"):
 
 EXPORTS = ("kvq_check_layout", "kvq_tile_bytes", "kvq_pool_bytes", "kvq_decode_workspace_bytes",
            "kvq_status_string", "kvq_quantize_blocks", "kvq_dequantize_blocks", "kvq_copy_blocks",
-           "kvq_append_tokens", "kvq_decode_attention")
+           "kvq_append_tokens", "kvq_decode_attention", "kvq_decode_attention_static")
 
 
 def lib():

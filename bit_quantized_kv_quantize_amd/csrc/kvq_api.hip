@@ -4,6 +4,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #ifdef KVQ_DEBUG
 #include <stdio.h>
 
@@ -239,6 +240,116 @@ static float unrot_scale(int n) { return (float)(1.0 / ((double)n * (double)rot_
 
 using namespace kvq;
 
+// ---------------------------------------------------------------------------------- static scratch
+// kvq_decode_attention_static's workspace: one file-scope device array per GPU, held until the process ends.
+// Its first kStaticBody bytes take the partials and row lists, the last kStaticCtrBytes the split-K arrival
+// counters, which are cleared once per GPU (before the first call's kernels, on its stream) and left at zero
+// by every completed call. Host code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per GPU with that GPU current.
+constexpr size_t kStaticBytes = (size_t)KVQ_STATIC_WORKSPACE_BYTES;
+constexpr size_t kStaticCtrBytes = (size_t)1 << 20;
+constexpr size_t kStaticBody = kStaticBytes - kStaticCtrBytes;
+static __device__ __align__(256) uint8_t scratch[kStaticBytes];
+
+namespace {
+__global__ void clear_words_k(unsigned* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+}  // namespace
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch[kMaxDevices];
+
+// The current GPU's scratch address in *base (set up on the first call on that GPU).
+static int static_scratch(hipStream_t stream, uint8_t** base) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVQ_ERR_HIP;
+    hipLaunchKernelGGL(clear_words_k, dim3(256), dim3(256), 0, stream, (unsigned*)((uint8_t*)ptr + kStaticBody),
+                       kStaticCtrBytes / sizeof(unsigned));
+    if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+    g_scratch[dev] = (uint8_t*)ptr;
+  }
+  *base = g_scratch[dev];
+  return KVQ_OK;
+}
+
+// Both decode entry points. With ctr == nullptr the workspace is the caller's (workspace_bytes of it, split-K
+// counters at its end); otherwise `workspace` holds the body regions (workspace_bytes of room for them) and
+// `ctr` the counters (ctr_words of room).
+static int decode_entry(const char* fn, const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+                        int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
+                        int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,
+                        size_t workspace_bytes, unsigned* ctr, size_t ctr_words, void* stream) {
+  int st = check_layout(L);
+  if (st != KVQ_OK) return st;
+  if (n_seqs < 0 || n_seqs > 65535 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return KVQ_ERR_ARG;
+  if (num_q_heads % L->num_kv_heads != 0) return KVQ_ERR_ARG;
+  if ((long)max_seq_len > (long)max_blocks_per_seq * kRows) return KVQ_ERR_ARG;
+  if (sentinel_mask && (long)mask_words_per_seq * 32 < (long)max_seq_len) return KVQ_ERR_ARG;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
+  if (n_seqs == 0) return KVQ_OK;
+  if (!pool || !q || !block_table || !seq_lens || !out) return KVQ_ERR_ARG;
+  TileGeom g = make_geom(L);
+  const int G = num_q_heads / g.H;
+  if (G > 16) return KVQ_ERR_UNSUPPORTED;
+#ifdef KVQ_DEBUG
+  {
+    std::vector<int32_t> len, first(n_seqs, 0), last(n_seqs);
+    if (!fetch_i32(seq_lens, (size_t)n_seqs, len, (hipStream_t)stream)) return KVQ_ERR_HIP;
+    for (int s = 0; s < n_seqs; ++s) {
+      if (len[s] < 0 || len[s] > max_seq_len)
+        return debug_fail(fn, "sequence length outside [0, max_seq_len]", s, len[s]);
+      last[s] = (len[s] + kRows - 1) / kRows;
+    }
+    if ((st = check_table(fn, g, pool, block_table, n_seqs, max_blocks_per_seq, first, last,
+                          (hipStream_t)stream)) != KVQ_OK)
+      return st;
+  }
+#endif
+  const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
+  const size_t need = ctr ? wl.body : wl.total;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVQ_ERR_WORKSPACE;
+  if (ctr && wl.ctr_bytes > ctr_words * sizeof(unsigned)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a{};
+  a.pool = (const uint8_t*)pool;
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.mask = sentinel_mask;
+  a.out = out;
+  a.plan = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
+  if ((size_t)n_seqs * num_q_heads * a.plan.stride > wl.parts) return KVQ_ERR_UNSUPPORTED;  // never, by the bound
+  uint8_t* ws = (uint8_t*)workspace;
+  a.ws_ctr = ctr ? ctr : (unsigned*)(ws + ctr_offset(wl, workspace_bytes));
+  a.ws_ml = (float*)(ws + wl.ml);
+  a.ws_acc = (float*)(ws + wl.acc);
+  a.ws_cnt = (int*)(ws + wl.cnt);
+  a.ws_list = (uint32_t*)(ws + wl.list);
+  a.list_cap = wl.list_cap;
+  a.ws_bcnt = (int*)(ws + wl.bcnt);
+  a.bcnt_blocks = wl.bcnt_blocks;
+  a.ws_cflag = (int*)(ws + wl.cflag);
+  a.casc = 0;  // set by the dispatcher when the cascade kernel runs
+  a.n_seqs = n_seqs;
+  a.num_q_heads = num_q_heads;
+  a.G = G;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.mask_words = sentinel_mask ? mask_words_per_seq : 0;
+  a.q_scale64 = (double)softmax_scale * 1.4426950408889634;  // log2(e)
+  a.q_scale = (float)a.q_scale64;
+  a.unrot_c = unrot_scale(g.d);
+  a.unrot_cv = unrot_scale(g.dv);
+  return hip_status(launch_decode(g, a, (hipStream_t)stream));
+}
+
+
 extern "C" {
 
 int kvq_check_layout(const kvq_layout* L) { return check_layout(L); }
@@ -359,66 +470,22 @@ int kvq_decode_attention(const kvq_layout* L, const void* pool, const uint16_t* 
                          const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
                          int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  int st = check_layout(L);
+  return decode_entry("kvq_decode_attention", L, pool, q, n_seqs, num_q_heads, block_table, max_blocks_per_seq,
+                      seq_lens, max_seq_len, sentinel_mask, mask_words_per_seq, softmax_scale, out, workspace,
+                      workspace_bytes, nullptr, 0, stream);
+}
+
+int kvq_decode_attention_static(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+                                int32_t num_q_heads, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len, const uint32_t* sentinel_mask,
+                                int32_t mask_words_per_seq, float softmax_scale, float* out, void* stream) {
+  uint8_t* base = nullptr;
+  const int st = static_scratch((hipStream_t)stream, &base);
   if (st != KVQ_OK) return st;
-  if (n_seqs < 0 || n_seqs > 65535 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_seq_len < 0)
-    return KVQ_ERR_ARG;
-  if (num_q_heads % L->num_kv_heads != 0) return KVQ_ERR_ARG;
-  if ((long)max_seq_len > (long)max_blocks_per_seq * kRows) return KVQ_ERR_ARG;
-  if (sentinel_mask && (long)mask_words_per_seq * 32 < (long)max_seq_len) return KVQ_ERR_ARG;
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_ARG;
-  if (n_seqs == 0) return KVQ_OK;
-  if (!pool || !q || !block_table || !seq_lens || !out) return KVQ_ERR_ARG;
-  TileGeom g = make_geom(L);
-  const int G = num_q_heads / g.H;
-  if (G > 16) return KVQ_ERR_UNSUPPORTED;
-#ifdef KVQ_DEBUG
-  {
-    std::vector<int32_t> len, first(n_seqs, 0), last(n_seqs);
-    if (!fetch_i32(seq_lens, (size_t)n_seqs, len, (hipStream_t)stream)) return KVQ_ERR_HIP;
-    for (int s = 0; s < n_seqs; ++s) {
-      if (len[s] < 0 || len[s] > max_seq_len)
-        return debug_fail("kvq_decode_attention", "sequence length outside [0, max_seq_len]", s, len[s]);
-      last[s] = (len[s] + kRows - 1) / kRows;
-    }
-    if ((st = check_table("kvq_decode_attention", g, pool, block_table, n_seqs, max_blocks_per_seq, first, last,
-                          (hipStream_t)stream)) != KVQ_OK)
-      return st;
-  }
-#endif
-  size_t need = decode_workspace_bytes(g, n_seqs, num_q_heads, max_seq_len);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return KVQ_ERR_WORKSPACE;
-  DecodeArgs a{};
-  a.pool = (const uint8_t*)pool;
-  a.q = q;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.mask = sentinel_mask;
-  a.out = out;
-  a.plan = plan_splits(g, n_seqs, num_q_heads, max_seq_len);
-  const WorkspaceLayout wl = workspace_layout(g, n_seqs, num_q_heads, max_seq_len);
-  if ((size_t)n_seqs * num_q_heads * a.plan.stride > wl.parts) return KVQ_ERR_UNSUPPORTED;  // never, by the bound
-  uint8_t* ws = (uint8_t*)workspace;
-  a.ws_ctr = (unsigned*)(ws + ctr_offset(wl, workspace_bytes));
-  a.ws_ml = (float*)(ws + wl.ml);
-  a.ws_acc = (float*)(ws + wl.acc);
-  a.ws_cnt = (int*)(ws + wl.cnt);
-  a.ws_list = (uint32_t*)(ws + wl.list);
-  a.list_cap = wl.list_cap;
-  a.ws_bcnt = (int*)(ws + wl.bcnt);
-  a.bcnt_blocks = wl.bcnt_blocks;
-  a.ws_cflag = (int*)(ws + wl.cflag);
-  a.casc = 0;  // set by the dispatcher when the cascade kernel runs
-  a.n_seqs = n_seqs;
-  a.num_q_heads = num_q_heads;
-  a.G = G;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.mask_words = sentinel_mask ? mask_words_per_seq : 0;
-  a.q_scale64 = (double)softmax_scale * 1.4426950408889634;  // log2(e)
-  a.q_scale = (float)a.q_scale64;
-  a.unrot_c = unrot_scale(g.d);
-  a.unrot_cv = unrot_scale(g.dv);
-  return hip_status(launch_decode(g, a, (hipStream_t)stream));
+  return decode_entry("kvq_decode_attention_static", L, pool, q, n_seqs, num_q_heads, block_table,
+                      max_blocks_per_seq, seq_lens, max_seq_len, sentinel_mask, mask_words_per_seq, softmax_scale,
+                      out, base, kStaticBody, (unsigned*)(base + kStaticBody), kStaticCtrBytes / sizeof(unsigned),
+                      stream);
 }
 
 }  // extern "C"

@@ -241,6 +241,32 @@ KVQ_API int kvq_decode_attention(const kvq_layout* L, const void* pool, const ui
                          int32_t mask_words_per_seq, float softmax_scale, float* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Bytes of the per-GPU device array that kvq_decode_attention_static uses as its workspace: the last 1 MiB
+ * holds the split-K arrival counters, the rest the partials and live-row lists. */
+#define KVQ_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/*
+ * kvq_decode_attention_static - kvq_decode_attention with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library routine); its scratch is a
+ * file-scope device array of KVQ_STATIC_WORKSPACE_BYTES that each GPU the library runs on holds until the
+ * process ends. The first call on a GPU looks up that GPU's copy (hipGetSymbolAddress) and clears its counter
+ * span with a small kernel on `stream`, ahead of its own kernels; every completed call leaves the counters at
+ * zero again. Arguments, results and errors are those of kvq_decode_attention, plus:
+ *   - KVQ_ERR_WORKSPACE when the call needs more than KVQ_STATIC_WORKSPACE_BYTES - 1 MiB of partials and row
+ *     lists (kvq_decode_workspace_bytes minus the counters) or more than 1 MiB of counters (n_seqs * H_kv >
+ *     262144); nothing is launched;
+ *   - KVQ_ERR_HIP when the current GPU's copy of the array cannot be found.
+ * Every call on one GPU shares that GPU's array and it keeps the last call's contents: calls that may overlap
+ * on one GPU (different streams without ordering between them, or different host threads) race and must be
+ * serialised by the caller.
+ */
+KVQ_API int kvq_decode_attention_static(const kvq_layout* L, const void* pool, const uint16_t* q, int32_t n_seqs,
+                                        int32_t num_q_heads, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                        const uint32_t* sentinel_mask, int32_t mask_words_per_seq,
+                                        float softmax_scale, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
