@@ -690,12 +690,16 @@ int orc_decode_attention(const orc_layout* L, const uint8_t* pool, const uint16_
   return ORC_OK;
 }
 
-/* Threads the OpenMP runtime will use for a parallel region (1 without OpenMP). */
 /* Threads of the parallel loops that take no thread count (quantisation); 0 keeps OpenMP's default. */
 void orc_set_threads(int32_t n) {
+#ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
 }
 
+/* Threads the OpenMP runtime will use for a parallel region (1 without OpenMP). */
 int32_t orc_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
