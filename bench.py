@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama31_8b_pool_8k", choices=W.CONFIG_ORDER)
-    ap.add_argument("--kernel-reps", type=int, default=10, help="graph replays of all layers' decode kernels")
+    ap.add_argument("--kernel-reps", type=int, default=50, help="graph replays of all layers' decode kernels")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -51,11 +51,20 @@ def parse():
     ap.add_argument("--workload-table", default="",
                     help="comma-separated workloads for the per-workload table (default: every workload)")
     ap.add_argument("--workload-launches", type=int, default=16, help="decode launches per workload graph")
+    ap.add_argument("--workload-reps", type=int, default=20, help="timed replays of each workload graph")
+    ap.add_argument("--cpu-budget", type=float, default=1.0,
+                    help="scale of the CPU oracle samples (1.0: about half a minute of oracle time)")
     return ap.parse_args()
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def pct(xs):
+    """median, p10 and p90 of a list of times."""
+    a = np.asarray(xs, np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
 
 
 def live_rows(case: W.Case, width_words=None, appended_prec=None):
@@ -137,6 +146,8 @@ def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if not os.path.isfile(os.path.join(csrc, f)):
+            continue  # (the probe library's sources are not libkvq's)
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -253,11 +264,15 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         run()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t_start) / args.steps
+    step_med, step_p10, step_p90 = pct([evs[i].elapsed_time(evs[i + 1]) / 1e3 for i in range(args.steps)])
     dec_b = decode_bytes(cfg, case, live_rows(case))
     app_b = append_bytes(cfg, case.n_seqs)
     step_bytes = (dec_b + app_b) * layers
@@ -289,10 +304,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per_rep.append(e0.elapsed_time(e1) / 1e3 / layers)
-    kern_s = float(np.median(per_rep))
+    kern_s, kern_p10, kern_p90 = pct(per_rep)
     achieved = dec_b / kern_s / 1e9
-    log("decode kernel: %.2f us per launch (median of %d graph replays of %d launches) -> %.1f GB/s" %
-        (kern_s * 1e6, len(per_rep), layers, achieved))
+    log("decode kernel: %.2f us per launch (median of %d graph replays of %d launches; p10 %.2f, p90 %.2f) -> "
+        "%.1f GB/s" % (kern_s * 1e6, len(per_rep), layers, kern_p10 * 1e6, kern_p90 * 1e6, achieved))
+
+    # the streaming-read ceiling: the same tiles read with the decode's load pattern and no arithmetic, and a
+    # flat 2 GiB read
+    ceiling = read_ceiling(torch, cfg, case, pools, table, seq_lens, layers)
 
     # plain device copy of 2 GiB for context (read + write bandwidth the box delivers)
     a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
@@ -325,10 +344,15 @@ def main():
         for name in names:
             if name != cfg.name:
                 workloads[name] = measure_workload(kvq, torch, name, launches=args.workload_launches,
-                                                   graph=not args.no_graph)
-        workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2), "bytes": dec_b,
-                               "GBps": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4),
-                               "pool_instances": layers, "append_us": None}
+                                                   graph=not args.no_graph, reps=args.workload_reps)
+        workloads[cfg.name] = {"decode_us": round(kern_s * 1e6, 2),
+                               "decode_us_p10_p90": [round(kern_p10 * 1e6, 2), round(kern_p90 * 1e6, 2)],
+                               "bytes": dec_b, "GBps": round(achieved, 1),
+                               "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBPS, 4), "pool_instances": layers,
+                               "append_us": None,
+                               "quantize": None if q_tok_s is None else {
+                                   "blocks": int(n_prefill) * layers, "us": round(qs_t * 1e6, 2),
+                                   "token_layers_per_s": round(q_tok_s, 0), "GBps": round(q_gbps, 1)}}
 
     # ---------------------------------------------------------------- baselines of the pages' comparisons
     baselines = None
@@ -344,7 +368,13 @@ def main():
     # ---------------------------------------------------------------- CPU oracle on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, case, dec_b)
+        dec_bytes = {n: (workloads[n]["bytes"] if workloads and n in workloads else None) for n in CPU_SAMPLES}
+        for n in dec_bytes:
+            if dec_bytes[n] is None:
+                c = W.make_case(W.CONFIGS[n])
+                dec_bytes[n] = decode_bytes(c.cfg, c, live_rows(c)) if not c.cfg.mixed else None
+        dec_bytes = {n: b for n, b in dec_bytes.items() if b}
+        cpu = cpu_baseline(cfg.name, dec_bytes, args.cpu_budget) if cfg.name in dec_bytes else None
 
     line = {
         "metric": "Q4 decode-attention effective HBM GB/s (% of peak) + KV tokens/s quantized",
@@ -354,6 +384,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step_median_p10_p90": [round(step_med * 1e3, 4), round(step_p10 * 1e3, 4), round(step_p90 * 1e3, 4)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -371,6 +402,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "decode_rows_k<4, false, false>", "bytes_per_launch": dec_b,
                      "us_per_launch": round(kern_s * 1e6, 3),
+                     "us_per_launch_p10_p90": [round(kern_p10 * 1e6, 3), round(kern_p90 * 1e6, 3)],
+                     "launches_timed": len(per_rep) * layers,
+                     "ceiling": ceiling,
+                     "frac_of_flat_read": None if not ceiling else round(achieved / ceiling["flat_GBps"], 4),
+                     "frac_of_tile_read": None if not ceiling else round(achieved / ceiling["tiles_GBps"], 4),
                      "kernel_sources": digest},
         "cpu_baseline": cpu,
         "workloads": workloads,
@@ -393,6 +429,82 @@ MLA_POOL = "deepseek_v2_lite_mla_8k"
 
 def workload_config(name):
     return W.named_config(name)
+
+
+def read_ceiling(torch, cfg, case, pools, table, seq_lens, layers, reps=20):
+    """Streaming-read ceilings from libkvq_probe.so: the decode's own tiles of every layer read with its load
+    pattern (512 workgroups, 16-byte loads, rows below each sequence's length, no arithmetic), timed like the
+    decode kernel (a graph of one launch per layer between events), and a flat 2 GiB read."""
+    import ctypes
+
+    path = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        log("no libkvq_probe.so: read ceiling not measured")
+        return None
+    lib = ctypes.CDLL(path)
+    P, I, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
+    lib.kvq_probe_read_tiles.argtypes = [P, P, P, I, I, I, U, U, U, U, I, P, P]
+    lib.kvq_probe_read_linear.argtypes = [P, ctypes.c_size_t, I, P, P]
+    d, dv, H = cfg.head_dim, cfg.dv, cfg.num_kv_heads
+    rec = (d + dv) // 2
+    prow = 4 * (d // cfg.k_group + dv // cfg.v_group)
+    import bit_quantized_kv_quantize_amd as kvq
+    tb = kvq.tile_bytes(kvq.Layout(**cfg.layout()))
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def tiles(l):
+        st = lib.kvq_probe_read_tiles(P(pools[l].data_ptr()), P(table.data_ptr()), P(seq_lens.data_ptr()),
+                                      case.n_seqs, H, case.max_blocks_per_seq, tb, rec, 256 * rec, prow, 512,
+                                      P(sink.data_ptr()), P(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+
+    def timed(fn, n):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3 / n)
+        return pct(ts)
+
+    kv_bytes = int(case.seq_lens.sum()) * H * (rec + prow)
+    t_tiles, _, _ = timed(tiles, layers)
+    # flat reads of the decode's byte count, cycling through enough buffers to exceed the Infinity Cache
+    nbytes = kv_bytes // 16 * 16
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(max(4, (1 << 31) // nbytes + 1))]
+
+    def linear(i):
+        st = lib.kvq_probe_read_linear(P(bufs[i % len(bufs)].data_ptr()), nbytes, 2048, P(sink.data_ptr()),
+                                       P(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+
+    t_lin, _, _ = timed(linear, len(bufs))
+    res = {"tiles_GBps": round(kv_bytes / t_tiles / 1e9, 1), "tiles_us": round(t_tiles * 1e6, 2),
+           "flat_GBps": round(nbytes / t_lin / 1e9, 1), "flat_us": round(t_lin * 1e6, 2), "bytes": kv_bytes,
+           "kind": "libkvq_probe, per launch in a graph: the decode's tiles read with its load pattern and work "
+                   "split and no arithmetic (tiles), and a flat read of the same byte count from 2048 "
+                   "workgroups (flat)"}
+    del bufs
+    torch.cuda.empty_cache()
+    log("read ceiling (%.1f MB per launch): decode tiles %.1f us -> %.0f GB/s; flat read %.1f us -> %.0f GB/s" %
+        (kv_bytes / 1e6, t_tiles * 1e6, res["tiles_GBps"], t_lin * 1e6, res["flat_GBps"]))
+    return res
 
 
 def measure_restore(kvq, torch, name, launches=4):
@@ -439,21 +551,26 @@ def measure_restore(kvq, torch, name, launches=4):
             "GBps": round(moved / us / 1e3, 1)}
 
 
-def measure_workload(kvq, torch, name, launches=16, graph=True):
+def measure_workload(kvq, torch, name, launches=16, graph=True, reps=20):
     """One workload at full size: its layer quantised on the GPU (copied to INSTANCES pools), the append
     where the workload appends, then decode kernels captured back to back in a HIP graph (cycling the
-    pools) and timed between events on the launch stream (launched eagerly with graph=False). Returns
-    per-launch times and algorithmic bytes."""
+    pools) and timed between events on the launch stream (launched eagerly with graph=False); the prefill
+    quantiser timed the same way on the layer's first chunk of blocks (at most 2048, kept resident).
+    Returns per-launch times (median, p10, p90) and algorithmic bytes."""
     cfg = workload_config(name)
     case = W.make_case(cfg)
     lay = kvq.Layout(**cfg.layout())
     pool = kvq.new_pool(lay, case.num_blocks)
     prec = np.full(case.n_seqs, 4, np.uint8) if cfg.mixed else None
     wide = {} if cfg.mixed else None
+    qchunk = None
     for ids, k, v, bm in W.prefill_chunks(case, 0, max_blocks=2048, threads=16, prec_out=prec):
-        kvq.quantize_blocks(lay, pool, torch.from_numpy(ids).cuda(), torch.from_numpy(k).view(torch.float16).cuda(),
-                            torch.from_numpy(v).view(torch.float16).cuda(),
-                            None if bm is None else torch.from_numpy(bm.view(np.int32)).cuda())
+        dev_in = (torch.from_numpy(ids).cuda(), torch.from_numpy(k).view(torch.float16).cuda(),
+                  torch.from_numpy(v).view(torch.float16).cuda(),
+                  None if bm is None else torch.from_numpy(bm.view(np.int32)).cuda())
+        kvq.quantize_blocks(lay, pool, *dev_in)
+        if qchunk is None:
+            qchunk = dev_in
         if bm is not None:
             for i, b in enumerate(ids):
                 wide[int(b)] = bm[i]
@@ -496,68 +613,114 @@ def measure_workload(kvq, torch, name, launches=16, graph=True):
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         ts = []
-        for _ in range(5):
+        for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             run()
             e1.record(stream)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) * 1e3 / launches)
-        return float(np.median(ts))
+        return pct(ts)
 
-    dec_us = timed(lambda i: kvq.decode_attention(lay, pools[i % len(pools)], q, table, seq_lens, case.max_seq_len,
-                                                   mask, out=out, workspace=ws))
+    dec_us, dec_p10, dec_p90 = timed(lambda i: kvq.decode_attention(lay, pools[i % len(pools)], q, table, seq_lens,
+                                                                     case.max_seq_len, mask, out=out, workspace=ws))
     app_us = None
     if app is not None:
         app_us = timed(lambda i: kvq.append_tokens(lay, pools[i % len(pools)], app[0], app[1], table, positions,
-                                                   app[2]))
+                                                   app[2]))[0]
+    nq = int(qchunk[0].numel())
+    quant_us = timed(lambda i: kvq.quantize_blocks(lay, pools[i % len(pools)], *qchunk))[0]
+    quant = {"blocks": nq, "us": round(quant_us, 2), "token_layers_per_s": round(nq * W.BLOCK / quant_us * 1e6, 0),
+             "GBps": round(quantize_bytes(cfg, nq, kvq.tile_bytes(lay)) / quant_us / 1e3, 1)}
     counts = live_rows(case, wide, prec)
     b = decode_bytes(cfg, case, counts, unique=True)
-    res = {"decode_us": round(dec_us, 2), "bytes": b, "GBps": round(b / dec_us / 1e3, 1),
+    res = {"decode_us": round(dec_us, 2), "decode_us_p10_p90": [round(dec_p10, 2), round(dec_p90, 2)], "bytes": b,
+           "GBps": round(b / dec_us / 1e3, 1),
            "frac_of_hbm_peak": round(b / dec_us / 1e3 / HBM_PEAK_GBPS, 4), "pool_instances": len(pools),
-           "append_us": None if app_us is None else round(app_us, 2)}
+           "append_us": None if app_us is None else round(app_us, 2), "quantize": quant}
     b_log = decode_bytes(cfg, case, counts, unique=False)
     if b_log != b:
         res["logical_bytes"] = b_log
         res["logical_GBps"] = round(b_log / dec_us / 1e3, 1)
-    log("workload %s: decode %.2f us/launch, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)%s" %
-        (name, dec_us, b / dec_us / 1e3, b / dec_us / 1e3 / 80, "" if app_us is None else ", append %.2f us" % app_us))
-    del pools, pool
+    log("workload %s: decode %.2f us/launch, %.1f GB/s algorithmic (%.1f%% of 8 TB/s)%s; quantise %d blocks "
+        "%.1f us -> %.3g token-layers/s, %.0f GB/s" %
+        (name, dec_us, b / dec_us / 1e3, b / dec_us / 1e3 / 80, "" if app_us is None else ", append %.2f us" % app_us,
+         nq, quant_us, quant["token_layers_per_s"], quant["GBps"]))
+    del pools, pool, qchunk
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(cfg, case, dec_bytes_per_layer):
-    """The oracle as it stands, timed on this host: decode attention for one layer of the workload (all
-    agents) and quantisation of a few blocks; reported in the same units as the GPU figures."""
+# CPU oracle samples per workload: (sequences decoded with 1 thread, with all threads; blocks quantised with 1
+# thread, with all threads). Each workload's sample is a smaller case of the same shapes and distributions
+# (its first sequences); times are scaled to one whole layer of the full workload.
+CPU_SAMPLES = {
+    "tiny_1k": (1, 1, 4, 4),
+    "gemma3_12b_4k": (1, 1, 8, 16),
+    "llama31_8b_pool_8k": (1, 12, 8, 96),
+    "qwen25_14b_prefix_32k": (1, 8, 8, 96),
+    "mixed_sentinel_32k": (1, 16, 8, 96),
+}
+
+
+def cpu_baseline(headline, dec_bytes, budget=1.0):
+    """The oracle as it stands, timed on this host's cores: per workload, decode attention and quantisation
+    with one thread and with all threads (OpenMP over (sequence, KV head) and over tiles), on bounded samples
+    scaled to one layer of the full workload. ``dec_bytes``: the GPU's algorithmic decode bytes per layer of
+    each workload (the same bytes for the GB/s figures). ``value`` is the headline workload's decode GB/s
+    with all threads."""
     import oracle
 
-    cores = len(os.sched_getaffinity(0))
-    threads = min(cores, 16)
-    lay = oracle.make_layout(**cfg.layout())
-    tb = oracle.tile_bytes(lay)
-    layer = 0
-    k, v = W.blocks_kv(cfg, layer, case.prefill_blocks, threads=threads)
-    pool = np.zeros(tb * cfg.num_kv_heads * case.num_blocks, np.uint8)
-    nq = 32
-    t0 = time.perf_counter()
-    oracle.quantize_blocks(lay, pool, case.prefill_blocks[:nq], k[: nq * W.BLOCK], v[: nq * W.BLOCK])
-    tq = time.perf_counter() - t0
-    oracle.quantize_blocks(lay, pool, case.prefill_blocks[nq:], k[nq * W.BLOCK:], v[nq * W.BLOCK:])
-    ak, av = W.append_kv(cfg, layer, case.n_seqs)
-    oracle.append_tokens(lay, pool, ak, av, case.block_table, case.positions)
-    q = W.queries(cfg, layer, case.n_seqs)
-    t0 = time.perf_counter()
-    oracle.decode_attention(lay, pool, q, case.block_table, case.seq_lens, case.sentinel_mask, n_threads=threads)
-    td = time.perf_counter() - t0
-    log("cpu oracle: decode 1 layer %.2f s (%d threads), quantise %d blocks %.2f s (1 thread)" %
-        (td, threads, nq, tq))
-    return {"value": round(dec_bytes_per_layer / td / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "decode attention of layer 0 (%d agents x %d slots, %d threads); quantise of %d blocks "
-                      "(1 thread)" % (case.n_seqs, int(case.seq_lens[0]), threads, nq),
-            "decode_s_per_layer": round(td, 3),
-            "kv_tokens_quantized_per_s": round(nq * W.BLOCK / tq, 1)}
+    visible = len(os.sched_getaffinity(0))
+    threads = max(1, min(visible, 16))   # the host share of one GPU: 16 cores
+    per = {}
+    for name, (s1, sn, q1, qn) in CPU_SAMPLES.items():
+        if name not in dec_bytes:
+            continue
+        cfg = W.CONFIGS[name]
+        full = W.make_case(cfg)
+        sn = max(1, int(round(sn * budget)))
+        sub = W.make_case(cfg, n_seqs=min(sn, full.n_seqs))
+        lay = oracle.make_layout(**cfg.layout())
+        tb = oracle.tile_bytes(lay)
+        k, v = W.blocks_kv(cfg, 0, sub.prefill_blocks, threads=threads)
+        bitmaps, prec = W.mixed_precision_inputs(sub, 0, threads) if cfg.mixed else (None, None)
+        pool = np.zeros(tb * cfg.num_kv_heads * sub.num_blocks, np.uint8)
+        res = {}
+        for nt, nb in ((1, q1), (threads, qn)):
+            nb = min(nb, sub.prefill_blocks.size)
+            oracle.set_threads(nt)
+            t0 = time.perf_counter()
+            oracle.quantize_blocks(lay, pool, sub.prefill_blocks[:nb], k[: nb * W.BLOCK], v[: nb * W.BLOCK],
+                                   None if bitmaps is None else bitmaps[:nb])
+            res["quantize_token_layers_per_s_%dt" % nt] = round(nb * W.BLOCK / (time.perf_counter() - t0), 0)
+        oracle.set_threads(threads)
+        oracle.quantize_blocks(lay, pool, sub.prefill_blocks, k, v, bitmaps)
+        if sub.append:
+            ak, av = W.append_kv(cfg, 0, sub.n_seqs)
+            oracle.append_tokens(lay, pool, ak, av, sub.block_table, sub.positions, prec)
+        q = W.queries(cfg, 0, sub.n_seqs)
+        for nt, ns in ((1, s1), (threads, sub.n_seqs)):
+            ns = min(ns, sub.n_seqs)
+            mask = None if sub.sentinel_mask is None else np.ascontiguousarray(sub.sentinel_mask[:ns])
+            t0 = time.perf_counter()
+            oracle.decode_attention(lay, pool, q[:ns], sub.block_table[:ns], sub.seq_lens[:ns], mask, n_threads=nt)
+            t_layer = (time.perf_counter() - t0) * full.n_seqs / ns
+            res["decode_s_per_layer_%dt" % nt] = round(t_layer, 3)
+            res["decode_GBps_%dt" % nt] = round(dec_bytes[name] / t_layer / 1e9, 4)
+        res["sample"] = "%d of %d sequences decoded (1 thread: %d), %d / %d blocks quantised" % (
+            sub.n_seqs, full.n_seqs, min(s1, sub.n_seqs), min(qn, sub.prefill_blocks.size),
+            min(q1, sub.prefill_blocks.size))
+        per[name] = res
+        log("cpu oracle %s: decode %.3g s/layer (1 thread), %.3g s/layer (%d threads); quantise %.3g / %.3g "
+            "token-layers/s" % (name, res["decode_s_per_layer_1t"], res["decode_s_per_layer_%dt" % threads], threads,
+                                res["quantize_token_layers_per_s_1t"], res["quantize_token_layers_per_s_%dt" % threads]))
+    h = per[headline]
+    return {"value": h["decode_GBps_%dt" % threads], "unit": "GB/s", "cores": threads, "threads": threads,
+            "host_cpus_visible": visible, "kind": "oracle",
+            "sample": "one layer of each workload from bounded samples (per_workload[*].sample), scaled to the "
+                      "whole layer; value = %s decode attention with %d threads" % (headline, threads),
+            "per_workload": per}
 
 
 if __name__ == "__main__":

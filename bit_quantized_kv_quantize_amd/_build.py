@@ -59,8 +59,23 @@ def build(verbose: bool = False, jobs: int = 0, debug: bool = False) -> str:
     return lib
 
 
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The streaming-read probe the benchmark measures the decode kernels against (not part of libkvq)."""
+    cc = hipcc()
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [cc] + common_flags() + ["-shared", os.path.join(CSRC, "probe", "kvq_stream_probe.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build_all(verbose: bool = False):
-    return build(verbose), build(verbose, debug=True)
+    return build(verbose), build(verbose, debug=True), build_probe(verbose)
 
 
 if __name__ == "__main__":

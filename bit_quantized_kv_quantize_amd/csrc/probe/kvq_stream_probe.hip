@@ -1,0 +1,105 @@
+// kvq_stream_probe.hip - the streaming-read ceiling the decode kernels are measured against (a measurement
+// aid loaded only by the benchmark; it is not part of libkvq).
+//
+// kvq_probe_read_tiles reads the bytes the 4-bit streaming decode reads from a pool - for every (sequence, KV
+// head) pair, every live block's tile, each row's 128 code bytes and 16 parameter bytes (rows past a sequence's
+// end re-read row 0, as the decode does) - with the same work split (512 workgroups of 4 waves, each wave 64
+// rows of every block of its range) and 16-byte loads, and does no arithmetic beyond folding the loaded words
+// into one value per workgroup (written out so nothing is optimised away). Its time is the floor of a kernel with that decode's
+// load pattern. kvq_probe_read_linear streams a flat buffer with 16-byte loads from 2048 workgroups: the
+// chip's plain read bandwidth.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// grid (wgs), 256 threads. The work split of the decode's one-dimensional plan: with P pairs and W workgroups,
+// k = W / P, the first nA = P - (W - k P) pairs take k even pieces of their blocks and the others k + 1; the
+// first half of the grid takes pieces in order and the second half in reverse. Each wave reads its 64 rows of
+// four blocks at a time (twelve 16-byte loads per lane in flight), then folds them.
+__global__ __launch_bounds__(256) void read_tiles_k(const uint8_t* pool, const int32_t* table, const int32_t* lens,
+                                                    int n_seqs, int H, int max_blocks, uint32_t tile_bytes,
+                                                    uint32_t rec, uint32_t off_prow, uint32_t prow, int wgs,
+                                                    uint32_t* sink) {
+  const int pairs = n_seqs * H;
+  const int k = wgs / pairs, nA = pairs - (wgs - k * pairs);
+  const int half = (wgs + 1) / 2;
+  const int slot = (int)blockIdx.x < half ? (int)blockIdx.x : wgs - 1 - ((int)blockIdx.x - half);
+  int pair, split, ns;
+  if (slot < k * nA) {
+    split = slot / nA;
+    pair = slot - split * nA;
+    ns = k;
+  } else {
+    const int nB = pairs - nA, t = slot - k * nA;
+    split = t / nB;
+    pair = nA + (t - split * nB);
+    ns = k + 1;
+  }
+  const int seq = pair / H, h = pair % H;
+  const int len = lens[seq];
+  const int nblk = (len + 255) / 256;
+  const int q = nblk / ns, rem = nblk % ns;
+  const int b0 = split * q + (split < rem ? split : rem), b1 = b0 + q + (split < rem ? 1 : 0);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int b = b0; b < b1; b += 4) {
+    u32x4 x[4][4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = min(b + i, b1 - 1);
+      const uint8_t* tile = pool + ((size_t)table[(size_t)seq * max_blocks + bb] * H + h) * tile_bytes;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = 64 * w + 16 * c + lj;
+        const bool on = b + i < b1 && bb * 256 + row < len;
+        const uint8_t* rp = tile + (uint32_t)(on ? row : 0) * rec + la * 16;
+        x[i][c][0] = *reinterpret_cast<const u32x4*>(rp);
+        x[i][c][1] = *reinterpret_cast<const u32x4*>(rp + 64);
+        x[i][c][2] = *reinterpret_cast<const u32x4*>(tile + off_prow + (uint32_t)(on ? row : 0) * prow);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc ^= x[i][c][0] ^ x[i][c][1] ^ (la == 0 ? x[i][c][2] : u32x4{0u, 0u, 0u, 0u});
+  }
+  const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (v == 0x9E3779B9u) sink[blockIdx.x] = v;  // practically never true; keeps the loads live
+}
+
+__global__ __launch_bounds__(256) void read_linear_k(const u32x4* buf, size_t n16, uint32_t* sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) acc ^= buf[i];
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Returns 0, or -1 for bad sizes, -4 for a launch error. sink: device uint32 [wgs] (written only in the
+// practically impossible case that a workgroup's fold equals a fixed constant).
+__attribute__((visibility("default"))) int kvq_probe_read_tiles(const void* pool, const int32_t* table,
+                                                                const int32_t* lens, int n_seqs, int H,
+                                                                int max_blocks, uint32_t tile_bytes, uint32_t rec,
+                                                                uint32_t off_prow, uint32_t prow, int wgs,
+                                                                uint32_t* sink, void* stream) {
+  if (n_seqs <= 0 || H <= 0 || wgs < n_seqs * H || max_blocks <= 0) return -1;
+  hipLaunchKernelGGL(read_tiles_k, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)pool, table, lens,
+                     n_seqs, H, max_blocks, tile_bytes, rec, off_prow, prow, wgs, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+__attribute__((visibility("default"))) int kvq_probe_read_linear(const void* buf, size_t bytes, int wgs,
+                                                                 uint32_t* sink, void* stream) {
+  if (bytes % 16 || wgs <= 0 || ((uintptr_t)buf & 15u)) return -1;
+  hipLaunchKernelGGL(read_linear_k, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const u32x4*)buf, bytes / 16,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"
