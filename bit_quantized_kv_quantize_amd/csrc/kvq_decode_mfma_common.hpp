@@ -108,6 +108,10 @@ __device__ int stage_columns(int n, int tid, int* s_tbl, Idx* s_idx, int* s_cnt,
 // not depend on which split that is - finalises the output and resets the counter to zero. The merge also
 // takes the n_pre partials that the cascade kernel left in the last n_pre slots of each row (earlier in
 // stream order, so plain loads see them); those carry no arrival.
+// An agent-scope release on the counter increment would make the hand-over an ordering of the memory model
+// rather than of the stores' coherence, but on gfx950 it compiles to an L2 write-back (buffer_wbl2) in every
+// workgroup, which made the 12 x 8K call 36 % slower (33 -> 45 us). The partials are agent-scope atomic
+// stores, coherent across the XCDs by themselves, and each is acknowledged before the increment.
 template <int D, int G>
 __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int seq, int h, int split, int ns, int len,
                               int tid, const float* part_m, const float* part_l, const float* part_acc, float* s_o,

@@ -101,7 +101,7 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
 
 // Store one lane's share of a code row (8 codes): 2-bit codes as one uint16 (lowest bits first), 4-bit codes
 // as one uint32 (low nibble first), 8-bit codes as two. With tail > 0 (the V row of a row narrower than the
-// pool's widest) the lane also zeroes its share (tail / lpr bytes) of the record after the row.
+// pool's widest) the row's lanes also zero the tail bytes of the record after the row.
 __device__ __forceinline__ void store_codes(uint8_t* row, int li, int lpr, int bits, int tail,
                                             const uint32_t (&code)[8]) {
   if (bits == 8) {
@@ -121,9 +121,10 @@ __device__ __forceinline__ void store_codes(uint8_t* row, int li, int lpr, int b
     *reinterpret_cast<uint16_t*>(row + li * 2) = (uint16_t)w;
   }
   if (tail > 0) {
-    const int share = tail / lpr;  // a multiple of 4 bytes
-    uint32_t* z = reinterpret_cast<uint32_t*>(row + lpr * bits + li * share);
-    for (int k = 0; k < share / 4; ++k) z[k] = 0u;
+    // the record's rest starts 4-byte aligned ((d + dv) * bits / 8 bytes in) and holds tail / 4 words: the
+    // row's lanes zero them in turn
+    uint32_t* z = reinterpret_cast<uint32_t*>(row + lpr * bits);
+    for (int q = li; q < tail / 4; q += lpr) z[q] = 0u;
   }
 }
 
@@ -331,9 +332,42 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
   }
 }
 
-// Quantise this lane's 16 values at 4 bits as part of a group spanning gl lanes: the same fp32 operations
-// per value as quantize8, so the same codes and parameters. Codes are packed low nibble first.
-__device__ __forceinline__ void quantize16_q4(const float (&x)[16], int gl, uint2& codes, uint32_t& param) {
+// y = c * H * x for one row spread over L16 lanes, lane li holding elements 16 li .. 16 li + 15: the butterflies
+// of rotate_row in the same order (strides 1, 2, 4, 8 inside the lane, then 16, 32, ... across lanes), so the
+// rotated values are the same bits.
+template <int L16>
+__device__ __forceinline__ void rotate_row16(float (&x)[16], int li, float c) {
+#pragma unroll
+  for (int h = 1; h < 16; h *= 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < L16; m *= 2) {
+    const bool upper = (li & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = __shfl_xor(x[i], m);
+      x[i] = upper ? (p - x[i]) : (x[i] + p);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = x[i] * c;
+}
+
+// Quantise this lane's 16 values at `bits` (2, 4 or 8) as part of a group spanning gl lanes: the same fp32
+// operations per value as quantize8 (the clamp as one fmed3, which equals max then min for the non-NaN
+// values here), so the same codes and parameters. Codes are packed into w low bits first (8-bit: four words,
+// 4-bit: two, 2-bit: one): the codes of a byte are first combined exactly in fp32 (q0 + 16 q1, or q0 + 4 q1 +
+// 16 q2 + 64 q3, integers below 256) and the byte placed with v_cvt_pk_u8_f32 (exact for such integers).
+__device__ __forceinline__ void quantize16(const float (&x)[16], int gl, int bits, uint32_t (&w)[4],
+                                           uint32_t& param) {
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
@@ -346,56 +380,130 @@ __device__ __forceinline__ void quantize16_q4(const float (&x)[16], int gl, uint
   }
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
-  const float s32 = (mx - mn) / 15.0f;
+  const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
+  const float s32 = (mx - mn) / L;
   const uint32_t sh = f2h(s32), zh = f2h(mn);
   param = sh | (zh << 16);
   const float s = h2f(sh), z = h2f(zh);
-  uint32_t w[2] = {0u, 0u};
-  if (s != 0.0f) {
-    const float r = 1.0f / s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float qv = __builtin_rintf((x[i] - z) * r);
-      qv = fminf(fmaxf(qv, 0.0f), 15.0f);
-      w[i >> 3] |= (uint32_t)qv << (4 * (i & 7));
+  for (int k = 0; k < 4; ++k) w[k] = 0u;
+  if (s == 0.0f) return;
+  const float r = 1.0f / s;
+  float q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float t = x[i] - z;
+    const float u = t * r;
+    q[i] = __builtin_amdgcn_fmed3f(__builtin_rintf(u), 0.0f, L);
+  }
+  if (bits == 8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(q[i], i & 3, w[i >> 2]);
+  } else if (bits == 4) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      w[j >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(q[2 * j + 1], 16.0f, q[2 * j]), j & 3, w[j >> 2]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float b = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(q[4 * j + 3], 4.0f, q[4 * j + 2]), 4.0f,
+                                                    q[4 * j + 1]), 4.0f, q[4 * j]);
+      w[0] = __builtin_amdgcn_cvt_pk_u8_f32(b, j, w[0]);
     }
   }
-  codes = uint2{w[0], w[1]};
 }
 
-// quantize_rows_k for 4-bit pools without rotation whose groups span whole 16-channel lanes: LPR = d / 16
-// lanes per row with 16 values each, so the per-row work (group extremes, the two divisions, addressing)
-// is shared by twice as many values. Grid and output as quantize_rows_k.
-template <int LPR>
+// quantize_rows_k with 16 values per lane (L16 = d / 16 lanes per row, 256 / L16 rows per pass) for pools with
+// groups of 16 channels or more: rotation (ROT, rotate_row16) and per-token widths (MIX = the layout's mixed:
+// {4, 8} or {2, 4, 8, FP16}) as compile-time variants, with the same codes, parameters, headers and zero
+// padding. The per-row work (group extremes, the two divisions, addressing) is shared by twice as many values
+// as with 8 per lane, and each pass's rows are loaded while the previous pass is quantised. Grid and output
+// as quantize_rows_k.
+template <int L16, bool ROT, int MIX>
 __global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __restrict__ pool,
                                                          const int32_t* __restrict__ block_ids,
                                                          const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v, int kv_base) {
-  constexpr int D = LPR * 16;
-  constexpr int kRowsPerPass = 256 / LPR;
+                                                         const uint16_t* __restrict__ v,
+                                                         const uint32_t* __restrict__ prec_bits, float rot_c,
+                                                         int kv_base) {
+  constexpr int D = L16 * 16;
+  constexpr int RPP = 256 / L16;                  // rows per pass (21 at L16 = 12: threads 252..255 idle)
+  constexpr int NPASS = (kRows + RPP - 1) / RPP;  // passes (the last one partial at L16 = 12)
+  static_assert(!ROT || (L16 & (L16 - 1)) == 0, "rotation needs a power-of-two head dim");
   const int i = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
-  const int li = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
-  uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
+  const int li = threadIdx.x % L16, r0 = threadIdx.x / L16;
   const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 16;
+  uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
   const int gl = (kv ? g.vg : g.kg) / 16;
-  for (int t = r0; t < kRows; t += kRowsPerPass) {
-    float a[8], b[8], x[16];
-    load8(src + (size_t)t * g.H * D, a);
-    load8(src + (size_t)t * g.H * D + 8, b);
+  const uint32_t* bitmap = MIX && prec_bits ? prec_bits + (size_t)i * (g.header_bytes() / 4) : nullptr;
+  // Rows past the block (the idle threads and the partial last pass when L16 does not divide 256) load the
+  // block's last row instead, so every load is unconditional, and skip the work.
+  auto row_ptr = [&](int t) { return src + (size_t)min(t, kRows - 1) * g.H * D; };
+  const uint16_t* rp = row_ptr(r0);
+  uint4 nxt0 = *reinterpret_cast<const uint4*>(rp), nxt1 = *reinterpret_cast<const uint4*>(rp + 8);
+#pragma unroll 1
+  for (int p = 0; p < NPASS; ++p) {
+    const uint4 a = nxt0, b = nxt1;
+    if (p + 1 < NPASS) {  // the next pass's row is in flight while this one is quantised
+      rp = row_ptr(r0 + (p + 1) * RPP);
+      nxt0 = *reinterpret_cast<const uint4*>(rp);
+      nxt1 = *reinterpret_cast<const uint4*>(rp + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int t = r0 + p * RPP;
+    if (t >= kRows) continue;
+    float x[16];
+    const uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] = a[e];
-      x[8 + e] = b[e];
+      x[2 * e] = h2f(ww[e] & 0xffffu);
+      x[2 * e + 1] = h2f(ww[e] >> 16);
     }
-    uint2 codes;
-    uint32_t param;
-    quantize16_q4(x, gl, codes, param);
-    *reinterpret_cast<uint2*>(tile + (kv ? g.vcode(t, 4) : g.kcode(t)) + li * 8) = codes;
-    if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(tile + (kv ? g.vpar(t) : g.kpar(t)))[li / gl] = param;
+    if constexpr (ROT) rotate_row16<L16>(x, li, rot_c);
+    int bits = 4;
+    if constexpr (MIX == 2) bits = 2 << (bitmap ? (bitmap[t >> 4] >> (2 * (t & 15))) & 3u : 1u);
+    if constexpr (MIX == 1) bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
+    uint8_t* row = tile + (kv ? g.vcode(t, bits) : g.kcode(t));
+    uint32_t* prow = reinterpret_cast<uint32_t*>(tile + (kv ? g.vpar(t) : g.kpar(t)));
+    if (MIX == 2 && bits == 16) {
+      uint4 o0, o1;
+      o0.x = f2h(x[0]) | (f2h(x[1]) << 16);
+      o0.y = f2h(x[2]) | (f2h(x[3]) << 16);
+      o0.z = f2h(x[4]) | (f2h(x[5]) << 16);
+      o0.w = f2h(x[6]) | (f2h(x[7]) << 16);
+      o1.x = f2h(x[8]) | (f2h(x[9]) << 16);
+      o1.y = f2h(x[10]) | (f2h(x[11]) << 16);
+      o1.z = f2h(x[12]) | (f2h(x[13]) << 16);
+      o1.w = f2h(x[14]) | (f2h(x[15]) << 16);
+      *reinterpret_cast<uint4*>(row + li * 32) = o0;
+      *reinterpret_cast<uint4*>(row + li * 32 + 16) = o1;
+      if ((li & (gl - 1)) == 0) prow[li / gl] = 0u;
+      continue;
+    }
+    uint32_t w[4], param;
+    quantize16(x, gl, bits, w, param);
+    if (MIX && bits == 8) {
+      *reinterpret_cast<uint4*>(row + li * 16) = uint4{w[0], w[1], w[2], w[3]};
+    } else if (MIX == 2 && bits == 2) {
+      *reinterpret_cast<uint32_t*>(row + li * 4) = w[0];
+    } else {
+      *reinterpret_cast<uint2*>(row + li * 8) = uint2{w[0], w[1]};
+    }
+    if (MIX && kv) {  // the rest of a narrower row's record is zero (4-byte aligned, as in store_codes)
+      uint32_t* z = reinterpret_cast<uint32_t*>(row + L16 * 2 * bits);
+      const int nw = (g.rec - (g.d + g.dv) * bits / 8) / 4;
+      for (int q = li; q < nw; q += L16) z[q] = 0u;
+    }
+    if ((li & (gl - 1)) == 0) prow[li / gl] = param;
   }
-  if (kv == 1) {  // zero the tail padding
-    for (uint32_t o = g.off_hdr + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
+  if (kv == 1) {
+    // zero the tail padding (and write the width words of pools with per-token widths)
+    const uint32_t end = g.off_hdr + g.header_bytes();
+    for (uint32_t o = end + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
       *reinterpret_cast<uint32_t*>(tile + o) = 0u;
+    if (MIX && threadIdx.x < g.header_bytes() / 4)
+      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[threadIdx.x] =
+          bitmap ? bitmap[threadIdx.x] : (MIX == 2 ? 0x55555555u : 0u);
   }
 }
 
@@ -410,11 +518,30 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
     n_tensors -= 1;
   }
   if (n_tensors > 0) {
-    const bool k_lanes = kv_base > 0 || g.kg % 16 == 0;  // the K rows' groups span whole 16-channel lanes
-    if (LPR == 16 && !g.fp8 && !g.mixed && !g.rotate && g.dv == g.d && k_lanes && g.vg % 16 == 0)
-      hipLaunchKernelGGL(quantize_rows16_k<8>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
-                         block_ids, k, v, kv_base);
-    else
+    // 16 values per lane where the tensors' groups span whole 16-channel lanes and a row's lanes divide a
+    // wave (head dims 64, 128, 256)
+    const bool k_lanes = kv_base > 0 || g.kg % 16 == 0;
+    const bool v_lanes = kv_base + n_tensors < 2 || g.vg % 16 == 0;
+    if (!g.fp8 && k_lanes && v_lanes) {
+      constexpr int L16 = LPR / 2;
+      const dim3 grid(n_blocks, g.H, n_tensors);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g, pool, block_ids, k, v, prec_bits, rot_c, kv_base);
+      };
+      if constexpr ((L16 & (L16 - 1)) == 0) {
+        if (g.rotate) {
+          if (g.mixed == 2) go(quantize_rows16_k<L16, true, 2>);
+          else if (g.mixed) go(quantize_rows16_k<L16, true, 1>);
+          else go(quantize_rows16_k<L16, true, 0>);
+          return hipGetLastError();
+        }
+      }
+      {
+        if (g.mixed == 2) go(quantize_rows16_k<L16, false, 2>);
+        else if (g.mixed) go(quantize_rows16_k<L16, false, 1>);
+        else go(quantize_rows16_k<L16, false, 0>);
+      }
+    } else
       hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,
                          block_ids, k, v, prec_bits, rot_c, kv_base);
   }

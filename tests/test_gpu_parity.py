@@ -43,6 +43,37 @@ def test_pool_bytes_bit_exact(env, orc, name):
     assert diff.size == 0, "first differing bytes at %s" % diff[:16]
 
 
+GARBAGE_LAYOUTS = [  # head dim, V head dim, k_group, v_group, rotate, mixed, format
+    (128, 0, 64, 64, 0, 0, 0), (128, 0, 64, 64, 1, 1, 0), (128, 0, 32, 64, 0, 2, 0), (128, 0, -1, 32, 1, 0, 0),
+    (64, 0, 16, 32, 1, 2, 0), (256, 0, 64, 8, 1, 1, 0), (192, 128, 64, 32, 0, 2, 0), (192, 128, 64, 64, 0, 1, 0),
+    (256, 128, 64, 32, 1, 2, 0), (128, 0, 0, 0, 1, 0, 1)]
+
+
+@pytest.mark.parametrize("layout", GARBAGE_LAYOUTS)
+def test_quantize_overwrites_every_byte_of_its_tiles(env, orc, layout):
+    # Whole blocks quantised into a pool whose bytes were all 0xFF (a reused pool): every byte of the
+    # written tiles - codes, the zeroed rest of narrower records, parameters, headers, padding - equals the
+    # oracle's (which clears each tile first); tiles of other blocks keep their bytes.
+    kvq, torch = env
+    d, dv, kg, vg, rotate, mixed, fmt = layout
+    cfg = W.Config(9, "garbage", d, 4, 2, 1, kg, vg, rotate, mixed, 3, 0, "perm", False, 3, 10.0, 1.0,
+                   top_fraction=0.3 if mixed == 1 else 0.0, fmt=fmt,
+                   width_fracs=(0.1, 0.2, 0.3) if mixed == 2 else (0.0, 0.0, 0.0), v_head_dim=dv)
+    case = W.make_case(cfg, context=[700, 257, 1024])
+    inp = host_inputs(case)
+    lay_o = orc.make_layout(**cfg.layout())
+    ref = np.full(orc.tile_bytes(lay_o) * cfg.num_kv_heads * (case.num_blocks + 2), 0xFF, np.uint8)
+    orc.quantize_blocks(lay_o, ref, case.prefill_blocks, inp["k"], inp["v"], inp["bitmaps"])
+    lay = kvq.Layout(**cfg.layout())
+    pool = torch.full((ref.size,), 0xFF, dtype=torch.uint8, device="cuda")
+    kvq.quantize_blocks(lay, pool, to_dev(case.prefill_blocks, torch), to_dev(inp["k"], torch, torch.float16),
+                        to_dev(inp["v"], torch, torch.float16),
+                        None if inp["bitmaps"] is None else to_dev(inp["bitmaps"].view(np.int32), torch))
+    got = pool.cpu().numpy()
+    diff = np.nonzero(got != ref)[0]
+    assert diff.size == 0, "first differing bytes at %s" % diff[:16]
+
+
 @pytest.fixture(params=["dispatch", "mfma", "generic"])
 def decode_path(request, monkeypatch, env):
     """Run decode through the release library's normal dispatch (the row-list matrix-core kernel where
