@@ -25,6 +25,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build libkvq")
 
 
+# Per-source flags. The cascade kernel's maxima run over finite logits only: without NaNs the compiler
+# drops the canonicalising moves it otherwise puts before every fmaxf of a matrix-core result.
+SOURCE_FLAGS = {"kvq_decode_cascade.hip": ["-fno-honor-nans"]}
+
+
 def common_flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
             # packed fp32 instructions stay disabled in every kernel of this library
@@ -41,7 +46,7 @@ def build(verbose: bool = False, jobs: int = 0, debug: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
-        cmd = [cc] + common_flags() + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + common_flags() + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)

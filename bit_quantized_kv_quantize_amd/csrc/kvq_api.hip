@@ -97,18 +97,23 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_se
   p.nA = (int)(units - (W - (long)p.k * units));
   p.max_blocks = nb;
   const int rows_max = p.nA < units ? p.k + 1 : p.k;
-  // Cascade (per-channel K layouts, two or more sequences): about kCascUnits workgroups of kCascRows rows;
-  // block ranges of at most 512 blocks.
+  // Cascade (per-channel K layouts, two or more sequences): row groups of at most kCascRows rows, one
+  // workgroup per (block range, KV head, row group) and one workgroup per CU; block ranges of at most 512
+  // blocks.
   const int G = g.H > 0 ? num_q_heads / g.H : 1;
   p.casc = 0;
   p.casc_rg = 0;
+  p.casc_nt = 0;
   if (n_seqs >= 2 && decode_cascade_supported(g, G)) {
-    const long rg = ((long)n_seqs * G + kCascRows - 1) / kCascRows;
+    const long n_rows = (long)n_seqs * G;  // rows of one KV head
+    const long rg = (n_rows + kCascRows - 1) / kCascRows;
+    const long tiles = (n_rows + 15) / 16;
     const long pairs = rg * g.H;
     // block ranges S: the count that minimises the work of the busiest CU, (units per CU) x (blocks per
-    // unit), with at most 2 * kCascUnits units, 64 ranges and 512 blocks per range
+    // unit), with at most kCascSlots / (rows of the call) ranges (the workspace bound), 64 ranges and 512
+    // blocks per range
     long s_lo = std::max(1L, (long)(nb + 511) / 512);
-    long s_hi = std::min(std::min(64L, (long)nb), std::max(1L, 2L * kCascUnits / pairs));
+    long s_hi = std::min(std::min(64L, (long)nb), std::max(1L, (long)kCascSlots / (n_rows * g.H)));
     if (s_hi < s_lo) s_hi = s_lo;
     long S = s_lo, best = -1;
     for (long c = s_lo; c <= s_hi; ++c) {
@@ -120,6 +125,7 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_se
     }
     p.casc = (int)S;
     p.casc_rg = (int)rg;
+    p.casc_nt = (int)((tiles + rg - 1) / rg);
   }
   p.stride = (p.n_splits > rows_max ? p.n_splits : rows_max) + p.casc;
   return p;
@@ -133,14 +139,13 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   // regions are sized by a bound that never decreases with n_seqs or max_seq_len, so that a workspace
   // sized for one call serves every smaller one. With G = num_q_heads / H, units = n_seqs * H and
   // c = ceil(blocks / 512): both per-sequence plans give at most G * max(512, units * c) + n_seqs *
-  // num_q_heads slots, and the cascade at most 2 * kCascUnits * kCascRows + n_seqs * num_q_heads * c more
-  // (row groups hold kCascRows rows and the plan takes at most 2 * kCascUnits / (row groups * H) ranges, so
-  // n_seqs * num_q_heads * S <= 2 * kCascUnits * kCascRows).
+  // num_q_heads slots, and the cascade at most kCascSlots + n_seqs * num_q_heads * c more (the plan takes
+  // at most kCascSlots / (n_seqs * num_q_heads) ranges, or c when that is fewer).
   const size_t G = g.H > 0 ? (size_t)(num_q_heads / g.H) : 1;
   const size_t c512 = (size_t)(p.max_blocks + 511) / 512;
   const size_t rows = ns * (size_t)num_q_heads;
   size_t parts = G * std::max((size_t)512, ns * g.H * c512) + rows;
-  if (p.casc > 0) parts += (size_t)2 * kCascUnits * kCascRows + rows * c512;
+  if (p.casc > 0) parts += (size_t)kCascSlots + rows * c512;
   WorkspaceLayout w{};
   w.parts = parts;
   w.ml = 0;

@@ -73,13 +73,13 @@ constexpr int kMaxSplits = 64;        // splits per (sequence, KV head)
 constexpr float kTwo20 = 1048576.0f;
 
 // Stages into s_tbl, in order, the block-table entries phys(i) of the columns 0 <= i < n for which keep(i)
-// holds, and into s_idx their column indices (both evaluated by thread i mod 256, all 256 threads taking
-// part); returns their number. s_cnt: four ints of scratch.
-template <class Idx, class Keep, class Phys>
+// holds, and into s_idx their column indices (both evaluated by thread i mod 64 NW, all 64 NW threads of
+// the workgroup taking part); returns their number. s_cnt: NW ints of scratch.
+template <int NW = 4, class Idx, class Keep, class Phys>
 __device__ int stage_columns(int n, int tid, int* s_tbl, Idx* s_idx, int* s_cnt, Keep keep, Phys phys) {
   const int w = tid >> 6, lane = tid & 63;
   int total = 0;
-  for (int base = 0; base < n; base += 256) {
+  for (int base = 0; base < n; base += 64 * NW) {
     const int i = base + tid;
     const bool k = i < n && keep(i);
     const int e = k ? phys(i) : 0;
@@ -93,7 +93,8 @@ __device__ int stage_columns(int n, int tid, int* s_tbl, Idx* s_idx, int* s_cnt,
       s_tbl[o] = e;
       s_idx[o] = (Idx)i;
     }
-    total += s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) total += s_cnt[ww];
     __syncthreads();
   }
   return total;

@@ -58,7 +58,7 @@ TileGeom make_geom(const kvq_layout* L);
 // the others k + 1 (rows_work), which fills exactly two workgroups per CU when there are fewer pairs.
 // The cascade kernel (blocks shared by every sequence of the batch, per-channel K layouts) cuts the logical
 // block range into casc even ranges and the (sequence, query head) rows of each KV head into casc_rg
-// groups; its partials take the last casc slots of each row's partial slots.
+// groups of casc_nt 16-row tiles; its partials take the last casc slots of each row's partial slots.
 // `stride` is the number of partial slots per (sequence, query head) in the workspace: the largest split
 // count of the per-sequence plans, plus casc.
 struct SplitPlan {
@@ -71,6 +71,7 @@ struct SplitPlan {
   int max_blocks;  // logical blocks of the longest sequence
   int casc;        // cascade block ranges (0: no cascade slots)
   int casc_rg;     // cascade row groups per KV head
+  int casc_nt;     // 16-row tiles per cascade row group (at most kCascRows / 16)
 };
 // Blocks [b0, b1) of split `split` out of ns over a sequence of nblk blocks: even ranges, so the
 // splits of a pair differ by at most one block.
@@ -182,8 +183,8 @@ hipError_t launch_decode_fp8(const TileGeom& g, const DecodeArgs& a, hipStream_t
 // Cascade kernel for blocks shared by all sequences: layouts of the per-channel-K kernel; the caller then
 // runs that kernel with a.casc set.
 bool decode_cascade_supported(const TileGeom& g, int G);
-constexpr int kCascRows = 16;   // (sequence, query head) rows of one cascade workgroup
-constexpr int kCascUnits = 512; // cascade workgroups aimed for: two per CU
+constexpr int kCascRows = 128;     // (sequence, query head) rows of one cascade workgroup at most
+constexpr int kCascSlots = 32768;  // bound on (query rows of the call) x (cascade block ranges)
 hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 

@@ -329,19 +329,30 @@ def cascade_mode(request, monkeypatch, env):
 
 
 CASCADE_CASES = {
-    # 40 sequences x 5 query heads = 200 rows: seven row groups of 32, the last one partial; ragged suffixes
-    "rows_40": dict(n_seqs=40, shared_prefix=1024, context=[1024 + (97 * i) % 1100 for i in range(40)]),
+    # 40 sequences x 5 query heads = 200 rows per KV head: two row groups of seven 16-row tiles, the second
+    # with a partial tile and idle waves; ragged suffixes
+    "rows_40": ({}, dict(n_seqs=40, shared_prefix=1024, context=[1024 + (97 * i) % 1100 for i in range(40)])),
     # more block ranges than shared blocks (empty cascade units); one sequence ends where the prefix ends
-    "prefix_8": dict(n_seqs=4, shared_prefix=2048, context=[2048, 2100, 4000, 2304]),
+    "prefix_8": ({}, dict(n_seqs=4, shared_prefix=2048, context=[2048, 2100, 4000, 2304])),
+    # 17 sequences x 8 query heads = 136 rows (two row groups of five tiles), V groups of 64, no rotation
+    "g8_vg64": (dict(num_q_heads=64, v_group=64, rotate=0),
+                dict(n_seqs=17, shared_prefix=1536, context=[1536 + (131 * i) % 900 for i in range(17)])),
+    # one query head per KV head: 3 rows, one partial tile
+    "g1": (dict(num_q_heads=8), dict(n_seqs=3, shared_prefix=768, context=[768, 1000, 1300])),
 }
 
 
 @pytest.mark.parametrize("name", sorted(CASCADE_CASES))
 def test_cascade_shared_blocks(env, orc, name, cascade_mode):
-    # The shared-prefix layout (K per channel, V groups of 32, rotation, G = 5) with the prefix blocks
-    # aliased in every sequence's table, against the oracle (which reads each sequence's table as given).
+    # The shared-prefix layout (K per channel, V groups of 32, rotation, G = 5, and the variants above) with
+    # the prefix blocks aliased in every sequence's table, against the oracle (which reads each sequence's
+    # table as given).
+    import dataclasses
+
     kvq, torch = env
-    case = W.make_case(W.CONFIGS["qwen25_14b_prefix_32k"], **CASCADE_CASES[name])
+    over, kw = CASCADE_CASES[name]
+    cfg = dataclasses.replace(W.CONFIGS["qwen25_14b_prefix_32k"], name="prefix_" + name, **over)
+    case = W.make_case(cfg, **kw)
     inp = host_inputs(case)
     _, ref = oracle_run(orc, case, inp)
     _, got = gpu_run(kvq, torch, case, inp)
