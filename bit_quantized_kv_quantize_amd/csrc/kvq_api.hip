@@ -97,23 +97,23 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_se
   p.nA = (int)(units - (W - (long)p.k * units));
   p.max_blocks = nb;
   const int rows_max = p.nA < units ? p.k + 1 : p.k;
-  // Cascade (per-channel K layouts, two or more sequences): row groups of at most kCascRows rows, one
+  // Cascade (per-channel K layouts, 2 .. kCascMaxSeqs sequences): row groups of at most kCascRows rows, one
   // workgroup per (block range, KV head, row group) and one workgroup per CU; block ranges of at most 512
-  // blocks.
+  // blocks. The range count is chosen as if every sequence shared every block.
   const int G = g.H > 0 ? num_q_heads / g.H : 1;
   p.casc = 0;
-  p.casc_rg = 0;
-  p.casc_nt = 0;
-  if (n_seqs >= 2 && decode_cascade_supported(g, G)) {
+  p.casc_slots = 0;
+  if (n_seqs >= 2 && n_seqs <= kCascMaxSeqs && decode_cascade_supported(g, G) &&
+      nb <= kCascMaxRanges * kCascRangeCols) {
     const long n_rows = (long)n_seqs * G;  // rows of one KV head
     const long rg = (n_rows + kCascRows - 1) / kCascRows;
-    const long tiles = (n_rows + 15) / 16;
     const long pairs = rg * g.H;
     // block ranges S: the count that minimises the work of the busiest CU, (units per CU) x (blocks per
-    // unit), with at most kCascSlots / (rows of the call) ranges (the workspace bound), 64 ranges and 512
-    // blocks per range
-    long s_lo = std::max(1L, (long)(nb + 511) / 512);
-    long s_hi = std::min(std::min(64L, (long)nb), std::max(1L, (long)kCascSlots / (n_rows * g.H)));
+    // unit), with at most kCascSlots / (rows of the call) ranges (the workspace bound), kCascMaxRanges
+    // ranges and kCascRangeCols blocks per range
+    long s_lo = std::max(1L, (long)(nb + kCascRangeCols - 1) / kCascRangeCols);
+    long s_hi = std::min(std::min((long)kCascMaxRanges, (long)nb),
+                         std::max(1L, (long)kCascSlots / (n_rows * g.H)));
     if (s_hi < s_lo) s_hi = s_lo;
     long S = s_lo, best = -1;
     for (long c = s_lo; c <= s_hi; ++c) {
@@ -124,8 +124,7 @@ SplitPlan plan_splits(const TileGeom& g, int n_seqs, int num_q_heads, int max_se
       }
     }
     p.casc = (int)S;
-    p.casc_rg = (int)rg;
-    p.casc_nt = (int)((tiles + rg - 1) / rg);
+    p.casc_slots = casc_slots(n_seqs, G);
   }
   p.stride = (p.n_splits > rows_max ? p.n_splits : rows_max) + p.casc;
   return p;
@@ -139,13 +138,17 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   // regions are sized by a bound that never decreases with n_seqs or max_seq_len, so that a workspace
   // sized for one call serves every smaller one. With G = num_q_heads / H, units = n_seqs * H and
   // c = ceil(blocks / 512): both per-sequence plans give at most G * max(512, units * c) + n_seqs *
-  // num_q_heads slots, and the cascade at most kCascSlots + n_seqs * num_q_heads * c more (the plan takes
-  // at most kCascSlots / (n_seqs * num_q_heads) ranges, or c when that is fewer).
+  // num_q_heads slots, and the cascade at most kCascSlots + n_seqs * num_q_heads * c64 more (the plan takes
+  // at most kCascSlots / (n_seqs * num_q_heads) ranges, or c64 = ceil(blocks / 64) when that is more).
   const size_t G = g.H > 0 ? (size_t)(num_q_heads / g.H) : 1;
   const size_t c512 = (size_t)(p.max_blocks + 511) / 512;
   const size_t rows = ns * (size_t)num_q_heads;
+  // The cascade regions exist for every call of two or more sequences on a layout the cascade takes, also
+  // where the plan leaves the cascade out (more than kCascMaxSeqs sequences), so that they never shrink.
+  const bool casc = ns >= 2 && decode_cascade_supported(g, (int)G);
   size_t parts = G * std::max((size_t)512, ns * g.H * c512) + rows;
-  if (p.casc > 0) parts += (size_t)kCascSlots + rows * c512;
+  const size_t c64 = (size_t)(p.max_blocks + kCascRangeCols - 1) / kCascRangeCols;
+  if (casc) parts += (size_t)kCascSlots + rows * c64;
   WorkspaceLayout w{};
   w.parts = parts;
   w.ml = 0;
@@ -160,7 +163,13 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   // at least one block per sequence, so the count kernels always have a grid
   w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
   w.cflag = w.bcnt + up(ns * nwd * (size_t)w.bcnt_blocks * sizeof(int));
-  w.body = w.cflag + up(p.casc > 0 ? (size_t)p.max_blocks * sizeof(int) : 0);
+  // cascade: a flag per (sequence, logical block), the member lists and row groups of every block range
+  const size_t slots = casc ? (size_t)casc_slots((int)ns, (int)G) : 0;
+  w.cperm = w.cflag + up(casc ? ns * (size_t)p.max_blocks * sizeof(int) : 0);
+  w.cdesc = w.cperm + up(casc ? (size_t)kCascMaxRanges * ns * sizeof(int) : 0);
+  w.cnrg = w.cdesc + up(slots * kCascMaxRanges * 4 * sizeof(int));
+  w.cmask = w.cnrg + up(casc ? (size_t)kCascMaxRanges * sizeof(int) : 0);
+  w.body = w.cmask + up(casc ? (size_t)kCascMaxRanges * ns * sizeof(uint64_t) : 0);
   // The split-K arrival counters sit at the end of the caller's workspace (ctr_offset), after every other
   // region: the other regions grow with n_seqs and max_seq_len, so no smaller call sharing the workspace
   // can write partials over a larger call's counters, and a smaller call's counters are a subset of the
@@ -341,6 +350,10 @@ static int decode_entry(const char* fn, const kvq_layout* L, const void* pool, c
   a.ws_bcnt = (int*)(ws + wl.bcnt);
   a.bcnt_blocks = wl.bcnt_blocks;
   a.ws_cflag = (int*)(ws + wl.cflag);
+  a.ws_cperm = (int*)(ws + wl.cperm);
+  a.ws_cdesc = (int*)(ws + wl.cdesc);
+  a.ws_cnrg = (int*)(ws + wl.cnrg);
+  a.ws_cmask = (uint64_t*)(ws + wl.cmask);
   a.casc = 0;  // set by the dispatcher when the cascade kernel runs
   a.n_seqs = n_seqs;
   a.num_q_heads = num_q_heads;

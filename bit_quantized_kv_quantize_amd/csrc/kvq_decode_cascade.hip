@@ -1,28 +1,30 @@
-// kvq_decode_cascade.hip - decode attention over the blocks that every sequence of a batch shares, for head_dim
-// 128 pools whose K is grouped per channel over each 256-token block (the long shared-prefix serving workload
-// of the UltraQuant article's technology section, with the prefix reuse of "Agent Memory Below the Prompt",
+// kvq_decode_cascade.hip - decode attention over the blocks that several sequences of a batch share, for
+// head_dim 128 pools whose K is grouped per channel over each 256-token block (the long shared-prefix serving
+// workload of the UltraQuant article's technology section, the prefix cache of the IntentKV article's section
+// on the hidden cost of dropping old tokens, with the prefix reuse of "Agent Memory Below the Prompt",
 // technical summary 2.1-2.2, and its packed-block decode).
 //
-// A logical block that all sequences map to the same physical block (a shared prompt prefix) is read once for
-// all of them. The work unit is (range of logical blocks, KV head, row group), a row being one (sequence,
-// query head) pair of that KV head and a row group up to eight 16-row tiles, one per wave. The unit's partial
-// softmax state per row goes to the split-K workspace; the per-sequence kernel (decode_kchan_k) then skips
-// those blocks and merges these partials with its own. Every unit finds the shared blocks of its range itself
-// (same physical block in every sequence's table, and full in the shortest sequence), and the units of KV
-// head 0 and row group 0 publish them.
+// A block that several sequences map to (a shared prompt prefix, also one shared by a subset of the batch) is
+// read once for all of them. The planning kernel groups the sequences of every block range by the physical
+// block at the range's first logical block (an inverted index of the block tables) and flags, per sequence
+// and logical block, the blocks the cascade takes; the work items are (block range, KV head, row group), a
+// row being one (member sequence, query head) pair and a row group up to eight 16-row tiles, one per wave.
+// An item's partial softmax state per row goes to the split-K workspace; the per-sequence kernel
+// (decode_kchan_k) then skips the flagged blocks and merges these partials with its own.
 //
 // The blocks are walked in 64-token chunks. All 512 threads stage a chunk once for the eight waves: its K codes
 // as stored, its V rows dequantised to fp16 (v_scale * code + v_zero, one rounding) and, with a block's first
 // chunk, the block's K channel parameters. Each wave then takes its 16 rows against the chunk:
 // * QK token-major on the matrix cores (v_mfma_f32_16x16x32_f16): A = the K codes of 16 tokens as exact fp16
 //   subnormals (lane = token), B = q_c s_c of the wave's 16 rows as fp16 hi and lo (two MFMAs into one
-//   accumulator), rebuilt from the fp32 query in registers at every block; the channel zeros enter as the
+//   accumulator), rebuilt from the fp32 query in LDS at every block; the channel zeros enter as the
 //   per-row constant sum_c q_c z_c (q . k_t = sum_c (q_c s_c) code_tc + sum_c q_c z_c).
 // * The logits of a row sit in one column of the result: the row maximum is four lanes' worth of in-lane
-//   maxima, and p (fp16) is already laid out as the B operand of PV.
+//   maxima, and p (fp16) is already laid out as the B operand of PV. A row whose sequence does not take the
+//   block sees its logits as -inf.
 // * PV channel-major: A = the staged fp16 V rows through the 16-bit LDS transpose load (lane = channel),
 //   B = p. The values are centred on zero, so neither operand needs a hi/lo split.
-// The result of a wave is its rows' partial state over the unit's blocks; no merge inside the workgroup.
+// The result of a wave is its rows' partial state over the item's blocks; no merge inside the workgroup.
 #include "kvq_decode_mfma_common.hpp"
 
 namespace kvq {
@@ -78,8 +80,186 @@ __device__ __forceinline__ float rows4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// One-dimensional grid: workgroup wg -> unit u = (wg >> 3) / casc_rg * 8 + (wg & 7), row group
-// (wg >> 3) mod casc_rg, so every workgroup of KV head h (u mod H = h) and one block range shares an XCD.
+// Exclusive prefix sums of x[0 .. n) in place (n <= 2 * blockDim.x = 512) and their total, by all 256 threads;
+// s_w: four ints of scratch.
+__device__ int block_scan(int* x, int n, int tid, int* s_w) {
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int a0 = i0 < n ? x[i0] : 0, a1 = i1 < n ? x[i1] : 0;
+  int v = a0 + a1, incl = v;
+  const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_w[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int k = 0; k < w; ++k) base += s_w[k];
+  const int total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+  const int excl = base + incl - v;
+  if (i0 < n) x[i0] = excl;
+  if (i1 < n) x[i1] = excl + a0;
+  __syncthreads();
+  return total;
+}
+
+// Groups of sequences per block range (an inverted index of the block tables at the range's first logical
+// block), one workgroup of 256 threads per range:
+// * a sequence's key is its physical block at the range's first column if that block is full in it; the
+//   sequences of one key form a group, led by its lowest-numbered member, and groups of two or more take the
+//   cascade;
+// * the members of those groups go to the range's member list, group by group in leader order with the
+//   leader first, and each group's (member, query head) rows are cut into row groups of at most kCascRows
+//   rows (the work items);
+// * a member takes column c of the range when its block there is the leader's and full in it: its flag is
+//   set (the per-sequence kernel skips the block for it) and the column's bit in its mask (the group's item
+//   reads the block for it);
+// * every row's partial slot of the range starts empty (m = -inf, l = 0), for the rows no group covers.
+__global__ __launch_bounds__(256) void cascade_plan_k(TileGeom g, DecodeArgs a) {
+  __shared__ int s_len[kCascMaxSeqs], s_key[kCascMaxSeqs], s_lead[kCascMaxSeqs], s_cnt[kCascMaxSeqs];
+  __shared__ int s_rank[kCascMaxSeqs], s_pos[kCascMaxSeqs], s_mstart[kCascMaxSeqs], s_rstart[kCascMaxSeqs];
+  __shared__ uint32_t s_m[kCascMaxSeqs][2];
+  __shared__ int s_w[4];
+  constexpr int kHashBits = 10, kHashSlots = 1 << kHashBits;  // 2 * kCascMaxSeqs slots
+  static_assert(kHashSlots >= 2 * kCascMaxSeqs, "hash table at most half full");
+  __shared__ int s_hkey[kHashSlots], s_hlead[kHashSlots], s_hcnt[kHashSlots], s_slot[kCascMaxSeqs];
+  const int split = blockIdx.x, tid = threadIdx.x, n = a.n_seqs, S = a.plan.casc, G = a.G;
+  const int MB = a.plan.max_blocks;
+  const size_t mbs = (size_t)a.max_blocks_per_seq;
+  int c0, c1;
+  split_range(split, S, MB, c0, c1);
+  const int ncol = c1 - c0;  // at most kCascRangeCols
+  const size_t pslot = (size_t)(a.plan.stride - S + split);
+  // The range's slice of the block tables goes to LDS with one round of loads when it fits (n * ncol <=
+  // kSlice), else the table is read from memory where needed.
+  constexpr int kSlice = 8192;
+  __shared__ int s_tab[kSlice];
+  const bool in_lds = n * ncol <= kSlice;
+  auto table = [&](int s, int c) {
+    return in_lds ? s_tab[s * ncol + c - c0] : a.block_table[(size_t)s * mbs + c];
+  };
+  for (int r = tid; r < n * a.num_q_heads; r += 256) {
+    a.ws_ml[2 * ((size_t)r * a.plan.stride + pslot)] = kNegInf;
+    a.ws_ml[2 * ((size_t)r * a.plan.stride + pslot) + 1] = 0.0f;
+  }
+  if (in_lds) {
+    for (int base = 0; base < n * ncol; base += 4 * 256) {
+      int x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = min(base + tid + 256 * k, n * ncol - 1), sq = idx / ncol;
+        x[k] = a.block_table[(size_t)sq * mbs + c0 + idx - sq * ncol];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (base + tid + 256 * k < n * ncol) s_tab[base + tid + 256 * k] = x[k];
+    }
+  }
+  for (int s = tid; s < n; s += 256) {
+    s_len[s] = a.seq_lens[s];
+    s_cnt[s] = 0;
+    s_m[s][0] = 0u;
+    s_m[s][1] = 0u;
+  }
+  for (int i = tid; i < kHashSlots; i += 256) {
+    s_hkey[i] = -1;
+    s_hlead[i] = 0x7fffffff;
+    s_hcnt[i] = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < n; s += 256) s_key[s] = (ncol > 0 && (c0 + 1) * kRows <= s_len[s]) ? table(s, c0) : -1;
+  __syncthreads();
+  // Groups through an LDS hash table keyed by physical block: a sequence claims its key's slot (linear
+  // probing; at most kCascMaxSeqs keys in twice as many slots), the slot keeps the lowest member (the
+  // leader) and counts the members; a member's place in its group is the order in which it arrived (the
+  // place decides only which item row holds the sequence, not what is computed for it).
+  for (int s = tid; s < n; s += 256) {
+    const int key = s_key[s];
+    int hs = -1, rank = 0;
+    if (key >= 0) {
+      hs = (int)(((uint32_t)key * 2654435761u) >> (32 - kHashBits));
+      for (int probe = 0; probe < kHashSlots; ++probe) {
+        const int prev = atomicCAS(&s_hkey[hs], -1, key);
+        if (prev == -1 || prev == key) break;
+        hs = (hs + 1) & (kHashSlots - 1);
+      }
+      atomicMin(&s_hlead[hs], s);
+      rank = atomicAdd(&s_hcnt[hs], 1);
+    }
+    s_slot[s] = hs;
+    s_rank[s] = rank;
+  }
+  __syncthreads();
+  for (int s = tid; s < n; s += 256) {
+    const int hs = s_slot[s];
+    const int lead = hs >= 0 ? s_hlead[hs] : s;
+    s_lead[s] = lead;
+    if (lead == s) s_cnt[s] = hs >= 0 ? s_hcnt[hs] : 1;
+  }
+  __syncthreads();
+  // the leader first in its group, the others after it in arrival order
+  for (int s = tid; s < n; s += 256) {
+    const int lead = s_lead[s], r = s_rank[s], rl = s_rank[lead];
+    s_pos[s] = s == lead ? 0 : (r < rl ? r + 1 : r);
+  }
+  for (int s = tid; s < n; s += 256) {
+    const bool grp = s_lead[s] == s && s_cnt[s] >= 2;
+    s_mstart[s] = grp ? s_cnt[s] : 0;
+    s_rstart[s] = grp ? (s_cnt[s] * G + kCascRows - 1) / kCascRows : 0;
+  }
+  __syncthreads();
+  block_scan(s_mstart, n, tid, s_w);
+  const int n_rg = block_scan(s_rstart, n, tid, s_w);
+  int* perm = a.ws_cperm + (size_t)split * n;
+  int* desc = a.ws_cdesc + (size_t)split * a.plan.casc_slots * 4;
+  for (int s = tid; s < n; s += 256) {
+    const int lead = s_lead[s];
+    if (s_cnt[lead] < 2) continue;
+    perm[s_mstart[lead] + s_pos[s]] = s;
+    if (lead == s) {
+      const int nrg = (s_cnt[s] * G + kCascRows - 1) / kCascRows;
+      for (int q = 0; q < nrg; ++q) {
+        int* d = desc + 4 * (s_rstart[s] + q);
+        d[0] = s_mstart[s];
+        d[1] = s_cnt[s];
+        d[2] = q * kCascRows;
+        d[3] = 0;
+      }
+    }
+  }
+  if (tid == 0) a.ws_cnrg[split] = n_rg;
+  // every (sequence, column) pair of the range at once, four independent pairs per thread per round
+  const int total = n * ncol;
+  for (int base = 0; base < total; base += 4 * 256) {
+    int x[4], y[4], sq[4], c[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = min(base + tid + 256 * k, total - 1);
+      sq[k] = idx / ncol;
+      c[k] = idx - sq[k] * ncol;
+      x[k] = table(sq[k], c0 + c[k]);
+      y[k] = table(s_lead[sq[k]], c0 + c[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (base + tid + 256 * k >= total) continue;
+      const bool take = s_cnt[s_lead[sq[k]]] >= 2 && (c0 + c[k] + 1) * kRows <= s_len[sq[k]] && x[k] == y[k];
+      a.ws_cflag[(size_t)sq[k] * MB + c0 + c[k]] = take ? 1 : 0;
+      if (take) atomicOr(&s_m[sq[k]][c[k] >> 5], 1u << (c[k] & 31));
+    }
+  }
+  __syncthreads();
+  uint64_t* cmask = a.ws_cmask + (size_t)split * n;
+  for (int s = tid; s < n; s += 256) {
+    const int lead = s_lead[s];
+    if (s_cnt[lead] >= 2) cmask[s_mstart[lead] + s_pos[s]] = ((uint64_t)s_m[s][1] << 32) | s_m[s][0];
+  }
+}
+
+// Persistent grid of at most kCascGrid workgroups looping over the work items: item i is row group k of
+// block range r for KV head i mod H (items ordered by range, row group, head), so with H = 8 every item of
+// KV head h runs on XCD h and the row groups of one block range share that XCD's L2.
 template <int VG>
 __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs a) {
   constexpr int D = kD, NW = kCW;
@@ -87,71 +267,72 @@ __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs 
   constexpr int kKBytes = 64 * kKP, kBuf = kKBytes + 64 * kVP;  // one staged chunk: K rows, then V rows
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[3][kBuf];
   __shared__ __attribute__((aligned(16))) float2 s_kc[2][D];  // (scale / 16 on odd channels, zero) per channel
-  __shared__ int s_tbl[kMaxSplitBlocks], s_col[kMaxSplitBlocks];
-  __shared__ int s_bad[kMaxSplitBlocks];
-  __shared__ int s_ccnt[NW], s_minlen;
+  __shared__ int s_tbl[kCascRangeCols], s_col[kCascRangeCols];
+  __shared__ uint32_t s_cm[2];
+  __shared__ int s_first[kCascMaxRanges + 1];
   // the scaled (and rotated) query of each lane: 32 channels at a pitch of 36 floats (conflict-free reads)
   __shared__ __attribute__((aligned(16))) float s_qv[NW][64][36];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
-  const int H = g.H, S = a.plan.casc, RG = a.plan.casc_rg, NT = a.plan.casc_nt;
-  const int wg = blockIdx.x, rest = wg >> 3;
-  const int rg = rest % RG, u = (rest / RG) * 8 + (wg & 7);
-  if (u >= S * H) return;
-  const int h = u % H, split = u / H;
-  const int n_rows = a.n_seqs * a.G;
-  int c0, c1;
-  split_range(split, S, a.plan.max_blocks, c0, c1);
-  const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;
+  const int H = g.H, S = a.plan.casc, G = a.G;
+  const int MB = a.plan.max_blocks;
+  const uint8_t* pool_base = a.pool;
   const size_t tstride = (size_t)H * g.tile_bytes;
-  const size_t mbs = (size_t)a.max_blocks_per_seq;
-
-  // ------------------------------------------------------------ shared blocks of [c0, c1)
-  if (tid == 0) s_minlen = 0x7fffffff;
-  for (int i = tid; i < c1 - c0; i += 64 * NW) s_bad[i] = 0;
+  if (tid < S) s_first[tid + 1] = a.ws_cnrg[tid];
   __syncthreads();
-  for (int s = tid; s < a.n_seqs; s += 64 * NW) atomicMin(&s_minlen, a.seq_lens[s]);
-  {
-    // every (sequence, column) pair once, four independent loads per thread per round
-    const int ncol = c1 - c0, total = ncol * a.n_seqs;
-    for (int base = 0; base < total; base += 4 * 64 * NW) {
-      int x[4], y[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = min(base + tid + 64 * NW * k, total - 1);
-        const int s = idx / ncol, i = idx - s * ncol;
-        x[k] = a.block_table[(size_t)s * mbs + c0 + i];
-        y[k] = a.block_table[c0 + i];
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = base + tid + 64 * NW * k;
-        if (idx < total && x[k] != y[k]) s_bad[idx % ncol] = 1;
-      }
-    }
+  if (tid == 0) {
+    s_first[0] = 0;
+    for (int r = 1; r <= S; ++r) s_first[r] += s_first[r - 1];
   }
   __syncthreads();
-  const int nfull = s_minlen / kRows;  // blocks that are full in every sequence
-  const int nc = stage_columns<NW>(
-      c1 - c0, tid, s_tbl, s_col, s_ccnt, [&](int i) { return c0 + i < nfull && s_bad[i] == 0; },
-      [&](int i) { return a.block_table[c0 + i]; });
-  if (h == 0 && rg == 0)
-    for (int i = tid; i < c1 - c0; i += 64 * NW) a.ws_cflag[c0 + i] = (c0 + i < nfull && s_bad[i] == 0) ? 1 : 0;
+  const int n_items = s_first[S] * H;
 
-  // this wave's rows: row0 + lj, lane (la, lj) holding channels 32 la .. 32 la + 31 of row lj in the query
-  const int row0 = (rg * NT + w) * 16, row = row0 + lj;
-  const bool wave_rows = w < NT && row0 < n_rows;
-  const bool row_ok = w < NT && row < n_rows;
-  const int seq = row_ok ? row / a.G : 0, jj = row_ok ? row - seq * a.G : 0;
-  const size_t pslot = (size_t)(a.plan.stride - S + split);  // this unit's partial slot in each row
-  const size_t pi = ((size_t)seq * a.num_q_heads + h * a.G + jj) * a.plan.stride + pslot;
-  if (nc == 0) {
-    if (row_ok && la == 0) {
-      a.ws_ml[2 * pi] = kNegInf;
-      a.ws_ml[2 * pi + 1] = 0.0f;
-    }
-    return;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int h = item % H, ri = item / H;
+  int split = 0;
+  while (s_first[split + 1] <= ri) ++split;
+  const int* d = a.ws_cdesc + ((size_t)split * a.plan.casc_slots + (ri - s_first[split])) * 4;
+  const int m0 = d[0], n_mem = d[1], row_base = d[2];
+  const int* members = a.ws_cperm + (size_t)split * a.n_seqs + m0;
+  const int n_rows = min(kCascRows, n_mem * G - row_base);  // rows of this item
+  const int NT = (n_rows + 15) / 16;
+  const int lead = members[0];
+  int c0, c1;
+  split_range(split, S, MB, c0, c1);
+  const uint8_t* pool_h = pool_base + (size_t)h * g.tile_bytes;
+
+  // ------------------------------------------------------------ the group's blocks of [c0, c1)
+  __syncthreads();  // the previous item's LDS is free
+  const uint64_t* cmask = a.ws_cmask + (size_t)split * a.n_seqs + m0;
+  if (tid < 2) s_cm[tid] = 0u;
+  __syncthreads();
+  // the group's columns: those any member takes
+  for (int m = tid; m < n_mem; m += 64 * NW) {
+    const uint64_t x = cmask[m];
+    if ((uint32_t)x) atomicOr(&s_cm[0], (uint32_t)x);
+    if ((uint32_t)(x >> 32)) atomicOr(&s_cm[1], (uint32_t)(x >> 32));
   }
+  __syncthreads();
+  const uint64_t cols = ((uint64_t)s_cm[1] << 32) | s_cm[0];
+  const int nc = __builtin_popcountll(cols);
+  if (tid < kCascRangeCols && ((cols >> tid) & 1u)) {
+    const int b = __builtin_popcountll(cols & ((1ull << tid) - 1ull));
+    s_tbl[b] = a.block_table[(size_t)lead * a.max_blocks_per_seq + c0 + tid];
+    s_col[b] = tid;
+  }
+  __syncthreads();
+
+  // this wave's rows: 16 w + lj of the item, lane (la, lj) holding channels 32 la .. 32 la + 31 of row lj in
+  // the query; item row r is (member (row_base + r) / G, query head (row_base + r) mod G)
+  const int row = 16 * w + lj;
+  const bool wave_rows = w < NT;
+  const bool row_ok = row < n_rows;
+  const int gr = row_base + (row_ok ? row : 0);
+  const int seq = members[gr / G], jj = gr % G;
+  const uint64_t row_cols = row_ok ? cmask[gr / G] : 0ull;  // the columns this row's sequence takes
+  const size_t pslot = (size_t)(a.plan.stride - S + split);  // this range's partial slot in each row
+  const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * a.plan.stride + pslot;
+  if (nc == 0) continue;  // (the row's slot stays empty, as the planning kernel left it)
 
   // ------------------------------------------------------------ chunk loads and staging
   const int tt = tid >> 3, part = tid & 7;  // staging: token tt of the chunk, codes of channels 16 part ..
@@ -321,14 +502,17 @@ __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs 
   // rescale factor of the running state. The running maximum moves only when a logit exceeds it by more than
   // kSlack (or on the first chunk), so p <= 2^kSlack and the rescale is rare.
   constexpr float kSlack = 8.0f;
-  auto softmax = [&](const floatx4 (&acc)[4], float zq, u32x4 (&pb)[2]) __attribute__((always_inline)) -> float {
+  // A row that does not take the chunk's block (tk false) sees its logits as -inf: p = 0, state unchanged.
+  auto softmax = [&](const floatx4 (&acc)[4], float zq, bool tk, u32x4 (&pb)[2])
+                     __attribute__((always_inline)) -> float {
     float m4[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) m4[c] = fmaxf(fmaxf(acc[c][0], acc[c][1]), fmaxf(acc[c][2], acc[c][3]));
-    const float mx = __builtin_fmaf(rows4_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))), kTwo24, zq);
+    const float mr = rows4_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+    const float mx = tk ? __builtin_fmaf(mr, kTwo24, zq) : kNegInf;
     const float mnew = mx > m_run + kSlack ? mx : m_run;
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
-    const float off = zq - mnew;
+    const float off = tk ? zq - mnew : kNegInf;
     float p[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -381,17 +565,23 @@ __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs 
     b_nxt = b_stg;
     b_stg = t;
   };
+  // whether this lane's row takes staged block b
+  auto takes = [&](int b) __attribute__((always_inline)) {
+    return ((row_cols >> s_col[min(b, nc - 1)]) & 1u) != 0u;
+  };
   if (wave_rows) {
     floatx4 sc[4];
     float zc = build(0);
+    bool tc = takes(0);
     qk(b_cur, sc);
     auto step = [&](Raw& nxt, int j, auto kc) __attribute__((always_inline)) {
       constexpr int k = decltype(kc)::value;
       floatx4 sn[4];
       const float zn = k == 3 ? build((j + 1) >> 2) : zc;
+      const bool tn = k == 3 ? takes((j + 1) >> 2) : tc;
       qk(b_nxt, sn);
       u32x4 pb[2];
-      const float alpha = softmax(sc, zc, pb);
+      const float alpha = softmax(sc, zc, tc, pb);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) o[t] *= alpha;
@@ -402,6 +592,7 @@ __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs 
 #pragma unroll
       for (int c = 0; c < 4; ++c) sc[c] = sn[c];
       zc = zn;
+      tc = tn;
       rotate();
       lds_barrier();
     };
@@ -426,18 +617,22 @@ __global__ __launch_bounds__(64 * kCW, 1) void cascade_k(TileGeom g, DecodeArgs 
   }
 
   // ------------------------------------------------------------ this wave's rows: partial state
-  if (!row_ok) return;
-  const float lsum = rows4_sum(l_run);
-  // o[t][i]: staged column 16 t + 4 la + i, channel 8 (2 t + (la >> 1)) + nib(4 (la & 1) + i)
-  float* acc = a.ws_acc + pi * D;
+  if (wave_rows) {
+    const float lsum = rows4_sum(l_run);
+    if (row_ok) {
+      // o[t][i]: staged column 16 t + 4 la + i, channel 8 (2 t + (la >> 1)) + nib(4 (la & 1) + i)
+      float* acc = a.ws_acc + pi * D;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[8 * (2 * t + (la >> 1)) + nib(4 * (la & 1) + i)] = o[t][i];
-  if (la == 0) {
-    a.ws_ml[2 * pi] = m_run;
-    a.ws_ml[2 * pi + 1] = lsum;
+        for (int i = 0; i < 4; ++i) acc[8 * (2 * t + (la >> 1)) + nib(4 * (la & 1) + i)] = o[t][i];
+      if (la == 0) {
+        a.ws_ml[2 * pi] = m_run;
+        a.ws_ml[2 * pi + 1] = lsum;
+      }
+    }
   }
+  }  // items
 }
 
 }  // namespace
@@ -448,8 +643,9 @@ bool decode_cascade_supported(const TileGeom& g, int G) {
 }
 
 hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
-  const int units = a.plan.casc * g.H;
-  const dim3 grid(8 * a.plan.casc_rg * ((units + 7) / 8));
+  hipLaunchKernelGGL(cascade_plan_k, dim3(a.plan.casc), dim3(256), 0, stream, g, a);
+  const long items = (long)a.plan.casc * a.plan.casc_slots * g.H;  // bound on the work items
+  const dim3 grid((unsigned)std::min<long>(kCascGrid, items));
   if (g.vg == 32)
     hipLaunchKernelGGL(cascade_k<32>, grid, dim3(64 * kCW), 0, stream, g, a);
   else

@@ -14,7 +14,7 @@
 //   4-bit transpose load, one output channel per lane; each 16-channel output tile uses its group's A.
 // Sentinel slots are skipped (their exact term is added when the output is finalised), and the split-K
 // merge runs in the split that arrives last (splitk_arrive). After the cascade kernel (a.casc > 0) the blocks
-// it flagged as shared by every sequence are skipped, and its partials join the merge.
+// it took for the sequence (shared with other sequences) are skipped, and its partials join the merge.
 #include "kvq_decode_mfma_common.hpp"
 #include "kvq_decode_precise.hpp"
 
@@ -72,10 +72,12 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   const int nblk = (len + kRows - 1) / kRows;
   int b0, b1;
   split_range(split, a.plan.n_splits, nblk, b0, b1);
-  // Blocks the cascade kernel took for every sequence are skipped here; its partials join the merge.
+  // Blocks the cascade kernel took for this sequence are skipped here; its partials join the merge.
   const int n_pre = a.casc;
+  const int* cflag = a.ws_cflag + (size_t)seq * a.plan.max_blocks;
   const int nchunk = stage_columns(
-      max(b1 - b0, 0), tid, s_tbl, s_col, reinterpret_cast<int*>(&s_wm[0][0]), [&](int i) { return n_pre == 0 || a.ws_cflag[b0 + i] == 0; },
+      max(b1 - b0, 0), tid, s_tbl, s_col, reinterpret_cast<int*>(&s_wm[0][0]),
+      [&](int i) { return n_pre == 0 || cflag[b0 + i] == 0; },
       [&](int i) { return a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i]; });
   const uint32_t* mask_row = a.mask ? a.mask + (size_t)seq * a.mask_words : nullptr;
   const uint8_t* pool_h = a.pool + (size_t)h * g.tile_bytes;

@@ -56,9 +56,10 @@ TileGeom make_geom(const kvq_layout* L);
 // (split_range) on a (split, KV head, sequence) grid; no range is longer than blocks_per_split.
 // The row-list kernel runs a one-dimensional grid of `wgs` workgroups: the first nA pairs get k splits and
 // the others k + 1 (rows_work), which fills exactly two workgroups per CU when there are fewer pairs.
-// The cascade kernel (blocks shared by every sequence of the batch, per-channel K layouts) cuts the logical
-// block range into casc even ranges and the (sequence, query head) rows of each KV head into casc_rg
-// groups of casc_nt 16-row tiles; its partials take the last casc slots of each row's partial slots.
+// The cascade kernel (blocks shared by two or more sequences, per-channel K layouts) cuts the logical block
+// range into casc even ranges; in each range the sequences that share the range's first block form a
+// group, whose (sequence, query head) rows are cut into row groups of at most kCascRows rows (at most
+// casc_slots row groups per range); its partials take the last casc slots of each row's partial slots.
 // `stride` is the number of partial slots per (sequence, query head) in the workspace: the largest split
 // count of the per-sequence plans, plus casc.
 struct SplitPlan {
@@ -70,8 +71,7 @@ struct SplitPlan {
   int nA;
   int max_blocks;  // logical blocks of the longest sequence
   int casc;        // cascade block ranges (0: no cascade slots)
-  int casc_rg;     // cascade row groups per KV head
-  int casc_nt;     // 16-row tiles per cascade row group (at most kCascRows / 16)
+  int casc_slots;  // bound on the cascade row groups of one block range (over all groups of sequences)
 };
 // Blocks [b0, b1) of split `split` out of ns over a sequence of nblk blocks: even ranges, so the
 // splits of a pair differ by at most one block.
@@ -111,7 +111,7 @@ size_t decode_workspace_bytes(const TileGeom& g, int n_seqs, int num_q_heads, in
 // cascade flags) for a call of this size, all below `body`; the split-K arrival counters (ctr_bytes) take
 // the end of the caller's workspace (ctr_offset). `total` is the size a call of this size needs.
 struct WorkspaceLayout {
-  size_t ml, acc, cnt, list, bcnt, cflag, body, ctr_bytes, total;
+  size_t ml, acc, cnt, list, bcnt, cflag, cperm, cdesc, cnrg, cmask, body, ctr_bytes, total;
   size_t parts;  // partial slots the ml / acc regions hold
   int list_cap;
   int bcnt_blocks;  // blocks per sequence in the per-block live-row counts
@@ -152,7 +152,13 @@ struct DecodeArgs {
   int list_cap;
   int* ws_bcnt;      // [n_seqs][bcnt_blocks][W] live rows per width list of each logical block
   int bcnt_blocks;
-  int* ws_cflag;     // [plan.max_blocks] 1 where the cascade kernel took the logical block for every sequence
+  int* ws_cflag;     // [n_seqs][plan.max_blocks] 1 where the cascade kernel took the sequence's logical block
+  int* ws_cperm;     // [kCascMaxRanges][n_seqs] per block range: the members of its groups, group by group
+  int* ws_cdesc;     // [kCascMaxRanges][plan.casc_slots][4] per range: row groups {first member, members,
+                     // first row, 0}
+  int* ws_cnrg;      // [kCascMaxRanges] row groups of each range
+  uint64_t* ws_cmask;  // [kCascMaxRanges][n_seqs] per range, at each member's place in the member list: the
+                       // range's columns (bit i = column c0 + i) the member takes
   int casc;          // cascade partial slots merged by the per-sequence kernel in this call (0 or plan.casc)
   int n_seqs;
   int num_q_heads;
@@ -183,8 +189,15 @@ hipError_t launch_decode_fp8(const TileGeom& g, const DecodeArgs& a, hipStream_t
 // Cascade kernel for blocks shared by all sequences: layouts of the per-channel-K kernel; the caller then
 // runs that kernel with a.casc set.
 bool decode_cascade_supported(const TileGeom& g, int G);
-constexpr int kCascRows = 128;     // (sequence, query head) rows of one cascade workgroup at most
-constexpr int kCascSlots = 32768;  // bound on (query rows of the call) x (cascade block ranges)
+constexpr int kCascRows = 128;      // (sequence, query head) rows of one cascade workgroup at most
+constexpr int kCascSlots = 32768;   // bound on (query rows of the call) x (cascade block ranges)
+constexpr int kCascMaxSeqs = 512;   // sequences of a call that the cascade groups (more: no cascade)
+constexpr int kCascMaxRanges = 64;  // cascade block ranges
+constexpr int kCascRangeCols = 64;  // logical blocks of one cascade block range at most
+constexpr int kCascGrid = 256;      // cascade workgroups (one per CU), each looping over the row groups
+// Bound on the row groups of one block range: groups of two or more members (at most n_seqs / 2 of them),
+// each cut into ceil(members * G / kCascRows) row groups.
+inline int casc_slots(int n_seqs, int G) { return (n_seqs * G + kCascRows - 1) / kCascRows + n_seqs / 2; }
 hipError_t launch_decode_cascade(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 

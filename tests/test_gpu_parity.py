@@ -373,11 +373,56 @@ def _two_prefix_case(n_seqs, prefix_blocks, context):
     return case
 
 
+def _nested_prefix_case(over):
+    """Sharing among subsets of the batch, nested as in a prefix tree: blocks 0-3 are shared by sequences 0-10
+    (sequence 10 ends inside block 3), blocks 4-7 by sequences 0-4 and, as other blocks, by sequences 5-9,
+    blocks 8-9 by sequences 0-1 and by 5-7; sequence 11 shares nothing; the rest of every table is private."""
+    import dataclasses
+
+    cfg = dataclasses.replace(W.CONFIGS["qwen25_14b_prefix_32k"], name="prefix_nested", **over)
+    ctx = [2560 + (37 * i) % 700 for i in range(10)] + [900, 3000]
+    case = W.make_case(cfg, n_seqs=12, shared_prefix=0, context=ctx)
+    nb = case.num_blocks
+    new = iter(range(nb, nb + 100))
+    shared = {}
+
+    def put(seqs, cols, tag):
+        for c in cols:
+            key = (tag, c)
+            if key not in shared:
+                shared[key] = next(new)
+            for sq in seqs:
+                case.block_table[sq, c] = shared[key]
+
+    put(range(11), range(4), "all")
+    put(range(5), range(4, 8), "A")
+    put(range(5, 10), range(4, 8), "B")
+    put(range(2), range(8, 10), "C")
+    put(range(5, 8), range(8, 10), "D")
+    case.num_blocks = nb + len(shared)
+    case.prefill_blocks = np.array(sorted(set(case.prefill_blocks.tolist()) | set(shared.values())), np.int32)
+    return case
+
+
+@pytest.mark.parametrize("over", [{}, dict(num_q_heads=64, v_group=64, rotate=0)], ids=["g5", "g8_vg64"])
+def test_cascade_nested_subsets(env, orc, over, cascade_mode):
+    # Blocks shared by subsets of the sequences (a prefix tree of four levels, a sequence that ends inside a
+    # shared block, one that shares nothing) against the oracle, which reads every table as given.
+    kvq, torch = env
+    case = _nested_prefix_case(over)
+    inp = host_inputs(case)
+    _, ref = oracle_run(orc, case, inp)
+    _, got = gpu_run(kvq, torch, case, inp)
+    err = rel_err(got, ref)
+    print("nested subsets %s [%s]: max rel err %.3g" % (over, cascade_mode, err))
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("n_seqs", [8, 13])
 def test_cascade_groups_sharing_different_prefixes(env, orc, n_seqs, cascade_mode):
     # Two prompts, each shared by half of the sequences: blocks aliased by several tables but not by all of
-    # them. The cascade takes only blocks every sequence shares, so here the per-sequence kernel reads each
-    # prompt block once per sequence; the output must not depend on which kernel took which block.
+    # them. The cascade takes each prompt's blocks for its half; the output must not depend on which kernel
+    # took which block.
     kvq, torch = env
     case = _two_prefix_case(n_seqs, 4, [1024 + (211 * i) % 700 for i in range(n_seqs)])
     inp = host_inputs(case)
