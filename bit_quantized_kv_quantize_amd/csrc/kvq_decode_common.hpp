@@ -72,20 +72,20 @@ __device__ void finalize_head(const TileGeom& g, const DecodeArgs& a, int seq, i
   if (n_sent > 0) Lt += (float)n_sent * exp2f(kSentinelLog2 - Mt);
   o = (len > 0 && Lt > 0.0f) ? o / Lt : 0.0f;
   if (g.rotate) {
-    __syncthreads();
-    if (tid < D) s_o[tid] = o;
-    __syncthreads();
-    for (int hs = 1; hs < D; hs *= 2) {
-      float r = 0.0f;
-      if (tid < D) {
-        const float x = s_o[tid], y = s_o[tid ^ hs];
-        r = (tid & hs) ? (y - x) : (x + y);
-      }
-      __syncthreads();
-      if (tid < D) s_o[tid] = r;
-      __syncthreads();
+    // butterflies of channel strides 1 .. 32 between the lanes of a wave (channel c in lane c mod 64), the
+    // wider strides through LDS
+    for (int hs = 1; hs < D && hs < 64; hs *= 2) {
+      const float y = __shfl_xor(o, hs);
+      o = (tid & hs) ? (y - o) : (o + y);
     }
-    if (tid < D) o = s_o[tid] * a.unrot_cv;
+    for (int hs = 64; hs < D; hs *= 2) {
+      __syncthreads();
+      if (tid < D) s_o[tid] = o;
+      __syncthreads();
+      const float y = tid < D ? s_o[tid ^ hs] : 0.0f;
+      o = (tid & hs) ? (y - o) : (o + y);
+    }
+    o *= a.unrot_cv;
   }
   if (tid < D) a.out[((size_t)seq * a.num_q_heads + j) * D + tid] = o;
 }

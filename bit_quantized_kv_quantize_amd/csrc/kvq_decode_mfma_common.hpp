@@ -120,6 +120,10 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
   __shared__ int s_last;
   __shared__ int s_cnt[4];
   const int st = a.plan.stride;
+  // A unit with one split merges its own partials (still in LDS) with the n_pre earlier ones directly: no
+  // store, arrival or reload.
+  const bool local = ns == 1;
+  if (!local) {
   for (int i = tid; i < G * D; i += 256) {
     const int jj = i / D, c = i % D;
     const size_t pi = ((size_t)seq * a.num_q_heads + h * G + jj) * st + split;
@@ -139,6 +143,7 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
   }
   __syncthreads();
   if (!s_last) return;
+  }
   // Merge in one round of loads: thread (head jj, channel c) reads (m, l) and the accumulator of up to
   // eight splits at a time and folds them into a running (M, L, o); the merged rows go through LDS to
   // the finalisation, which wants channel c of one head in thread c.
@@ -148,13 +153,20 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
     const int jj = i / D, c = i % D;
     const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * st;
     float M = kNegInf, L = 0.0f, o = 0.0f;
-    const int nt = ns + n_pre, pre0 = st - n_pre - ns;  // slot of merged index k >= ns: k + pre0
+    if (local && part_l[jj] > 0.0f) {
+      M = part_m[jj];
+      L = part_l[jj];
+      o = part_acc[i];
+    }
+    // merged index k: split k (k < ns), then the earlier partials in slots k + pre0; with a local split
+    // only the earlier partials, in slots st - n_pre + k
+    const int nt = local ? n_pre : ns + n_pre, pre0 = st - n_pre - ns;
     for (int base = 0; base < nt; base += 8) {
       float mi[8], li[8], xi[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int kk = min(base + k, nt - 1);
-        const int sp = kk < ns ? kk : kk + pre0;
+        const int sp = local ? st - n_pre + kk : kk < ns ? kk : kk + pre0;
         li[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         mi[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         xi[k] = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
