@@ -336,7 +336,7 @@ def main():
         del pools, aks, avs, qs, outs
         torch.cuda.empty_cache()
         workloads = {}
-        names = W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL, MLA_POOL]
+        names = W.CONFIG_ORDER + [FP8_BASELINE, WIDTHS_POOL, MLA_POOL] + MLA_VARIANTS
         if args.workload_table:
             names = [n for n in args.workload_table.split(",") if n]
             for n in names:
@@ -425,6 +425,17 @@ FP8_BASELINE = "llama31_8b_pool_8k_fp8"
 WIDTHS_POOL = "llama31_8b_pool_8k_widths"
 # 12 agents x 8K of an MLA model: K head dim 192, V 128 ("Agent Memory Below the Prompt", 2.2).
 MLA_POOL = "deepseek_v2_lite_mla_8k"
+# The MLA pool with half of the cached slots remapped to the sentinel (IntentKV), and with per-token widths
+# {2, 4, 8, FP16} (QKVShare, methodology section; this one decodes on the generic kernel).
+MLA_VARIANTS = ["deepseek_v2_lite_mla_8k_sentinel", "deepseek_v2_lite_mla_8k_widths"]
+
+
+def base_name(name):
+    """The workload a variant name derives from."""
+    for suffix in ("_fp8", "_widths", "_sentinel"):
+        if name.endswith(suffix):
+            return base_name(name[:-len(suffix)])
+    return name
 
 
 def workload_config(name):
@@ -587,8 +598,7 @@ def measure_workload(kvq, torch, name, launches=16, graph=True, reps=20):
         app = (torch.from_numpy(ak).view(torch.float16).cuda(), torch.from_numpy(av).view(torch.float16).cuda(),
                None if prec is None else torch.from_numpy(prec).cuda())
         kvq.append_tokens(lay, pool, app[0], app[1], table, positions, app[2])
-    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(name.replace("_fp8", "").replace("_widths", ""),
-                                                                    1) - 1)]
+    pools = [pool] + [pool.clone() for _ in range(INSTANCES.get(base_name(name), 1) - 1)]
     torch.cuda.synchronize()
 
     def timed(fn):

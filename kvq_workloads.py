@@ -119,12 +119,18 @@ def widths_variant(cfg: Config, fracs: Tuple[float, float, float] = (0.05, 0.15,
     return dataclasses.replace(cfg, name=cfg.name + "_widths", mixed=2, top_fraction=0.0, width_fracs=fracs)
 
 
+def sentinel_variant(cfg: Config, dead: float = 0.5) -> Config:
+    """The same workload with a fraction ``dead`` of every sequence's cached slots remapped to the sentinel
+    (the IntentKV article's invalidation instead of compaction)."""
+    return dataclasses.replace(cfg, name=cfg.name + "_sentinel", dead_fraction=dead)
+
+
 def named_config(name: str) -> Config:
-    """A workload by name; the suffixes _fp8 and _widths name its FP8 and per-token-width variants."""
-    if name.endswith("_fp8"):
-        return fp8_variant(CONFIGS[name[:-len("_fp8")]])
-    if name.endswith("_widths"):
-        return widths_variant(CONFIGS[name[:-len("_widths")]])
+    """A workload by name; the suffixes _fp8, _widths and _sentinel name its FP8, per-token-width and
+    sentinel-slot variants (they compose, innermost first)."""
+    for suffix, variant in (("_fp8", fp8_variant), ("_widths", widths_variant), ("_sentinel", sentinel_variant)):
+        if name.endswith(suffix):
+            return variant(named_config(name[:-len(suffix)]))
     return CONFIGS[name] if name in CONFIGS else EXTRA[name]
 
 
