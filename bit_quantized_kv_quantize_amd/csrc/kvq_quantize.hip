@@ -35,6 +35,44 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
   }
 }
 
+// v of lane (this lane ^ m), m a power of two below 64: DPP moves inside a 16-lane row for m = 1, 2, 4, 8
+// (m = 4 as the quad reversal followed by the half-row mirror, (i ^ 3) ^ 7 = i ^ 4 within eight lanes),
+// so the rotations' and group reductions' exchanges stay on the VALU; a lane shuffle for m >= 16. The
+// lanes exchanging values must be active (every caller runs these with its whole row group active).
+__device__ __forceinline__ float lane_xor(float v, int m) {
+  const int x = __float_as_int(v);
+  switch (m) {
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    case 4:
+      return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false), 0x141,
+                                                     0xF, 0xF, false));  // quad_perm 3,2,1,0; row_half_mirror
+    case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror 8
+    default: return __shfl_xor(v, m);
+  }
+}
+
+// Min and max over the gl lanes of a group (gl a power of two, at most MAXL): every exchange width up to
+// MAXL is issued with its width known to the compiler and applied where it lies below gl, so the DPP
+// exchanges need no branch on the runtime group width (widths of 16 lanes and more take a lane shuffle
+// behind a uniform branch).
+template <int MAXL>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, int gl) {
+#pragma unroll
+  for (int m = 1; m < MAXL; m *= 2) {
+    if (m >= 16) {
+      if (m < gl) {
+        mn = fminf(mn, __shfl_xor(mn, m));
+        mx = fmaxf(mx, __shfl_xor(mx, m));
+      }
+    } else {
+      const float a = lane_xor(mn, m), b = lane_xor(mx, m);
+      mn = m < gl ? fminf(mn, a) : mn;
+      mx = m < gl ? fmaxf(mx, b) : mx;
+    }
+  }
+}
+
 // y = c * H * x for one row spread over LPR lanes, lane li holding elements li*8 .. li*8+7.
 template <int LPR>
 __device__ __forceinline__ void rotate_row(float (&x)[8], int li, float c) {
@@ -54,7 +92,7 @@ __device__ __forceinline__ void rotate_row(float (&x)[8], int li, float c) {
     const bool upper = (li & m) != 0;  // this lane holds the second element of each pair
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float p = __shfl_xor(x[i], m);
+      float p = lane_xor(x[i], m);
       x[i] = upper ? (p - x[i]) : (x[i] + p);
     }
   }
@@ -64,6 +102,7 @@ __device__ __forceinline__ void rotate_row(float (&x)[8], int li, float c) {
 
 // Quantise this lane's 8 values as part of a group spanning gl lanes (gl a power of two dividing the
 // row's lanes). Returns the 8 codes; every lane of the group gets the same packed {scale, zero}.
+template <int MAXL>
 __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits, uint32_t (&code)[8],
                                           uint32_t& param) {
   float mn = x[0], mx = x[0];
@@ -72,10 +111,7 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
     mn = fminf(mn, x[i]);
     mx = fmaxf(mx, x[i]);
   }
-  for (int m = 1; m < gl; m *= 2) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
+  group_minmax<MAXL>(mn, mx, gl);
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
   const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
@@ -168,7 +204,7 @@ __device__ __forceinline__ void quantize_token_row(const TileGeom& g, float (&x)
   }
   uint32_t code[8];
   uint32_t param;
-  quantize8(x, gl, bits, code, param);
+  quantize8<LPR>(x, gl, bits, code, param);
   store_codes(code_row, li, LPR, bits, tail, code);
   if ((li & (gl - 1)) == 0) reinterpret_cast<uint32_t*>(param_row)[li / gl] = param;
 }
@@ -218,15 +254,17 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
 
 // K grouped per channel over the block's 256 rows (always 4-bit). Two passes over the rows: the first
 // finds every column's min/max of the (rotated) values, the second recomputes the identical rotated
-// values and encodes them against the column's parameters.
+// values and encodes them against the column's parameters. A thread's rows (one lane of kRows / RPP rows)
+// stay in registers as the raw fp16 words between the passes, all loaded at once.
 template <int LPR>
 __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __restrict__ pool,
                                                         const int32_t* __restrict__ block_ids,
                                                         const uint16_t* __restrict__ k, float rot_c) {
   constexpr int D = LPR * 8;
-  constexpr int kRowsPerPass = 256 / LPR;
-  __shared__ float s_min[kRowsPerPass][D];
-  __shared__ float s_max[kRowsPerPass][D];
+  constexpr int RPP = 256 / LPR;     // rows per pass of the workgroup
+  constexpr int NR = kRows / RPP;    // rows of one thread
+  __shared__ float s_min[RPP][D];
+  __shared__ float s_max[RPP][D];
   __shared__ float s_z[D], s_r[D];
   __shared__ int s_zero_scale[D];
   const int i = blockIdx.x, h = blockIdx.y;
@@ -234,16 +272,29 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
   uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
   const uint16_t* src = k + ((size_t)i * kRows * g.H + h) * D + li * 8;
 
-  float cmin[8], cmax[8];
-  for (int t = r0; t < kRows; t += kRowsPerPass) {
-    float x[8];
-    load8(src + (size_t)t * g.H * D, x);
+  uint4 raw[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) raw[j] = *reinterpret_cast<const uint4*>(src + (size_t)(r0 + j * RPP) * g.H * D);
+  auto row = [&](int j, float (&x)[8]) __attribute__((always_inline)) {
+    const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = h2f(w[e] & 0xffffu);
+      x[2 * e + 1] = h2f(w[e] >> 16);
+    }
     if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+  };
+  float cmin[8], cmax[8];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float x[8];
+    row(j, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      cmin[e] = t == r0 ? x[e] : fminf(cmin[e], x[e]);
-      cmax[e] = t == r0 ? x[e] : fmaxf(cmax[e], x[e]);
+      cmin[e] = j == 0 ? x[e] : fminf(cmin[e], x[e]);
+      cmax[e] = j == 0 ? x[e] : fmaxf(cmax[e], x[e]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // one row's values live at a time
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -253,7 +304,7 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     float mn = s_min[0][c], mx = s_max[0][c];
-    for (int r = 1; r < kRowsPerPass; ++r) {
+    for (int r = 1; r < RPP; ++r) {
       mn = fminf(mn, s_min[r][c]);
       mx = fmaxf(mx, s_max[r][c]);
     }
@@ -268,25 +319,37 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
     s_r[c] = s == 0.0f ? 0.0f : 1.0f / s;
   }
   __syncthreads();
-  for (int t = r0; t < kRows; t += kRowsPerPass) {
+  // The second pass converts and rotates the raw words again; hiding their values from the compiler keeps it
+  // from holding the first pass's converted rows live across the reduction instead (NR x 8 more registers).
+#pragma unroll
+  for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y), "+v"(raw[j].z), "+v"(raw[j].w));
+  float zc[8], rc[8];
+  bool zs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    zc[e] = s_z[li * 8 + e];
+    rc[e] = s_r[li * 8 + e];
+    zs[e] = s_zero_scale[li * 8 + e] != 0;
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
     float x[8];
-    load8(src + (size_t)t * g.H * D, x);
-    if (g.rotate) rotate_row<LPR>(x, li, rot_c);
+    row(j, x);
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int c = li * 8 + e;
       uint32_t code = 0;
-      if (!s_zero_scale[c]) {
-        float tt = x[e] - s_z[c];
-        float u = tt * s_r[c];
+      if (!zs[e]) {
+        const float tt = x[e] - zc[e];
+        const float u = tt * rc[e];
         float qv = __builtin_rintf(u);
         qv = fminf(fmaxf(qv, 0.0f), 15.0f);
         code = (uint32_t)qv;
       }
       w |= code << (4 * e);
     }
-    reinterpret_cast<uint32_t*>(tile + g.kcode(t))[li] = w;
+    reinterpret_cast<uint32_t*>(tile + g.kcode(r0 + j * RPP))[li] = w;
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -334,7 +397,8 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
 
 // y = c * H * x for one row spread over L16 lanes, lane li holding elements 16 li .. 16 li + 15: the butterflies
 // of rotate_row in the same order (strides 1, 2, 4, 8 inside the lane, then 16, 32, ... across lanes), so the
-// rotated values are the same bits.
+// rotated values are the same bits. The exchanges are LDS lane shuffles here: with 16 values per lane they
+// overlap the butterflies' VALU work better than DPP moves did (48 against 55 us per 256 blocks).
 template <int L16>
 __device__ __forceinline__ void rotate_row16(float (&x)[16], int li, float c) {
 #pragma unroll
@@ -366,6 +430,7 @@ __device__ __forceinline__ void rotate_row16(float (&x)[16], int li, float c) {
 // values here), so the same codes and parameters. Codes are packed into w low bits first (8-bit: four words,
 // 4-bit: two, 2-bit: one): the codes of a byte are first combined exactly in fp32 (q0 + 16 q1, or q0 + 4 q1 +
 // 16 q2 + 64 q3, integers below 256) and the byte placed with v_cvt_pk_u8_f32 (exact for such integers).
+template <int MAXL>
 __device__ __forceinline__ void quantize16(const float (&x)[16], int gl, int bits, uint32_t (&w)[4],
                                            uint32_t& param) {
   float mn = x[0], mx = x[0];
@@ -374,10 +439,7 @@ __device__ __forceinline__ void quantize16(const float (&x)[16], int gl, int bit
     mn = fminf(mn, x[i]);
     mx = fmaxf(mx, x[i]);
   }
-  for (int m = 1; m < gl; m *= 2) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
+  group_minmax<MAXL>(mn, mx, gl);
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
   const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
@@ -481,7 +543,7 @@ __global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __
       continue;
     }
     uint32_t w[4], param;
-    quantize16(x, gl, bits, w, param);
+    quantize16<L16>(x, gl, bits, w, param);
     if (MIX && bits == 8) {
       *reinterpret_cast<uint4*>(row + li * 16) = uint4{w[0], w[1], w[2], w[3]};
     } else if (MIX == 2 && bits == 2) {
