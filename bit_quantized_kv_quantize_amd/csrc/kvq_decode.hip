@@ -377,7 +377,8 @@ hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t str
   const bool mfma = force && !strcmp(force, "mfma");
   if (!generic && !mfma && decode_rows_supported(g, a.G)) return launch_decode_rows(g, a, stream);
   if (!generic && !mfma && decode_kchan_supported(g, a.G)) {
-    // Blocks shared by all sequences go through the cascade kernel first (not for pools with sentinel slots).
+    // Blocks shared by two or more sequences go through the cascade kernel first (not for pools with sentinel
+    // slots).
     const bool nocasc = force && !strcmp(force, "nocascade");
     if (!nocasc && a.plan.casc > 0 && !a.mask && a.n_seqs >= 2 && decode_cascade_supported(g, a.G)) {
       DecodeArgs b = a;

@@ -43,8 +43,8 @@ constexpr int kPP = 20;  // halves per position of a position-major p * v_scale 
 struct RawC {
   u32x4 k[4];     // K codes of tokens 16c + lj, channels 32 la .. 32 la + 31
   u32x4 v[4];     // V codes of the same tokens and channels
-  u32x4 vp[4];    // V parameter records of tokens 16c + lj (first NGV entries used)
   uint32_t live;  // bit c: token 16c + lj is below seq_len and not a sentinel slot
+  uint32_t kc;    // K channel record (fp16 scale, fp16 zero) of channel tid mod 128
 };
 
 // Grid (n_splits, H_kv, n_seqs), 256 threads = 4 waves; wave w owns rows 64w .. 64w+63 of each block.
@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
   __shared__ uint16_t s_col[kMaxSplitBlocks];
   static_assert(sizeof(float) * 4 * G * D <= sizeof(_Float16) * 4 * NGV * 64 * kPP, "s_wacc fits in s_p");
   float (*s_wacc)[G][D] = reinterpret_cast<float (*)[G][D]>(&s_p[0][0][0]);  // used after the token loop
+  uint32_t* s_kch = reinterpret_cast<uint32_t*>(&s_p[0][0][0]);  // K channel records of one block (in build_block)
 
   const int split = blockIdx.x, h = blockIdx.y, seq = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
@@ -102,38 +103,62 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     return;
   }
 
+  // Addresses are a wave-uniform part (tile, row 64 w + 16 c) plus one lane offset each, so that few
+  // per-lane values stay live across the token loop.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t code_lane = (uint32_t)lj * (uint32_t)g.rec + 16u * (uint32_t)la;
+  const uint32_t prow_lane = (uint32_t)lj * (uint32_t)g.prow;
   auto load = [&](RawC& r, int i) __attribute__((always_inline)) {
     const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
     const uint8_t* tile = pool_h + (size_t)phys * tstride;
+    const int pos0 = (b0 + s_col[i]) * kRows + 64 * wu;  // position of row 64 w of the block
     uint32_t live = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t row = 64 * w + 16 * c + lj;
-      const uint8_t* rp = tile + (row * (uint32_t)g.rec + la * 16);
-      r.k[c] = *reinterpret_cast<const u32x4*>(rp);
-      r.v[c] = *reinterpret_cast<const u32x4*>(rp + D / 2);
-      const uint8_t* pp = tile + (g.off_prow + row * (uint32_t)g.prow);
-      if (NGV == 4) {
-        r.vp[c] = *reinterpret_cast<const u32x4*>(pp);
-      } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(pp);
-        r.vp[c] = u32x4{x.x, x.y, 0u, 0u};
-      }
-      const int pos = (b0 + s_col[i]) * kRows + (int)row;
-      const uint32_t mw = (mask_row && pos < len) ? mask_row[pos >> 5] : 0u;
-      live |= (pos < len && !((mw >> (row & 31)) & 1u)) ? (1u << c) : 0u;
+      const uint8_t* tc = tile + (uint32_t)(64 * wu + 16 * c) * (uint32_t)g.rec;
+      r.k[c] = *reinterpret_cast<const u32x4*>(tc + code_lane);
+      r.v[c] = *reinterpret_cast<const u32x4*>(tc + code_lane + D / 2);
+      const int pos = pos0 + 16 * c + lj;
+      // the 16 rows 64 w + 16 c .. + 15 share one mask word
+      const uint32_t mw = (mask_row && pos0 + 16 * c < len) ? mask_row[(pos0 + 16 * c) >> 5] : 0u;
+      live |= (pos < len && !((mw >> (pos & 31)) & 1u)) ? (1u << c) : 0u;
     }
     r.live = live;
+    r.kc = *reinterpret_cast<const uint32_t*>(tile + g.off_kch + 4u * (uint32_t)(threadIdx.x & (D - 1)));
+  };
+  // V parameter records of tokens 16c + lj of block i (first NGV entries used). One set only: the next
+  // block's records are loaded once this block's have been used, and arrive during its PV.
+  u32x4 vp[4];
+  auto load_vp = [&](int i) __attribute__((always_inline)) {
+    const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
+    const uint8_t* tile = pool_h + (size_t)phys * tstride;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint8_t* pp = tile + (g.off_prow + (uint32_t)(64 * wu + 16 * c) * (uint32_t)g.prow) + prow_lane;
+      if (NGV == 4) {
+        vp[c] = *reinterpret_cast<const u32x4*>(pp);
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(pp);
+        vp[c] = u32x4{x.x, x.y, 0u, 0u};
+      }
+    }
   };
 
-  // QK A operand and head constants of block i into buffer buf (all 256 threads; caller synchronises).
+  // QK A operand and head constants of block i into buffer buf from its K channel records kc (loaded with the
+  // block's codes, staged in s_kch here; all 256 threads; caller synchronises).
   // Lane (la', lj') of k-step s holds A[row lj'][k = 8 la' + e] = part(lj') of q[hq][c] * s_c * f(e),
   // hq = lj' / 2, c = 32 la' + 8 s + nib(e), nib = 0,4,1,5,2,6,3,7, f = 1/16 on the high nibbles.
-  auto build_block = [&](int i, int buf) __attribute__((always_inline)) {
-    const int phys = s_tbl[i];
-    const uint32_t* kch = reinterpret_cast<const uint32_t*>(pool_h + (size_t)phys * tstride + g.off_kch);
+  auto build_block = [&](uint32_t kc, int buf) __attribute__((always_inline)) {
+    lds_barrier();  // every wave is done with the p tiles, which s_kch aliases
+    if (tid < D) s_kch[tid] = kc;
+    lds_barrier();
+    const uint32_t* kch = s_kch;
+    // the thread index passes through an opaque copy, so that the addresses below are recomputed here
+    // rather than hoisted out of the token loop, where they would be live (and spilled) throughout
+    int t = tid;
+    asm volatile("" : "+v"(t));
     {
-      const int s = tid >> 6, ln = tid & 63, lap = ln >> 4, ljp = ln & 15;
+      const int s = t >> 6, ln = t & 63, lap = ln >> 4, ljp = ln & 15;
       const int hq = ljp >> 1, part = ljp & 1;
       uint32_t wv[4];
 #pragma unroll
@@ -154,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     }
     {
       // head constants: 8 heads x 32 threads, each thread 4 channels of the 128-channel dot product
-      const int hq = tid >> 5, part = tid & 31;
+      const int hq = t >> 5, part = t & 31;
       float zs = 0.0f;
       if (hq < G)
 #pragma unroll
@@ -166,6 +191,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
 
   RawC ra, rb;
   load(ra, 0);
+  load_vp(0);
 
   // ------------------------------------------------------------ query: scale and rotation
   for (int i = tid; i < G * D; i += 256)
@@ -186,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] *= a.unrot_c;
     __syncthreads();
   }
-  build_block(0, 0);
+  build_block(ra.kc, 0);
   __syncthreads();
 
   // lane (la, lj): heads 2 la + u (u = 0, 1) in MFMA rows 4 la + 2u + part
@@ -220,6 +246,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
         const u32x4 b = {wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
         acc[c] = mfma16(qa, b, acc[c]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // one k-step's B operands live at a time
     }
     const float zq0 = s_zq[buf][min(h0, 7)], zq1 = s_zq[buf][min(h0 + 1, 7)];
     float sc[2][4];
@@ -273,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int gm = 0; gm < NGV; ++gm) vmax = fmaxf(vmax, h2f(r.vp[c][gm] & 0xffffu));
+      for (int gm = 0; gm < NGV; ++gm) vmax = fmaxf(vmax, h2f(vp[c][gm] & 0xffffu));
     float pv_inv;
     const float pv_scale = chunk_pv_scale(vmax, pv_inv);
 #pragma unroll
@@ -286,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
       const bool on = p[0][c] != 0.0f || p[1][c] != 0.0f;
 #pragma unroll
       for (int gm = 0; gm < NGV; ++gm) {
-        const uint32_t pr = r.vp[c][gm];
+        const uint32_t pr = vp[c][gm];
         const float vs = on ? h2f(pr & 0xffffu) : 0.0f, vz = on ? h2f(pr >> 16) : 0.0f;
         zacc[0][gm] += p[0][c] * (vz + Lc * vs);
         zacc[1][gm] += p[1][c] * (vz + Lc * vs);
@@ -295,9 +322,11 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
         uint2 wv;
         wv.x = pack_h2(a0, (_Float16)(pv0 - (float)a0));
         wv.y = pack_h2(a1, (_Float16)(pv1 - (float)a1));
-        if (ok0) *reinterpret_cast<uint2*>(&s_p[w][gm][pos * kPP + la * 4]) = wv;
+        // (lanes of heads >= G store zeros: their p is 0)
+        *reinterpret_cast<uint2*>(&s_p[w][gm][pos * kPP + la * 4]) = wv;
       }
     }
+    load_vp(min(i + 1, nchunk - 1));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -305,12 +334,12 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     // The chunk accumulates into fresh MFMA tiles that are then added to the running output in fp32: the
     // code sum p * v_scale * code is much larger than the output it cancels down to (the group zeros'
     // term is added separately), and a long chain of MFMA accumulations would lose that difference.
-    floatx4 ob[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) ob[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     const int tok = lj < 8 ? 8 * la + lj : 32 + 8 * la + (lj - 8);
 #pragma unroll
     for (int gm = 0; gm < NGV; ++gm) {
+      floatx4 ob[8 / NGV];
+#pragma unroll
+      for (int tt = 0; tt < 8 / NGV; ++tt) ob[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
       u32x4 pa[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -328,12 +357,12 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
           // high nibbles (odd tokens) complemented: 15 - code
           const uint32_t wd = (uint32_t)(kb ? x.y : x.x) ^ 0xF0F0F0F0u, w8 = wd >> 8;
           const u32x4 b = {wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
-          ob[t] = mfma16(pa[kb], b, ob[t]);
+          ob[tt] = mfma16(pa[kb], b, ob[tt]);
         }
       }
-    }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] += ob[t] * pv_inv;
+      for (int tt = 0; tt < 8 / NGV; ++tt) o[gm * (8 / NGV) + tt] += ob[tt] * pv_inv;
+    }
     __builtin_amdgcn_wave_barrier();
   };
 
@@ -343,13 +372,17 @@ __global__ __launch_bounds__(256, 2) void decode_kchan_k(TileGeom g, DecodeArgs 
     load(rb, min(i + 1, nchunk - 1));
     __builtin_amdgcn_sched_barrier(0);
     process(ra, i);
-    if (i + 1 < nchunk) build_block(i + 1, (i + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < nchunk) build_block(rb.kc, (i + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     if (i + 1 >= nchunk) break;
     load(ra, min(i + 2, nchunk - 1));
     __builtin_amdgcn_sched_barrier(0);
     process(rb, i + 1);
-    if (i + 2 < nchunk) build_block(i + 2, (i + 2) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < nchunk) build_block(ra.kc, (i + 2) & 1);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
 
