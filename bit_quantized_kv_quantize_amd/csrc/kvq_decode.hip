@@ -359,6 +359,9 @@ hipError_t launch_t(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 
 template <int D, int DV>
 hipError_t launch_d(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  // the head loops run over GMAX heads: the smallest instance that holds G
+  if (a.G == 1) return launch_t<D, DV, 1>(g, a, stream);
+  if (a.G == 2) return launch_t<D, DV, 2>(g, a, stream);
   if (a.G <= 4) return launch_t<D, DV, 4>(g, a, stream);
   if (a.G <= 8) return launch_t<D, DV, 8>(g, a, stream);
   return launch_t<D, DV, 16>(g, a, stream);

@@ -144,55 +144,78 @@ __device__ inline void splitk_arrive(const TileGeom& g, const DecodeArgs& a, int
   __syncthreads();
   if (!s_last) return;
   }
-  // Merge in one round of loads: thread (head jj, channel c) reads (m, l) and the accumulator of up to
-  // eight splits at a time and folds them into a running (M, L, o); the merged rows go through LDS to
-  // the finalisation, which wants channel c of one head in thread c.
+  // Merge: thread (head jj, channel c) for each of its NI items (jj, c) reads (m, l) and the accumulator of
+  // up to KB splits at a time - the loads of all its items in one round - and folds them into a running
+  // (M, L, o); the merged rows go through LDS to the finalisation, which wants channel c of one head in
+  // thread c.
   __shared__ float s_hM[G], s_hL[G];
   float* s_merged = const_cast<float*>(part_acc);  // this split's own partials are no longer needed
-  for (int i = tid; i < G * D; i += 256) {
-    const int jj = i / D, c = i % D;
-    const size_t p0 = ((size_t)seq * a.num_q_heads + h * G + jj) * st;
-    float M = kNegInf, L = 0.0f, o = 0.0f;
+  constexpr int NI = (G * D + 255) / 256;
+  constexpr int KB = 8;
+  float M[NI], L[NI], o[NI];
+  size_t p0[NI];
+  int cc[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = min(tid + 256 * j, G * D - 1);
+    const int jj = i / D;
+    cc[j] = i % D;
+    p0[j] = ((size_t)seq * a.num_q_heads + h * G + jj) * st;
+    M[j] = kNegInf;
+    L[j] = 0.0f;
+    o[j] = 0.0f;
     if (local && part_l[jj] > 0.0f) {
-      M = part_m[jj];
-      L = part_l[jj];
-      o = part_acc[i];
+      M[j] = part_m[jj];
+      L[j] = part_l[jj];
+      o[j] = part_acc[i];
     }
-    // merged index k: split k (k < ns), then the earlier partials in slots k + pre0; with a local split
-    // only the earlier partials, in slots st - n_pre + k
-    const int nt = local ? n_pre : ns + n_pre, pre0 = st - n_pre - ns;
-    for (int base = 0; base < nt; base += 8) {
-      float mi[8], li[8], xi[8];
+  }
+  // merged index k: split k (k < ns), then the earlier partials in slots k + pre0; with a local split
+  // only the earlier partials, in slots st - n_pre + k
+  const int nt = local ? n_pre : ns + n_pre, pre0 = st - n_pre - ns;
+  for (int base = 0; base < nt; base += KB) {
+    float mi[NI][KB], li[NI][KB], xi[NI][KB];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int kk = min(base + k, nt - 1);
-        const int sp = local ? st - n_pre + kk : kk < ns ? kk : kk + pre0;
-        li[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        mi[k] = __hip_atomic_load(&a.ws_ml[2 * (p0 + sp)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        xi[k] = __hip_atomic_load(&a.ws_acc[(p0 + sp) * D + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int k = 0; k < KB; ++k) {
+      const int kk = min(base + k, nt - 1);
+      const int sp = local ? st - n_pre + kk : kk < ns ? kk : kk + pre0;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        li[j][k] = __hip_atomic_load(&a.ws_ml[2 * (p0[j] + sp) + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        mi[j][k] = __hip_atomic_load(&a.ws_ml[2 * (p0[j] + sp)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        xi[j][k] = __hip_atomic_load(&a.ws_acc[(p0[j] + sp) * D + cc[j]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      float mb = M;
+    }
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (base + k < nt && li[k] > 0.0f) mb = fmaxf(mb, mi[k]);
+    for (int j = 0; j < NI; ++j) {
+      float mb = M[j];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (base + k < nt && li[j][k] > 0.0f) mb = fmaxf(mb, mi[j][k]);
       if (mb == kNegInf) continue;
-      const float r = M == kNegInf ? 0.0f : exp2f(M - mb);
-      L *= r;
-      o *= r;
+      const float r = M[j] == kNegInf ? 0.0f : exp2f(M[j] - mb);
+      L[j] *= r;
+      o[j] *= r;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (base + k < nt && li[k] > 0.0f) {  // splits without live rows left their accumulators unwritten
-          const float wgt = exp2f(mi[k] - mb);
-          L += li[k] * wgt;
-          o += xi[k] * wgt;
+      for (int k = 0; k < KB; ++k) {
+        if (base + k < nt && li[j][k] > 0.0f) {  // splits without live rows left their accumulators unwritten
+          const float wgt = exp2f(mi[j][k] - mb);
+          L[j] += li[j][k] * wgt;
+          o[j] += xi[j][k] * wgt;
         }
       }
-      M = mb;
+      M[j] = mb;
     }
-    s_merged[i] = o;
-    if (c == 0) {
-      s_hM[jj] = M;
-      s_hL[jj] = L;
+  }
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int i = tid + 256 * j;
+    if (i < G * D) {
+      s_merged[i] = o[j];
+      if (cc[j] == 0) {
+        s_hM[i / D] = M[j];
+        s_hL[i / D] = L[j];
+      }
     }
   }
   __syncthreads();
