@@ -313,6 +313,10 @@ def main():
     # flat 2 GiB read
     ceiling = read_ceiling(torch, cfg, case, pools, table, seq_lens, layers)
 
+    # the prefill quantiser's read-plus-write ceiling: one layer's fp16 K/V in, its tiles out
+    q_ceiling = stream_rw_ceiling(torch, n_prefill * W.BLOCK * cfg.num_kv_heads * (cfg.head_dim + cfg.dv) * 2,
+                                  n_prefill * cfg.num_kv_heads * tb)
+
     # plain device copy of 2 GiB for context (read + write bandwidth the box delivers)
     a = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
@@ -397,6 +401,12 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_tokens_quantized_per_s": None if q_tok_s is None else round(q_tok_s, 0),
         "quantize_GBps": None if q_gbps is None else round(q_gbps, 1),
+        "quantize_roofline": None if q_gbps is None else {
+            "bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(q_gbps / HBM_PEAK_GBPS, 4), "kernel": "quantize_rows16_k<8, false, 0, 2, 2>",
+            "bytes_per_layer": quantize_bytes(cfg, n_prefill, tb), "us_per_layer": round(qs_t * 1e6 / layers, 2),
+            "ceiling": q_ceiling,
+            "frac_of_rw_ceiling": None if not q_ceiling else round(q_gbps / q_ceiling["GBps"], 4)},
         "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -515,6 +525,62 @@ def read_ceiling(torch, cfg, case, pools, table, seq_lens, layers, reps=20):
     torch.cuda.empty_cache()
     log("read ceiling (%.1f MB per launch): decode tiles %.1f us -> %.0f GB/s; flat read %.1f us -> %.0f GB/s" %
         (kv_bytes / 1e6, t_tiles * 1e6, res["tiles_GBps"], t_lin * 1e6, res["flat_GBps"]))
+    return res
+
+
+def stream_rw_ceiling(torch, in_bytes, out_bytes, reps=20):
+    """Read-plus-write ceiling for the prefill quantiser (libkvq_probe.so): in_bytes read and out_bytes written
+    per launch, interleaved at their ratio, from 2048 workgroups; launches cycle through enough buffers to
+    exceed the Infinity Cache and are timed in a graph between events."""
+    import ctypes
+
+    path = os.path.join(ROOT, "bit_quantized_kv_quantize_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.kvq_probe_stream_rw.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, ctypes.c_int, P]
+    in_bytes, out_bytes = in_bytes // 16 * 16, out_bytes // 16 * 16
+    n = max(2, (1 << 30) // (in_bytes + out_bytes) + 1)
+    ins = [torch.empty(in_bytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+    outs = [torch.empty(out_bytes, dtype=torch.uint8, device="cuda") for _ in range(n)]
+
+    def launch(i):
+        st = lib.kvq_probe_stream_rw(P(ins[i % n].data_ptr()), in_bytes, P(outs[i % n].data_ptr()), out_bytes, 2048,
+                                     P(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            launch(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3 / n)
+    t, _, _ = pct(ts)
+    del ins, outs
+    torch.cuda.empty_cache()
+    res = {"GBps": round((in_bytes + out_bytes) / t / 1e9, 1), "us": round(t * 1e6, 2), "read_bytes": in_bytes,
+           "write_bytes": out_bytes,
+           "kind": "libkvq_probe stream_rw: a flat read of the quantiser's input bytes and a flat write of its "
+                   "tile bytes, interleaved at their ratio, 2048 workgroups, per launch in a graph"}
+    log("read+write ceiling (%.1f MB in, %.1f MB out): %.1f us -> %.0f GB/s" %
+        (in_bytes / 1e6, out_bytes / 1e6, t * 1e6, res["GBps"]))
     return res
 
 

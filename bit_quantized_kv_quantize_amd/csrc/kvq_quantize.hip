@@ -22,7 +22,13 @@ namespace {
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
-__device__ __forceinline__ uint32_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+// fp32 -> fp16 bits, rounded from the fp32 value. The empty asm makes f an opaque fp32 register: otherwise the
+// compiler may fuse the conversion into the fma that produced f (v_fma_mixlo_f16 rounds once, straight to
+// fp16), which differs from rounding the fp32 result.
+__device__ __forceinline__ uint32_t f2h(float f) {
+  __asm__("" : "+v"(f));
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
 
 // Eight consecutive fp16 values (one 16-byte load) -> fp32.
 __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
@@ -73,6 +79,27 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx, int gl) {
   }
 }
 
+// The scale before rounding, (mx - mn) / L for L = 3, 15 or 255 levels: the product with c = fp32(1/L) and one
+// remainder correction. For these three divisors this equals the IEEE quotient for every non-negative finite
+// fp32 dividend (an exhaustive comparison with the division over all 2^31 such values), in three
+// instructions where the division takes about ten.
+__device__ __forceinline__ float div_levels(float x, int bits) {
+  const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
+  const float c = bits == 8 ? 0x1.010102p-8f : bits == 2 ? 0x1.555556p-2f : 0x1.111112p-4f;
+  const float q0 = x * c;
+  const float r = __builtin_fmaf(-q0, L, x);
+  return __builtin_fmaf(r, c, q0);
+}
+
+// 1 / s for a stored fp16 scale s > 0: the hardware reciprocal (within one ulp of 1 / s) and one Newton
+// correction. For every positive fp16 value and any start within two ulps of 1 / s the result is the IEEE
+// quotient (an exhaustive comparison over the 31743 values and five starts each).
+__device__ __forceinline__ float rcp_scale(float s) {
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
+
 // y = c * H * x for one row spread over LPR lanes, lane li holding elements li*8 .. li*8+7.
 template <int LPR>
 __device__ __forceinline__ void rotate_row(float (&x)[8], int li, float c) {
@@ -115,7 +142,7 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
   const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
-  const float s32 = (mx - mn) / L;
+  const float s32 = div_levels(mx - mn, bits);
   const uint32_t sh = f2h(s32), zh = f2h(mn);
   param = sh | (zh << 16);
   const float s = h2f(sh), z = h2f(zh);
@@ -124,7 +151,7 @@ __device__ __forceinline__ void quantize8(const float (&x)[8], int gl, int bits,
     for (int i = 0; i < 8; ++i) code[i] = 0;
     return;
   }
-  const float r = 1.0f / s;
+  const float r = rcp_scale(s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float t = x[i] - z;
@@ -430,27 +457,45 @@ __device__ __forceinline__ void rotate_row16(float (&x)[16], int li, float c) {
 // values here), so the same codes and parameters. Codes are packed into w low bits first (8-bit: four words,
 // 4-bit: two, 2-bit: one): the codes of a byte are first combined exactly in fp32 (q0 + 16 q1, or q0 + 4 q1 +
 // 16 q2 + 64 q3, integers below 256) and the byte placed with v_cvt_pk_u8_f32 (exact for such integers).
-template <int MAXL>
-__device__ __forceinline__ void quantize16(const float (&x)[16], int gl, int bits, uint32_t (&w)[4],
-                                           uint32_t& param) {
-  float mn = x[0], mx = x[0];
+// The lane's extremes of 16 values, from the fp32 values, or (for values that are the stored fp16 inputs
+// themselves) from the packed fp16 words two at a time: min and max are exact in either precision.
+__device__ __forceinline__ void lane_extremes(const float (&x)[16], float& mn, float& mx) {
+  mn = x[0];
+  mx = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
     mn = fminf(mn, x[i]);
     mx = fmaxf(mx, x[i]);
   }
+}
+__device__ __forceinline__ void lane_extremes_h(const uint32_t (&ww)[8], float& mn, float& mx) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  h2 lo = __builtin_bit_cast(h2, ww[0]), hi = lo;
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    const h2 y = __builtin_bit_cast(h2, ww[e]);
+    lo = __builtin_elementwise_min(lo, y);
+    hi = __builtin_elementwise_max(hi, y);
+  }
+  mn = fminf((float)lo.x, (float)lo.y);
+  mx = fmaxf((float)hi.x, (float)hi.y);
+}
+
+template <int MAXL>
+__device__ __forceinline__ void quantize16(const float (&x)[16], float mn, float mx, int gl, int bits,
+                                           uint32_t (&w)[4], uint32_t& param) {
   group_minmax<MAXL>(mn, mx, gl);
   mn = mn + 0.0f;  // a -0 extreme becomes +0
   mx = mx + 0.0f;
   const float L = bits == 8 ? 255.0f : bits == 2 ? 3.0f : 15.0f;
-  const float s32 = (mx - mn) / L;
+  const float s32 = div_levels(mx - mn, bits);
   const uint32_t sh = f2h(s32), zh = f2h(mn);
   param = sh | (zh << 16);
   const float s = h2f(sh), z = h2f(zh);
 #pragma unroll
   for (int k = 0; k < 4; ++k) w[k] = 0u;
   if (s == 0.0f) return;
-  const float r = 1.0f / s;
+  const float r = rcp_scale(s);
   float q[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -479,9 +524,12 @@ __device__ __forceinline__ void quantize16(const float (&x)[16], int gl, int bit
 // groups of 16 channels or more: rotation (ROT, rotate_row16) and per-token widths (MIX = the layout's mixed:
 // {4, 8} or {2, 4, 8, FP16}) as compile-time variants, with the same codes, parameters, headers and zero
 // padding. The per-row work (group extremes, the two divisions, addressing) is shared by twice as many values
-// as with 8 per lane, and each pass's rows are loaded while the previous pass is quantised. Grid and output
-// as quantize_rows_k.
-template <int L16, bool ROT, int MIX>
+// as with 8 per lane, and PF passes' rows are loaded while a pass is quantised. NT = 1: grid and output as
+// quantize_rows_k (one tensor per workgroup). NT = 2: grid (n_blocks, H, 1), the workgroup quantises K and V of
+// its tile, so each row record and parameter record is written whole by one wave (measured on the 12 x 8K
+// pool: 133 -> 115 us per layer, the mixed workload 902 -> 705 us per 2048 blocks). Without rotation the
+// lane's extremes come from the packed fp16 inputs (exact in fp16).
+template <int L16, bool ROT, int MIX, int NT, int PF>
 __global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __restrict__ pool,
                                                          const int32_t* __restrict__ block_ids,
                                                          const uint16_t* __restrict__ k,
@@ -492,73 +540,92 @@ __global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __
   constexpr int RPP = 256 / L16;                  // rows per pass (21 at L16 = 12: threads 252..255 idle)
   constexpr int NPASS = (kRows + RPP - 1) / RPP;  // passes (the last one partial at L16 = 12)
   static_assert(!ROT || (L16 & (L16 - 1)) == 0, "rotation needs a power-of-two head dim");
-  const int i = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
+  static_assert(NT == 1 || NT == 2, "one tensor, or K and V of the tile");
+  const int i = blockIdx.x, h = blockIdx.y, kv0 = NT == 2 ? 0 : blockIdx.z + kv_base;
   const int li = threadIdx.x % L16, r0 = threadIdx.x / L16;
-  const uint16_t* src = (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 16;
   uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
-  const int gl = (kv ? g.vg : g.kg) / 16;
   const uint32_t* bitmap = MIX && prec_bits ? prec_bits + (size_t)i * (g.header_bytes() / 4) : nullptr;
   // Rows past the block (the idle threads and the partial last pass when L16 does not divide 256) load the
   // block's last row instead, so every load is unconditional, and skip the work.
-  auto row_ptr = [&](int t) { return src + (size_t)min(t, kRows - 1) * g.H * D; };
-  const uint16_t* rp = row_ptr(r0);
-  uint4 nxt0 = *reinterpret_cast<const uint4*>(rp), nxt1 = *reinterpret_cast<const uint4*>(rp + 8);
-#pragma unroll 1
-  for (int p = 0; p < NPASS; ++p) {
-    const uint4 a = nxt0, b = nxt1;
-    if (p + 1 < NPASS) {  // the next pass's row is in flight while this one is quantised
-      rp = row_ptr(r0 + (p + 1) * RPP);
-      nxt0 = *reinterpret_cast<const uint4*>(rp);
-      nxt1 = *reinterpret_cast<const uint4*>(rp + 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const int t = r0 + p * RPP;
-    if (t >= kRows) continue;
-    float x[16];
-    const uint32_t ww[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  auto row_ptr = [&](int kv, int t) {
+    return (kv ? v : k) + ((size_t)i * kRows * g.H + h) * D + li * 16 + (size_t)min(t, kRows - 1) * g.H * D;
+  };
+  // PF passes' rows are in flight while one pass is quantised (a ring of PF + 1 register sets; the pass loop
+  // is unrolled, so the ring indices are constants)
+  uint4 buf[PF + 1][NT][2];
+  auto issue = [&](uint4 (&b)[NT][2], int p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[2 * e] = h2f(ww[e] & 0xffffu);
-      x[2 * e + 1] = h2f(ww[e] >> 16);
+    for (int n = 0; n < NT; ++n) {
+      const uint16_t* rp = row_ptr(kv0 + n, r0 + p * RPP);
+      b[n][0] = *reinterpret_cast<const uint4*>(rp);
+      b[n][1] = *reinterpret_cast<const uint4*>(rp + 8);
     }
-    if constexpr (ROT) rotate_row16<L16>(x, li, rot_c);
+  };
+  auto work = [&](const uint4 (&b)[NT][2], int p) __attribute__((always_inline)) {
+    const int t = r0 + p * RPP;
+    if (t >= kRows) return;
     int bits = 4;
     if constexpr (MIX == 2) bits = 2 << (bitmap ? (bitmap[t >> 4] >> (2 * (t & 15))) & 3u : 1u);
     if constexpr (MIX == 1) bits = (bitmap && ((bitmap[t >> 5] >> (t & 31)) & 1u)) ? 8 : 4;
-    uint8_t* row = tile + (kv ? g.vcode(t, bits) : g.kcode(t));
-    uint32_t* prow = reinterpret_cast<uint32_t*>(tile + (kv ? g.vpar(t) : g.kpar(t)));
-    if (MIX == 2 && bits == 16) {
-      uint4 o0, o1;
-      o0.x = f2h(x[0]) | (f2h(x[1]) << 16);
-      o0.y = f2h(x[2]) | (f2h(x[3]) << 16);
-      o0.z = f2h(x[4]) | (f2h(x[5]) << 16);
-      o0.w = f2h(x[6]) | (f2h(x[7]) << 16);
-      o1.x = f2h(x[8]) | (f2h(x[9]) << 16);
-      o1.y = f2h(x[10]) | (f2h(x[11]) << 16);
-      o1.z = f2h(x[12]) | (f2h(x[13]) << 16);
-      o1.w = f2h(x[14]) | (f2h(x[15]) << 16);
-      *reinterpret_cast<uint4*>(row + li * 32) = o0;
-      *reinterpret_cast<uint4*>(row + li * 32 + 16) = o1;
-      if ((li & (gl - 1)) == 0) prow[li / gl] = 0u;
-      continue;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int kv = kv0 + n;
+      const int gl = (kv ? g.vg : g.kg) / 16;
+      float x[16];
+      const uint32_t ww[8] = {b[n][0].x, b[n][0].y, b[n][0].z, b[n][0].w, b[n][1].x, b[n][1].y, b[n][1].z, b[n][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[2 * e] = h2f(ww[e] & 0xffffu);
+        x[2 * e + 1] = h2f(ww[e] >> 16);
+      }
+      if constexpr (ROT) rotate_row16<L16>(x, li, rot_c);
+      uint8_t* row = tile + (kv ? g.vcode(t, bits) : g.kcode(t));
+      uint32_t* prow = reinterpret_cast<uint32_t*>(tile + (kv ? g.vpar(t) : g.kpar(t)));
+      if (MIX == 2 && bits == 16) {
+        uint4 o0, o1;
+        o0.x = f2h(x[0]) | (f2h(x[1]) << 16);
+        o0.y = f2h(x[2]) | (f2h(x[3]) << 16);
+        o0.z = f2h(x[4]) | (f2h(x[5]) << 16);
+        o0.w = f2h(x[6]) | (f2h(x[7]) << 16);
+        o1.x = f2h(x[8]) | (f2h(x[9]) << 16);
+        o1.y = f2h(x[10]) | (f2h(x[11]) << 16);
+        o1.z = f2h(x[12]) | (f2h(x[13]) << 16);
+        o1.w = f2h(x[14]) | (f2h(x[15]) << 16);
+        *reinterpret_cast<uint4*>(row + li * 32) = o0;
+        *reinterpret_cast<uint4*>(row + li * 32 + 16) = o1;
+        if ((li & (gl - 1)) == 0) prow[li / gl] = 0u;
+        continue;
+      }
+      uint32_t w[4], param;
+      float mn, mx;
+      if constexpr (ROT) lane_extremes(x, mn, mx);
+      else lane_extremes_h(ww, mn, mx);
+      quantize16<L16>(x, mn, mx, gl, bits, w, param);
+      if (MIX && bits == 8) {
+        *reinterpret_cast<uint4*>(row + li * 16) = uint4{w[0], w[1], w[2], w[3]};
+      } else if (MIX == 2 && bits == 2) {
+        *reinterpret_cast<uint32_t*>(row + li * 4) = w[0];
+      } else {
+        *reinterpret_cast<uint2*>(row + li * 8) = uint2{w[0], w[1]};
+      }
+      if (MIX && kv) {  // the rest of a narrower row's record is zero (4-byte aligned, as in store_codes)
+        uint32_t* z = reinterpret_cast<uint32_t*>(row + L16 * 2 * bits);
+        const int nw = (g.rec - (g.d + g.dv) * bits / 8) / 4;
+        for (int q = li; q < nw; q += L16) z[q] = 0u;
+      }
+      if ((li & (gl - 1)) == 0) prow[li / gl] = param;
     }
-    uint32_t w[4], param;
-    quantize16<L16>(x, gl, bits, w, param);
-    if (MIX && bits == 8) {
-      *reinterpret_cast<uint4*>(row + li * 16) = uint4{w[0], w[1], w[2], w[3]};
-    } else if (MIX == 2 && bits == 2) {
-      *reinterpret_cast<uint32_t*>(row + li * 4) = w[0];
-    } else {
-      *reinterpret_cast<uint2*>(row + li * 8) = uint2{w[0], w[1]};
-    }
-    if (MIX && kv) {  // the rest of a narrower row's record is zero (4-byte aligned, as in store_codes)
-      uint32_t* z = reinterpret_cast<uint32_t*>(row + L16 * 2 * bits);
-      const int nw = (g.rec - (g.d + g.dv) * bits / 8) / 4;
-      for (int q = li; q < nw; q += L16) z[q] = 0u;
-    }
-    if ((li & (gl - 1)) == 0) prow[li / gl] = param;
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < NPASS) issue(buf[p], p);
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    if (p + PF < NPASS) issue(buf[(p + PF) % (PF + 1)], p + PF);
+    __builtin_amdgcn_sched_barrier(0);
+    work(buf[p % (PF + 1)], p);
   }
-  if (kv == 1) {
+  if (kv0 + NT - 1 == 1) {
     // zero the tail padding (and write the width words of pools with per-token widths)
     const uint32_t end = g.off_hdr + g.header_bytes();
     for (uint32_t o = end + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
@@ -586,22 +653,29 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
     const bool v_lanes = kv_base + n_tensors < 2 || g.vg % 16 == 0;
     if (!g.fp8 && k_lanes && v_lanes) {
       constexpr int L16 = LPR / 2;
-      const dim3 grid(n_blocks, g.H, n_tensors);
-      auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, g, pool, block_ids, k, v, prec_bits, rot_c, kv_base);
+      // K and V of a tile in one workgroup (whole row records and parameter records written by one wave, two
+      // passes in flight) once there are enough tiles to fill the chip with them (4 per CU); small calls keep
+      // one workgroup per tensor.
+      const bool both = n_tensors == 2 && (long)n_blocks * g.H >= 1024;
+      const dim3 grid(n_blocks, g.H, both ? 1 : n_tensors);
+      auto go = [&](auto kern1, auto kern2) {
+        if (both)
+          hipLaunchKernelGGL(kern2, grid, dim3(256), 0, stream, g, pool, block_ids, k, v, prec_bits, rot_c, kv_base);
+        else
+          hipLaunchKernelGGL(kern1, grid, dim3(256), 0, stream, g, pool, block_ids, k, v, prec_bits, rot_c, kv_base);
       };
       if constexpr ((L16 & (L16 - 1)) == 0) {
         if (g.rotate) {
-          if (g.mixed == 2) go(quantize_rows16_k<L16, true, 2>);
-          else if (g.mixed) go(quantize_rows16_k<L16, true, 1>);
-          else go(quantize_rows16_k<L16, true, 0>);
+          if (g.mixed == 2) go(quantize_rows16_k<L16, true, 2, 1, 1>, quantize_rows16_k<L16, true, 2, 2, 2>);
+          else if (g.mixed) go(quantize_rows16_k<L16, true, 1, 1, 1>, quantize_rows16_k<L16, true, 1, 2, 2>);
+          else go(quantize_rows16_k<L16, true, 0, 1, 1>, quantize_rows16_k<L16, true, 0, 2, 2>);
           return hipGetLastError();
         }
       }
       {
-        if (g.mixed == 2) go(quantize_rows16_k<L16, false, 2>);
-        else if (g.mixed) go(quantize_rows16_k<L16, false, 1>);
-        else go(quantize_rows16_k<L16, false, 0>);
+        if (g.mixed == 2) go(quantize_rows16_k<L16, false, 2, 1, 1>, quantize_rows16_k<L16, false, 2, 2, 2>);
+        else if (g.mixed) go(quantize_rows16_k<L16, false, 1, 1, 1>, quantize_rows16_k<L16, false, 1, 2, 2>);
+        else go(quantize_rows16_k<L16, false, 0, 1, 1>, quantize_rows16_k<L16, false, 0, 2, 2>);
       }
     } else
       hipLaunchKernelGGL(quantize_rows_k<LPR>, dim3(n_blocks, g.H, n_tensors), dim3(256), 0, stream, g, pool,

@@ -7,7 +7,8 @@
 // rows of every block of its range) and 16-byte loads, and does no arithmetic beyond folding the loaded words
 // into one value per workgroup (written out so nothing is optimised away). Its time is the floor of a kernel with that decode's
 // load pattern. kvq_probe_read_linear streams a flat buffer with 16-byte loads from 2048 workgroups: the
-// chip's plain read bandwidth.
+// chip's plain read bandwidth. kvq_probe_stream_rw reads one flat buffer and writes a smaller one at a given
+// ratio: the read-plus-write ceiling the prefill quantiser is measured against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,6 +78,19 @@ __global__ __launch_bounds__(256) void read_linear_k(const u32x4* buf, size_t n1
   if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
 }
 
+// Streams n_in16 16-byte words in and n_out16 out (n_out16 <= n_in16) with 16-byte loads and stores from a
+// grid-stride loop, the output interleaved with the input at their ratio: after input word i the words up to
+// floor((i + 1) * n_out16 / n_in16) are written (each the running fold of the thread's input). The
+// read-plus-write ceiling of a kernel that transforms one stream into a smaller one, as quantisation does.
+__global__ __launch_bounds__(256) void stream_rw_k(const u32x4* in, size_t n_in16, u32x4* out, size_t n_out16) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n_in16; i += (size_t)gridDim.x * 256) {
+    acc ^= in[i];
+    const size_t o0 = i * n_out16 / n_in16, o1 = (i + 1) * n_out16 / n_in16;
+    for (size_t o = o0; o < o1; ++o) out[o] = acc;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,6 +113,18 @@ __attribute__((visibility("default"))) int kvq_probe_read_linear(const void* buf
   if (bytes % 16 || wgs <= 0 || ((uintptr_t)buf & 15u)) return -1;
   hipLaunchKernelGGL(read_linear_k, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const u32x4*)buf, bytes / 16,
                      sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Returns 0, or -1 for bad sizes, -4 for a launch error. in, out: device buffers of in_bytes and out_bytes
+// (16-byte multiples, out_bytes <= in_bytes, 16-byte aligned); out is overwritten.
+__attribute__((visibility("default"))) int kvq_probe_stream_rw(const void* in, size_t in_bytes, void* out,
+                                                               size_t out_bytes, int wgs, void* stream) {
+  if (in_bytes % 16 || out_bytes % 16 || out_bytes > in_bytes || wgs <= 0 || ((uintptr_t)in & 15u) ||
+      ((uintptr_t)out & 15u))
+    return -1;
+  hipLaunchKernelGGL(stream_rw_k, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const u32x4*)in, in_bytes / 16,
+                     (u32x4*)out, out_bytes / 16);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
