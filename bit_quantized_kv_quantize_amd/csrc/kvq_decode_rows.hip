@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_k(TileGeom g, De
 struct Raw {
   u32x4 k[4];
   u32x4 v[4];
-  uint32_t kp[4][2], vp[4][2];
+  u32x4 prm;       // the parameter record of token 16 la + lj (K groups {scale, zero} x 2, then V groups x 2)
   uint32_t valid;  // bit c: token 16c + lj of the chunk exists
 };
 
@@ -244,6 +244,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   __shared__ float s_qsum[G][2];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][64 * kVP];   // staged V rows, per wave
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][64 * kPP];  // p * v_scale, position-major, per wave
+  __shared__ __attribute__((aligned(16))) u32x4 s_par[4][64];         // the chunk's parameter records, per wave
   __shared__ float s_wm[4][G], s_wl[4][G];
   __shared__ float s_wacc[4][G][D];
   __shared__ int s_tbl[GATHER ? 1 : kMaxSplitBlocks];
@@ -429,15 +430,19 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + kD + 16);
       }
     }
+    // One parameter record per lane: the record of token 16 la + lj (lane (c, lj) holds the record every
+    // lane with token 16c + lj needs; they are exchanged through LDS when the chunk is processed). Loading
+    // each token's record in all four lanes of its 16-lane group instead (four loads per lane, each reading
+    // one 128-byte line in four) made a read of the 12 x 8K pool with this work split 33 % slower.
+    {
+      const uint8_t* tp = tile[0];
+      uint32_t rp = row[0];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // parameter record of the row: K groups {scale, zero} x 2, then V groups x 2
-      const uint4 pr = *reinterpret_cast<const uint4*>(tile[c] + (g.off_prow + row[c] * 16));
-      const uint2 kpv = {pr.x, pr.y}, vpv = {pr.z, pr.w};
-      r.kp[c][0] = kpv.x;
-      r.kp[c][1] = kpv.y;
-      r.vp[c][0] = vpv.x;
-      r.vp[c][1] = vpv.y;
+      for (int c = 1; c < 4; ++c) {
+        tp = la == c ? tile[c] : tp;
+        rp = la == c ? row[c] : rp;
+      }
+      r.prm = *reinterpret_cast<const u32x4*>(tp + (g.off_prow + rp * 16));
     }
   };
 
@@ -531,6 +536,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 
   uint8_t* sv = s_v[w];
   _Float16* sp = s_p[w];
+  u32x4* spar = s_par[w];
   // Set when a chunk of this wave had logit terms above kPreciseAbove: the wave's rows then go through the fp64
   // pass (precise_wave_pass) after the main loop (wave-uniform).
   bool wave_big = false;
@@ -560,6 +566,22 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(sv + lj * kVP16 + la * 64 + 16 * c) = r.v[c];
+    }
+    // ---------------------------------------------------------- parameter records of tokens 16c + lj
+    uint32_t kp[NC][2], vp[NC][2];
+    if constexpr (!F16) {
+      spar[16 * la + lj] = r.prm;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 x = spar[16 * c + lj];
+        kp[c][0] = x[0];
+        kp[c][1] = x[1];
+        vp[c][0] = x[2];
+        vp[c][1] = x[3];
+      }
     }
     // ---------------------------------------------------------- logits: QK on the matrix cores
     floatx4 acc[NC];
@@ -596,9 +618,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         sc[c] = live ? dk : kNegInf;
         big |= live && fabsf(dk) > kPreciseAbove;
       } else {
-        const float dot = h2f(r.kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
-                          h2f(r.kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
-        const float zq = h2f(r.kp[c][0] >> 16) * qs0 + h2f(r.kp[c][1] >> 16) * qs1;
+        const float dot = h2f(kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
+                          h2f(kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
+        const float zq = h2f(kp[c][0] >> 16) * qs0 + h2f(kp[c][1] >> 16) * qs1;
         const float dk = dot * kTwo24;
         sc[c] = live ? dk + zq : kNegInf;
         big |= live && fabsf(dk) + fabsf(zq) > kPreciseAbove;
@@ -651,7 +673,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       float vmax = 0.0f;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        vmax = fmaxf(vmax, fmaxf(h2f(r.vp[c][0] & 0xffffu), h2f(r.vp[c][1] & 0xffffu)));
+        vmax = fmaxf(vmax, fmaxf(h2f(vp[c][0] & 0xffffu), h2f(vp[c][1] & 0xffffu)));
       const float pv_scale = chunk_pv_scale(vmax, pv_inv);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -662,8 +684,8 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         const bool odd = u & 1;
         const float f = odd ? (W8 ? -pv_scale : -0.0625f * pv_scale) : pv_scale;
         const float Lc = odd ? (W8 ? 255.0f : 15.0f) : 0.0f;
-        const float vs0 = on ? h2f(r.vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(r.vp[c][0] >> 16) : 0.0f;
-        const float vs1 = on ? h2f(r.vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(r.vp[c][1] >> 16) : 0.0f;
+        const float vs0 = on ? h2f(vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(vp[c][0] >> 16) : 0.0f;
+        const float vs1 = on ? h2f(vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(vp[c][1] >> 16) : 0.0f;
         zacc0 += pp * (vz0 + Lc * vs0);
         zacc1 += pp * (vz1 + Lc * vs1);
         const float pv0 = (pp * f) * vs0, pv1 = (pp * f) * vs1;
