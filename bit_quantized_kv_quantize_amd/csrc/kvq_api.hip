@@ -158,10 +158,10 @@ WorkspaceLayout workspace_layout(const TileGeom& g, int n_seqs, int num_q_heads,
   const size_t nwd = g.mixed == 2 ? 4 : 2;
   w.cnt = w.acc + up(parts * g.dv * sizeof(float));
   w.list = w.cnt + up(ns * nwd * sizeof(int));
-  w.list_cap = decode_rows_supported(g, num_q_heads / g.H) ? (max_seq_len + 63) / 64 * 64 : 0;
+  w.list_cap = decode_rows_supported(g, num_q_heads / g.H, true) ? (max_seq_len + 63) / 64 * 64 : 0;
   w.bcnt = w.list + up(ns * nwd * (size_t)w.list_cap * sizeof(uint32_t));
   // at least one block per sequence, so the count kernels always have a grid
-  w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
+  w.bcnt_blocks = decode_rows_supported(g, num_q_heads / g.H, true) ? max(1, (max_seq_len + kRows - 1) / kRows) : 0;
   w.cflag = w.bcnt + up(ns * nwd * (size_t)w.bcnt_blocks * sizeof(int));
   // cascade: a flag per (sequence, logical block), the member lists and row groups of every block range
   const size_t slots = casc ? (size_t)casc_slots((int)ns, (int)G) : 0;

@@ -378,7 +378,7 @@ hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t str
 #endif
   const bool generic = force && !strcmp(force, "generic");
   const bool mfma = force && !strcmp(force, "mfma");
-  if (!generic && !mfma && decode_rows_supported(g, a.G)) return launch_decode_rows(g, a, stream);
+  if (!generic && !mfma && decode_rows_supported(g, a.G, a.mask != nullptr)) return launch_decode_rows(g, a, stream);
   if (!generic && !mfma && decode_kchan_supported(g, a.G)) {
     // Blocks shared by two or more sequences go through the cascade kernel first (not for pools with sentinel
     // slots).

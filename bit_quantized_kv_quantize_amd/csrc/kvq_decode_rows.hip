@@ -214,11 +214,16 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_k(TileGeom g, De
 // chunks: tokens 16c + lj (c = 0..3), 16 bytes each of K and V. 8-bit chunks: tokens 16c + lj (c = 0, 1),
 // 32 bytes each (k[2c], k[2c + 1]). 2-bit chunks: tokens 16c + lj (c = 0..3), 8 bytes each (k[c].x, .y).
 // FP16 chunks: token lj, 64 bytes each (k[0..3]).
-struct Raw {
+// X: a K head dim of 192 (MLA pools), whose channels 128 .. 191 (K group 2) come as `kx`: 4-bit chunks 8 bytes
+// per token (kx[2c], kx[2c + 1]), 8-bit chunks 16 bytes (kx[4c .. 4c + 3]), 2-bit chunks 4 bytes (kx[c]), FP16
+// chunks 32 bytes (kx[0 .. 7]): channels 128 + 16 la .. 128 + 16 la + 15.
+template <bool X>
+struct RawT {
   u32x4 k[4];
   u32x4 v[4];
-  u32x4 prm;       // the parameter record of token 16 la + lj (K groups {scale, zero} x 2, then V groups x 2)
-  uint32_t valid;  // bit c: token 16c + lj of the chunk exists
+  uint32_t prm[X ? 5 : 4];  // the parameter record of token 16 la + lj (K groups {scale, zero}, then V groups)
+  uint32_t kx[X ? 8 : 1];
+  uint32_t valid;           // bit c: token 16c + lj of the chunk exists
 };
 
 // Chunk kinds, in the order of the row lists: 4-bit chunks of 64 rows, 8-bit chunks of 32 rows, and in
@@ -234,17 +239,22 @@ __device__ __forceinline__ uint32_t spread2(uint32_t w, uint32_t sel) {
   return ((x << 2) | x) & 0x33333333u;
 }
 
-template <int G, bool GATHER, bool MIX2>
+template <int G, bool GATHER, bool MIX2, int DK>
 __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a) {
   static_assert(G == 1 || G == 2 || G == 4, "GQA ratio 1, 2 or 4");
   static_assert(GATHER || !MIX2, "pools of four widths are read through the row lists");
-  constexpr int D = kD;
+  static_assert(DK == 128 || DK == 192, "K head dim 128, or 192 (MLA: 128 + 64 channels, V 128)");
+  constexpr int D = kD;                  // V's head dim, and the first 128 channels of K
+  constexpr bool X = DK == 192;          // K channels 128 .. 191 (K group 2)
+  constexpr int NGK = DK / 64;           // K groups per row
+  constexpr int NP = NGK + 2;            // parameter words per row
   constexpr int NWD = MIX2 ? 4 : 2;  // row lists per sequence
-  __shared__ float s_q[G][D];
-  __shared__ float s_qsum[G][2];
+  using Raw = RawT<X>;
+  __shared__ float s_q[G][DK];
+  __shared__ float s_qsum[G][NGK];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[4][64 * kVP];   // staged V rows, per wave
   __shared__ __attribute__((aligned(16))) _Float16 s_p[4][64 * kPP];  // p * v_scale, position-major, per wave
-  __shared__ __attribute__((aligned(16))) u32x4 s_par[4][64];         // the chunk's parameter records, per wave
+  __shared__ uint32_t s_par[4][64 * NP];                              // the chunk's parameter records, per wave
   __shared__ float s_wm[4][G], s_wl[4][G];
   __shared__ float s_wacc[4][G][D];
   __shared__ int s_tbl[GATHER ? 1 : kMaxSplitBlocks];
@@ -264,12 +274,12 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   // The query and (streaming) the block-table slice are loaded into registers first: neither depends on the
   // sequence length, so their loads overlap its load. Streaming splits cut the longest sequence's blocks;
   // a shorter sequence clips them.
-  constexpr int kQPer = (G * D + 255) / 256;
+  constexpr int kQPer = (G * DK + 255) / 256;
   uint16_t qraw[kQPer];
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
-    const int i = min(tid + 256 * k, G * D - 1);  // unconditional loads: no branch waits for them
-    qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / D) * D + i % D];
+    const int i = min(tid + 256 * k, G * DK - 1);  // unconditional loads: no branch waits for them
+    qraw[k] = a.q[((size_t)seq * a.num_q_heads + h * G + i / DK) * DK + i % DK];
   }
   // rows per chunk of each kind, and the kind of chunk ci (wave-uniform)
   auto chunk_rows = [](int kind) __attribute__((always_inline)) {
@@ -400,34 +410,53 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     if (kind == kK4) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint8_t* rp = tile[c] + (row[c] * R + la * 16);
-        r.k[c] = *reinterpret_cast<const u32x4*>(rp);
-        r.v[c] = *reinterpret_cast<const u32x4*>(rp + kD / 2);  // V codes follow the row's 4-bit K codes
+        const uint8_t* rp = tile[c] + row[c] * R;
+        r.k[c] = *reinterpret_cast<const u32x4*>(rp + la * 16);
+        r.v[c] = *reinterpret_cast<const u32x4*>(rp + DK / 2 + la * 16);  // V codes follow the 4-bit K codes
+        if constexpr (X) {
+          const uint2 xx = *reinterpret_cast<const uint2*>(rp + 64 + la * 8);
+          r.kx[2 * c] = xx.x;
+          r.kx[2 * c + 1] = xx.y;
+        }
       }
     } else if (MIX2 && kind == kK2) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint8_t* rp = tile[c] + (row[c] * R + la * 8);
-        const uint2 kk = *reinterpret_cast<const uint2*>(rp);
-        const uint2 vv = *reinterpret_cast<const uint2*>(rp + kD / 4);  // V codes follow the 2-bit K codes
+        const uint8_t* rp = tile[c] + row[c] * R;
+        const uint2 kk = *reinterpret_cast<const uint2*>(rp + la * 8);
+        const uint2 vv = *reinterpret_cast<const uint2*>(rp + DK / 4 + la * 8);  // V codes follow the 2-bit K codes
         r.k[c] = u32x4{kk.x, kk.y, 0u, 0u};
         r.v[c] = u32x4{vv.x, vv.y, 0u, 0u};
+        if constexpr (X) r.kx[c] = *reinterpret_cast<const uint32_t*>(rp + 32 + la * 4);
       }
     } else if (MIX2 && kind == kK16) {
-      const uint8_t* rp = tile[0] + (row[0] * R + la * 64);
+      const uint8_t* rp = tile[0] + row[0] * R;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        r.k[c] = *reinterpret_cast<const u32x4*>(rp + 16 * c);
-        r.v[c] = *reinterpret_cast<const u32x4*>(rp + 2 * kD + 16 * c);  // V values follow the K values
+        r.k[c] = *reinterpret_cast<const u32x4*>(rp + la * 64 + 16 * c);
+        r.v[c] = *reinterpret_cast<const u32x4*>(rp + 2 * DK + la * 64 + 16 * c);  // V values follow the K values
+      }
+      if constexpr (X) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4 xx = *reinterpret_cast<const u32x4*>(rp + 256 + la * 32 + 16 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r.kx[4 * c + e] = xx[e];
+        }
       }
     } else {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint8_t* rp = tile[c] + (row[c] * R + la * 32);
-        r.k[2 * c] = *reinterpret_cast<const u32x4*>(rp);
-        r.k[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + 16);
-        r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + kD);  // V codes follow the row's 8-bit K codes
-        r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + kD + 16);
+        const uint8_t* rp = tile[c] + row[c] * R;
+        r.k[2 * c] = *reinterpret_cast<const u32x4*>(rp + la * 32);
+        r.k[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + la * 32 + 16);
+        r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + DK + la * 32);  // V codes follow the 8-bit K codes
+        r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + DK + la * 32 + 16);
+        if constexpr (X) {
+          const u32x4 xx = *reinterpret_cast<const u32x4*>(rp + 128 + la * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r.kx[4 * c + e] = xx[e];
+        }
       }
     }
     // One parameter record per lane: the record of token 16 la + lj (lane (c, lj) holds the record every
@@ -442,7 +471,15 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         tp = la == c ? tile[c] : tp;
         rp = la == c ? row[c] : rp;
       }
-      r.prm = *reinterpret_cast<const u32x4*>(tp + (g.off_prow + rp * 16));
+      if constexpr (X) {
+        const uint32_t* pr = reinterpret_cast<const uint32_t*>(tp + (g.off_prow + rp * (4 * NP)));
+#pragma unroll
+        for (int e = 0; e < NP; ++e) r.prm[e] = pr[e];
+      } else {
+        const u32x4 pr = *reinterpret_cast<const u32x4*>(tp + (g.off_prow + rp * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.prm[e] = pr[e];
+      }
     }
   };
 
@@ -465,11 +502,11 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 #pragma unroll
   for (int k = 0; k < kQPer; ++k) {
     const int i = tid + 256 * k;
-    if (i < G * D) s_q[i / D][i % D] = h2f(qraw[k]) * a.q_scale;
+    if (i < G * DK) s_q[i / DK][i % DK] = h2f(qraw[k]) * a.q_scale;
   }
   for (int i = tid; i < 4 * 64 * kPP; i += 256) (&s_p[0][0])[i] = (_Float16)0.0f;
   lds_barrier();
-  if (g.rotate) {
+  if (!X && g.rotate) {  // (rotated pools have power-of-two head dims)
     for (int hs = 1; hs < D; hs *= 2) {
       for (int i = tid; i < G * D / 2; i += 256) {
         const int j = i / (D / 2), pi = i % (D / 2);
@@ -483,10 +520,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     for (int i = tid; i < G * D; i += 256) s_q[i / D][i % D] *= a.unrot_c;
     lds_barrier();
   }
-  for (int i = tid; i < G * 2; i += 256) {
+  for (int i = tid; i < G * NGK; i += 256) {
     float sum = 0.0f;
-    for (int c = 0; c < 64; ++c) sum += s_q[i / 2][(i % 2) * 64 + c];
-    s_qsum[i / 2][i % 2] = sum;
+    for (int c = 0; c < 64; ++c) sum += s_q[i / NGK][(i % NGK) * 64 + c];
+    s_qsum[i / NGK][i % NGK] = sum;
   }
   lds_barrier();
 
@@ -524,10 +561,44 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
     }
   };
+  // K channels 128 .. 191 (X): A operand for extra k-step s of row lj = 4 hq + part (only rows whose
+  // (lj >> 1) & 1 is 0), lane group la supplying channels 128 + 16 la + ch(s, e) in the unpacking order of
+  // the chunk's width: 4- and 8-bit ch = 8 s + p + 4 k, 2-bit ch = 4 s + p + 8 k, FP16 ch = 8 s + 2 p + k.
+  u32x4 qax[X ? 2 : 1];
+  auto build_qax = [&](int kind) __attribute__((always_inline)) {
+    if constexpr (X) {
+      const int hq = lj >> 2, part = lj & 1;
+      const bool in_group = hq < G && ((lj >> 1) & 1) == 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          _Float16 x[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            int ch = 8 * s + p + 4 * k;
+            float f = (kind == kK4 && (p & 1)) ? 0.0625f : 1.0f;
+            if (MIX2 && kind == kK2) {
+              ch = 4 * s + p + 8 * k;
+              f = p == 0 ? 1.0f : p == 1 ? 0.25f : p == 2 ? 0.0625f : 0.015625f;
+            } else if (MIX2 && kind == kK16) {
+              ch = 8 * s + 2 * p + k;
+            }
+            const float v = in_group ? s_q[hq][128 + 16 * la + ch] * f : 0.0f;
+            const _Float16 hi = (_Float16)v;
+            x[k] = part ? (_Float16)(v - (float)hi) : hi;
+          }
+          qax[s][p] = pack_h2(x[0], x[1]);
+        }
+      }
+    }
+  };
   build_qa(kK4);
+  build_qax(kK4);
   int cur_kind = kK4;
   const bool head_ok = la < G;
   const float qs0 = head_ok ? s_qsum[la][0] : 0.0f, qs1 = head_ok ? s_qsum[la][1] : 0.0f;
+  const float qs2 = X && head_ok ? s_qsum[la][NGK - 1] : 0.0f;
 
   float m_run = kNegInf, l_run = 0.0f, zacc0 = 0.0f, zacc1 = 0.0f;
   floatx4 o[8];
@@ -536,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 
   uint8_t* sv = s_v[w];
   _Float16* sp = s_p[w];
-  u32x4* spar = s_par[w];
+  uint32_t* spar = s_par[w];
   // Set when a chunk of this wave had logit terms above kPreciseAbove: the wave's rows then go through the fp64
   // pass (precise_wave_pass) after the main loop (wave-uniform).
   bool wave_big = false;
@@ -568,19 +639,32 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(sv + lj * kVP16 + la * 64 + 16 * c) = r.v[c];
     }
     // ---------------------------------------------------------- parameter records of tokens 16c + lj
-    uint32_t kp[NC][2], vp[NC][2];
+    uint32_t kp[NC][NGK], vp[NC][2];
     if constexpr (!F16) {
-      spar[16 * la + lj] = r.prm;
+      if constexpr (X) {
+#pragma unroll
+        for (int e = 0; e < NP; ++e) spar[NP * (16 * la + lj) + e] = r.prm[e];
+      } else {
+        *reinterpret_cast<u32x4*>(spar + 4 * (16 * la + lj)) = u32x4{r.prm[0], r.prm[1], r.prm[2], r.prm[3]};
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 x = spar[16 * c + lj];
-        kp[c][0] = x[0];
-        kp[c][1] = x[1];
-        vp[c][0] = x[2];
-        vp[c][1] = x[3];
+        uint32_t x[NP];
+        if constexpr (X) {
+#pragma unroll
+          for (int e = 0; e < NP; ++e) x[e] = spar[NP * (16 * c + lj) + e];
+        } else {
+          const u32x4 y = *reinterpret_cast<const u32x4*>(spar + 4 * (16 * c + lj));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = y[e];
+        }
+#pragma unroll
+        for (int e = 0; e < NGK; ++e) kp[c][e] = x[e];
+        vp[c][0] = x[NGK];
+        vp[c][1] = x[NGK + 1];
       }
     }
     // ---------------------------------------------------------- logits: QK on the matrix cores
@@ -608,19 +692,50 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         }
         acc[c] = mfma16(qa[s], b, acc[c]);
       }
+    // K channels 128 .. 191: two more k-steps into their own tiles (rows 4 hq + part)
+    floatx4 accx[X ? NC : 1];
+    if constexpr (X) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) accx[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          u32x4 b;
+          if constexpr (KIND == kK4) {
+            const uint32_t wd = r.kx[2 * c + s], w8 = wd >> 8;
+            b = u32x4{wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
+          } else if constexpr (KIND == kK2) {
+            const uint32_t wd = r.kx[c] >> (8 * s);
+            b = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
+          } else if constexpr (W8) {
+            const uint32_t lo = r.kx[4 * c + 2 * s], hi = r.kx[4 * c + 2 * s + 1];
+            b = u32x4{__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
+                      __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
+          } else {
+            b = u32x4{r.kx[4 * s], r.kx[4 * s + 1], r.kx[4 * s + 2], r.kx[4 * s + 3]};
+          }
+          accx[c] = mfma16(qax[s], b, accx[c]);
+        }
+    }
     float sc[NC];
     bool big = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const bool live = head_ok && ((r.valid >> c) & 1u);
       if constexpr (F16) {
-        const float dk = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+        float dk = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+        if constexpr (X) dk += accx[c][0] + accx[c][1];
         sc[c] = live ? dk : kNegInf;
         big |= live && fabsf(dk) > kPreciseAbove;
       } else {
-        const float dot = h2f(kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
-                          h2f(kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
-        const float zq = h2f(kp[c][0] >> 16) * qs0 + h2f(kp[c][1] >> 16) * qs1;
+        float dot = h2f(kp[c][0] & 0xffffu) * (acc[c][0] + acc[c][1]) +
+                    h2f(kp[c][1] & 0xffffu) * (acc[c][2] + acc[c][3]);
+        float zq = h2f(kp[c][0] >> 16) * qs0 + h2f(kp[c][1] >> 16) * qs1;
+        if constexpr (X) {
+          dot += h2f(kp[c][NGK - 1] & 0xffffu) * (accx[c][0] + accx[c][1]);
+          zq += h2f(kp[c][NGK - 1] >> 16) * qs2;
+        }
         const float dk = dot * kTwo24;
         sc[c] = live ? dk + zq : kNegInf;
         big |= live && fabsf(dk) + fabsf(zq) > kPreciseAbove;
@@ -768,6 +883,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       const int kind = kind_of(c0 + w + 4 * i);
       if (kind != cur_kind) {
         build_qa(kind);
+        build_qax(kind);
         cur_kind = kind;
       }
       if (kind == kK8) {
@@ -830,7 +946,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     // this wave's rows again with fp64 logits; the pass writes the wave's merge slots itself
     auto qv = [&](int j, int c) __attribute__((always_inline)) -> double {
       return g.rotate ? (double)s_q[j][c]
-                      : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * D + c]) * a.q_scale64;
+                      : (double)h2f(a.q[((size_t)seq * a.num_q_heads + h * G + j) * DK + c]) * a.q_scale64;
     };
     if constexpr (GATHER) {
       auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
@@ -850,7 +966,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         row = (int)(e & 255u);
         return ok;
       };
-      precise_wave_pass<D, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
+      precise_wave_pass<DK, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
                                  &s_wacc[w][0][0]);
     } else {
       auto tok = [&](int p, int i, const uint8_t*& tile, int& row) __attribute__((always_inline)) -> bool {
@@ -858,7 +974,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         row = 64 * w + i;
         return (b0 + p) * kRows + row < len;
       };
-      precise_wave_pass<D, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
+      precise_wave_pass<DK, D, G>(g, nchunk, tok, qv, reinterpret_cast<float*>(sp), &s_wm[w][0], &s_wl[w][0],
                                  &s_wacc[w][0][0]);
     }
   } else {
@@ -925,34 +1041,47 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 
-template <int G>
+template <int G, int DK>
 hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.plan.wgs);
   if (g.mixed == 2) {
     hipLaunchKernelGGL(compact_rows_k<4>, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
-    hipLaunchKernelGGL((decode_rows_k<G, true, true>), grid, dim3(256), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, true, true, DK>), grid, dim3(256), 0, stream, g, a);
   } else if (a.mask || g.mixed) {
     hipLaunchKernelGGL(compact_rows_k<2>, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
-    hipLaunchKernelGGL((decode_rows_k<G, true, false>), grid, dim3(256), 0, stream, g, a);
+    hipLaunchKernelGGL((decode_rows_k<G, true, false, DK>), grid, dim3(256), 0, stream, g, a);
+  } else if constexpr (DK == 128) {
+    hipLaunchKernelGGL((decode_rows_k<G, false, false, DK>), grid, dim3(256), 0, stream, g, a);
   } else {
-    hipLaunchKernelGGL((decode_rows_k<G, false, false>), grid, dim3(256), 0, stream, g, a);
+    return hipErrorInvalidValue;  // (pure 4-bit MLA pools take the block kernel)
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Layouts with this kernel: head_dim 128, per-token K and V groups of 64, 4-bit pools and pools of per-token
-// widths, G = 1, 2, 4.
-bool decode_rows_supported(const TileGeom& g, int G) {
-  return g.d == 128 && g.dv == 128 && g.kg == 64 && g.vg == 64 && !g.fp8 && (G == 1 || G == 2 || G == 4);
+// Layouts with this kernel: per-token K and V groups of 64, 4-bit pools and pools of per-token widths, G = 1, 2,
+// 4; head dim 128, or (MLA pools) K 192 and V 128 without rotation, read through the row lists (pools with
+// sentinel slots or per-token widths; pure 4-bit MLA pools stream through the block kernel).
+bool decode_rows_supported(const TileGeom& g, int G, bool masked) {
+  if (g.kg != 64 || g.vg != 64 || g.fp8 || !(G == 1 || G == 2 || G == 4)) return false;
+  if (g.d == 128 && g.dv == 128) return true;
+  return g.d == 192 && g.dv == 128 && !g.rotate && (masked || g.mixed);
 }
 
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {
+  if (g.d == 192) {
+    switch (a.G) {
+      case 1: return launch_g<1, 192>(g, a, stream);
+      case 2: return launch_g<2, 192>(g, a, stream);
+      case 4: return launch_g<4, 192>(g, a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.G) {
-    case 1: return launch_g<1>(g, a, stream);
-    case 2: return launch_g<2>(g, a, stream);
-    case 4: return launch_g<4>(g, a, stream);
+    case 1: return launch_g<1, 128>(g, a, stream);
+    case 2: return launch_g<2, 128>(g, a, stream);
+    case 4: return launch_g<4, 128>(g, a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -177,7 +177,7 @@ struct DecodeArgs {
 // "generic" or "mfma" to skip the kernels before it, or "nocascade" to keep shared blocks in the
 // per-sequence kernel.
 hipError_t launch_decode(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
-bool decode_rows_supported(const TileGeom& g, int G);
+bool decode_rows_supported(const TileGeom& g, int G, bool masked);  // masked: the call has a sentinel mask
 bool decode_kchan_supported(const TileGeom& g, int G);
 hipError_t launch_decode_kchan(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream);

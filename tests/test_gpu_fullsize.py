@@ -84,11 +84,12 @@ def build_both(kvq, torch, orc, case, layer):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", W.CONFIG_ORDER + ["llama31_8b_pool_8k_fp8", "llama31_8b_pool_8k_widths",
                                                    "mixed_sentinel_32k_widths", "deepseek_v2_lite_mla_8k",
-                                                   "deepseek_v2_lite_mla_8k_sentinel"])
+                                                   "deepseek_v2_lite_mla_8k_sentinel",
+                                                   "deepseek_v2_lite_mla_8k_widths"])
 def test_full_size_every_sequence(env, orc, name):
     # (the last cases: the 12 x 8K pool stored as FP8 E4M3, the baseline the 4-bit pool is measured against,
     # two workloads stored with per-token widths {2, 4, 8, FP16}, and an MLA model's pool: K head dim 192,
-    # V head dim 128, also with half of its cached slots remapped to the sentinel)
+    # V head dim 128, also with half of its cached slots remapped to the sentinel and with per-token widths)
     kvq, torch = env
     base = name
     while base not in FULL:  # strip the variant suffixes (_fp8, _widths, _sentinel)

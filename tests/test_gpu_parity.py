@@ -154,7 +154,10 @@ SENTINEL_LAYOUTS = {
     "d128_g2_fp16": (128, 0, 2, 64, 64, 0, 2, 0, 16),    # row-list kernel, FP16 chunks
     "d128_g8": (128, 0, 8, 64, 64, 0, 0, 0, None),       # block matrix-core kernel
     "d256_g2": (256, 0, 2, 64, 64, 0, 0, 0, None),       # block matrix-core kernel, head dim 256
-    "mla_g1": (192, 128, 1, 64, 64, 0, 0, 0, None),      # block matrix-core kernel, K 192 / V 128
+    "mla_g1": (192, 128, 1, 64, 64, 0, 0, 0, None),      # row-list kernel, K 192 / V 128; forced block, generic
+    "mla_g2_8bit": (192, 128, 2, 64, 64, 0, 1, 0, 8),    # row-list kernel, K 192, 8-bit chunks
+    "mla_g1_2bit": (192, 128, 1, 64, 64, 0, 2, 0, 2),    # row-list kernel, K 192, 2-bit chunks
+    "mla_g4_fp16": (192, 128, 4, 64, 64, 0, 2, 0, 16),   # row-list kernel, K 192, FP16 chunks
     "kchan_g5": (128, 0, 5, -1, 32, 0, 0, 0, None),      # per-channel-K kernel
     "kchan_g5_rot": (128, 0, 5, -1, 32, 1, 0, 0, None),  # per-channel-K kernel, rotated pool
     "fp8_g4": (128, 0, 4, 0, 0, 0, 0, 1, None),          # FP8 pool with a sentinel mask: generic kernel
@@ -646,7 +649,8 @@ def test_row_lists_of_a_sequence_past_256k_slots(env, orc, mixed):
 
 MLA_VARIANTS = [  # K head dim, rotate, mixed, k_group, v_group, G (V head dim 128)
     (192, 0, 0, 64, 64, 1), (192, 0, 0, 64, 64, 2), (192, 0, 0, 64, 64, 4), (192, 0, 2, 64, 32, 2),
-    (256, 1, 0, 64, 32, 4), (256, 1, 1, 32, 64, 1), (192, 0, 1, 32, 128, 16), (192, 0, 0, 8, 16, 3)]
+    (256, 1, 0, 64, 32, 4), (256, 1, 1, 32, 64, 1), (192, 0, 1, 32, 128, 16), (192, 0, 0, 8, 16, 3),
+    (192, 0, 2, 64, 64, 1), (192, 0, 1, 64, 64, 4), (192, 0, 2, 64, 64, 2)]
 
 
 @pytest.mark.parametrize("variant", MLA_VARIANTS)
