@@ -436,7 +436,7 @@ WIDTHS_POOL = "llama31_8b_pool_8k_widths"
 # 12 agents x 8K of an MLA model: K head dim 192, V 128 ("Agent Memory Below the Prompt", 2.2).
 MLA_POOL = "deepseek_v2_lite_mla_8k"
 # The MLA pool with half of the cached slots remapped to the sentinel (IntentKV), and with per-token widths
-# {2, 4, 8, FP16} (QKVShare, methodology section; this one decodes on the generic kernel).
+# {2, 4, 8, FP16} (QKVShare, methodology section); both read through the row lists.
 MLA_VARIANTS = ["deepseek_v2_lite_mla_8k_sentinel", "deepseek_v2_lite_mla_8k_widths"]
 
 
