@@ -1050,10 +1050,8 @@ hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
   } else if (a.mask || g.mixed) {
     hipLaunchKernelGGL(compact_rows_k<2>, dim3(a.n_seqs), dim3(kCompactThreads), 0, stream, g, a);
     hipLaunchKernelGGL((decode_rows_k<G, true, false, DK>), grid, dim3(256), 0, stream, g, a);
-  } else if constexpr (DK == 128) {
-    hipLaunchKernelGGL((decode_rows_k<G, false, false, DK>), grid, dim3(256), 0, stream, g, a);
   } else {
-    return hipErrorInvalidValue;  // (pure 4-bit MLA pools take the block kernel)
+    hipLaunchKernelGGL((decode_rows_k<G, false, false, DK>), grid, dim3(256), 0, stream, g, a);
   }
   return hipGetLastError();
 }
@@ -1061,12 +1059,13 @@ hipError_t launch_g(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) 
 }  // namespace
 
 // Layouts with this kernel: per-token K and V groups of 64, 4-bit pools and pools of per-token widths, G = 1, 2,
-// 4; head dim 128, or (MLA pools) K 192 and V 128 without rotation, read through the row lists (pools with
-// sentinel slots or per-token widths; pure 4-bit MLA pools stream through the block kernel).
+// 4; head dim 128, or (MLA pools) K 192 and V 128 without rotation. (`masked`, whether the call has a sentinel
+// mask, does not restrict it.)
 bool decode_rows_supported(const TileGeom& g, int G, bool masked) {
+  (void)masked;
   if (g.kg != 64 || g.vg != 64 || g.fp8 || !(G == 1 || G == 2 || G == 4)) return false;
   if (g.d == 128 && g.dv == 128) return true;
-  return g.d == 192 && g.dv == 128 && !g.rotate && (masked || g.mixed);
+  return g.d == 192 && g.dv == 128 && !g.rotate;
 }
 
 hipError_t launch_decode_rows(const TileGeom& g, const DecodeArgs& a, hipStream_t stream) {

@@ -653,18 +653,24 @@ MLA_VARIANTS = [  # K head dim, rotate, mixed, k_group, v_group, G (V head dim 1
     (192, 0, 2, 64, 64, 1), (192, 0, 1, 64, 64, 4), (192, 0, 2, 64, 64, 2)]
 
 
-@pytest.mark.parametrize("variant", MLA_VARIANTS)
+# The same without sentinel slots (pure 4-bit MLA pools stream through the row-list kernel)
+MLA_STREAMING = [(192, 0, 0, 64, 64, 1, 0.0), (192, 0, 0, 64, 64, 2, 0.0), (192, 0, 0, 64, 64, 4, 0.0)]
+
+
+@pytest.mark.parametrize("variant", [v + (0.5,) for v in MLA_VARIANTS] + MLA_STREAMING)
 def test_unequal_head_dims(env, orc, variant, decode_path):
     # MLA layouts (K and V head dims differ): pool bytes (quantise and append) bit-exact, decode within
-    # tolerance over ragged lengths with sentinel slots (one sequence all sentinel), restore within one ulp.
+    # tolerance over ragged lengths, with sentinel slots (one sequence all sentinel) or without, restore
+    # within one ulp.
     kvq, torch = env
-    d, rotate, mixed, kg, vg, G = variant
+    d, rotate, mixed, kg, vg, G, dead = variant
     H = 2
     cfg = W.Config(9, "mla", d, H * G, H, 1, kg, vg, rotate, mixed, 6, 0, "perm", True, 3, 10.0, 1.0,
-                   dead_fraction=0.5, top_fraction=0.2 if mixed == 1 else 0.0,
+                   dead_fraction=dead, top_fraction=0.2 if mixed == 1 else 0.0,
                    width_fracs=(0.1, 0.2, 0.3) if mixed == 2 else (0.0, 0.0, 0.0), v_head_dim=128)
-    case = W.make_case(cfg, context=[0, 1, 255, 256, 700, 1500])
-    case.sentinel_mask[4] = 0xFFFFFFFF
+    case = W.make_case(cfg, context=[0, 1, 255, 256, 700, 1500] if dead else [0, 1, 255, 256, 700, 2900])
+    if dead:
+        case.sentinel_mask[4] = 0xFFFFFFFF
     inp = host_inputs(case)
     ref_pool, ref = oracle_run(orc, case, inp)
     got_pool, got = gpu_run(kvq, torch, case, inp)
@@ -672,10 +678,11 @@ def test_unequal_head_dims(env, orc, variant, decode_path):
     assert diff.size == 0, "first differing bytes at %s" % diff[:16]
     assert got.shape == (6, H * G, 128)
     err = rel_err(got, ref)
-    print("mla d=%d rotate=%d mixed=%d kg=%d vg=%d G=%d [%s]: max rel err %.3g" % (d, rotate, mixed, kg, vg, G,
-                                                                              decode_path, err))
+    print("mla d=%d rotate=%d mixed=%d kg=%d vg=%d G=%d dead=%.1f [%s]: max rel err %.3g" % (
+        d, rotate, mixed, kg, vg, G, dead, decode_path, err))
     assert err <= TOL
-    assert not got[4].any()                                  # every slot remapped to the sentinel
+    if dead:
+        assert not got[4].any()                              # every slot remapped to the sentinel
     ids = np.unique(case.prefill_blocks).astype(np.int32)
     kr, vr = orc.dequantize_blocks(orc.make_layout(**cfg.layout()), ref_pool, ids)
     kg_, vg_ = kvq.dequantize_blocks(kvq.Layout(**cfg.layout()), to_dev(got_pool, torch), to_dev(ids, torch))
