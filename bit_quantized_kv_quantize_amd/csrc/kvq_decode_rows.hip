@@ -215,14 +215,14 @@ __global__ __launch_bounds__(kCompactThreads) void compact_rows_k(TileGeom g, De
 // 32 bytes each (k[2c], k[2c + 1]). 2-bit chunks: tokens 16c + lj (c = 0..3), 8 bytes each (k[c].x, .y).
 // FP16 chunks: token lj, 64 bytes each (k[0..3]).
 // X: a K head dim of 192 (MLA pools), whose channels 128 .. 191 (K group 2) come as `kx`: 4-bit chunks 8 bytes
-// per token (kx[2c], kx[2c + 1]), 8-bit chunks 16 bytes (kx[4c .. 4c + 3]), 2-bit chunks 4 bytes (kx[c]), FP16
-// chunks 32 bytes (kx[0 .. 7]): channels 128 + 16 la .. 128 + 16 la + 15.
+// per token (words 2c, 2c + 1 of kx), 8-bit chunks 16 bytes (kx[c]), 2-bit chunks 4 bytes (word c of kx[0]),
+// FP16 chunks 32 bytes (kx[0], kx[1]): channels 128 + 16 la .. 128 + 16 la + 15.
 template <bool X>
 struct RawT {
   u32x4 k[4];
   u32x4 v[4];
   uint32_t prm[X ? 5 : 4];  // the parameter record of token 16 la + lj (K groups {scale, zero}, then V groups)
-  uint32_t kx[X ? 8 : 1];
+  u32x4 kx[X ? 2 : 1];      // (vectors: whole-register values the compiler keeps out of scratch)
   uint32_t valid;           // bit c: token 16c + lj of the chunk exists
 };
 
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         r.v[c] = *reinterpret_cast<const u32x4*>(rp + DK / 2 + la * 16);  // V codes follow the 4-bit K codes
         if constexpr (X) {
           const uint2 xx = *reinterpret_cast<const uint2*>(rp + 64 + la * 8);
-          r.kx[2 * c] = xx.x;
-          r.kx[2 * c + 1] = xx.y;
+          r.kx[c >> 1][2 * (c & 1)] = xx.x;
+          r.kx[c >> 1][2 * (c & 1) + 1] = xx.y;
         }
       }
     } else if (MIX2 && kind == kK2) {
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         const uint2 vv = *reinterpret_cast<const uint2*>(rp + DK / 4 + la * 8);  // V codes follow the 2-bit K codes
         r.k[c] = u32x4{kk.x, kk.y, 0u, 0u};
         r.v[c] = u32x4{vv.x, vv.y, 0u, 0u};
-        if constexpr (X) r.kx[c] = *reinterpret_cast<const uint32_t*>(rp + 32 + la * 4);
+        if constexpr (X) r.kx[0][c] = *reinterpret_cast<const uint32_t*>(rp + 32 + la * 4);
       }
     } else if (MIX2 && kind == kK16) {
       const uint8_t* rp = tile[0] + row[0] * R;
@@ -438,11 +438,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
       if constexpr (X) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4 xx = *reinterpret_cast<const u32x4*>(rp + 256 + la * 32 + 16 * c);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r.kx[4 * c + e] = xx[e];
-        }
+        for (int c = 0; c < 2; ++c) r.kx[c] = *reinterpret_cast<const u32x4*>(rp + 256 + la * 32 + 16 * c);
       }
     } else {
 #pragma unroll
@@ -452,11 +448,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         r.k[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + la * 32 + 16);
         r.v[2 * c] = *reinterpret_cast<const u32x4*>(rp + DK + la * 32);  // V codes follow the 8-bit K codes
         r.v[2 * c + 1] = *reinterpret_cast<const u32x4*>(rp + DK + la * 32 + 16);
-        if constexpr (X) {
-          const u32x4 xx = *reinterpret_cast<const u32x4*>(rp + 128 + la * 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r.kx[4 * c + e] = xx[e];
-        }
+        if constexpr (X) r.kx[c] = *reinterpret_cast<const u32x4*>(rp + 128 + la * 16);
       }
     }
     // One parameter record per lane: the record of token 16 la + lj (lane (c, lj) holds the record every
@@ -564,7 +556,11 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   // K channels 128 .. 191 (X): A operand for extra k-step s of row lj = 4 hq + part (only rows whose
   // (lj >> 1) & 1 is 0), lane group la supplying channels 128 + 16 la + ch(s, e) in the unpacking order of
   // the chunk's width: 4- and 8-bit ch = 8 s + p + 4 k, 2-bit ch = 4 s + p + 8 k, FP16 ch = 8 s + 2 p + k.
-  u32x4 qax[X ? 2 : 1];
+  // (in pools of four widths the operand is kept in LDS, one slot per wave and lane: their K 192 instances are
+  // short of registers; the others keep it in registers)
+  constexpr bool kQaxLds = X && MIX2;
+  u32x4 qax[X && !kQaxLds ? 2 : 1];
+  __shared__ __attribute__((aligned(16))) u32x4 s_qax[kQaxLds ? 4 : 1][2][64];
   auto build_qax = [&](int kind) __attribute__((always_inline)) {
     if constexpr (X) {
       const int hq = lj >> 2, part = lj & 1;
@@ -588,7 +584,8 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
             const _Float16 hi = (_Float16)v;
             x[k] = part ? (_Float16)(v - (float)hi) : hi;
           }
-          qax[s][p] = pack_h2(x[0], x[1]);
+          if constexpr (kQaxLds) s_qax[w][s][l][p] = pack_h2(x[0], x[1]);
+          else qax[s][p] = pack_h2(x[0], x[1]);
         }
       }
     }
@@ -695,6 +692,11 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     // K channels 128 .. 191: two more k-steps into their own tiles (rows 4 hq + part)
     floatx4 accx[X ? NC : 1];
     if constexpr (X) {
+      u32x4 qx[2];
+      if constexpr (kQaxLds) {
+        qx[0] = s_qax[w][0][l];
+        qx[1] = s_qax[w][1][l];
+      }
 #pragma unroll
       for (int c = 0; c < NC; ++c) accx[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -703,19 +705,19 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         for (int c = 0; c < NC; ++c) {
           u32x4 b;
           if constexpr (KIND == kK4) {
-            const uint32_t wd = r.kx[2 * c + s], w8 = wd >> 8;
+            const uint32_t wd = r.kx[c >> 1][2 * (c & 1) + s], w8 = wd >> 8;
             b = u32x4{wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
           } else if constexpr (KIND == kK2) {
-            const uint32_t wd = r.kx[c] >> (8 * s);
+            const uint32_t wd = r.kx[0][c] >> (8 * s);
             b = u32x4{wd & 0x00030003u, wd & 0x000C000Cu, wd & 0x00300030u, wd & 0x00C000C0u};
           } else if constexpr (W8) {
-            const uint32_t lo = r.kx[4 * c + 2 * s], hi = r.kx[4 * c + 2 * s + 1];
+            const uint32_t lo = r.kx[c][2 * s], hi = r.kx[c][2 * s + 1];
             b = u32x4{__builtin_amdgcn_perm(hi, lo, pair_sel(0)), __builtin_amdgcn_perm(hi, lo, pair_sel(1)),
                       __builtin_amdgcn_perm(hi, lo, pair_sel(2)), __builtin_amdgcn_perm(hi, lo, pair_sel(3))};
           } else {
-            b = u32x4{r.kx[4 * s], r.kx[4 * s + 1], r.kx[4 * s + 2], r.kx[4 * s + 3]};
+            b = r.kx[s];
           }
-          accx[c] = mfma16(qax[s], b, accx[c]);
+          accx[c] = mfma16(kQaxLds ? qx[s] : qax[s], b, accx[c]);
         }
     }
     float sc[NC];
