@@ -65,21 +65,6 @@ struct Raw {
 // Channel order of the staged V rows inside each group of 8: the pairs (c, c + 4) that one and-or extracts.
 __device__ __forceinline__ constexpr int nib(int e) { return (e >> 1) + 4 * (e & 1); }
 
-// Sum and maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row) with the gfx950 row and
-// half-wave swaps; every lane ends with the same value.
-__device__ __forceinline__ float rows4_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Exclusive prefix sums of x[0 .. n) in place (n <= 2 * blockDim.x = 512) and their total, by all 256 threads;
 // s_w: four ints of scratch.
 __device__ int block_scan(int* x, int n, int tid, int* s_w) {

@@ -52,6 +52,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Sum and maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row) with the gfx950 row and
+// half-wave swaps; every lane ends with the same value.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Wave-uniform power-of-two scale for the fp16 p * v_scale operands of one chunk, from the chunk's largest
 // V scale vmax (this lane's value; reduced over the wave here): with p <= 1 every p * v_scale * scale is
 // below 2^15, and the weights that matter stay far above the fp16 subnormal range instead of flushing to
@@ -62,8 +77,7 @@ __device__ __forceinline__ float chunk_pv_scale(float vmax, float& inv) {
   vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x124, 0xf, 0xf, false)));
   vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x122, 0xf, 0xf, false)));
   vmax = fmaxf(vmax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(vmax), 0x121, 0xf, 0xf, false)));
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+  vmax = rows4_max(vmax);  // across the four rows: lane swaps, no LDS round trip
   const int ex = vmax > 0.0f ? ((__float_as_int(vmax) >> 23) & 0xff) - 126 : 0;  // vmax < 2^ex
   inv = __builtin_amdgcn_ldexpf(1.0f, ex - 15);
   return __builtin_amdgcn_ldexpf(1.0f, 15 - ex);

@@ -36,6 +36,11 @@ namespace {
 using namespace dec;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
+// Buffer resources for raw (untyped) loads on gfx950: the descriptor's fourth word with a 32-bit data format
+// (a zero format would make every load return zeros), and the cache-policy operand of a non-temporal load.
+// A raw load at an offset at or past the resource's size returns zeros without a memory access.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNT = 2;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -390,7 +395,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     }
   };
   // Issue the code and parameter loads of chunk i (rows from en) into r.
-  auto load = [&](Raw& r, const Ent& en, int i) __attribute__((always_inline)) {
+  // live: false for a streaming chunk past the split's end, whose loads the loop still issues so that it
+  // has no exit between chunks; those loads go through an empty buffer range and read nothing.
+  auto load = [&](Raw& r, const Ent& en, int i, bool live = true) __attribute__((always_inline)) {
     const uint8_t* tile[4];
     uint32_t row[4];
     int kind = kK4;
@@ -413,7 +420,16 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
     }
     r.valid = en.valid;
+    // Streaming 4-bit chunks at K 128 read through a buffer resource over the tile (wave-uniform: four
+    // scalar registers). A chunk past the split's end gets a resource of zero bytes, so its loads return
+    // zeros at once and fetch nothing, instead of re-reading the last chunk and holding the workgroup's
+    // merge until they return.
+    auto slab_rsrc = [&]() __attribute__((always_inline)) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tile[0]), (short)0,
+                                               live ? (int)g.tile_bytes : 0, kBufWord3);
+    };
     if constexpr (kSlab) {
+      const __amdgpu_buffer_rsrc_t rs = slab_rsrc();
       // The wave's 64 records (8 KB) as eight 1 KB slabs in address order: lane l takes the 16-byte piece
       // l % 8 of row 8 j + l / 8 of slab j, so every 8 consecutive lanes read one whole record. Slab 2c
       // holds rows 16c .. 16c+7 (in r.k[c]) and slab 2c + 1 rows 16c+8 .. 16c+15 (in r.v[c]); the chunk's
@@ -423,8 +439,8 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int rw = 8 * j + 2 * la + (lj >> 3);  // lane l = 16 la + lj: row 8 j + l / 8, piece l % 8
-        const uint8_t* rp = tile[0] + (rw < en.lim ? (uint32_t)(64 * w + rw) : 0u) * R + (lj & 7) * 16;
-        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp));
+        const uint32_t off = (rw < en.lim ? (uint32_t)(64 * w + rw) : 0u) * R + (lj & 7) * 16;
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNT);
         if (j & 1) r.v[j >> 1] = x;
         else r.k[j >> 1] = x;
       }
@@ -488,6 +504,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         const uint32_t* pr = reinterpret_cast<const uint32_t*>(tp + (g.off_prow + rp * (4 * NP)));
 #pragma unroll
         for (int e = 0; e < NP; ++e) r.prm[e] = pr[e];
+      } else if constexpr (kSlab) {
+        const u32x4 pr = __builtin_amdgcn_raw_buffer_load_b128(slab_rsrc(), g.off_prow + rp * 16, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r.prm[e] = pr[e];
       } else {
         const u32x4 pr = *reinterpret_cast<const u32x4*>(tp + (g.off_prow + rp * 16));
 #pragma unroll
@@ -505,7 +525,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     load(ra, en, 0);
     fetch(en, min(1, nchunk - 1));
     if (!GATHER) {
-      load(rb, en, min(1, nchunk - 1));
+      load(rb, en, min(1, nchunk - 1), nchunk > 1);
       fetch(en, min(2, nchunk - 1));
     }
   }
@@ -788,10 +808,10 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     const float mnew = fmaxf(m_run, mx);
     const float alpha = mnew == m_run ? 1.0f : __builtin_amdgcn_exp2f(m_run - mnew);
     float p[NC], ps = 0.0f;
+    const float mref = mnew == kNegInf ? 0.0f : mnew;  // no live logit yet: every p is exp2(-inf) = 0
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      p[c] = __builtin_amdgcn_exp2f(sc[c] - mnew);  // -inf - finite -> 0
-      p[c] = mnew == kNegInf ? 0.0f : p[c];
+      p[c] = __builtin_amdgcn_exp2f(sc[c] - mref);  // -inf - finite -> 0
       ps += p[c];
     }
     l_run = l_run * alpha + ps;
@@ -878,9 +898,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         const v2i x = lds_tr4(kSlab ? sv + tok * kRP + 64 + 8 * t : sv + tok * kVP + 8 * t);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          // high nibbles (odd tokens) complemented: 15 - code
-          const uint32_t wd = (uint32_t)(kb ? x.y : x.x) ^ 0xF0F0F0F0u, w8 = wd >> 8;
-          const u32x4 b = {wd & kLo4, wd & kHi4, w8 & kLo4, w8 & kHi4};
+          // high nibbles (odd tokens) complemented: 15 - code, i.e. the inverted bits under the mask
+          const uint32_t wd = (uint32_t)(kb ? x.y : x.x), w8 = wd >> 8;
+          const u32x4 b = {wd & kLo4, ~wd & kHi4, w8 & kLo4, ~w8 & kHi4};
           ob[t] = mfma16(pa[kb], b, ob[t]);
         }
       }
@@ -951,7 +971,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
     // on which it places over-strict waits); the last one or two chunks follow it.
     auto issue = [&](Raw& r, int j) __attribute__((always_inline)) {
       fetch(en, min(j, nchunk - 1));
-      load(r, en, min(j, nchunk - 1));
+      load(r, en, min(j, nchunk - 1), j < nchunk);
       __builtin_amdgcn_sched_barrier(0);
     };
     int i = 0;
@@ -1031,7 +1051,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       }
     }
   }
-  __syncthreads();
+  // The waves' partials are exchanged through LDS only: a full barrier would also wait for loads still in
+  // flight (the precise pass's, or a gather loop's last prefetch).
+  lds_barrier();
   if (ns == 1) {
     __shared__ int s_cnt[4];
     __shared__ float s_o[D];
@@ -1075,7 +1097,7 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
       s_pl[jj] = L;
     }
   }
-  __syncthreads();
+  lds_barrier();
   splitk_arrive<D, G>(g, a, seq, h, split, ns, len, tid, s_pm, s_pl, &s_pacc[0][0], &s_wacc[0][0][0]);
 }
 

@@ -3,8 +3,9 @@
 //
 // kvq_probe_read_tiles reads the bytes the 4-bit streaming decode reads from a pool - for every (sequence, KV
 // head) pair, every live block's tile, each row's 128 code bytes and 16 parameter bytes (rows past a sequence's
-// end re-read row 0, as the decode does) - with the same work split (512 workgroups of 4 waves, each wave 64
-// rows of every block of its range) and 16-byte loads, and does no arithmetic beyond folding the loaded words
+// end re-read row 0 of the wave's rows, as the decode does) - with the same work split (512 workgroups of 4
+// waves, each wave 64 rows of every block of its range) and the same loads (whole records in address order
+// with non-temporal 16-byte buffer loads, one parameter record per lane), and does no arithmetic beyond folding the loaded words
 // into one value per workgroup (written out so nothing is optimised away). Its time is the floor of a kernel with that decode's
 // load pattern. kvq_probe_read_linear streams a flat buffer with 16-byte loads from 2048 workgroups: the
 // chip's plain read bandwidth. kvq_probe_stream_rw reads one flat buffer and writes a smaller one at a given
@@ -15,11 +16,15 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// raw buffer resources on gfx950: the descriptor's fourth word (32-bit data format) and the cache-policy
+// operand of a non-temporal load
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNT = 2;
 
 // grid (wgs), 256 threads. The work split of the decode's one-dimensional plan: with P pairs and W workgroups,
 // k = W / P, the first nA = P - (W - k P) pairs take k even pieces of their blocks and the others k + 1; the
 // first half of the grid takes pieces in order and the second half in reverse. Each wave reads its 64 rows of
-// four blocks at a time (twelve 16-byte loads per lane in flight), then folds them.
+// four blocks at a time (36 16-byte loads per lane in flight), then folds them.
 __global__ __launch_bounds__(256) void read_tiles_k(const uint8_t* pool, const int32_t* table, const int32_t* lens,
                                                     int n_seqs, int H, int max_blocks, uint32_t tile_bytes,
                                                     uint32_t rec, uint32_t off_prow, uint32_t prow, int wgs,
@@ -47,25 +52,35 @@ __global__ __launch_bounds__(256) void read_tiles_k(const uint8_t* pool, const i
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, la = l >> 4, lj = l & 15;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (int b = b0; b < b1; b += 4) {
-    u32x4 x[4][4][3];
+    u32x4 x[4][9];
+    int phys[4];  // the four blocks' table entries first (the decode stages its table slice before its loads)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) phys[i] = table[(size_t)seq * max_blocks + min(b + i, b1 - 1)];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int bb = min(b + i, b1 - 1);
-      const uint8_t* tile = pool + ((size_t)table[(size_t)seq * max_blocks + bb] * H + h) * tile_bytes;
+      const uint8_t* tile = pool + ((size_t)phys[i] * H + h) * tile_bytes;
+      // a block past the range's end reads nothing (a zero-byte buffer resource), as in the decode
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(tile), (short)0, b + i < b1 ? (int)tile_bytes : 0, kBufWord3);
+      const int lim = len - (bb * 256 + 64 * w);  // rows of the wave's 64 below the sequence's end
+      // the wave's 64 records as eight 1 KB slabs in address order, lane l reading piece l % 8 of row
+      // 8 j + l / 8 of slab j (non-temporal), then one parameter record per lane (token 16 la + lj)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int row = 64 * w + 16 * c + lj;
-        const bool on = b + i < b1 && bb * 256 + row < len;
-        const uint8_t* rp = tile + (uint32_t)(on ? row : 0) * rec + la * 16;
-        x[i][c][0] = *reinterpret_cast<const u32x4*>(rp);
-        x[i][c][1] = *reinterpret_cast<const u32x4*>(rp + 64);
-        x[i][c][2] = *reinterpret_cast<const u32x4*>(tile + off_prow + (uint32_t)(on ? row : 0) * prow);
+      for (int j = 0; j < 8; ++j) {
+        const int rw = 8 * j + 2 * la + (lj >> 3);
+        const uint32_t off = (rw < lim ? (uint32_t)(64 * w + rw) : 0u) * rec + (lj & 7) * 16;
+        x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNT);
       }
+      const int pr = 16 * la + lj;
+      x[i][8] = __builtin_amdgcn_raw_buffer_load_b128(rs, off_prow + (uint32_t)(pr < lim ? 64 * w + pr : 0) * prow,
+                                                      0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the four blocks is issued before the first fold
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc ^= x[i][c][0] ^ x[i][c][1] ^ (la == 0 ? x[i][c][2] : u32x4{0u, 0u, 0u, 0u});
+      for (int j = 0; j < 9; ++j) acc ^= x[i][j];
   }
   const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (v == 0x9E3779B9u) sink[blockIdx.x] = v;  // practically never true; keeps the loads live
