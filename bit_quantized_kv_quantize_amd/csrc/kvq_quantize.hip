@@ -279,17 +279,22 @@ __global__ __launch_bounds__(256) void quantize_rows_k(TileGeom g, uint8_t* __re
   }
 }
 
-// K grouped per channel over the block's 256 rows (always 4-bit). Two passes over the rows: the first
-// finds every column's min/max of the (rotated) values, the second recomputes the identical rotated
-// values and encodes them against the column's parameters. A thread's rows (one lane of kRows / RPP rows)
-// stay in registers as the raw fp16 words between the passes, all loaded at once.
+// K grouped per channel over the block's 256 rows (always 4-bit), kKchanThreads threads per tile. Two passes
+// over the rows: the first finds every column's min/max of the (rotated) values, the second encodes the same
+// values against the column's parameters. A thread's rows (one lane of kRows / RPP rows) are all loaded at
+// once. Where they fit (8 rows of 8 values: head dims up to 128) the rotated fp32 values stay in registers
+// between the passes, so each row is converted and rotated once; otherwise the raw fp16 words stay and the
+// second pass converts and rotates them again (the identical operations, so the identical values).
+constexpr int kKchanThreads = 512;
 template <int LPR>
-__global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __restrict__ pool,
-                                                        const int32_t* __restrict__ block_ids,
-                                                        const uint16_t* __restrict__ k, float rot_c) {
+__global__ __launch_bounds__(kKchanThreads) void quantize_kchan_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                                  const int32_t* __restrict__ block_ids,
+                                                                  const uint16_t* __restrict__ k, float rot_c) {
   constexpr int D = LPR * 8;
-  constexpr int RPP = 256 / LPR;     // rows per pass of the workgroup
-  constexpr int NR = kRows / RPP;    // rows of one thread
+  constexpr int RPP = kKchanThreads / LPR;  // rows per pass of the workgroup
+  constexpr int NR = kRows / RPP;           // rows of one thread
+  constexpr bool kHold = NR <= 8;           // rotated values held between the passes
+  static_assert(RPP * LPR == kKchanThreads && NR * RPP == kRows, "a row's lanes divide the workgroup");
   __shared__ float s_min[RPP][D];
   __shared__ float s_max[RPP][D];
   __shared__ float s_z[D], s_r[D];
@@ -311,6 +316,7 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
     }
     if (g.rotate) rotate_row<LPR>(x, li, rot_c);
   };
+  float held[kHold ? NR : 1][8];
   float cmin[8], cmax[8];
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
@@ -320,8 +326,9 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
     for (int e = 0; e < 8; ++e) {
       cmin[e] = j == 0 ? x[e] : fminf(cmin[e], x[e]);
       cmax[e] = j == 0 ? x[e] : fmaxf(cmax[e], x[e]);
+      if constexpr (kHold) held[j][e] = x[e];
     }
-    __builtin_amdgcn_sched_barrier(0);  // one row's values live at a time
+    if constexpr (!kHold) __builtin_amdgcn_sched_barrier(0);  // one row's values live at a time
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -346,10 +353,13 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
     s_r[c] = s == 0.0f ? 0.0f : 1.0f / s;
   }
   __syncthreads();
-  // The second pass converts and rotates the raw words again; hiding their values from the compiler keeps it
-  // from holding the first pass's converted rows live across the reduction instead (NR x 8 more registers).
+  if constexpr (!kHold) {
+    // The second pass converts and rotates the raw words again; hiding their values from the compiler keeps
+    // it from holding the first pass's converted rows live across the reduction instead (NR x 8 more
+    // registers).
 #pragma unroll
-  for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y), "+v"(raw[j].z), "+v"(raw[j].w));
+    for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y), "+v"(raw[j].z), "+v"(raw[j].w));
+  }
   float zc[8], rc[8];
   bool zs[8];
 #pragma unroll
@@ -361,7 +371,12 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
     float x[8];
-    row(j, x);
+    if constexpr (kHold) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = held[j][e];
+    } else {
+      row(j, x);
+    }
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -376,7 +391,7 @@ __global__ __launch_bounds__(256) void quantize_kchan_k(TileGeom g, uint8_t* __r
       w |= code << (4 * e);
     }
     reinterpret_cast<uint32_t*>(tile + g.kcode(r0 + j * RPP))[li] = w;
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!kHold) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -641,8 +656,12 @@ hipError_t launch_quantize_t(const TileGeom& g, uint8_t* pool, const int32_t* bl
                              const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits, float rot_c,
                              int kv_base, int n_tensors, hipStream_t stream) {
   if (kv_base == 0 && !(g.kg > 0 || g.fp8)) {  // per-channel K first, then the V rows
-    hipLaunchKernelGGL(quantize_kchan_k<LPR>, dim3(n_blocks, g.H, 1), dim3(256), 0, stream, g, pool,
-                       block_ids, k, rot_c);
+    // (head dims whose lanes divide the workgroup: the layout check admits per-channel K at 64, 128, 256)
+    if constexpr (kKchanThreads % LPR == 0)
+      hipLaunchKernelGGL(quantize_kchan_k<LPR>, dim3(n_blocks, g.H, 1), dim3(kKchanThreads), 0, stream, g, pool,
+                         block_ids, k, rot_c);
+    else
+      return hipErrorInvalidValue;
     kv_base = 1;
     n_tensors -= 1;
   }
