@@ -95,17 +95,21 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_k(TileGeom g, DecodeArgs a)
   for (int i = tid; i < nchunk; i += 256) s_tbl[i] = a.block_table[(size_t)seq * a.max_blocks_per_seq + b0 + i];
   __syncthreads();
 
-  auto load = [&](RawF& r, int i) __attribute__((always_inline)) {
+  // on: false for a chunk past the split's end, whose loads the loop still issues (it has no exit between
+  // chunks): they go through a zero-byte buffer resource, return zeros at once and fetch nothing.
+  auto load = [&](RawF& r, int i, bool on = true) __attribute__((always_inline)) {
     const int phys = __builtin_amdgcn_readfirstlane(s_tbl[i]);
     const uint8_t* tile = pool_h + (size_t)phys * tstride;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tile), (short)0, on ? (int)g.tile_bytes : 0, kBufWord3);
     uint32_t live = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) live |= ((b0 + i) * kRows + 64 * w + 16 * c + lj < len) ? (1u << c) : 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint8_t* rp = tile + ((uint32_t)(64 * w + 8 * j + 2 * la + (lj >> 3)) * (uint32_t)g.rec + (lj & 7) * 16);
-      r.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp));
-      r.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rp + D));
+      const uint32_t off = (uint32_t)(64 * w + 8 * j + 2 * la + (lj >> 3)) * (uint32_t)g.rec + (lj & 7) * 16;
+      r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kBufNT);
+      r.v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + D, 0, kBufNT);
     }
     r.live = live;
   };
@@ -270,19 +274,18 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_k(TileGeom g, DecodeArgs a)
   };
 
   // Whole pairs with no exit in between (an exit there gives the compiler a path into the loop head on which
-  // it waits for every load in flight before issuing the next chunk's); past the end the last chunk is
-  // reloaded (an L2 hit) and not used.
+  // it waits for every load in flight before issuing the next chunk's); past the end the loads read nothing.
   int i = 0;
   for (; i + 1 < nchunk; i += 2) {
     load(rb, i + 1);
     __builtin_amdgcn_sched_barrier(0);
     process(ra);
-    load(ra, min(i + 2, nchunk - 1));
+    load(ra, min(i + 2, nchunk - 1), i + 2 < nchunk);
     __builtin_amdgcn_sched_barrier(0);
     process(rb);
   }
   if (i < nchunk) process(ra);
-  __syncthreads();
+  lds_barrier();  // the waves' LDS work is done (nothing else is exchanged through memory here)
 
   // ---------------------------------------------------------------- merge the four waves
 #pragma unroll

@@ -11,6 +11,12 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Buffer resources for raw (untyped) loads on gfx950: the descriptor's fourth word with a 32-bit data format
+// (a zero format would make every load return zeros), and the cache-policy operand of a non-temporal load.
+// A raw load at an offset at or past the resource's size returns zeros without a memory access.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNT = 2;
+
 __device__ __forceinline__ floatx4 mfma16(const u32x4& a, const u32x4& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c,
                                                 0, 0, 0);

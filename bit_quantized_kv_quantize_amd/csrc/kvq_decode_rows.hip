@@ -36,11 +36,6 @@ namespace {
 using namespace dec;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
-// Buffer resources for raw (untyped) loads on gfx950: the descriptor's fourth word with a 32-bit data format
-// (a zero format would make every load return zeros), and the cache-policy operand of a non-temporal load.
-// A raw load at an offset at or past the resource's size returns zeros without a memory access.
-constexpr int kBufWord3 = 0x00020000;
-constexpr int kBufNT = 2;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
