@@ -838,20 +838,30 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
         *reinterpret_cast<uint2*>(sp + lj * kPP + la * 4) = uint2{x, x};
       }
     } else {
+      // The chunk's largest V scale. At K 128 from each lane's own parameter record (one token per lane,
+      // every token of the chunk once; the exchanged copies convert each token's scales in four lanes). At
+      // K 192 from the exchanged copies: holding the own record that long makes those instances spill.
       float vmax = 0.0f;
+      if constexpr (!X) {
+        vmax = fmaxf(h2f(r.prm[NGK] & 0xffffu), h2f(r.prm[NGK + 1] & 0xffffu));
+      } else {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        vmax = fmaxf(vmax, fmaxf(h2f(vp[c][0] & 0xffffu), h2f(vp[c][1] & 0xffffu)));
+        for (int c = 0; c < NC; ++c)
+          vmax = fmaxf(vmax, fmaxf(h2f(vp[c][0] & 0xffffu), h2f(vp[c][1] & 0xffffu)));
+      }
       const float pv_scale = chunk_pv_scale(vmax, pv_inv);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int t = 16 * c + lj, u = lj & 7;
         const int pos = (t & ~7) | (((u & 3) << 1) | (u >> 2));
         const float pp = p[c];
-        const bool on = pp != 0.0f;
+        const bool on = X ? pp != 0.0f : true;
         const bool odd = u & 1;
         const float f = odd ? (W8 ? -pv_scale : -0.0625f * pv_scale) : pv_scale;
         const float Lc = odd ? (W8 ? 255.0f : 15.0f) : 0.0f;
+        // Every record read is one the quantiser wrote (a row past the end reads a live row's), so its scales
+        // and zeros are finite and a token of weight 0 adds exact zeros without a select. (The K 192 instances
+        // keep the selects: without them their register allocation spills more.)
         const float vs0 = on ? h2f(vp[c][0] & 0xffffu) : 0.0f, vz0 = on ? h2f(vp[c][0] >> 16) : 0.0f;
         const float vs1 = on ? h2f(vp[c][1] & 0xffffu) : 0.0f, vz1 = on ? h2f(vp[c][1] >> 16) : 0.0f;
         zacc0 += pp * (vz0 + Lc * vs0);
