@@ -968,8 +968,9 @@ __global__ __launch_bounds__(256, 2) void decode_rows_k(TileGeom g, DecodeArgs a
   };
 
   // sched_barrier keeps a chunk's loads (and the list entries of the one after) ahead of the arithmetic
-  // that follows, so they are in flight while it runs; past the end the last chunk is reloaded (an L2 hit)
-  // and not used.
+  // that follows, so they are in flight while it runs. Past the end the loads of streaming 4-bit chunks at
+  // K 128 read nothing (a zero-byte buffer resource); the other kinds reload the last chunk (an L2 hit), and
+  // the reload is not used.
   if constexpr (!GATHER) {
     // Streaming: three register sets, two chunks in flight while one is processed. The loop runs over
     // whole triples with no exit in between (an exit there gives the compiler a path into the loop head
