@@ -544,20 +544,20 @@ __device__ __forceinline__ void quantize16(const float (&x)[16], float mn, float
 // its tile, so each row record and parameter record is written whole by one wave (measured on the 12 x 8K
 // pool: 133 -> 115 us per layer, the mixed workload 902 -> 705 us per 2048 blocks). Without rotation the
 // lane's extremes come from the packed fp16 inputs (exact in fp16).
+// The work of one 256-thread group (thread tid of nthr = 256) on tile (blockIdx.x, blockIdx.y): tensor kv0 (NT = 1)
+// or both (NT = 2). No workgroup barrier, so two groups of one workgroup may run different instances.
 template <int L16, bool ROT, int MIX, int NT, int PF>
-__global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __restrict__ pool,
-                                                         const int32_t* __restrict__ block_ids,
-                                                         const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v,
-                                                         const uint32_t* __restrict__ prec_bits, float rot_c,
-                                                         int kv_base) {
+__device__ __forceinline__ void rows16_tile(const TileGeom& g, uint8_t* __restrict__ pool,
+                                            const int32_t* __restrict__ block_ids, const uint16_t* __restrict__ k,
+                                            const uint16_t* __restrict__ v, const uint32_t* __restrict__ prec_bits,
+                                            float rot_c, int kv0, int tid, int nthr) {
   constexpr int D = L16 * 16;
   constexpr int RPP = 256 / L16;                  // rows per pass (21 at L16 = 12: threads 252..255 idle)
   constexpr int NPASS = (kRows + RPP - 1) / RPP;  // passes (the last one partial at L16 = 12)
   static_assert(!ROT || (L16 & (L16 - 1)) == 0, "rotation needs a power-of-two head dim");
   static_assert(NT == 1 || NT == 2, "one tensor, or K and V of the tile");
-  const int i = blockIdx.x, h = blockIdx.y, kv0 = NT == 2 ? 0 : blockIdx.z + kv_base;
-  const int li = threadIdx.x % L16, r0 = threadIdx.x / L16;
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int li = tid % L16, r0 = tid / L16;
   uint8_t* tile = pool + ((size_t)block_ids[i] * g.H + h) * g.tile_bytes;
   const uint32_t* bitmap = MIX && prec_bits ? prec_bits + (size_t)i * (g.header_bytes() / 4) : nullptr;
   // Rows past the block (the idle threads and the partial last pass when L16 does not divide 256) load the
@@ -643,12 +643,38 @@ __global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __
   if (kv0 + NT - 1 == 1) {
     // zero the tail padding (and write the width words of pools with per-token widths)
     const uint32_t end = g.off_hdr + g.header_bytes();
-    for (uint32_t o = end + 4u * threadIdx.x; o < g.tile_bytes; o += 4u * blockDim.x)
+    for (uint32_t o = end + 4u * (uint32_t)tid; o < g.tile_bytes; o += 4u * (uint32_t)nthr)
       *reinterpret_cast<uint32_t*>(tile + o) = 0u;
-    if (MIX && threadIdx.x < g.header_bytes() / 4)
-      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[threadIdx.x] =
-          bitmap ? bitmap[threadIdx.x] : (MIX == 2 ? 0x55555555u : 0u);
+    if (MIX && tid < (int)(g.header_bytes() / 4))
+      reinterpret_cast<uint32_t*>(tile + g.off_hdr)[tid] = bitmap ? bitmap[tid] : (MIX == 2 ? 0x55555555u : 0u);
   }
+}
+
+template <int L16, bool ROT, int MIX, int NT, int PF>
+__global__ __launch_bounds__(256) void quantize_rows16_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                         const int32_t* __restrict__ block_ids,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const uint32_t* __restrict__ prec_bits, float rot_c,
+                                                         int kv_base) {
+  rows16_tile<L16, ROT, MIX, NT, PF>(g, pool, block_ids, k, v, prec_bits, rot_c, NT == 2 ? 0 : blockIdx.z + kv_base,
+                                     threadIdx.x, blockDim.x);
+}
+
+// K and V of a tile whose head dims differ (no rotation): waves 0-3 quantise K with LK lanes per row, waves 4-7
+// V with LV lanes per row. Both halves of each row record (K codes, then V codes, 160 bytes at K 192 / V 128)
+// are written at about the same time, so L2 merges them into whole lines; with a launch per tensor each half
+// reached HBM as partial lines of two 128-byte lines (the V-only launch ran at 2.6 TB/s).
+template <int LK, int LV, int MIX>
+__global__ __launch_bounds__(512) void quantize_rows16_pair_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                              const int32_t* __restrict__ block_ids,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              const uint32_t* __restrict__ prec_bits) {
+  if (threadIdx.x < 256)
+    rows16_tile<LK, false, MIX, 1, 2>(g, pool, block_ids, k, v, prec_bits, 1.0f, 0, threadIdx.x, 256);
+  else
+    rows16_tile<LV, false, MIX, 1, 2>(g, pool, block_ids, k, v, prec_bits, 1.0f, 1, threadIdx.x - 256, 256);
 }
 
 template <int LPR>
@@ -816,6 +842,24 @@ static hipError_t per_tensor(const TileGeom& g, F&& launch) {
 hipError_t launch_quantize_blocks(const TileGeom& g, uint8_t* pool, const int32_t* block_ids, int n_blocks,
                                   const uint16_t* k, const uint16_t* v, const uint32_t* prec_bits,
                                   float rot_c, float rot_cv, hipStream_t stream) {
+  // Unequal head dims with per-token groups spanning whole 16-channel lanes and no rotation (the MLA pools): K
+  // and V of each tile in one workgroup once there are enough tiles to fill the chip (4 per CU).
+  if (g.dv != g.d && !g.fp8 && !g.rotate && g.kg > 0 && g.kg % 16 == 0 && g.vg % 16 == 0 && g.dv == 128 &&
+      (g.d == 192 || g.d == 256) && (long)n_blocks * g.H >= 1024) {
+    const dim3 grid(n_blocks, g.H, 1);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(512), 0, stream, g, pool, block_ids, k, v, prec_bits);
+      return hipGetLastError();
+    };
+    if (g.d == 192) {
+      if (g.mixed == 2) return go(quantize_rows16_pair_k<12, 8, 2>);
+      if (g.mixed == 1) return go(quantize_rows16_pair_k<12, 8, 1>);
+      return go(quantize_rows16_pair_k<12, 8, 0>);
+    }
+    if (g.mixed == 2) return go(quantize_rows16_pair_k<16, 8, 2>);
+    if (g.mixed == 1) return go(quantize_rows16_pair_k<16, 8, 1>);
+    return go(quantize_rows16_pair_k<16, 8, 0>);
+  }
   return per_tensor(g, [&](auto lpr, int kv_base, int n_tensors) {
     return launch_quantize_t<decltype(lpr)::value>(g, pool, block_ids, n_blocks, k, v, prec_bits,
                                                    kv_base ? rot_cv : rot_c, kv_base, n_tensors, stream);
