@@ -398,14 +398,13 @@ __global__ __launch_bounds__(kKchanThreads) void quantize_kchan_k(TileGeom g, ui
 // Grid (n_seqs, H, tensors), LPR threads: row positions[s] % 256 of block block_table[s][positions[s] / 256];
 // tensor kv_base + blockIdx.z (0 = K, 1 = V) of head dim D = 8 LPR.
 template <int LPR>
-__global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict__ pool,
-                                                const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                                                const int32_t* __restrict__ block_table, int max_blocks_per_seq,
-                                                const int32_t* __restrict__ positions,
-                                                const uint8_t* __restrict__ prec, float rot_c, int kv_base) {
+__device__ __forceinline__ void append_row(const TileGeom& g, uint8_t* __restrict__ pool,
+                                           const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                           const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+                                           const int32_t* __restrict__ positions, const uint8_t* __restrict__ prec,
+                                           float rot_c, int kv, int li) {
   constexpr int D = LPR * 8;
-  const int s = blockIdx.x, h = blockIdx.y, kv = blockIdx.z + kv_base;
-  const int li = threadIdx.x;
+  const int s = blockIdx.x, h = blockIdx.y;
   const int p = positions[s];
   const int row = p % kRows;
   const int blk = block_table[(size_t)s * max_blocks_per_seq + p / kRows];
@@ -435,6 +434,33 @@ __global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict_
     atomicAnd(word, ~(3u << sh));
     atomicOr(word, code << sh);
   }
+}
+
+template <int LPR>
+__global__ __launch_bounds__(LPR) void append_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+                                                const int32_t* __restrict__ positions,
+                                                const uint8_t* __restrict__ prec, float rot_c, int kv_base) {
+  append_row<LPR>(g, pool, k, v, block_table, max_blocks_per_seq, positions, prec, rot_c, blockIdx.z + kv_base,
+                  threadIdx.x);
+}
+
+// K and V rows of unequal head dims in one wave: K on lanes 0 .. LK - 1, V on lanes 32 .. 32 + LV - 1 (each
+// row's lane exchanges stay inside its own lanes, which are the only active ones in its branch); one launch
+// instead of one per tensor.
+template <int LK, int LV>
+__global__ __launch_bounds__(64) void append_pair_k(TileGeom g, uint8_t* __restrict__ pool,
+                                                    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                    const int32_t* __restrict__ block_table, int max_blocks_per_seq,
+                                                    const int32_t* __restrict__ positions,
+                                                    const uint8_t* __restrict__ prec, float rot_c, float rot_cv) {
+  static_assert(LK <= 32 && LV <= 32, "each tensor's row within half a wave");
+  const int l = threadIdx.x;
+  if (l < LK)
+    append_row<LK>(g, pool, k, v, block_table, max_blocks_per_seq, positions, prec, rot_c, 0, l);
+  else if (l >= 32 && l < 32 + LV)
+    append_row<LV>(g, pool, k, v, block_table, max_blocks_per_seq, positions, prec, rot_cv, 1, l - 32);
 }
 
 // y = c * H * x for one row spread over L16 lanes, lane li holding elements 16 li .. 16 li + 15: the butterflies
@@ -870,6 +896,15 @@ hipError_t launch_append_tokens(const TileGeom& g, uint8_t* pool, int n_seqs, co
                                 const uint16_t* v, const int32_t* block_table, int max_blocks_per_seq,
                                 const int32_t* positions, const uint8_t* prec, float rot_c, float rot_cv,
                                 hipStream_t stream) {
+  if (g.dv != g.d && g.dv == 128 && (g.d == 192 || g.d == 256)) {  // unequal head dims: one launch
+    if (g.d == 192)
+      hipLaunchKernelGGL((append_pair_k<24, 16>), dim3(n_seqs, g.H, 1), dim3(64), 0, stream, g, pool, k, v,
+                         block_table, max_blocks_per_seq, positions, prec, rot_c, rot_cv);
+    else
+      hipLaunchKernelGGL((append_pair_k<32, 16>), dim3(n_seqs, g.H, 1), dim3(64), 0, stream, g, pool, k, v,
+                         block_table, max_blocks_per_seq, positions, prec, rot_c, rot_cv);
+    return hipGetLastError();
+  }
   return per_tensor(g, [&](auto lpr, int kv_base, int n_tensors) {
     constexpr int LPR = decltype(lpr)::value;
     hipLaunchKernelGGL(append_k<LPR>, dim3(n_seqs, g.H, n_tensors), dim3(LPR), 0, stream, g, pool, k, v,
